@@ -1,0 +1,173 @@
+// C ABI of the lightning-indexer library: host-side argument validation,
+// workspace sizing and kernel launches on the caller's stream.  Nothing here
+// allocates device memory or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/li.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+li_status fail(li_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+li_status ok() {
+  g_err[0] = 0;
+  return LI_OK;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+li_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LI_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Shared validation of the indexer scoring arguments.
+li_status check_score_args(const void* q, li_dtype qt, const float* w, const void* k, li_dtype kt, const float* ks,
+                           const int32_t* nv, int B, int T, int S, int H, int d) {
+  if (!q || !w || !k) return fail(LI_ERR_NULL, "q, w and k must be non-NULL");
+  if (qt != LI_BF16 && qt != LI_F32) return fail(LI_ERR_DTYPE, "q_type must be LI_BF16 or LI_F32");
+  if (kt != LI_BF16 && kt != LI_F32 && kt != LI_FP8_E4M3)
+    return fail(LI_ERR_DTYPE, "k_type must be LI_FP8_E4M3, LI_BF16 or LI_F32");
+  if (kt == LI_FP8_E4M3 && !ks) return fail(LI_ERR_NULL, "fp8 keys need k_scale");
+  if (kt != LI_FP8_E4M3 && ks) return fail(LI_ERR_DTYPE, "k_scale is only accepted with fp8 keys");
+  if (d != LI_INDEX_DIM) return fail(LI_ERR_SHAPE, "d must be %d (got %d)", LI_INDEX_DIM, d);
+  if (H < 1 || H > 128) return fail(LI_ERR_SHAPE, "H must be in [1, 128] (got %d)", H);
+  if (B < 1 || T < 1 || S < 1) return fail(LI_ERR_SHAPE, "B, T and S must be >= 1");
+  if ((int64_t)B * T >= (1ll << 31) || (int64_t)B * T * S >= (1ll << 40))
+    return fail(LI_ERR_SHAPE, "B*T*S too large");
+  if (misaligned(q) || misaligned(w) || misaligned(k) || misaligned(ks) || misaligned(nv))
+    return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  return LI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* li_status_string(li_status s) {
+  switch (s) {
+    case LI_OK: return "ok";
+    case LI_ERR_NULL: return "null pointer";
+    case LI_ERR_SHAPE: return "unsupported shape";
+    case LI_ERR_DTYPE: return "unsupported dtype";
+    case LI_ERR_ALIGN: return "misaligned pointer";
+    case LI_ERR_WORKSPACE: return "workspace too small";
+    case LI_ERR_LAUNCH: return "launch failed";
+  }
+  return "unknown status";
+}
+
+const char* li_last_error(void) { return g_err; }
+
+const char* li_version(void) { return "lightning-indexer-gfx950 0.1"; }
+
+li_status li_indexer_score(const void* q, li_dtype q_type, const float* w, const void* k, li_dtype k_type,
+                           const float* k_scale, const int32_t* nv, int B, int T, int S, int H, int d, float* scores,
+                           hipStream_t stream) {
+  li_status s = check_score_args(q, q_type, w, k, k_type, k_scale, nv, B, T, S, H, d);
+  if (s != LI_OK) return s;
+  if (!scores) return fail(LI_ERR_NULL, "scores must be non-NULL");
+  if (misaligned(scores)) return fail(LI_ERR_ALIGN, "scores must be 16-byte aligned");
+  return launched(li::launch_score(q, q_type, w, k, k_type, k_scale, nv, B, T, S, H, scores, stream),
+                  "li_indexer_score");
+}
+
+size_t li_topk_workspace_bytes(int R, int S, int k) {
+  (void)R; (void)S; (void)k;
+  return 0;
+}
+
+li_status li_topk_select(const float* scores, const int32_t* nv, int R, int S, int k, int32_t* idx, float* val,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!scores || !idx) return fail(LI_ERR_NULL, "scores and idx must be non-NULL");
+  if (R < 1 || S < 1) return fail(LI_ERR_SHAPE, "R and S must be >= 1");
+  if (k < 1 || k > LI_TOPK_MAX) return fail(LI_ERR_SHAPE, "k must be in [1, %d] (got %d)", LI_TOPK_MAX, k);
+  if ((int64_t)R * S >= (1ll << 40)) return fail(LI_ERR_SHAPE, "R*S too large");
+  if (misaligned(scores) || misaligned(nv) || misaligned(idx) || misaligned(val))
+    return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = li_topk_workspace_bytes(R, S, k);
+  if (need && (!ws || ws_bytes < need)) return fail(LI_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  return launched(li::launch_topk_f32(scores, nv, R, S, k, idx, val, stream), "li_topk_select");
+}
+
+size_t li_indexer_topk_workspace_bytes(int B, int T, int S, int H, int topk) {
+  return li::indexer_topk_ws_bytes(B, T, S, H, topk);
+}
+
+li_status li_indexer_topk(const void* q, li_dtype q_type, const float* w, const void* k, li_dtype k_type,
+                          const float* k_scale, const int32_t* nv, int B, int T, int S, int H, int d, int topk,
+                          int32_t* idx, float* val, void* ws, size_t ws_bytes, hipStream_t stream) {
+  li_status s = check_score_args(q, q_type, w, k, k_type, k_scale, nv, B, T, S, H, d);
+  if (s != LI_OK) return s;
+  if (!idx) return fail(LI_ERR_NULL, "idx must be non-NULL");
+  if (topk < 1 || topk > LI_TOPK_MAX) return fail(LI_ERR_SHAPE, "topk must be in [1, %d]", LI_TOPK_MAX);
+  if (misaligned(idx) || misaligned(val)) return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = li::indexer_topk_ws_bytes(B, T, S, H, topk);
+  if (need && (!ws || ws_bytes < need)) return fail(LI_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (misaligned(ws)) return fail(LI_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return launched(li::launch_indexer_topk(q, q_type, w, k, k_type, k_scale, nv, B, T, S, H, topk, idx, val, ws,
+                                          stream),
+                  "li_indexer_topk");
+}
+
+size_t li_compact_workspace_bytes(int B, int S, int H, int m, int k) {
+  if (B < 1 || S < 1 || H < 1 || m < 1) return 0;
+  return li::compact_ws_bytes(B, S, H, m, k);
+}
+
+li_status li_compact_search_rerank(const void* q, const float* w, const float* P, const int8_t* ck,
+                                   const float* ck_scale, const void* k_full, const int32_t* nv, int B, int S, int H,
+                                   int d, int dc, int m, int k, int32_t* shortlist, int32_t* idx, double* val,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !w || !P || !ck || !ck_scale || !k_full || !idx)
+    return fail(LI_ERR_NULL, "q, w, P, ck, ck_scale, k_full and idx must be non-NULL");
+  if (d != LI_INDEX_DIM) return fail(LI_ERR_SHAPE, "d must be %d", LI_INDEX_DIM);
+  if (dc != LI_COMPACT_DIM) return fail(LI_ERR_SHAPE, "dc must be %d", LI_COMPACT_DIM);
+  if (H < 1 || H > 128) return fail(LI_ERR_SHAPE, "H must be in [1, 128]");
+  if (B < 1 || S < 1) return fail(LI_ERR_SHAPE, "B and S must be >= 1");
+  if (k < 1 || m < k || m > LI_TOPK_MAX) return fail(LI_ERR_SHAPE, "need 1 <= k <= m <= %d", LI_TOPK_MAX);
+  if ((int64_t)B * S >= (1ll << 40)) return fail(LI_ERR_SHAPE, "B*S too large");
+  if (misaligned(q) || misaligned(w) || misaligned(P) || misaligned(ck) || misaligned(ck_scale) ||
+      misaligned(k_full) || misaligned(nv) || misaligned(shortlist) || misaligned(idx) || misaligned(val) ||
+      misaligned(ws))
+    return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = li::compact_ws_bytes(B, S, H, m, k);
+  if (!ws || ws_bytes < need) return fail(LI_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  return launched(li::launch_compact((const uint16_t*)q, w, P, ck, ck_scale, (const uint16_t*)k_full, nv, B, S, H, m,
+                                     k, shortlist, idx, val, ws, stream),
+                  "li_compact_search_rerank");
+}
+
+size_t li_sparse_attn_workspace_bytes(int B, int Hq, int k, int dv) { return li::attn_ws_bytes(B, Hq, k, dv); }
+
+li_status li_sparse_attn_gather(const void* q, const void* kv, const int32_t* idx, int B, int Hq, int S, int k,
+                                int dqk, int dv, float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  if (!q || !kv || !idx || !out) return fail(LI_ERR_NULL, "q, kv, idx and out must be non-NULL");
+  if (dqk != 576 || dv != 512) return fail(LI_ERR_SHAPE, "dqk must be 576 and dv 512");
+  if (Hq < 1 || Hq > 128 || Hq % 32) return fail(LI_ERR_SHAPE, "Hq must be a multiple of 32 in [32, 128]");
+  if (B < 1 || S < 1 || k < 1 || k > LI_TOPK_MAX) return fail(LI_ERR_SHAPE, "need B, S >= 1 and 1 <= k <= %d",
+                                                              LI_TOPK_MAX);
+  if (misaligned(q) || misaligned(kv) || misaligned(idx) || misaligned(out) || misaligned(lse) || misaligned(ws))
+    return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = li::attn_ws_bytes(B, Hq, k, dv);
+  if (need && (!ws || ws_bytes < need)) return fail(LI_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  return launched(li::launch_attn((const uint16_t*)q, (const uint16_t*)kv, idx, B, Hq, S, k, sm_scale,
+                                  (uint16_t*)out, lse, ws, stream),
+                  "li_sparse_attn_gather");
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+// Two-stage decode search over compact keys for gfx950.
+//
+// LeanSparse podcast transcript, cues 07:12-08:00: a cheap, lossy pass over compact
+// indexer keys keeps a shortlist of 2,048 candidates, only their original keys are
+// fetched, and an exact rerank picks the final 512.  The compact keys here are a
+// fixed Gaussian 128 -> 32 projection stored as int8 with a per-key fp32 scale.
+//
+// Every step is defined to be bit-reproducible on any IEEE machine:
+//   query   y_h = P q_h (fp64 fma chain over the 128 dims, ascending),
+//           qs_h = max|y_h| / 127 (1 if zero), q8_h = rint(y_h / qs_h) clamped to
+//           [-127, 127], W_h = w_h * qs_h (fp64);
+//   stage 1 D_h = q8_h . c_s (exact int32), s1 = cs_s * chain_h(W_h, max(D_h, 0))
+//           (fp64 fma chain over h ascending), shortlist = top-m of s1;
+//   stage 2 s2 = chain_h(w_h, max(chain_j(q_hj, k_sj), 0)) over the shortlisted
+//           original bf16 keys (fp64 fma chains, ascending), result = top-k of s2.
+// Selections order by (score desc, key index asc).
+#include "common.h"
+#include "launch.h"
+
+namespace li {
+
+constexpr int DC = 32;
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// One wave per (b, h).
+__global__ __launch_bounds__(64) void compact_query_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                                                           const float* __restrict__ P, int H,
+                                                           int8_t* __restrict__ q8, double* __restrict__ W) {
+  const int bh = blockIdx.x;
+  const int i = threadIdx.x;
+  const uint16_t* qr = q + (int64_t)bh * 128;
+  double y = 0.0;
+  if (i < DC) {
+    for (int j = 0; j < 128; ++j) y = fma((double)P[i * 128 + j], (double)bf16_to_f32(qr[j]), y);
+  }
+  const double amax = wave_max_d(i < DC ? fabs(y) : 0.0);
+  const double s = amax > 0.0 ? amax / 127.0 : 1.0;
+  if (i < DC) {
+    double t = rint(y / s);
+    t = fmin(fmax(t, -127.0), 127.0);
+    q8[(int64_t)bh * DC + i] = (int8_t)(int)t;
+  }
+  if (i == 0) W[bh] = (double)w[bh] * s;
+}
+
+// One thread per key: exact int8 dots, fp64 head chain.
+__global__ __launch_bounds__(256) void compact_stage1_kernel(const int8_t* __restrict__ q8,
+                                                             const double* __restrict__ W,
+                                                             const int8_t* __restrict__ ck,
+                                                             const float* __restrict__ cks, int S, int H,
+                                                             double* __restrict__ s1) {
+  __shared__ int sq[128 * DC / 4];
+  __shared__ double sw[128];
+  const int b = blockIdx.y;
+  for (int i = threadIdx.x; i < H * DC / 4; i += blockDim.x) sq[i] = ((const int*)(q8 + (int64_t)b * H * DC))[i];
+  for (int i = threadIdx.x; i < H; i += blockDim.x) sw[i] = W[(int64_t)b * H + i];
+  __syncthreads();
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= S) return;
+  const int64_t row = (int64_t)b * S + s;
+  const uint4* cp = (const uint4*)(ck + row * DC);
+  const uint4 c0 = cp[0], c1 = cp[1];
+  const int cw[8] = {(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
+  double acc = 0.0;
+  for (int h = 0; h < H; ++h) {
+    int D = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) D = __builtin_amdgcn_sdot4(sq[h * 8 + i], cw[i], D, false);
+    acc = fma(sw[h], (double)(D > 0 ? D : 0), acc);
+  }
+  s1[row] = (double)cks[row] * acc;
+}
+
+// One thread per shortlisted candidate: exact fp64 rescoring.
+__global__ __launch_bounds__(256) void compact_stage2_kernel(const uint16_t* __restrict__ q,
+                                                             const float* __restrict__ w,
+                                                             const uint16_t* __restrict__ kf,
+                                                             const int32_t* __restrict__ sl,
+                                                             const int32_t* __restrict__ nv, int S, int H, int m,
+                                                             double* __restrict__ s2, int32_t* __restrict__ cnt) {
+  extern __shared__ double sqd[];  // [H * 128] query as fp64, then [H] weights
+  const int b = blockIdx.y;
+  for (int i = threadIdx.x; i < H * 128; i += blockDim.x) sqd[i] = (double)bf16_to_f32(q[(int64_t)b * H * 128 + i]);
+  for (int i = threadIdx.x; i < H; i += blockDim.x) sqd[H * 128 + i] = (double)w[(int64_t)b * H + i];
+  __syncthreads();
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c == 0) {
+    int n = S;
+    if (nv) n = min(max(nv[b], 0), S);
+    cnt[b] = min(n, m);
+  }
+  if (c >= m) return;
+  const int id = sl[(int64_t)b * m + c];
+  if (id < 0 || id >= S) {
+    s2[(int64_t)b * m + c] = -INFINITY;
+    return;
+  }
+  const uint4* kp = (const uint4*)(kf + ((int64_t)b * S + id) * 128);
+  uint4 kr[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) kr[i] = kp[i];
+  double acc = 0.0;
+  for (int h = 0; h < H; ++h) {
+    const double* qh = sqd + h * 128;
+    double dot = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t wds[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double k0 = (double)__uint_as_float(wds[e] << 16);
+        const double k1 = (double)__uint_as_float(wds[e] & 0xFFFF0000u);
+        dot = fma(qh[8 * i + 2 * e], k0, dot);
+        dot = fma(qh[8 * i + 2 * e + 1], k1, dot);
+      }
+    }
+    acc = fma(sqd[H * 128 + h], dot > 0.0 ? dot : 0.0, acc);
+  }
+  s2[(int64_t)b * m + c] = acc;
+}
+
+size_t compact_ws_bytes(int B, int S, int H, int m, int k) {
+  (void)k;
+  size_t n = 0;
+  n += align256((size_t)B * H * DC);          // q8
+  n += align256((size_t)B * H * 8);           // W
+  n += align256((size_t)B * S * 8);           // s1
+  n += align256((size_t)B * m * 4);           // shortlist
+  n += align256((size_t)B * m * 8);           // s2
+  n += align256((size_t)B * 4);               // cnt
+  return n;
+}
+
+hipError_t launch_compact(const uint16_t* q, const float* w, const float* P, const int8_t* ck, const float* cks,
+                          const uint16_t* kf, const int32_t* nv, int B, int S, int H, int m, int k,
+                          int32_t* shortlist, int32_t* idx, double* val, void* ws, hipStream_t st) {
+  uint8_t* p = (uint8_t*)ws;
+  int8_t* q8 = (int8_t*)p;
+  p += align256((size_t)B * H * DC);
+  double* W = (double*)p;
+  p += align256((size_t)B * H * 8);
+  double* s1 = (double*)p;
+  p += align256((size_t)B * S * 8);
+  int32_t* sl_ws = (int32_t*)p;
+  p += align256((size_t)B * m * 4);
+  double* s2 = (double*)p;
+  p += align256((size_t)B * m * 8);
+  int32_t* cnt = (int32_t*)p;
+  int32_t* sl = shortlist ? shortlist : sl_ws;
+
+  compact_query_kernel<<<B * H, 64, 0, st>>>(q, w, P, H, q8, W);
+  compact_stage1_kernel<<<dim3((S + 255) / 256, B), 256, 0, st>>>(q8, W, ck, cks, S, H, s1);
+  hipError_t e = launch_topk_f64(s1, S, nv, nullptr, B, S, m, sl, nullptr, st);
+  if (e != hipSuccess) return e;
+  const size_t lds = sizeof(double) * (size_t)H * 129;
+  static const bool attr_set = [] {
+    // H <= 128 needs up to 132 KB of dynamic LDS (the query in fp64)
+    (void)hipFuncSetAttribute((const void*)compact_stage2_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    return true;
+  }();
+  (void)attr_set;
+  compact_stage2_kernel<<<dim3((m + 255) / 256, B), 256, lds, st>>>(q, w, kf, sl, nv, S, H, m, s2, cnt);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topk_f64(s2, m, cnt, sl, B, m, k, idx, val, st);
+}
+
+}  // namespace li

@@ -1,0 +1,45 @@
+// Internal host-side launchers shared by the C ABI (capi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define LI_TOPK_MAX_DEV 2048
+
+namespace li {
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_I8 = 3 };
+
+// scores [B*T, S] of q [B,T,H,128] against k [B,S,128]
+hipError_t launch_score(const void* q, int q_type, const float* w, const void* k, int k_type, const float* ks,
+                        const int32_t* nv, int B, int T, int S, int H, float* scores, hipStream_t st);
+
+// per-row top-k of fp32 scores [R, S]
+hipError_t launch_topk_f32(const float* scores, const int32_t* nv, int R, int S, int k, int32_t* idx, float* val,
+                           hipStream_t st);
+
+// per-row top-k of fp64 scores (row r starts at r * row_stride); ids [R, row_stride]
+// gives each entry's id (NULL = its position); ties go to the smaller id
+hipError_t launch_topk_f64(const double* scores, int64_t row_stride, const int32_t* nv, const int32_t* ids, int R,
+                           int S, int k, int32_t* idx, double* val, hipStream_t st);
+
+// two-stage compact search (workspace layout in compact.hip)
+size_t compact_ws_bytes(int B, int S, int H, int m, int k);
+hipError_t launch_compact(const uint16_t* q, const float* w, const float* P, const int8_t* ck, const float* cks,
+                          const uint16_t* kf, const int32_t* nv, int B, int S, int H, int m, int k,
+                          int32_t* shortlist, int32_t* idx, double* val, void* ws, hipStream_t st);
+
+// sparse attention over selected rows (workspace layout in attn.hip)
+size_t attn_ws_bytes(int B, int Hq, int k, int dv);
+hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int B, int Hq, int S, int k,
+                       float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t st);
+
+// fused scoring + selection for many query rows (prefill); falls back to
+// score-then-select where the fused kernel does not apply
+size_t indexer_topk_ws_bytes(int B, int T, int S, int H, int topk);
+hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const void* k, int k_type, const float* ks,
+                               const int32_t* nv, int B, int T, int S, int H, int topk, int32_t* idx, float* val,
+                               void* ws, hipStream_t st);
+
+}  // namespace li

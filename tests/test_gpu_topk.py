@@ -1,0 +1,52 @@
+"""GPU parity of li_topk_select: on the same fp32 scores the GPU selection must equal
+the oracle's (score desc, index asc) selection bit for bit, including ties, masks,
+padding and negative, infinite and signed-zero scores."""
+import numpy as np
+import pytest
+import torch
+
+import lightning_indexer_top_amd as li
+import oracle
+from helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+
+def check(scores, k, nv=None):
+    g_idx, g_val = li.topk_select(dev(scores), k, dev(nv) if nv is not None else None)
+    torch.cuda.synchronize()
+    o_idx, o_val = oracle.topk(scores.astype(np.float64), k, nv)
+    g_idx = g_idx.cpu().numpy()
+    g_val = g_val.cpu().numpy().astype(np.float64)
+    assert np.array_equal(g_idx, o_idx)
+    fin = o_idx >= 0
+    assert np.array_equal(g_val[fin], o_val[fin])
+    assert np.isneginf(g_val[~fin]).all()
+
+
+@pytest.mark.parametrize("S,k", [(1, 1), (7, 3), (100, 100), (1000, 64), (4097, 512), (5000, 2048), (3000, 2048)])
+def test_random_rows(S, k):
+    print("topk", S, k, flush=True)
+    rng = np.random.default_rng(S + k)
+    check(rng.standard_normal((5, S)).astype(np.float32), k)
+
+
+def test_heavy_ties_and_masks():
+    print("topk ties", flush=True)
+    rng = np.random.default_rng(1)
+    R, S = 9, 6000
+    s = rng.integers(-20, 20, (R, S)).astype(np.float32)
+    s[0] = 1.0                      # all equal
+    s[1, ::3] = -np.inf             # infinities
+    s[2] = -np.abs(s[2]) - 1        # all negative
+    s[3, :100] = 0.0                # signed zeros among ties
+    s[3, 100:200] = -0.0
+    nv = np.array([6000, 6000, 6000, 6000, 0, 1, 511, 513, 7000], np.int32)
+    for k in (1, 32, 512, 2048):
+        check(s, k, nv)
+
+
+def test_large_row_decode_shape():
+    print("topk 131072", flush=True)
+    rng = np.random.default_rng(2)
+    check(rng.standard_normal((3, 131072)).astype(np.float32), 512)
