@@ -132,12 +132,15 @@ def indexer_score(q, w, k, k_scale=None, nv=None, out=None):
     return out
 
 
-def topk_select(scores, k, nv=None, with_values=True, workspace=None):
+def topk_select(scores, k, nv=None, with_values=True, workspace=None, out=None):
     """(idx [R, k] int32, val [R, k] fp32 or None) of scores [R, S]."""
     _dev(scores, "scores")
     R, S = scores.shape
-    idx = torch.empty((R, k), dtype=torch.int32, device=scores.device)
-    val = torch.empty((R, k), dtype=torch.float32, device=scores.device) if with_values else None
+    if out is None:
+        idx = torch.empty((R, k), dtype=torch.int32, device=scores.device)
+        val = torch.empty((R, k), dtype=torch.float32, device=scores.device) if with_values else None
+    else:
+        idx, val = out
     ws, nb = _workspace(lib().li_topk_workspace_bytes(R, S, k), scores.device, workspace)
     st = lib().li_topk_select(_ptr(scores), _ptr(nv), R, S, k, _ptr(idx), _ptr(val), _ptr(ws), nb,
                               _stream(scores.device))

@@ -86,8 +86,8 @@ li_status li_indexer_score(const void* q, li_dtype q_type, const float* w, const
 }
 
 size_t li_topk_workspace_bytes(int R, int S, int k) {
-  (void)R; (void)S; (void)k;
-  return 0;
+  if (R < 1 || S < 1 || k < 1) return 0;
+  return li::topk_ws_bytes(R, S, k);
 }
 
 li_status li_topk_select(const float* scores, const int32_t* nv, int R, int S, int k, int32_t* idx, float* val,
@@ -100,7 +100,8 @@ li_status li_topk_select(const float* scores, const int32_t* nv, int R, int S, i
     return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
   const size_t need = li_topk_workspace_bytes(R, S, k);
   if (need && (!ws || ws_bytes < need)) return fail(LI_ERR_WORKSPACE, "workspace needs %zu bytes", need);
-  return launched(li::launch_topk_f32(scores, nv, R, S, k, idx, val, stream), "li_topk_select");
+  if (misaligned(ws)) return fail(LI_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return launched(li::launch_topk_f32(scores, nv, R, S, k, idx, val, ws, stream), "li_topk_select");
 }
 
 size_t li_indexer_topk_workspace_bytes(int B, int T, int S, int H, int topk) {

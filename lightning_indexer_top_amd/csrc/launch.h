@@ -15,9 +15,10 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_I8 = 3 };
 hipError_t launch_score(const void* q, int q_type, const float* w, const void* k, int k_type, const float* ks,
                         const int32_t* nv, int B, int T, int S, int H, float* scores, hipStream_t st);
 
-// per-row top-k of fp32 scores [R, S]
+// per-row top-k of fp32 scores [R, S]; ws holds topk_ws_bytes(R, S, k) bytes
+size_t topk_ws_bytes(int R, int S, int k);
 hipError_t launch_topk_f32(const float* scores, const int32_t* nv, int R, int S, int k, int32_t* idx, float* val,
-                           hipStream_t st);
+                           void* ws, hipStream_t st);
 
 // per-row top-k of fp64 scores (row r starts at r * row_stride); ids [R, row_stride]
 // gives each entry's id (NULL = its position); ties go to the smaller id

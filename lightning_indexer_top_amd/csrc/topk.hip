@@ -11,7 +11,9 @@
 //   2. if more entries equal T than are needed, a second radix select over the
 //      inverted ids of those entries finds the id cut (smallest ids win);
 //   3. one pass gathers the selected entries into LDS, a bitonic sort puts them in
-//      canonical order (score descending, id ascending), and they are written out.
+//      ascending id order (the set is unique; attention does not depend on the
+//      order, and ascending ids keep the later gather sequential), and they are
+//      written out.
 // One workgroup of 1024 threads handles one row.
 #include "common.h"
 #include "launch.h"
@@ -83,20 +85,35 @@ __device__ int find_cut(const uint32_t* hist, uint32_t need, uint32_t* above, ui
   return d;
 }
 
+// hist[d] += 1 for every lane with valid set; when all such lanes of the wave
+// share one digit (scores concentrated in few bins) a single atomic adds them.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t d, bool valid) {
+  const uint64_t act = __ballot(valid);
+  if (!act) return;
+  const int first = __ffsll((unsigned long long)act) - 1;
+  const uint32_t d0 = __shfl(d, first, 64);
+  const uint64_t same = __ballot(valid && d == d0);
+  if (same == act) {
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[d0], (uint32_t)__popcll(act));
+  } else if (valid) {
+    atomicAdd(&hist[d], 1u);
+  }
+}
+
 struct Sel {
   uint64_t key;  // orderable score bits (float: in the low 32 bits)
   uint32_t inv_id;
 };
 
-__device__ __forceinline__ bool sel_greater(const Sel& a, const Sel& b) {
-  return a.key > b.key || (a.key == b.key && a.inv_id > b.inv_id);
-}
+// list order: ascending id (inverted id descending); ids in a list are unique
+__device__ __forceinline__ bool sel_greater(const Sel& a, const Sel& b) { return a.inv_id > b.inv_id; }
 
+// Exact selection of the k best of row[0..n) (ids: idrow, or the position) by one
+// workgroup of TK_THREADS threads; results in canonical order into idx_out[0..k)
+// and val_out[0..k).
 template <typename S>
-__global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restrict__ scores, int64_t row_stride,
-                                                              const int32_t* __restrict__ nv,
-                                                              const int32_t* __restrict__ ids, int S_len, int k,
-                                                              int32_t* __restrict__ idx_out, S* __restrict__ val_out) {
+__device__ void select_block(const S* __restrict__ row, const int32_t* __restrict__ idrow, int n, int k,
+                             int32_t* __restrict__ idx_out, S* __restrict__ val_out) {
   typedef typename ScoreTraits<S>::K K;
   constexpr int BITS = ScoreTraits<S>::BITS;
   __shared__ uint32_t hist[TK_BINS];
@@ -105,12 +122,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restric
   __shared__ uint32_t sh_count;
   __shared__ Sel list[LI_TOPK_MAX_DEV];
 
-  const int r = blockIdx.x;
   const int tid = threadIdx.x;
-  const S* row = scores + (int64_t)r * row_stride;
-  const int32_t* idrow = ids ? ids + (int64_t)r * row_stride : nullptr;
-  int n = S_len;
-  if (nv) n = min(max(nv[r], 0), S_len);
   const int take = min(n, k);
 
   K prefix = 0, mask = 0;  // score-bit prefix of T
@@ -128,9 +140,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restric
       const uint32_t dmask = (1u << width) - 1;
       for (int i = tid; i < TK_BINS; i += TK_THREADS) hist[i] = 0;
       __syncthreads();
-      for (int i = tid; i < n; i += TK_THREADS) {
-        const K key = ScoreTraits<S>::ord(row[i]);
-        if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & dmask], 1u);
+      for (int i0 = 0; i0 < n; i0 += TK_THREADS) {
+        const int i = i0 + tid;
+        K key = 0;
+        if (i < n) key = ScoreTraits<S>::ord(row[i]);
+        hist_add(hist, (uint32_t)(key >> shift) & dmask, i < n && (key & mask) == prefix);
       }
       __syncthreads();
       uint32_t above;
@@ -154,11 +168,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restric
         const uint32_t dmask = (1u << width) - 1;
         for (int i = tid; i < TK_BINS; i += TK_THREADS) hist[i] = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += TK_THREADS) {
-          const K key = ScoreTraits<S>::ord(row[i]);
-          if (key != prefix) continue;
-          const uint32_t inv = ~(uint32_t)(idrow ? idrow[i] : i);
-          if ((inv & imask) == iprefix) atomicAdd(&hist[(inv >> ishift) & dmask], 1u);
+        for (int i0 = 0; i0 < n; i0 += TK_THREADS) {
+          const int i = i0 + tid;
+          bool v = false;
+          uint32_t inv = 0;
+          if (i < n && ScoreTraits<S>::ord(row[i]) == prefix) {
+            inv = ~(uint32_t)(idrow ? idrow[i] : i);
+            v = (inv & imask) == iprefix;
+          }
+          hist_add(hist, (inv >> ishift) & dmask, v);
         }
         __syncthreads();
         uint32_t above;
@@ -226,13 +244,339 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restric
       else
         ov = unord_f64(list[j].key);
     }
-    idx_out[(int64_t)r * k + j] = oi;
-    if (val_out) val_out[(int64_t)r * k + j] = ov;
+    idx_out[j] = oi;
+    if (val_out) val_out[j] = ov;
   }
 }
 
+template <typename S>
+__global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restrict__ scores, int64_t row_stride,
+                                                              const int32_t* __restrict__ nv,
+                                                              const int32_t* __restrict__ ids, int S_len, int k,
+                                                              int32_t* __restrict__ idx_out, S* __restrict__ val_out) {
+  const int r = blockIdx.x;
+  int n = S_len;
+  if (nv) n = min(max(nv[r], 0), S_len);
+  select_block<S>(scores + (int64_t)r * row_stride, ids ? ids + (int64_t)r * row_stride : nullptr, n, k,
+                  idx_out + (int64_t)r * k, val_out ? val_out + (int64_t)r * k : nullptr);
+}
+
+// ---- many workgroups per row (few, long rows) --------------------------------
+// After the threshold selection of the "Latent Sparse Attention" article (section
+// "What the kernels do about the top-p"): a threshold is estimated from a sample
+// of the row, a streaming pass keeps only the entries at or above it, and an
+// exact selection runs over the kept entries.  The threshold decides how many
+// entries are kept, never which are picked: whenever at least k entries clear it
+// (checked), the k best are among them.  A row whose estimate misses, or keeps
+// more entries than the final sort holds, falls back to the exact single-workgroup
+// selection over the whole row, so the result is always the exact top-k.
+//   1. one wave per row estimates tau as the j-th largest of m = min(n, 1024)
+//      samples (16 evenly spaced runs of 64 entries; bisection on the orderable
+//      bits, counting with ballots), j ~ 2 k m / n + 8;
+//   2. many workgroups per row append every entry with ord >= tau to the
+//      workgroup's own region of the list (no global atomics, nothing to clear);
+//   3. one workgroup per row gathers the regions and sorts them, or selects over
+//      the whole row.
+constexpr int MB_THREADS = 256;
+constexpr int MB_SAMPLES = 1024;
+constexpr int MB_BATCH = 16;  // loads in flight per thread
+
+__device__ uint32_t sample_threshold(const float* __restrict__ row, int n, int k) {
+  // one wave; returns the largest t with count(sample >= t) >= j
+  const int lane = threadIdx.x & 63;
+  const int m = min(n, MB_SAMPLES);
+  // 16 runs of 64 consecutive entries spread evenly over the row (each load is one
+  // contiguous 256-byte read); when n < 1024 every entry is a sample
+  uint32_t key[MB_SAMPLES / 64];
+#pragma unroll
+  for (int i = 0; i < MB_SAMPLES / 64; ++i) {
+    const int64_t start = (n >= MB_SAMPLES) ? (int64_t)i * (n - 64) / (MB_SAMPLES / 64 - 1) : 64 * i;
+    const int64_t pos = start + lane;
+    key[i] = (64 * i + lane < m && pos < n) ? ord_f32(row[pos]) : 0u;
+  }
+  int j = (int)(((int64_t)2 * k * m + n - 1) / n) + 8;
+  if (j > m) j = m;
+  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
+  while (lo < hi) {
+    const uint32_t mid = lo + (uint32_t)(((uint64_t)(hi - lo) + 1) >> 1);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < MB_SAMPLES / 64; ++i) c += __popcll(__ballot(key[i] >= mid));
+    if (c >= j) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(64) void topk_thresh_kernel(const float* __restrict__ scores,
+                                                        const int32_t* __restrict__ nv, int S, int k,
+                                                        uint32_t* __restrict__ tau) {
+  const int r = blockIdx.x;
+  int n = S;
+  if (nv) n = min(max(nv[r], 0), S);
+  if (n <= k) {
+    if (threadIdx.x == 0) tau[r] = 0u;
+    return;
+  }
+  const uint32_t t = sample_threshold(scores + (int64_t)r * S, n, k);
+  if (threadIdx.x == 0) tau[r] = t;
+}
+
+// Exclusive prefix sum of x over the workgroup (blockDim.x = NW * 64), in thread
+// order; scratch holds NW entries.
+template <int NW>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* scratch) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) scratch[wid] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) base += w < wid ? scratch[w] : 0u;
+  __syncthreads();
+  return base + incl - x;
+}
+
+// Kept entries go to this workgroup's region of the list in index order: a batch
+// holds entries base + tid + 256 u (u < MB_BATCH), so ordering by (u, wave, lane)
+// is index order; each wave's ballots give the counts, one prefix over the
+// (u, wave) counts gives every lane its position.
+__global__ __launch_bounds__(MB_THREADS) void topk_filter_kernel(const float* __restrict__ scores,
+                                                                const int32_t* __restrict__ nv, int S, int k,
+                                                                int chunk, const uint32_t* __restrict__ tau,
+                                                                float* __restrict__ cval, int32_t* __restrict__ cid,
+                                                                uint32_t* __restrict__ bcnt) {
+  constexpr int NW = MB_THREADS / 64;
+  __shared__ uint32_t cnt_uw[MB_BATCH * NW + 1];
+  const int r = blockIdx.y, p = blockIdx.x, P = gridDim.x, tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  int n = S;
+  if (nv) n = min(max(nv[r], 0), S);
+  if (n <= k) {  // the final pass takes the whole row
+    if (tid == 0) bcnt[(int64_t)r * P + p] = 0u;
+    return;
+  }
+  const float* row = scores + (int64_t)r * S;
+  const int lo = p * chunk, hi = min(lo + chunk, n);
+  const uint32_t t = tau[r];
+  float* ov = cval + (int64_t)r * S + lo;  // this workgroup's region
+  int32_t* oi = cid + (int64_t)r * S + lo;
+  uint32_t written = 0;
+  for (int base = lo; base < hi; base += MB_THREADS * MB_BATCH) {
+    float x[MB_BATCH];
+#pragma unroll
+    for (int u = 0; u < MB_BATCH; ++u) {
+      const int i = base + tid + MB_THREADS * u;
+      x[u] = i < hi ? row[i] : -INFINITY;
+    }
+    uint64_t mk[MB_BATCH];
+#pragma unroll
+    for (int u = 0; u < MB_BATCH; ++u) {
+      const int i = base + tid + MB_THREADS * u;
+      mk[u] = __ballot(i < hi && ord_f32(x[u]) >= t);
+      if (lane == 0) cnt_uw[u * NW + wid] = (uint32_t)__popcll(mk[u]);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t acc = 0;
+      for (int e = 0; e < MB_BATCH * NW; ++e) {
+        const uint32_t c = cnt_uw[e];
+        cnt_uw[e] = acc;
+        acc += c;
+      }
+      cnt_uw[MB_BATCH * NW] = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < MB_BATCH; ++u) {
+      if ((mk[u] >> lane) & 1ull) {
+        const uint32_t pos = written + cnt_uw[u * NW + wid] + (uint32_t)__popcll(mk[u] & ((1ull << lane) - 1));
+        ov[pos] = x[u];
+        oi[pos] = base + tid + MB_THREADS * u;
+      }
+    }
+    written += cnt_uw[MB_BATCH * NW];
+    __syncthreads();
+  }
+  if (tid == 0) bcnt[(int64_t)r * P + p] = written;
+}
+
+// Exact selection over the kept entries (at most MB_KEEP, in index order): the
+// k-th best orderable score T by bisection (ballot counts), then every entry
+// above T and the first (k - count above T) entries equal to T, written in index
+// order at positions from a prefix scan.  Rows whose list cannot be used take the
+// whole-row path.
+constexpr int MB_KEEP = 4096;
+
+__global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const float* __restrict__ scores,
+                                                                  const int32_t* __restrict__ nv, int S, int k,
+                                                                  int P, int chunk,
+                                                                  const uint32_t* __restrict__ bcnt,
+                                                                  const float* __restrict__ cval,
+                                                                  const int32_t* __restrict__ cid,
+                                                                  int32_t* __restrict__ idx_out,
+                                                                  float* __restrict__ val_out) {
+  constexpr int NW = TK_THREADS / 64;
+  constexpr int E = MB_KEEP / TK_THREADS;
+  __shared__ uint32_t off[257];
+  __shared__ uint32_t part[2][NW];
+  __shared__ uint32_t scan1[NW], scan2[NW];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int n = S;
+  if (nv) n = min(max(nv[r], 0), S);
+  // exclusive prefix of the region counts (P <= 256): one wave, four per lane
+  if (tid < 64) {
+    uint32_t c4[4], tot = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int b = 4 * tid + e;
+      c4[e] = b < P ? bcnt[(int64_t)r * P + b] : 0u;
+      tot += c4[e];
+    }
+    uint32_t incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t u = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += u;
+    }
+    uint32_t ex = incl - tot;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int b = 4 * tid + e;
+      if (b <= P) off[b] = ex;
+      ex += c4[e];
+    }
+  }
+  __syncthreads();
+  const uint32_t c = off[P];
+  int32_t* io = idx_out + (int64_t)r * k;
+  float* vo = val_out ? val_out + (int64_t)r * k : nullptr;
+  // the list is usable when at least k entries cleared the threshold
+  if (n <= k || c < (uint32_t)k || c > (uint32_t)MB_KEEP) {
+    select_block<float>(scores + (int64_t)r * S, nullptr, n, k, io, vo);
+    return;
+  }
+  // entries E*tid .. E*tid+E-1 of the concatenated regions (index order)
+  uint32_t key[E];
+  float val[E];
+  int32_t id[E];
+  bool valid[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t j = (uint32_t)(E * tid + e);
+    valid[e] = j < c;
+    key[e] = 0u;
+    val[e] = 0.0f;
+    id[e] = 0;
+    if (valid[e]) {
+      int lo2 = 0, hi2 = P - 1;  // region b with off[b] <= j < off[b+1]
+      while (lo2 < hi2) {
+        const int mid = (lo2 + hi2 + 1) >> 1;
+        if (off[mid] <= j) lo2 = mid; else hi2 = mid - 1;
+      }
+      const int64_t src = (int64_t)r * S + (int64_t)lo2 * chunk + (j - off[lo2]);
+      val[e] = cval[src];
+      id[e] = cid[src];
+      key[e] = ord_f32(val[e]);
+    }
+  }
+  // T: the largest t with count(key >= t) >= k
+  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
+  int it = 0;
+  while (lo < hi) {
+    const uint32_t mid = lo + (uint32_t)(((uint64_t)(hi - lo) + 1) >> 1);
+    uint32_t cw = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) cw += (uint32_t)__popcll(__ballot(valid[e] && key[e] >= mid));
+    if (lane == 0) part[it & 1][wid] = cw;
+    __syncthreads();
+    uint32_t tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += part[it & 1][w];
+    if (tot >= (uint32_t)k) lo = mid; else hi = mid - 1;
+    ++it;
+  }
+  const uint32_t T = lo;
+  uint32_t gt = 0, ties = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    gt += valid[e] && key[e] > T ? 1u : 0u;
+    ties += valid[e] && key[e] == T ? 1u : 0u;
+  }
+  // entries above T (all selected) and the rank of this thread's first tie
+  uint32_t gw = gt;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) gw += __shfl_xor(gw, o, 64);
+  if (lane == 0) part[it & 1][wid] = gw;
+  const uint32_t tie_rank0 = block_exclusive_scan<NW>(ties, scan1);
+  uint32_t n_gt = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) n_gt += part[it & 1][w];
+  const uint32_t need = (uint32_t)k - n_gt;  // ties taken, smallest index first
+  bool sel[E];
+  uint32_t tr = tie_rank0, nsel = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool tie = valid[e] && key[e] == T;
+    sel[e] = (valid[e] && key[e] > T) || (tie && tr < need);
+    tr += tie ? 1u : 0u;
+    nsel += sel[e] ? 1u : 0u;
+  }
+  uint32_t pos = block_exclusive_scan<NW>(nsel, scan2);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (sel[e]) {
+      io[pos] = id[e];
+      if (vo) vo[pos] = val[e];
+      ++pos;
+    }
+  }
+}
+
+static int mb_chunks(int R, int S) {
+  int p = (512 + R - 1) / R;  // about two workgroups per CU over the rows
+  const int max_p = (S + MB_THREADS * MB_BATCH - 1) / (MB_THREADS * MB_BATCH);
+  if (p > max_p) p = max_p;
+  if (p > 256) p = 256;
+  return p < 1 ? 1 : p;
+}
+
+static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t topk_mb_ws_bytes(int R, int S, int k) {
+  (void)k;
+  return a256((size_t)R * 4) + a256((size_t)R * 256 * 4) + a256((size_t)R * S * 4) * 2;
+}
+
+bool topk_use_mb(int R, int S) { return R < 160 && S >= 16384; }
+
+hipError_t launch_topk_mb(const float* scores, const int32_t* nv, int R, int S, int k, int32_t* idx, float* val,
+                          void* ws, hipStream_t st) {
+  uint8_t* p = (uint8_t*)ws;
+  uint32_t* tau = (uint32_t*)p;
+  p += a256((size_t)R * 4);
+  uint32_t* bcnt = (uint32_t*)p;
+  p += a256((size_t)R * 256 * 4);
+  float* cval = (float*)p;
+  p += a256((size_t)R * S * 4);
+  int32_t* cid = (int32_t*)p;
+  const int P = mb_chunks(R, S);
+  const int chunk = (S + P - 1) / P;
+  topk_thresh_kernel<<<R, 64, 0, st>>>(scores, nv, S, k, tau);
+  topk_filter_kernel<<<dim3(P, R), MB_THREADS, 0, st>>>(scores, nv, S, k, chunk, tau, cval, cid, bcnt);
+  topk_finalize_kernel<<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val);
+  return hipGetLastError();
+}
+
+size_t topk_ws_bytes(int R, int S, int k) { return topk_use_mb(R, S) ? topk_mb_ws_bytes(R, S, k) : 0; }
+
 hipError_t launch_topk_f32(const float* scores, const int32_t* nv, int R, int S, int k, int32_t* idx, float* val,
-                           hipStream_t st) {
+                           void* ws, hipStream_t st) {
+  if (topk_use_mb(R, S)) return launch_topk_mb(scores, nv, R, S, k, idx, val, ws, st);
   topk_row_kernel<float><<<R, TK_THREADS, 0, st>>>(scores, S, nv, nullptr, S, k, idx, val);
   return hipGetLastError();
 }

@@ -103,7 +103,8 @@ def score_keys(q_row, q_type, w_row, keys, k_type, scales=None):
 
 
 def topk(scores, k, nv=None):
-    """(idx int32 [R, k], val fp64 [R, k]) in (score desc, index asc) order."""
+    """(idx int32 [R, k], val fp64 [R, k]): the k best by (score desc, index asc),
+    listed in ascending index order, padded with (-1, -inf)."""
     scores = _c(scores, np.float64)
     R, S = scores.shape
     nv = _c(nv, np.int32)

@@ -26,8 +26,11 @@
  *     code * row scale, exact in fp64.
  *   - every sum is an fma chain in ascending index order, starting from 0:
  *     dot_h = chain_j(q[h][j], k[j]); score = chain_h(w[h], max(dot_h, 0)).
- *   - top-k order is (score descending, index ascending); rows with fewer than k
- *     visible keys are padded with (-1, -inf); invisible keys score -inf.
+ *   - the top-k set is the first k entries in the order (score descending, index
+ *     ascending), i.e. equal scores prefer the smaller index; it is returned in
+ *     ascending index order (attention does not depend on the order); rows with
+ *     fewer than k visible keys are padded with (-1, -inf); invisible keys score
+ *     -inf.
  *   - compact stage 1 scores the weighted-ReLU form in the projected space with
  *     int8 query codes: y_h = P q_h (fma chain over j), qs_h = max|y_h| / 127
  *     (1 if zero), q8_h = rint(y_h / qs_h), W_h = w_h * qs_h, D = q8_h . c_s
@@ -202,6 +205,11 @@ void orc_score_keys(const void *q_row, int q_type, const float *w_row, const voi
 
 typedef struct { double v; int32_t i; } pair_t;
 
+static int cmp_index(const void *a, const void *b) {
+  const pair_t *x = (const pair_t *)a, *y = (const pair_t *)b;
+  return (x->i < y->i) ? -1 : (x->i > y->i);
+}
+
 static int cmp_desc(const void *a, const void *b) {
   const pair_t *x = (const pair_t *)a, *y = (const pair_t *)b;
   if (x->v > y->v) return -1;
@@ -209,12 +217,13 @@ static int cmp_desc(const void *a, const void *b) {
   return (x->i < y->i) ? -1 : (x->i > y->i);
 }
 
-/* Sort (score desc, index asc) of the first n entries of one row, keep min(k, n),
- * pad with (-1, -inf). */
+/* The min(k, n) best of the first n entries of one row by (score desc, index
+ * asc), returned in ascending index order, padded with (-1, -inf). */
 static void topk_one(const double *row, int64_t n, int64_t k, int32_t *idx, double *val) {
   pair_t *p = (pair_t *)malloc(sizeof(pair_t) * (n > 0 ? n : 1));
   for (int64_t i = 0; i < n; ++i) { p[i].v = row[i]; p[i].i = (int32_t)i; }
   qsort(p, (size_t)n, sizeof(pair_t), cmp_desc);
+  qsort(p, (size_t)(n < k ? n : k), sizeof(pair_t), cmp_index);
   for (int64_t j = 0; j < k; ++j) {
     if (j < n) { idx[j] = p[j].i; if (val) val[j] = p[j].v; }
     else { idx[j] = -1; if (val) val[j] = -INFINITY; }
@@ -318,6 +327,7 @@ static void compact_row(void *p, int64_t b) {
     pr[i].i = (int32_t)s;
   }
   qsort(pr, (size_t)nm, sizeof(pair_t), cmp_desc);
+  qsort(pr, (size_t)(nm < k ? nm : k), sizeof(pair_t), cmp_index);
   for (int64_t j = 0; j < k; ++j) {
     if (j < nm) { c->idx[b * k + j] = pr[j].i; if (c->val) c->val[b * k + j] = pr[j].v; }
     else { c->idx[b * k + j] = -1; if (c->val) c->val[b * k + j] = -INFINITY; }
@@ -326,8 +336,8 @@ static void compact_row(void *p, int64_t b) {
 }
 
 /* Two-stage search.  q: [B, H, d] bf16; w: [B, H]; P: [dc, d]; c: [B, S, dc] int8;
- * cs: [B, S]; k_full: [B, S, d] bf16; nv: [B] or NULL.  Outputs shortlist [B, m]
- * (stage-1 order), idx [B, k] and val [B, k] (stage-2 order), s1 [B, S] or NULL. */
+ * cs: [B, S]; k_full: [B, S, d] bf16; nv: [B] or NULL.  Outputs shortlist [B, m],
+ * idx [B, k] and val [B, k] (each set in ascending index order), s1 [B, S] or NULL. */
 void orc_compact_search(const uint16_t *q, const float *w, const float *P, const int8_t *c, const float *cs,
                         const uint16_t *k_full, const int32_t *nv, int64_t B, int64_t S, int64_t H, int64_t d,
                         int64_t dc, int64_t m, int64_t k, int32_t *shortlist, int32_t *idx, double *val,

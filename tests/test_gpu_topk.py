@@ -50,3 +50,21 @@ def test_large_row_decode_shape():
     print("topk 131072", flush=True)
     rng = np.random.default_rng(2)
     check(rng.standard_normal((3, 131072)).astype(np.float32), 512)
+
+
+def test_few_long_rows_multi_workgroup_path():
+    # few rows of >= 16384 entries take the many-workgroups-per-row path: random
+    # rows, heavy ties, a cut bin larger than the candidate list (whole-row
+    # fallback), visible counts below k and zero
+    print("topk multi-workgroup", flush=True)
+    rng = np.random.default_rng(4)
+    R, S = 7, 40000
+    s = rng.standard_normal((R, S)).astype(np.float32)
+    s[1] = 3.0                                         # all equal: cut bin overflows
+    s[2] = rng.integers(0, 6, S).astype(np.float32)    # 6 distinct values
+    s[3] = np.abs(s[3]) * 1e-30                        # tiny values
+    s[4, 1000:] = -np.inf
+    nv = np.array([40000, 39000, 40000, 20001, 40000, 300, 0], np.int32)
+    for k in (1, 64, 512, 2048):
+        check(s, k, nv)
+        check(s, k)
