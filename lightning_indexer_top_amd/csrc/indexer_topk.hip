@@ -1,4 +1,27 @@
 // Scoring followed by per-row selection.
+//
+// For a prefill chunk (many query rows against the same keys) the selection runs
+// inside the scoring kernel, so the [rows, S] score matrix is never written:
+// "Latent Sparse Attention" article, section "What the kernels do about the
+// top-p" (the score matrix of a prefill chunk is never written to memory; each
+// score is compared with a threshold as it comes off the matrix cores and only
+// the entries above it are listed).  Score: "Long context", llm-serving.xyz
+// lecture 03, section "The Architectural Answer", paragraph "Stage 1, the
+// lightning indexer".
+//
+// prefill_select_kernel: a workgroup owns 8 query rows of one sequence, one per
+// wave; each wave keeps its query block (H x 128 bf16) in VGPRs as the MFMA A
+// operand.  The workgroup streams every visible key of the sequence through LDS
+// in 64-key bf16 tiles (double buffered, loaded cooperatively, XOR-swizzled so
+// the operand reads are conflict free); each wave scores each 32-key sub-tile
+// with 16 v_mfma_f32_32x32x16_bf16 (64 heads) and reduces ReLU x weight over the
+// heads in registers.  Selection per row: a running threshold theta (the current
+// k-th best) and a candidate list of CAP entries in LDS kept in key-index order.
+// A score is listed when it beats theta; when the list is full the wave compacts
+// it to the exact current top-k (bisection on the orderable score bits for the
+// k-th value, ties to the smaller index, order-preserving) and raises theta.
+// Keys arrive in increasing index order, so an entry equal to theta loses its
+// tie and a strict comparison is exact.
 #include "common.h"
 #include "launch.h"
 
@@ -6,14 +29,253 @@ namespace li {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int PS_WAVES = 8;    // query rows per workgroup
+constexpr int PS_NK = 64;      // keys per LDS tile
+constexpr int PS_CAP = 1024;   // candidate list entries per row
+constexpr int PS_KMAX = 512;   // largest k the fused kernel takes (CAP - k >= 512)
+
+// max(x, 0) on the bit pattern (exact, -0 -> +0).
+__device__ __forceinline__ float relu_bits_f(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Wave-level exact compaction of a candidate list (entries [0, cnt) in index
+// order, orderable keys in sk, ids in si) to its best `keep` entries, preserving
+// order.  Returns the orderable key T of the worst kept entry (0 if nothing is
+// dropped).  Every lane handles PS_CAP / 64 consecutive entries.
+__device__ uint32_t ps_compact(uint32_t* sk, int32_t* si, int cnt, int keep) {
+  constexpr int E = PS_CAP / 64;
+  const int lane = threadIdx.x & 63;
+  if (cnt <= keep) return 0u;
+  uint32_t key[E];
+  int32_t id[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = E * lane + e;
+    key[e] = j < cnt ? sk[j] : 0u;
+    id[e] = j < cnt ? si[j] : 0;
+  }
+  // T: the largest t with count(key >= t) >= keep (padding keys are 0)
+  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
+  while (lo < hi) {
+    const uint32_t mid = lo + (uint32_t)(((uint64_t)(hi - lo) + 1) >> 1);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= mid));
+    if (c >= keep) lo = mid; else hi = mid - 1;
+  }
+  const uint32_t T = lo;
+  int gt = 0, ties = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    gt += __popcll(__ballot(key[e] > T));
+    ties += (key[e] == T && E * lane + e < cnt) ? 1 : 0;
+  }
+  const int need = keep - gt;  // entries equal to T to keep, smallest index first
+  // exclusive scan of the tie counts over lanes (index order)
+  int tincl = ties;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(tincl, o, 64);
+    if (lane >= o) tincl += u;
+  }
+  int tr = tincl - ties;
+  bool sel[E];
+  int ns = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool valid = E * lane + e < cnt;
+    const bool tie = valid && key[e] == T;
+    sel[e] = (valid && key[e] > T) || (tie && tr < need);
+    tr += tie ? 1 : 0;
+    ns += sel[e] ? 1 : 0;
+  }
+  int sincl = ns;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(sincl, o, 64);
+    if (lane >= o) sincl += u;
+  }
+  int pos = sincl - ns;
+  // every lane has read its entries before any lane writes (wave in lockstep,
+  // LDS accesses of one wave in order); positions only move down
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (sel[e]) {
+      sk[pos] = key[e];
+      si[pos] = id[e];
+      ++pos;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  return T;
+}
+
+template <int HT>
+__global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                           const uint16_t* __restrict__ k, const int32_t* __restrict__ nv, int T, int S, int H,
+                           int topk, int32_t* __restrict__ idx_out, float* __restrict__ val_out) {
+  // LDS: two key tiles (64 keys x 256 B, 16-byte chunks XOR-swizzled by key),
+  // then per wave a candidate list (orderable keys, ids)
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[2][PS_NK * 256];
+  __shared__ uint32_t cand_k[PS_WAVES][PS_CAP];
+  __shared__ int32_t cand_i[PS_WAVES][PS_CAP];
+
+  const int blocks_per_seq = (T + PS_WAVES - 1) / PS_WAVES;
+  const int b = blockIdx.x / blocks_per_seq;
+  const int t0 = (blockIdx.x % blocks_per_seq) * PS_WAVES;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hf = lane >> 5, col = lane & 31;
+  const int t = t0 + wave;
+  const bool active = t < T;
+  const int64_t r = (int64_t)b * T + (active ? t : t0);
+  int nvis = S;
+  if (nv) nvis = min(max(nv[r], 0), S);
+  if (!active) nvis = 0;
+
+  // keys needed by the workgroup: the largest visible count of its rows
+  __shared__ int s_kend;
+  if (tid == 0) s_kend = 0;
+  __syncthreads();
+  if (lane == 0) atomicMax(&s_kend, nvis);
+  __syncthreads();
+  const int kend = s_kend;
+
+  // query block (A operand) and head weights in accumulator row order
+  bf16x8 a[HT][8];
+  float wv[HT][16];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int h = ht * 32 + col;
+    const uint4* qp = (const uint4*)(q + (r * H + (h < H ? h : 0)) * 128 + 64 * hf);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint4 v = (h < H && active) ? qp[kk] : make_uint4(0, 0, 0, 0);
+      a[ht][kk] = __builtin_bit_cast(bf16x8, v);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int hh = ht * 32 + (i & 3) + 8 * (i >> 2) + 4 * hf;
+      wv[ht][i] = (hh < H && active) ? w[r * H + hh] : 0.0f;
+    }
+  }
+
+  const uint16_t* kbase = k + (int64_t)b * S * 128;
+  // cooperative tile load: thread tid moves 16-byte chunks tid and tid + 512
+  auto load_tile = [&](int kt, uint4 (&reg)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + PS_WAVES * 64 * u;
+      const int n = c >> 4, cc = c & 15;
+      const int key = min(kt + n, S - 1);
+      reg[u] = *(const uint4*)(kbase + (int64_t)key * 128 + cc * 8);
+    }
+  };
+  auto store_tile = [&](uint8_t* buf, const uint4 (&reg)[2]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + PS_WAVES * 64 * u;
+      const int n = c >> 4, cc = c & 15;
+      *(uint4*)(buf + n * 256 + ((cc ^ (n & 15)) << 4)) = reg[u];
+    }
+  };
+
+  uint32_t* sk = cand_k[wave];
+  int32_t* si = cand_i[wave];
+  int cnt = 0;          // listed entries
+  uint32_t theta = 0u;  // orderable key to beat
+
+  const int ntiles = (kend + PS_NK - 1) / PS_NK;
+  uint4 reg[2];
+  if (ntiles > 0) {
+    load_tile(0, reg);
+    store_tile(tiles[0], reg);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int kt = it * PS_NK;
+    const bool more = it + 1 < ntiles;
+    if (more) load_tile(kt + PS_NK, reg);
+    const uint8_t* buf = tiles[it & 1];
+#pragma unroll
+    for (int s = 0; s < PS_NK / 32; ++s) {
+      const int key0 = kt + 32 * s;
+      if (key0 >= nvis) break;  // uniform per wave
+      const int n = 32 * s + col;
+      bf16x8 bop[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        bop[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(buf + n * 256 + (((8 * hf + kk) ^ (n & 15)) << 4)));
+      float part = 0.0f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ht][kk], bop[kk], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) part = fmaf(wv[ht][i], relu_bits_f(acc[i]), part);
+      }
+      part += __shfl_xor(part, 32, 64);
+      const int key = key0 + col;
+      const uint32_t ok = ord_f32(part);
+      const uint64_t mk = __ballot(hf == 0 && key < nvis && ok > theta);
+      if (mk) {
+        if ((mk >> lane) & 1ull) {
+          const int pos = cnt + __popcll(mk & ((1ull << lane) - 1));
+          sk[pos] = ok;
+          si[pos] = key;
+        }
+        cnt += __popcll(mk);
+        if (cnt > PS_CAP - 32) {
+          theta = ps_compact(sk, si, cnt, topk);
+          cnt = topk;
+        }
+      }
+    }
+    if (more) store_tile(tiles[(it + 1) & 1], reg);
+    __syncthreads();
+  }
+  if (!active) return;
+  if (cnt > topk) {
+    ps_compact(sk, si, cnt, topk);
+    cnt = topk;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  int32_t* io = idx_out + r * topk;
+  float* vo = val_out ? val_out + r * topk : nullptr;
+  for (int j = lane; j < topk; j += 64) {
+    const bool v = j < cnt;
+    io[j] = v ? si[j] : -1;
+    if (vo) vo[j] = v ? unord_f32(sk[j]) : -INFINITY;
+  }
+}
+
+static bool use_fused(int q_type, int k_type, int T, int H, int topk) {
+  return q_type == DT_BF16 && k_type == DT_BF16 && T >= 2 * PS_WAVES && topk <= PS_KMAX && H <= 128;
+}
+
 size_t indexer_topk_ws_bytes(int B, int T, int S, int H, int topk) {
   (void)H;
+  // the fused path needs no workspace; sized for the score-then-select path,
+  // which any shape may take
   return align256((size_t)B * T * S * sizeof(float)) + topk_ws_bytes(B * T, S, topk);
 }
 
 hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const void* k, int k_type, const float* ks,
                                const int32_t* nv, int B, int T, int S, int H, int topk, int32_t* idx, float* val,
                                void* ws, hipStream_t st) {
+  if (use_fused(q_type, k_type, T, H, topk)) {
+    const int blocks = B * ((T + PS_WAVES - 1) / PS_WAVES);
+    const uint16_t* qq = (const uint16_t*)q;
+    const uint16_t* kk = (const uint16_t*)k;
+    if (H <= 32)
+      prefill_select_kernel<1><<<blocks, PS_WAVES * 64, 0, st>>>(qq, w, kk, nv, T, S, H, topk, idx, val);
+    else if (H <= 64)
+      prefill_select_kernel<2><<<blocks, PS_WAVES * 64, 0, st>>>(qq, w, kk, nv, T, S, H, topk, idx, val);
+    else
+      prefill_select_kernel<4><<<blocks, PS_WAVES * 64, 0, st>>>(qq, w, kk, nv, T, S, H, topk, idx, val);
+    return hipGetLastError();
+  }
   float* scores = (float*)ws;
   hipError_t e = launch_score(q, q_type, w, k, k_type, ks, nv, B, T, S, H, scores, st);
   if (e != hipSuccess) return e;

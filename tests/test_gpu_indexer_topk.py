@@ -46,3 +46,47 @@ def test_selection_matches_oracle(name, over):
     assert np.array_equal(g_idx, r_idx)
     fin = r_idx >= 0
     assert np.array_equal(g_val.cpu().numpy().astype(np.float64)[fin], r_val[fin])
+
+
+def _fused_check(x, sp, k, what):
+    d = dict(q=dev(x["q"], "bf16"), w=dev(x["w"]), k=dev(x["k"], "bf16"),
+             nv=dev(x["nv"]) if x["nv"] is not None else None)
+    g_idx, g_val = li.indexer_topk(d["q"], d["w"], d["k"], k, None, d["nv"])
+    g_scores = li.indexer_score(d["q"], d["w"], d["k"], None, d["nv"])
+    torch.cuda.synchronize()
+    g_idx = g_idx.cpu().numpy()
+    gs = g_scores.cpu().numpy().astype(np.float64)
+    r_idx, r_val = oracle.topk(gs, k, x["nv"])
+    assert np.array_equal(g_idx, r_idx), what
+    fin = r_idx >= 0
+    assert np.array_equal(g_val.cpu().numpy().astype(np.float64)[fin], r_val[fin]), what
+    o = oracle.indexer_score(x["q"], oracle.BF16, x["w"], x["k"], oracle.BF16, None, x["nv"])
+    assert_topk_band(g_idx, o, k, x["nv"], what)
+
+
+@pytest.mark.parametrize("T,S,H,k", [(100, 20000, 64, 512), (16, 5000, 8, 64), (40, 3000, 100, 200),
+                                     (24, 1500, 32, 512), (16, 70000, 64, 512)])
+def test_fused_prefill_shapes(T, S, H, k):
+    # query rows scored and selected in one kernel (the scores are never written)
+    print("fused prefill", T, S, H, k, flush=True)
+    sp = workloads.spec("prefill_chunk", T=T, S=S, H=H, seed=0x5EED0B00 + T + S)
+    x = workloads.indexer_inputs(sp)
+    _fused_check(x, sp, k, f"T={T} S={S} H={H} k={k}")
+
+
+def test_fused_prefill_ties_and_masks():
+    # integer-valued queries and keys: many exactly equal scores, so the list
+    # compactions resolve ties by index; visible counts 0, below k, at k, ragged
+    print("fused prefill ties", flush=True)
+    rng = np.random.default_rng(7)
+    T, S, H, k = 32, 9000, 64, 512
+    import synth
+    qf = rng.integers(-2, 3, (1, T, H, 128)).astype(np.float64)
+    kf = rng.integers(-1, 2, (1, S, 128)).astype(np.float64)
+    q = np.array([synth.bf16_rne(v) for v in qf.ravel()], np.uint16).reshape(qf.shape)
+    kk = np.array([synth.bf16_rne(v) for v in kf.ravel()], np.uint16).reshape(kf.shape)
+    w = rng.integers(0, 3, (1, T, H)).astype(np.float32)
+    nv = rng.integers(600, S + 1, T).astype(np.int32)
+    nv[:5] = [0, 1, 511, 512, 513]
+    x = {"q": q, "w": w, "k": kk, "nv": nv}
+    _fused_check(x, None, k, "ties")
