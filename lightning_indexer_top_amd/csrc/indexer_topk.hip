@@ -161,24 +161,13 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
   }
 
   const uint16_t* kbase = k + (int64_t)b * S * 128;
-  // cooperative tile load: thread tid moves 16-byte chunks tid and tid + 512
-  auto load_tile = [&](int kt, uint4 (&reg)[2]) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + PS_WAVES * 64 * u;
-      const int n = c >> 4, cc = c & 15;
-      const int key = min(kt + n, S - 1);
-      reg[u] = *(const uint4*)(kbase + (int64_t)key * 128 + cc * 8);
-    }
-  };
-  auto store_tile = [&](uint8_t* buf, const uint4 (&reg)[2]) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + PS_WAVES * 64 * u;
-      const int n = c >> 4, cc = c & 15;
-      *(uint4*)(buf + n * 256 + ((cc ^ (n & 15)) << 4)) = reg[u];
-    }
-  };
+  // cooperative tile load: thread tid moves 16-byte chunks c0 = tid and
+  // c1 = tid + 512 (key c >> 4, chunk c & 15); plain registers, no arrays
+  const int c0n = tid >> 4, c0c = tid & 15;
+  const int c1n = (tid + PS_WAVES * 64) >> 4, c1c = (tid + PS_WAVES * 64) & 15;
+  const int st0 = c0n * 256 + ((c0c ^ (c0n & 15)) << 4);
+  const int st1 = c1n * 256 + ((c1c ^ (c1n & 15)) << 4);
+  static_assert(PS_NK * 16 == 2 * PS_WAVES * 64, "two chunks per thread");
 
   uint32_t* sk = cand_k[wave];
   int32_t* si = cand_i[wave];
@@ -186,16 +175,24 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
   uint32_t theta = 0u;  // orderable key to beat
 
   const int ntiles = (kend + PS_NK - 1) / PS_NK;
-  uint4 reg[2];
+  uint4 reg0 = make_uint4(0, 0, 0, 0), reg1 = make_uint4(0, 0, 0, 0);
   if (ntiles > 0) {
-    load_tile(0, reg);
-    store_tile(tiles[0], reg);
+    reg0 = *(const uint4*)(kbase + (int64_t)min(c0n, S - 1) * 128 + c0c * 8);
+    reg1 = *(const uint4*)(kbase + (int64_t)min(c1n, S - 1) * 128 + c1c * 8);
+    *(uint4*)(tiles[0] + st0) = reg0;
+    *(uint4*)(tiles[0] + st1) = reg1;
   }
+  // every load issued so far (query block, weights, first tile) has landed: the
+  // loop then only waits on its own next-tile loads where they are stored
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int kt = it * PS_NK;
     const bool more = it + 1 < ntiles;
-    if (more) load_tile(kt + PS_NK, reg);
+    if (more) {
+      reg0 = *(const uint4*)(kbase + (int64_t)min(kt + PS_NK + c0n, S - 1) * 128 + c0c * 8);
+      reg1 = *(const uint4*)(kbase + (int64_t)min(kt + PS_NK + c1n, S - 1) * 128 + c1c * 8);
+    }
     const uint8_t* buf = tiles[it & 1];
 #pragma unroll
     for (int s = 0; s < PS_NK / 32; ++s) {
@@ -232,7 +229,13 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
         }
       }
     }
-    if (more) store_tile(tiles[(it + 1) & 1], reg);
+    // keep the store of the next tile after this tile's compute: hoisted above
+    // it, the store would wait for the tile's global loads before any MFMA issues
+    asm volatile("" ::: "memory");
+    if (more) {
+      *(uint4*)(tiles[(it + 1) & 1] + st0) = reg0;
+      *(uint4*)(tiles[(it + 1) & 1] + st1) = reg1;
+    }
     __syncthreads();
   }
   if (!active) return;
