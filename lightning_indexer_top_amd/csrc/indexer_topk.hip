@@ -30,7 +30,8 @@ namespace li {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int PS_WAVES = 8;    // query rows per workgroup
-constexpr int PS_NK = 64;      // keys per LDS tile
+constexpr int PS_NK = 128;     // keys per LDS tile
+constexpr int PS_CPT = PS_NK * 16 / (PS_WAVES * 64);  // 16-byte chunks per thread per tile
 constexpr int PS_CAP = 1024;   // candidate list entries per row
 constexpr int PS_KMAX = 512;   // largest k the fused kernel takes (CAP - k >= 512)
 
@@ -161,13 +162,11 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
   }
 
   const uint16_t* kbase = k + (int64_t)b * S * 128;
-  // cooperative tile load: thread tid moves 16-byte chunks c0 = tid and
-  // c1 = tid + 512 (key c >> 4, chunk c & 15); plain registers, no arrays
-  const int c0n = tid >> 4, c0c = tid & 15;
-  const int c1n = (tid + PS_WAVES * 64) >> 4, c1c = (tid + PS_WAVES * 64) & 15;
-  const int st0 = c0n * 256 + ((c0c ^ (c0n & 15)) << 4);
-  const int st1 = c1n * 256 + ((c1c ^ (c1n & 15)) << 4);
-  static_assert(PS_NK * 16 == 2 * PS_WAVES * 64, "two chunks per thread");
+  // cooperative tile load: thread tid moves the 16-byte chunks
+  // c = tid + 512 j (key c >> 4, chunk c & 15)
+  static_assert(PS_NK * 16 == PS_CPT * PS_WAVES * 64, "whole chunks per thread");
+  const int cn0 = tid >> 4, cc = tid & 15;  // key of chunk j: cn0 + 32 j
+  constexpr int KSTEP = PS_WAVES * 64 / 16;
 
   uint32_t* sk = cand_k[wave];
   int32_t* si = cand_i[wave];
@@ -175,12 +174,16 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
   uint32_t theta = 0u;  // orderable key to beat
 
   const int ntiles = (kend + PS_NK - 1) / PS_NK;
-  uint4 reg0 = make_uint4(0, 0, 0, 0), reg1 = make_uint4(0, 0, 0, 0);
+  // four named registers, not an array: an array here is kept in scratch memory
+  static_assert(PS_CPT == 4, "chunk registers below");
+  uint4 reg0, reg1, reg2, reg3;
+#define PS_LOAD(j, key0) \
+  reg##j = *(const uint4*)(kbase + (int64_t)min((key0) + cn0 + KSTEP * j, S - 1) * 128 + cc * 8)
+#define PS_STORE(j, buf) \
+  *(uint4*)((buf) + (cn0 + KSTEP * j) * 256 + ((cc ^ ((cn0 + KSTEP * j) & 15)) << 4)) = reg##j
   if (ntiles > 0) {
-    reg0 = *(const uint4*)(kbase + (int64_t)min(c0n, S - 1) * 128 + c0c * 8);
-    reg1 = *(const uint4*)(kbase + (int64_t)min(c1n, S - 1) * 128 + c1c * 8);
-    *(uint4*)(tiles[0] + st0) = reg0;
-    *(uint4*)(tiles[0] + st1) = reg1;
+    PS_LOAD(0, 0); PS_LOAD(1, 0); PS_LOAD(2, 0); PS_LOAD(3, 0);
+    PS_STORE(0, tiles[0]); PS_STORE(1, tiles[0]); PS_STORE(2, tiles[0]); PS_STORE(3, tiles[0]);
   }
   // every load issued so far (query block, weights, first tile) has landed: the
   // loop then only waits on its own next-tile loads where they are stored
@@ -190,42 +193,72 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
     const int kt = it * PS_NK;
     const bool more = it + 1 < ntiles;
     if (more) {
-      reg0 = *(const uint4*)(kbase + (int64_t)min(kt + PS_NK + c0n, S - 1) * 128 + c0c * 8);
-      reg1 = *(const uint4*)(kbase + (int64_t)min(kt + PS_NK + c1n, S - 1) * 128 + c1c * 8);
+      PS_LOAD(0, kt + PS_NK); PS_LOAD(1, kt + PS_NK); PS_LOAD(2, kt + PS_NK); PS_LOAD(3, kt + PS_NK);
     }
     const uint8_t* buf = tiles[it & 1];
-#pragma unroll
-    for (int s = 0; s < PS_NK / 32; ++s) {
-      const int key0 = kt + 32 * s;
-      if (key0 >= nvis) break;  // uniform per wave
-      const int n = 32 * s + col;
+    if (kt < nvis) {  // uniform per wave
+      // software pipeline over the tile's 32-key sub-tiles: the MFMAs of
+      // sub-tile s + 1 issue before the ReLU x weight reduction of sub-tile s,
+      // so that reduction runs in the shadow of the matrix cores
+      f32x16 acc[2][HT];
       bf16x8 bop[8];
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
-        bop[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(buf + n * 256 + (((8 * hf + kk) ^ (n & 15)) << 4)));
-      float part = 0.0f;
+        bop[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(buf + col * 256 + (((8 * hf + kk) ^ (col & 15)) << 4)));
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        f32x16 acc = {};
+        acc[0][ht] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ht][kk], bop[kk], acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) part = fmaf(wv[ht][i], relu_bits_f(acc[i]), part);
+        for (int kk = 0; kk < 8; ++kk)
+          acc[0][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ht][kk], bop[kk], acc[0][ht], 0, 0, 0);
       }
-      part += __shfl_xor(part, 32, 64);
-      const int key = key0 + col;
-      const uint32_t ok = ord_f32(part);
-      const uint64_t mk = __ballot(hf == 0 && key < nvis && ok > theta);
-      if (mk) {
-        if ((mk >> lane) & 1ull) {
-          const int pos = cnt + __popcll(mk & ((1ull << lane) - 1));
-          sk[pos] = ok;
-          si[pos] = key;
+#pragma unroll
+      for (int s = 0; s < PS_NK / 32; ++s) {
+        if (s + 1 < PS_NK / 32) {
+          const int n = 32 * (s + 1) + col;
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk)
+            bop[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(buf + n * 256 + (((8 * hf + kk) ^ (n & 15)) << 4)));
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            acc[(s + 1) & 1][ht] = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+              acc[(s + 1) & 1][ht] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ht][kk], bop[kk], acc[(s + 1) & 1][ht], 0, 0, 0);
+          }
         }
-        cnt += __popcll(mk);
-        if (cnt > PS_CAP - 32) {
-          theta = ps_compact(sk, si, cnt, topk);
-          cnt = topk;
+        float part = 0.0f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) part = fmaf(wv[ht][i], relu_bits_f(acc[s & 1][ht][i]), part);
+        }
+        // lanes 0..31 add the partial sum of lanes 32..63 (same key, other heads)
+        part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                                 false, false)[1]);
+        if (s + 1 < PS_NK / 32) {
+          // interleave: one MFMA, then four VALU operations of the reduction
+#pragma unroll
+          for (int g = 0; g < 8 * HT; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          }
+        }
+        const int key = kt + 32 * s + col;
+        const uint32_t ok = ord_f32(part);
+        const uint64_t mk = __ballot(hf == 0 && key < nvis && ok > theta);
+        if (mk) {
+          if ((mk >> lane) & 1ull) {
+            const int pos = cnt + __popcll(mk & ((1ull << lane) - 1));
+            sk[pos] = ok;
+            si[pos] = key;
+          }
+          cnt += __popcll(mk);
+          if (cnt > PS_CAP - 32) {
+            theta = ps_compact(sk, si, cnt, topk);
+            cnt = topk;
+          }
         }
       }
     }
@@ -233,11 +266,13 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
     // it, the store would wait for the tile's global loads before any MFMA issues
     asm volatile("" ::: "memory");
     if (more) {
-      *(uint4*)(tiles[(it + 1) & 1] + st0) = reg0;
-      *(uint4*)(tiles[(it + 1) & 1] + st1) = reg1;
+      uint8_t* nb = tiles[(it + 1) & 1];
+      PS_STORE(0, nb); PS_STORE(1, nb); PS_STORE(2, nb); PS_STORE(3, nb);
     }
     __syncthreads();
   }
+#undef PS_LOAD
+#undef PS_STORE
   if (!active) return;
   if (cnt > topk) {
     ps_compact(sk, si, cnt, topk);
