@@ -12,7 +12,7 @@
 // prefill_select_kernel: a workgroup owns 8 query rows of one sequence, one per
 // wave; each wave keeps its query block (H x 128 bf16) in VGPRs as the MFMA A
 // operand.  The workgroup streams every visible key of the sequence through LDS
-// in 64-key bf16 tiles (double buffered, loaded cooperatively, XOR-swizzled so
+// in 128-key bf16 tiles (double buffered, loaded cooperatively, XOR-swizzled so
 // the operand reads are conflict free); each wave scores each 32-key sub-tile
 // with 16 v_mfma_f32_32x32x16_bf16 (64 heads) and reduces ReLU x weight over the
 // heads in registers.  Selection per row: a running threshold theta (the current
@@ -33,27 +33,23 @@ constexpr int PS_WAVES = 8;    // query rows per workgroup
 constexpr int PS_NK = 128;     // keys per LDS tile
 constexpr int PS_CPT = PS_NK * 16 / (PS_WAVES * 64);  // 16-byte chunks per thread per tile
 constexpr int PS_CAP = 1024;   // candidate list entries per row
-constexpr int PS_KMAX = 512;   // largest k the fused kernel takes (CAP - k >= 512)
+constexpr int PS_KMAX = 512;   // largest k the fused kernel takes (CAP - NK - k >= 384)
 
 // max(x, 0) on the bit pattern (exact, -0 -> +0).
 __device__ __forceinline__ float relu_bits_f(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Wave-level exact compaction of a candidate list (entries [0, cnt) in index
-// order, orderable keys in sk, ids in si) to its best `keep` entries, preserving
-// order.  Returns the orderable key T of the worst kept entry (0 if nothing is
-// dropped).  Every lane handles PS_CAP / 64 consecutive entries.
+// order, orderable keys in sk, ids in si; every listed key is above 0) to its
+// best `keep` entries, preserving order.  Returns the orderable key T of the
+// worst kept entry.  Lane l handles entries l + 64 e, so the rank of an entry
+// among the kept ones is a ballot prefix: rows e' < e, then lanes below l.
 __device__ uint32_t ps_compact(uint32_t* sk, int32_t* si, int cnt, int keep) {
   constexpr int E = PS_CAP / 64;
   const int lane = threadIdx.x & 63;
-  if (cnt <= keep) return 0u;
+  const uint64_t below = (1ull << lane) - 1;
   uint32_t key[E];
-  int32_t id[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = E * lane + e;
-    key[e] = j < cnt ? sk[j] : 0u;
-    id[e] = j < cnt ? si[j] : 0;
-  }
+  for (int e = 0; e < E; ++e) key[e] = lane + 64 * e < cnt ? sk[lane + 64 * e] : 0u;
   // T: the largest t with count(key >= t) >= keep (padding keys are 0)
   uint32_t lo = 0u, hi = 0xFFFFFFFFu;
   while (lo < hi) {
@@ -64,48 +60,30 @@ __device__ uint32_t ps_compact(uint32_t* sk, int32_t* si, int cnt, int keep) {
     if (c >= keep) lo = mid; else hi = mid - 1;
   }
   const uint32_t T = lo;
-  int gt = 0, ties = 0;
+  int gt = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    gt += __popcll(__ballot(key[e] > T));
-    ties += (key[e] == T && E * lane + e < cnt) ? 1 : 0;
-  }
+  for (int e = 0; e < E; ++e) gt += __popcll(__ballot(key[e] > T));
   const int need = keep - gt;  // entries equal to T to keep, smallest index first
-  // exclusive scan of the tie counts over lanes (index order)
-  int tincl = ties;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(tincl, o, 64);
-    if (lane >= o) tincl += u;
-  }
-  int tr = tincl - ties;
-  bool sel[E];
-  int ns = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const bool valid = E * lane + e < cnt;
-    const bool tie = valid && key[e] == T;
-    sel[e] = (valid && key[e] > T) || (tie && tr < need);
-    tr += tie ? 1 : 0;
-    ns += sel[e] ? 1 : 0;
-  }
-  int sincl = ns;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(sincl, o, 64);
-    if (lane >= o) sincl += u;
-  }
-  int pos = sincl - ns;
-  // every lane has read its entries before any lane writes (wave in lockstep,
-  // LDS accesses of one wave in order); positions only move down
+  // a kept entry moves to its rank, never above its own position: the writes of
+  // row e land in rows <= e, and row e is read before it is written
+  int base = 0, tbase = 0;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    if (sel[e]) {
+    const int j = lane + 64 * e;
+    const bool valid = j < cnt;
+    const bool tie = valid && key[e] == T;
+    const uint64_t mt = __ballot(tie);
+    const bool sel = (valid && key[e] > T) || (tie && tbase + __popcll(mt & below) < need);
+    tbase += __popcll(mt);
+    const uint64_t ms = __ballot(sel);
+    const int32_t id = valid ? si[j] : 0;
+    if (sel) {
+      const int pos = base + __popcll(ms & below);
       sk[pos] = key[e];
-      si[pos] = id[e];
-      ++pos;
+      si[pos] = id;
     }
+    base += __popcll(ms);
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   return T;
@@ -197,47 +175,59 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
     }
     const uint8_t* buf = tiles[it & 1];
     if (kt < nvis) {  // uniform per wave
-      // software pipeline over the tile's 32-key sub-tiles: the MFMAs of
-      // sub-tile s + 1 issue before the ReLU x weight reduction of sub-tile s,
-      // so that reduction runs in the shadow of the matrix cores
-      f32x16 acc[2][HT];
+      // software pipeline over the tile's 32-key sub-tiles (up to 64 heads):
+      // the MFMAs of sub-tile s + 1 issue before the ReLU x weight reduction of
+      // sub-tile s, so that reduction runs in the shadow of the matrix cores.
+      // With 128 heads a second accumulator set does not fit the register file:
+      // each group of 32 heads is scored, then reduced.
+      constexpr bool PIPE = HT <= 2;
+      constexpr int NS = PS_NK / 32;
+      f32x16 acc[PIPE ? 2 : 1][PIPE ? HT : 1];
       bf16x8 bop[8];
+#define PS_BOP(sub)                                                                                             \
+  do {                                                                                                          \
+    const int n_ = 32 * (sub) + col;                                                                            \
+    _Pragma("unroll") for (int kk = 0; kk < 8; ++kk) bop[kk] =                                                  \
+        __builtin_bit_cast(bf16x8, *(const uint4*)(buf + n_ * 256 + (((8 * hf + kk) ^ (n_ & 15)) << 4)));       \
+  } while (0)
+#define PS_MMA(slot, ht, aset)                                                                                  \
+  do {                                                                                                          \
+    acc[slot][ht] = f32x16{};                                                                                   \
+    _Pragma("unroll") for (int kk = 0; kk < 8; ++kk) acc[slot][ht] =                                            \
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[aset][kk], bop[kk], acc[slot][ht], 0, 0, 0);                  \
+  } while (0)
+      if constexpr (PIPE) {
+        PS_BOP(0);
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        bop[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(buf + col * 256 + (((8 * hf + kk) ^ (col & 15)) << 4)));
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        acc[0][ht] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-          acc[0][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ht][kk], bop[kk], acc[0][ht], 0, 0, 0);
+        for (int ht = 0; ht < HT; ++ht) PS_MMA(0, ht, ht);
       }
 #pragma unroll
-      for (int s = 0; s < PS_NK / 32; ++s) {
-        if (s + 1 < PS_NK / 32) {
-          const int n = 32 * (s + 1) + col;
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk)
-            bop[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(buf + n * 256 + (((8 * hf + kk) ^ (n & 15)) << 4)));
+      for (int s = 0; s < NS; ++s) {
+        float part = 0.0f;
+        if constexpr (!PIPE) {
+          PS_BOP(s);
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht) {
-            acc[(s + 1) & 1][ht] = f32x16{};
+            PS_MMA(0, 0, ht);
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-              acc[(s + 1) & 1][ht] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ht][kk], bop[kk], acc[(s + 1) & 1][ht], 0, 0, 0);
+            for (int i = 0; i < 16; ++i) part = fmaf(wv[ht][i], relu_bits_f(acc[0][0][i]), part);
           }
-        }
-        float part = 0.0f;
+        } else {
+          if (s + 1 < NS) {
+            PS_BOP(s + 1);
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
+            for (int ht = 0; ht < HT; ++ht) PS_MMA((s + 1) & 1, ht, ht);
+          }
 #pragma unroll
-          for (int i = 0; i < 16; ++i) part = fmaf(wv[ht][i], relu_bits_f(acc[s & 1][ht][i]), part);
+          for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) part = fmaf(wv[ht][i], relu_bits_f(acc[s & 1][ht][i]), part);
+          }
         }
         // lanes 0..31 add the partial sum of lanes 32..63 (same key, other heads)
         part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
                                                                  false, false)[1]);
-        if (s + 1 < PS_NK / 32) {
+        if (PIPE && s + 1 < NS) {
           // interleave: one MFMA, then four VALU operations of the reduction
 #pragma unroll
           for (int g = 0; g < 8 * HT; ++g) {
@@ -255,11 +245,12 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
             si[pos] = key;
           }
           cnt += __popcll(mk);
-          if (cnt > PS_CAP - 32) {
-            theta = ps_compact(sk, si, cnt, topk);
-            cnt = topk;
-          }
         }
+      }
+      // room for the next tile's entries
+      if (cnt > PS_CAP - PS_NK) {
+        theta = ps_compact(sk, si, cnt, topk);
+        cnt = topk;
       }
     }
     // keep the store of the next tile after this tile's compute: hoisted above
@@ -271,6 +262,8 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
     }
     __syncthreads();
   }
+#undef PS_MMA
+#undef PS_BOP
 #undef PS_LOAD
 #undef PS_STORE
   if (!active) return;
