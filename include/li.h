@@ -36,9 +36,12 @@
  *   - Values in device arrays (nv, idx) are not validated on the host: nv entries
  *     are clamped to [0, S] by the kernels, idx entries outside [0, S) are
  *     treated as "no entry".  NaN scores are ordered above +inf (unspecified).
- *   - Top-k outputs are in canonical order: score descending, and among equal
- *     scores the smaller key index first.  Rows with fewer than k visible keys
- *     are padded with index -1 and value -inf.
+ *   - A top-k output is the selected set, which is unique because among equal
+ *     scores the smaller key index wins, listed in ascending key index (each
+ *     value beside its index).  The order carries no rank: attention over the
+ *     set does not depend on it, and ascending indices keep the later gather of
+ *     the selected rows sequential.  Rows with fewer than k visible keys list
+ *     their visible keys, then index -1 with value -inf.
  */
 #ifndef LIGHTNING_INDEXER_LI_H
 #define LIGHTNING_INDEXER_LI_H
@@ -112,7 +115,7 @@ li_status li_indexer_score(const void *q, li_dtype q_type, const float *w, const
  * li_topk_select -- the k best keys of each row of a score matrix.
  *
  *   scores [R, S] fp32; nv [R] int32 or NULL (row r considers s < nv[r] only)
- *   idx    [R, k] int32 output (canonical order, padded with -1)
+ *   idx    [R, k] int32 output (ascending key index, padded with -1)
  *   val    [R, k] fp32 output or NULL (the selected scores, padded with -inf)
  *   ws     workspace of at least li_topk_workspace_bytes(R, S, k) bytes
  *
@@ -130,7 +133,7 @@ li_status li_topk_select(const float *scores, const int32_t *nv, int R, int S, i
  * chunk) the selection runs inside the scoring kernel and the [B*T, S] scores are
  * never written to memory.
  *
- *   idx [B*T, topk] int32, val [B*T, topk] fp32 or NULL (canonical order)
+ *   idx [B*T, topk] int32, val [B*T, topk] fp32 or NULL (ascending key index)
  *   ws  workspace of at least li_indexer_topk_workspace_bytes(...) bytes
  *
  * Requires q_type == LI_BF16 and k_type in {LI_BF16, LI_FP8_E4M3}, or the fp32
@@ -150,8 +153,8 @@ li_status li_indexer_topk(const void *q, li_dtype q_type, const float *w, const 
  *   ck       [B, S, dc]  int8 compact keys; ck_scale [B, S] fp32 (key ~ code * scale)
  *   k_full   [B, S, d]   bf16 original keys
  *   nv       [B] int32 or NULL (= S)
- *   shortlist[B, m]      int32 output or NULL: the stage-1 shortlist, canonical order
- *   idx      [B, k]      int32 output: the final selection, canonical order
+ *   shortlist[B, m]      int32 output or NULL: the stage-1 shortlist, ascending key index
+ *   idx      [B, k]      int32 output: the final selection, ascending key index
  *   val      [B, k]      fp64 output or NULL: the exact scores of idx
  *
  * Stage 1 projects each query head with P (fp64 fma chain over d), quantises it

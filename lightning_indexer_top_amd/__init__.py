@@ -5,7 +5,7 @@ on torch's current stream.  torch provides device memory and streams.  The
 functions mirror the C entry points of include/li.h:
 
     indexer_score          scores of every key for every query row
-    topk_select            the k best keys per row, canonical order
+    topk_select            the k best keys per row, listed in ascending key index
     indexer_topk           scoring + selection without returning the scores
     compact_search_rerank  compact-key shortlist + exact rerank
     sparse_attn_gather     attention over only the selected latent rows

@@ -13,7 +13,8 @@
 //           (fp64 fma chain over h ascending), shortlist = top-m of s1;
 //   stage 2 s2 = chain_h(w_h, max(chain_j(q_hj, k_sj), 0)) over the shortlisted
 //           original bf16 keys (fp64 fma chains, ascending), result = top-k of s2.
-// Selections order by (score desc, key index asc).
+// A selection keeps the best entries by (score desc, key index asc) and lists them
+// in ascending key index.
 #include "common.h"
 #include "launch.h"
 

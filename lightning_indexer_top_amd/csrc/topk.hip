@@ -109,8 +109,8 @@ struct Sel {
 __device__ __forceinline__ bool sel_greater(const Sel& a, const Sel& b) { return a.inv_id > b.inv_id; }
 
 // Exact selection of the k best of row[0..n) (ids: idrow, or the position) by one
-// workgroup of TK_THREADS threads; results in canonical order into idx_out[0..k)
-// and val_out[0..k).
+// workgroup of TK_THREADS threads; results in ascending id order into
+// idx_out[0..k) and val_out[0..k).
 template <typename S>
 __device__ void select_block(const S* __restrict__ row, const int32_t* __restrict__ idrow, int n, int k,
                              int32_t* __restrict__ idx_out, S* __restrict__ val_out) {
@@ -217,7 +217,7 @@ __device__ void select_block(const S* __restrict__ row, const int32_t* __restric
   while (P2 < cnt) P2 <<= 1;
   for (int i = cnt + tid; i < P2; i += TK_THREADS) list[i] = Sel{0, 0};
   __syncthreads();
-  // bitonic sort, descending
+  // bitonic sort by id, ascending
   for (int size = 2; size <= P2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = tid; i < P2 / 2; i += TK_THREADS) {
