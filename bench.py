@@ -15,6 +15,8 @@ secondary: the other workloads (prefill chunk, compact search, select-and-attend
 each timed the same way, reported beside the main line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--main-only]
+       python bench.py --workload prefill_chunk|compact_search|select_attend [--steps K]
+         (one secondary workload alone, e.g. under a profiler; prints its own JSON line)
 """
 import argparse
 import ctypes
@@ -230,6 +232,8 @@ def bench_select_attend(torch, li, workloads, steps, warmup):
     for b in range(B):
         workloads.latent_seq(sp, b, out=buf)
         lat[b].copy_(torch.from_numpy(buf.view(np.int16)).view(torch.bfloat16))
+        if (b + 1) % 16 == 0:
+            log(f"[select_attend] {b + 1} of {B} sequences written")
     qa = to_dev(torch, workloads.attn_query(sp), "bf16")
     scores = torch.empty((B, S), dtype=torch.float32, device="cuda")
     idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
@@ -271,6 +275,9 @@ def bench_select_attend(torch, li, workloads, steps, warmup):
     return res
 
 
+SECONDARY = {"prefill_chunk": bench_prefill, "compact_search": bench_compact, "select_attend": bench_select_attend}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +287,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run four plain 1 GiB device copies (calibrates the HBM byte counters)")
+    ap.add_argument("--workload", choices=sorted(SECONDARY), default=None,
+                    help="only time this secondary workload and print its result")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the hot path is not sharded across "
@@ -303,6 +312,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": 1 << 30, "copies": 4}))
+        return
+    if args.workload:
+        res = SECONDARY[args.workload](torch, li, workloads, args.steps, args.warmup)
+        print(json.dumps(dict(res, steps=args.steps, warmup=args.warmup)), flush=True)
         return
     dec = bench_decode(torch, li, workloads, args.steps, args.warmup)
     ms = dec["ms"]
@@ -330,8 +343,7 @@ def main():
     del dec
     if not args.main_only:
         sec = {}
-        for name, fn in (("prefill_chunk", bench_prefill), ("compact_search", bench_compact),
-                         ("select_attend", bench_select_attend)):
+        for name, fn in SECONDARY.items():
             try:
                 sec[name] = fn(torch, li, workloads, max(3, args.steps // 2), 2)
             except Exception as e:  # report, keep the main line

@@ -270,55 +270,78 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restric
 // (checked), the k best are among them.  A row whose estimate misses, or keeps
 // more entries than the final sort holds, falls back to the exact single-workgroup
 // selection over the whole row, so the result is always the exact top-k.
-//   1. one wave per row estimates tau as the j-th largest of m = min(n, 1024)
-//      samples (16 evenly spaced runs of 64 entries; bisection on the orderable
-//      bits, counting with ballots), j ~ 2 k m / n + 8;
+//   1. one workgroup per row estimates tau as the j-th largest of m = min(n, 8192)
+//      evenly strided samples, j = max(ceil((2k + 1024) m / n), 16): about 2k + 1024
+//      entries (at least 16 sample gaps) should clear it, with a relative spread
+//      of 1/sqrt(j);
 //   2. many workgroups per row append every entry with ord >= tau to the
 //      workgroup's own region of the list (no global atomics, nothing to clear);
-//   3. one workgroup per row gathers the regions and sorts them, or selects over
-//      the whole row.
+//   3. one workgroup per row selects exactly among the kept entries, or over the
+//      whole row.
+// Both k-th searches are radix selects over LDS histograms (11-bit digits).
 constexpr int MB_THREADS = 256;
-constexpr int MB_SAMPLES = 1024;
+constexpr int MB_SAMPLES = 8192;
 constexpr int MB_BATCH = 16;  // loads in flight per thread
+constexpr int MB_KEEP = 8192;  // kept entries the exact final pass holds
 
-__device__ uint32_t sample_threshold(const float* __restrict__ row, int n, int k) {
-  // one wave; returns the largest t with count(sample >= t) >= j
-  const int lane = threadIdx.x & 63;
-  const int m = min(n, MB_SAMPLES);
-  // 16 runs of 64 consecutive entries spread evenly over the row (each load is one
-  // contiguous 256-byte read); when n < 1024 every entry is a sample
-  uint32_t key[MB_SAMPLES / 64];
+// The kth largest (1-based) of the valid keys, E per thread over a workgroup of
+// TK_THREADS threads; *n_above receives how many valid keys exceed it.
+template <int E>
+__device__ __forceinline__ uint32_t block_kth_u32(const uint32_t (&key)[E], const bool (&valid)[E], uint32_t kth,
+                                                  uint32_t* hist, uint32_t* sh_scan, int* sh_res,
+                                                  uint32_t* n_above) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0u, mask = 0u, need = kth;
+  int shift = 32;
+  while (shift > 0) {
+    const int width = shift >= 11 ? 11 : shift;
+    shift -= width;
+    const uint32_t dmask = (1u << width) - 1;
+    for (int i = tid; i < TK_BINS; i += TK_THREADS) hist[i] = 0;
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < MB_SAMPLES / 64; ++i) {
-    const int64_t start = (n >= MB_SAMPLES) ? (int64_t)i * (n - 64) / (MB_SAMPLES / 64 - 1) : 64 * i;
-    const int64_t pos = start + lane;
-    key[i] = (64 * i + lane < m && pos < n) ? ord_f32(row[pos]) : 0u;
+    for (int e = 0; e < E; ++e) hist_add(hist, (key[e] >> shift) & dmask, valid[e] && (key[e] & mask) == prefix);
+    __syncthreads();
+    uint32_t above;
+    const int d = find_cut(hist, need, &above, sh_scan, sh_res);
+    prefix |= (uint32_t)d << shift;
+    mask |= dmask << shift;
+    need -= above;
   }
-  int j = (int)(((int64_t)2 * k * m + n - 1) / n) + 8;
-  if (j > m) j = m;
-  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
-  while (lo < hi) {
-    const uint32_t mid = lo + (uint32_t)(((uint64_t)(hi - lo) + 1) >> 1);
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < MB_SAMPLES / 64; ++i) c += __popcll(__ballot(key[i] >= mid));
-    if (c >= j) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+  *n_above = kth - need;
+  return prefix;
 }
 
-__global__ __launch_bounds__(64) void topk_thresh_kernel(const float* __restrict__ scores,
-                                                        const int32_t* __restrict__ nv, int S, int k,
-                                                        uint32_t* __restrict__ tau) {
-  const int r = blockIdx.x;
+__global__ __launch_bounds__(TK_THREADS) void topk_thresh_kernel(const float* __restrict__ scores,
+                                                                const int32_t* __restrict__ nv, int S, int k,
+                                                                uint32_t* __restrict__ tau) {
+  constexpr int E = MB_SAMPLES / TK_THREADS;
+  __shared__ uint32_t hist[TK_BINS];
+  __shared__ uint32_t sh_scan[64];
+  __shared__ int sh_res[2];
+  const int r = blockIdx.x, tid = threadIdx.x;
   int n = S;
   if (nv) n = min(max(nv[r], 0), S);
-  if (n <= k) {
-    if (threadIdx.x == 0) tau[r] = 0u;
+  if (n <= k) {  // every entry is kept
+    if (tid == 0) tau[r] = 0u;
     return;
   }
-  const uint32_t t = sample_threshold(scores + (int64_t)r * S, n, k);
-  if (threadIdx.x == 0) tau[r] = t;
+  const float* row = scores + (int64_t)r * S;
+  const int m = min(n, MB_SAMPLES);
+  uint32_t key[E];
+  bool valid[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid + TK_THREADS * e;  // sample i sits at floor(i n / m)
+    valid[e] = i < m;
+    key[e] = valid[e] ? ord_f32(row[(int64_t)i * n / m]) : 0u;
+  }
+  int64_t j = ((int64_t)(2 * k + 1024) * m + n - 1) / n;
+  if (j < 16) j = 16;
+  if (j > m) j = m;
+  uint32_t n_above;
+  const uint32_t t = block_kth_u32<E>(key, valid, (uint32_t)j, hist, sh_scan, sh_res, &n_above);
+  if (tid == 0) tau[r] = t;
 }
 
 // Exclusive prefix sum of x over the workgroup (blockDim.x = NW * 64), in thread
@@ -406,11 +429,10 @@ __global__ __launch_bounds__(MB_THREADS) void topk_filter_kernel(const float* __
 }
 
 // Exact selection over the kept entries (at most MB_KEEP, in index order): the
-// k-th best orderable score T by bisection (ballot counts), then every entry
-// above T and the first (k - count above T) entries equal to T, written in index
-// order at positions from a prefix scan.  Rows whose list cannot be used take the
+// k-th best orderable score T by radix select, then every entry above T and the
+// first (k - count above T) entries equal to T, written in index order at
+// positions from a prefix scan.  Rows whose list cannot be used take the
 // whole-row path.
-constexpr int MB_KEEP = 4096;
 
 __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const float* __restrict__ scores,
                                                                   const int32_t* __restrict__ nv, int S, int k,
@@ -423,9 +445,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const float* 
   constexpr int NW = TK_THREADS / 64;
   constexpr int E = MB_KEEP / TK_THREADS;
   __shared__ uint32_t off[257];
-  __shared__ uint32_t part[2][NW];
   __shared__ uint32_t scan1[NW], scan2[NW];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ uint32_t hist[TK_BINS];
+  __shared__ uint32_t sh_scan[64];
+  __shared__ int sh_res[2];
+  const int r = blockIdx.x, tid = threadIdx.x;
   int n = S;
   if (nv) n = min(max(nv[r], 0), S);
   // exclusive prefix of the region counts (P <= 256): one wave, four per lane
@@ -484,38 +508,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const float* 
       key[e] = ord_f32(val[e]);
     }
   }
-  // T: the largest t with count(key >= t) >= k
-  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
-  int it = 0;
-  while (lo < hi) {
-    const uint32_t mid = lo + (uint32_t)(((uint64_t)(hi - lo) + 1) >> 1);
-    uint32_t cw = 0;
+  // T: the k-th best kept key; n_gt entries lie above it
+  uint32_t n_gt;
+  const uint32_t T = block_kth_u32<E>(key, valid, (uint32_t)k, hist, sh_scan, sh_res, &n_gt);
+  uint32_t ties = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) cw += (uint32_t)__popcll(__ballot(valid[e] && key[e] >= mid));
-    if (lane == 0) part[it & 1][wid] = cw;
-    __syncthreads();
-    uint32_t tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) tot += part[it & 1][w];
-    if (tot >= (uint32_t)k) lo = mid; else hi = mid - 1;
-    ++it;
-  }
-  const uint32_t T = lo;
-  uint32_t gt = 0, ties = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    gt += valid[e] && key[e] > T ? 1u : 0u;
-    ties += valid[e] && key[e] == T ? 1u : 0u;
-  }
-  // entries above T (all selected) and the rank of this thread's first tie
-  uint32_t gw = gt;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) gw += __shfl_xor(gw, o, 64);
-  if (lane == 0) part[it & 1][wid] = gw;
+  for (int e = 0; e < E; ++e) ties += valid[e] && key[e] == T ? 1u : 0u;
+  // rank of this thread's first tie in index order
   const uint32_t tie_rank0 = block_exclusive_scan<NW>(ties, scan1);
-  uint32_t n_gt = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) n_gt += part[it & 1][w];
   const uint32_t need = (uint32_t)k - n_gt;  // ties taken, smallest index first
   bool sel[E];
   uint32_t tr = tie_rank0, nsel = 0;
@@ -566,7 +566,7 @@ hipError_t launch_topk_mb(const float* scores, const int32_t* nv, int R, int S, 
   int32_t* cid = (int32_t*)p;
   const int P = mb_chunks(R, S);
   const int chunk = (S + P - 1) / P;
-  topk_thresh_kernel<<<R, 64, 0, st>>>(scores, nv, S, k, tau);
+  topk_thresh_kernel<<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, tau);
   topk_filter_kernel<<<dim3(P, R), MB_THREADS, 0, st>>>(scores, nv, S, k, chunk, tau, cval, cid, bcnt);
   topk_finalize_kernel<<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val);
   return hipGetLastError();
