@@ -91,7 +91,7 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t d, bool valid)
   const uint64_t act = __ballot(valid);
   if (!act) return;
   const int first = __ffsll((unsigned long long)act) - 1;
-  const uint32_t d0 = __shfl(d, first, 64);
+  const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, first);  // first is wave-uniform
   const uint64_t same = __ballot(valid && d == d0);
   if (same == act) {
     if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[d0], (uint32_t)__popcll(act));
@@ -270,56 +270,84 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restric
 // (checked), the k best are among them.  A row whose estimate misses, or keeps
 // more entries than the final sort holds, falls back to the exact single-workgroup
 // selection over the whole row, so the result is always the exact top-k.
-//   1. one workgroup per row estimates tau as the j-th largest of m = min(n, 8192)
-//      evenly strided samples, j = max(ceil((2k + 1024) m / n), 16): about 2k + 1024
-//      entries (at least 16 sample gaps) should clear it, with a relative spread
-//      of 1/sqrt(j);
+//   1. one workgroup per row estimates tau as the j-th largest of m = min(n, 4096)
+//      samples (64 runs of 64 consecutive entries spread evenly over the row:
+//      16 KB read), j = max(ceil((2k + 1024) m / n), 16): about 2k + 1024 entries
+//      (at least 16 sample gaps) should clear it, with a relative spread of
+//      1/sqrt(j); the estimate needs only the top 16 key bits;
 //   2. many workgroups per row append every entry with ord >= tau to the
 //      workgroup's own region of the list (no global atomics, nothing to clear);
 //   3. one workgroup per row selects exactly among the kept entries, or over the
 //      whole row.
 // Both k-th searches are radix selects over LDS histograms (11-bit digits).
 constexpr int MB_THREADS = 256;
-constexpr int MB_SAMPLES = 8192;
+constexpr int MB_SAMPLES = 4096;
 constexpr int MB_BATCH = 16;  // loads in flight per thread
 constexpr int MB_KEEP = 8192;  // kept entries the exact final pass holds
 
-// The kth largest (1-based) of the valid keys, E per thread over a workgroup of
-// TK_THREADS threads; *n_above receives how many valid keys exceed it.
-template <int E>
-__device__ __forceinline__ uint32_t block_kth_u32(const uint32_t (&key)[E], const bool (&valid)[E], uint32_t kth,
-                                                  uint32_t* hist, uint32_t* sh_scan, int* sh_res,
-                                                  uint32_t* n_above) {
-  const int tid = threadIdx.x;
+// The kth largest (1-based) of the valid keys held E per thread over a workgroup
+// of NT >= 256 threads, by PASSES 8-bit digits from the top (LDS histograms of
+// 256 bins).  With fewer than 4 passes the unresolved low bits come back zero:
+// the result is then the lower edge of the bucket holding the kth largest, so at
+// least kth keys are >= it.  With 4 passes *n_above receives how many valid keys
+// exceed the result.
+template <int NT, int E, int PASSES>
+__device__ __forceinline__ uint32_t block_kth8(const uint32_t (&key)[E], const bool (&valid)[E], uint32_t kth,
+                                               uint32_t* hist, uint32_t* wsum, uint32_t* res,
+                                               uint32_t* n_above = nullptr) {
+  static_assert(NT >= 256 && NT % 64 == 0, "one thread per bin");
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   uint32_t prefix = 0u, mask = 0u, need = kth;
-  int shift = 32;
-  while (shift > 0) {
-    const int width = shift >= 11 ? 11 : shift;
-    shift -= width;
-    const uint32_t dmask = (1u << width) - 1;
-    for (int i = tid; i < TK_BINS; i += TK_THREADS) hist[i] = 0;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int shift = 24 - 8 * p;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < E; ++e) hist_add(hist, (key[e] >> shift) & dmask, valid[e] && (key[e] & mask) == prefix);
+    for (int e = 0; e < E; ++e) hist_add(hist, (key[e] >> shift) & 255u, valid[e] && (key[e] & mask) == prefix);
     __syncthreads();
-    uint32_t above;
-    const int d = find_cut(hist, need, &above, sh_scan, sh_res);
-    prefix |= (uint32_t)d << shift;
-    mask |= dmask << shift;
+    // counts of digits 255, 254, ... accumulated in that order
+    const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;
+    uint32_t v = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t u = __shfl_up(v, o, 64);
+      if (lane >= o) v += u;
+    }
+    if (lane == 63) wsum[wid] = v;
+    __syncthreads();
+    uint32_t base = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) base += w < wid ? wsum[w] : 0u;
+    const uint32_t incl = base + v, excl = incl - c;
+    if (tid < 256 && excl < need && need <= incl) {
+      res[0] = 255u - (uint32_t)tid;
+      res[1] = excl;
+    }
+    __syncthreads();
+    const uint32_t d = res[0], above = res[1];
+    __syncthreads();
+    prefix |= d << shift;
+    mask |= 255u << shift;
     need -= above;
   }
-  *n_above = kth - need;
+  if (n_above) *n_above = kth - need;
   return prefix;
 }
+
+constexpr int MB_RUNS = 64;  // sample runs of 64 entries
 
 __global__ __launch_bounds__(TK_THREADS) void topk_thresh_kernel(const float* __restrict__ scores,
                                                                 const int32_t* __restrict__ nv, int S, int k,
                                                                 uint32_t* __restrict__ tau) {
-  constexpr int E = MB_SAMPLES / TK_THREADS;
-  __shared__ uint32_t hist[TK_BINS];
-  __shared__ uint32_t sh_scan[64];
-  __shared__ int sh_res[2];
-  const int r = blockIdx.x, tid = threadIdx.x;
+  constexpr int NW = TK_THREADS / 64;
+  constexpr int E = MB_RUNS * 64 / TK_THREADS;
+  static_assert(MB_RUNS * 64 == MB_SAMPLES, "sample count");
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wsum[NW];
+  __shared__ uint32_t res[2];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int n = S;
   if (nv) n = min(max(nv[r], 0), S);
   if (n <= k) {  // every entry is kept
@@ -327,20 +355,24 @@ __global__ __launch_bounds__(TK_THREADS) void topk_thresh_kernel(const float* __
     return;
   }
   const float* row = scores + (int64_t)r * S;
-  const int m = min(n, MB_SAMPLES);
+  const bool runs = n >= MB_SAMPLES;
+  const int m = runs ? MB_SAMPLES : n;
+  const int step = runs ? (n - 64) / (MB_RUNS - 1) : 64;  // run starts: the last at most n - 64
   uint32_t key[E];
   bool valid[E];
+  // unconditional loads at clamped positions, so all of them are in flight at once
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = row[min((NW * e + wid) * step + lane, n - 1)];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int i = tid + TK_THREADS * e;  // sample i sits at floor(i n / m)
-    valid[e] = i < m;
-    key[e] = valid[e] ? ord_f32(row[(int64_t)i * n / m]) : 0u;
+    valid[e] = (NW * e + wid) * step + lane < n;
+    key[e] = valid[e] ? ord_f32(x[e]) : 0u;
   }
   int64_t j = ((int64_t)(2 * k + 1024) * m + n - 1) / n;
   if (j < 16) j = 16;
   if (j > m) j = m;
-  uint32_t n_above;
-  const uint32_t t = block_kth_u32<E>(key, valid, (uint32_t)j, hist, sh_scan, sh_res, &n_above);
+  const uint32_t t = block_kth8<TK_THREADS, E, 2>(key, valid, (uint32_t)j, hist, wsum, res);
   if (tid == 0) tau[r] = t;
 }
 
@@ -446,9 +478,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const float* 
   constexpr int E = MB_KEEP / TK_THREADS;
   __shared__ uint32_t off[257];
   __shared__ uint32_t scan1[NW], scan2[NW];
-  __shared__ uint32_t hist[TK_BINS];
-  __shared__ uint32_t sh_scan[64];
-  __shared__ int sh_res[2];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wsum8[NW];
+  __shared__ uint32_t res8[2];
   const int r = blockIdx.x, tid = threadIdx.x;
   int n = S;
   if (nv) n = min(max(nv[r], 0), S);
@@ -489,34 +521,32 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const float* 
   float val[E];
   int32_t id[E];
   bool valid[E];
+  // every load is issued (entries past the list read entry 0) before any is used
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const uint32_t j = (uint32_t)(E * tid + e);
-    valid[e] = j < c;
-    key[e] = 0u;
-    val[e] = 0.0f;
-    id[e] = 0;
-    if (valid[e]) {
-      int lo2 = 0, hi2 = P - 1;  // region b with off[b] <= j < off[b+1]
-      while (lo2 < hi2) {
-        const int mid = (lo2 + hi2 + 1) >> 1;
-        if (off[mid] <= j) lo2 = mid; else hi2 = mid - 1;
-      }
-      const int64_t src = (int64_t)r * S + (int64_t)lo2 * chunk + (j - off[lo2]);
-      val[e] = cval[src];
-      id[e] = cid[src];
-      key[e] = ord_f32(val[e]);
+    const uint32_t j0 = (uint32_t)(E * tid + e);
+    valid[e] = j0 < c;
+    const uint32_t j = valid[e] ? j0 : 0u;
+    int lo2 = 0, hi2 = P - 1;  // region b with off[b] <= j < off[b+1]
+    while (lo2 < hi2) {
+      const int mid = (lo2 + hi2 + 1) >> 1;
+      if (off[mid] <= j) lo2 = mid; else hi2 = mid - 1;
     }
+    const int64_t src = (int64_t)r * S + (int64_t)lo2 * chunk + (j - off[lo2]);
+    val[e] = cval[src];
+    id[e] = cid[src];
   }
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = valid[e] ? ord_f32(val[e]) : 0u;
   // T: the k-th best kept key; n_gt entries lie above it
-  uint32_t n_gt;
-  const uint32_t T = block_kth_u32<E>(key, valid, (uint32_t)k, hist, sh_scan, sh_res, &n_gt);
+  uint32_t n_gt_all;
+  const uint32_t T = block_kth8<TK_THREADS, E, 4>(key, valid, (uint32_t)k, hist, wsum8, res8, &n_gt_all);
   uint32_t ties = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) ties += valid[e] && key[e] == T ? 1u : 0u;
   // rank of this thread's first tie in index order
   const uint32_t tie_rank0 = block_exclusive_scan<NW>(ties, scan1);
-  const uint32_t need = (uint32_t)k - n_gt;  // ties taken, smallest index first
+  const uint32_t need = (uint32_t)k - n_gt_all;  // ties taken, smallest index first
   bool sel[E];
   uint32_t tr = tie_rank0, nsel = 0;
 #pragma unroll
