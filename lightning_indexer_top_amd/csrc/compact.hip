@@ -45,80 +45,163 @@ __global__ __launch_bounds__(64) void compact_query_kernel(const uint16_t* __res
   if (i == 0) W[bh] = (double)w[bh] * s;
 }
 
-// One thread per key: exact int8 dots, fp64 head chain.
+// Stage 1.  A wave scores 64 keys at a time: the exact int32 dots D[h][s] of the
+// int8 query block (A operand, in VGPRs) against 32 compact keys (B operand) come
+// from v_mfma_i32_32x32x32_i8, 32 heads per instruction (a query row and a
+// compact key are one K = 32 step).  The accumulator tiles go to LDS transposed
+// (key rows padded to an odd word count, so neither side conflicts), and then
+// every lane runs the fp64 head chain of one key in ascending head order.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+template <int HT>
 __global__ __launch_bounds__(256) void compact_stage1_kernel(const int8_t* __restrict__ q8,
                                                              const double* __restrict__ W,
                                                              const int8_t* __restrict__ ck,
-                                                             const float* __restrict__ cks, int S, int H,
+                                                             const float* __restrict__ cks, int S, int H, int kpb,
                                                              double* __restrict__ s1) {
-  __shared__ int sq[128 * DC / 4];
-  __shared__ double sw[128];
+  constexpr int RS = 32 * HT + 1;  // LDS row stride (words) of one key's head dots
+  __shared__ int32_t dt[4][64 * RS];
+  __shared__ double sW[32 * HT];
   const int b = blockIdx.y;
-  for (int i = threadIdx.x; i < H * DC / 4; i += blockDim.x) sq[i] = ((const int*)(q8 + (int64_t)b * H * DC))[i];
-  for (int i = threadIdx.x; i < H; i += blockDim.x) sw[i] = W[(int64_t)b * H + i];
-  __syncthreads();
-  const int s = blockIdx.x * blockDim.x + threadIdx.x;
-  if (s >= S) return;
-  const int64_t row = (int64_t)b * S + s;
-  const uint4* cp = (const uint4*)(ck + row * DC);
-  const uint4 c0 = cp[0], c1 = cp[1];
-  const int cw[8] = {(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w, (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
-  double acc = 0.0;
-  for (int h = 0; h < H; ++h) {
-    int D = 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hf = lane >> 5, col = lane & 31;
+  for (int h = tid; h < 32 * HT; h += 256) sW[h] = h < H ? W[(int64_t)b * H + h] : 0.0;
+  // A operand: head ht*32 + col, query bytes [16 hf, 16 hf + 16)
+  i32x4 a[HT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) D = __builtin_amdgcn_sdot4(sq[h * 8 + i], cw[i], D, false);
-    acc = fma(sw[h], (double)(D > 0 ? D : 0), acc);
+  for (int ht = 0; ht < HT; ++ht) {
+    const int h = ht * 32 + col;
+    a[ht] = h < H ? *(const i32x4*)(q8 + ((int64_t)b * H + h) * DC + 16 * hf) : i32x4{0, 0, 0, 0};
   }
-  s1[row] = (double)cks[row] * acc;
+  __syncthreads();
+  int32_t* dw = dt[wave];
+  const int key0 = blockIdx.x * kpb, kend = min(key0 + kpb, S);
+  const int8_t* cbase = ck + (int64_t)b * S * DC;
+  for (int kb = key0 + 64 * wave; kb < kend; kb += 256) {
+    i32x4 bc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) bc[u] = *(const i32x4*)(cbase + (int64_t)min(kb + 32 * u + col, S - 1) * DC + 16 * hf);
+    const float csv = cks[(int64_t)b * S + min(kb + lane, S - 1)];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ht], bc[u], i32x16{}, 0, 0, 0);
+        // accumulator element (head i, key col): i = 8 (r >> 2) + 4 hf + (r & 3)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dw[(32 * u + col) * RS + ht * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)] = d[r];
+      }
+    }
+    // the wave's LDS operations run in order: every write above lands before the
+    // reads below, which land before the next iteration's writes
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    double acc = 0.0;
+    for (int h = 0; h < H; ++h) {
+      const int32_t dv = dw[lane * RS + h];
+      acc = fma(sW[h], (double)(dv > 0 ? dv : 0), acc);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (kb + lane < kend) s1[(int64_t)b * S + kb + lane] = (double)csv * acc;
+  }
 }
 
-// One thread per shortlisted candidate: exact fp64 rescoring.
-__global__ __launch_bounds__(256) void compact_stage2_kernel(const uint16_t* __restrict__ q,
-                                                             const float* __restrict__ w,
-                                                             const uint16_t* __restrict__ kf,
-                                                             const int32_t* __restrict__ sl,
-                                                             const int32_t* __restrict__ nv, int S, int H, int m,
-                                                             double* __restrict__ s2, int32_t* __restrict__ cnt) {
-  extern __shared__ double sqd[];  // [H * 128] query as fp64, then [H] weights
+// Stage 2.  Four lanes (a quad) per shortlisted candidate: lane g of the quad
+// computes the dots of heads g, g + 4, g + 8, ... (U per lane), eight fp64 fma
+// chains over the 128 dimensions at a time, ascending, against the query block
+// held as fp64 in LDS (rows padded to 129 doubles, so the quad's four heads sit
+// in different banks).  The candidate's bf16 key stays in VGPRs and each element
+// is widened once per eight FMAs.  The head chain then runs in ascending head
+// order in all four lanes, each step taking its dot from the owning lane with a
+// quad broadcast (DPP).
+constexpr int S2_THREADS = 256;
+constexpr int S2_QROW = 129;  // LDS row stride of the query block, doubles
+
+template <int G>
+__device__ __forceinline__ double quad_bcast(double v) {
+  const int64_t x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)x, G * 0x55, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(x >> 32), G * 0x55, 0xF, 0xF, false);
+  return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
+}
+
+template <int U>
+__global__ __launch_bounds__(S2_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void compact_stage2_kernel(const uint16_t* __restrict__ q,
+                                                                    const float* __restrict__ w,
+                                                                    const uint16_t* __restrict__ kf,
+                                                                    const int32_t* __restrict__ sl,
+                                                                    const int32_t* __restrict__ nv, int S, int H, int m,
+                                                                    double* __restrict__ s2, int32_t* __restrict__ cnt) {
+  static_assert(U % 8 == 0, "eight chains at a time");
+  extern __shared__ double sqd[];  // [4 U][S2_QROW] query as fp64 (zero past H), then [4 U] weights
+  constexpr int HP = 4 * U;
   const int b = blockIdx.y;
-  for (int i = threadIdx.x; i < H * 128; i += blockDim.x) sqd[i] = (double)bf16_to_f32(q[(int64_t)b * H * 128 + i]);
-  for (int i = threadIdx.x; i < H; i += blockDim.x) sqd[H * 128 + i] = (double)w[(int64_t)b * H + i];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < HP * 128; i += S2_THREADS) {
+    const int h = i >> 7, j = i & 127;
+    sqd[h * S2_QROW + j] = h < H ? (double)bf16_to_f32(q[((int64_t)b * H + h) * 128 + j]) : 0.0;
+  }
+  double* sw = sqd + HP * S2_QROW;
+  for (int i = tid; i < HP; i += S2_THREADS) sw[i] = i < H ? (double)w[(int64_t)b * H + i] : 0.0;
   __syncthreads();
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c == 0) {
+  const int c = blockIdx.x * (S2_THREADS / 4) + (tid >> 2), g = tid & 3;
+  if (c == 0 && g == 0) {
     int n = S;
     if (nv) n = min(max(nv[b], 0), S);
     cnt[b] = min(n, m);
   }
-  if (c >= m) return;
-  const int id = sl[(int64_t)b * m + c];
-  if (id < 0 || id >= S) {
-    s2[(int64_t)b * m + c] = -INFINITY;
-    return;
-  }
-  const uint4* kp = (const uint4*)(kf + ((int64_t)b * S + id) * 128);
+  const int cc = min(c, m - 1);  // lanes past the shortlist recompute its last entry and store nothing
+  const int id = sl[(int64_t)b * m + cc];
+  const bool valid = id >= 0 && id < S;
+  const uint4* kp = (const uint4*)(kf + ((int64_t)b * S + (valid ? id : 0)) * 128);
   uint4 kr[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) kr[i] = kp[i];
-  double acc = 0.0;
-  for (int h = 0; h < H; ++h) {
-    const double* qh = sqd + h * 128;
-    double dot = 0.0;
+  double dot[U];
+#pragma unroll
+  for (int ug = 0; ug < U; ug += 8) {
+    // groups of eight heads one after the other: the packed key counts as
+    // rewritten here, so no work of this group moves into the previous one
+#pragma unroll
+    for (int i = 0; i < 16; i += 4)
+      asm volatile("" : "+v"(kr[i].x), "+v"(kr[i].y), "+v"(kr[i].z), "+v"(kr[i].w), "+v"(kr[i + 1].x),
+                   "+v"(kr[i + 1].y), "+v"(kr[i + 1].z), "+v"(kr[i + 1].w), "+v"(kr[i + 2].x), "+v"(kr[i + 2].y),
+                   "+v"(kr[i + 2].z), "+v"(kr[i + 2].w), "+v"(kr[i + 3].x), "+v"(kr[i + 3].y), "+v"(kr[i + 3].z),
+                   "+v"(kr[i + 3].w));
+    const double* qrow = sqd + (4 * ug + g) * S2_QROW;  // head 4 (ug + t) + g is row 4 t ahead
+    double d[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t wds[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const double k0 = (double)__uint_as_float(wds[e] << 16);
-        const double k1 = (double)__uint_as_float(wds[e] & 0xFFFF0000u);
-        dot = fma(qh[8 * i + 2 * e], k0, dot);
-        dot = fma(qh[8 * i + 2 * e + 1], k1, dot);
+      for (int e = 0; e < 8; ++e) {
+        const int j = 8 * i + e;
+        const uint32_t bits = (e & 1) ? (wds[e >> 1] & 0xFFFF0000u) : (wds[e >> 1] << 16);
+        const double kv = (double)__uint_as_float(bits);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) d[t] = fma(qrow[4 * t * S2_QROW + j], kv, d[t]);
+        // advance the chains together, four elements at a time (one after the
+        // other they would keep every widened key value and query operand live)
+        if ((e & 3) == 3)
+          asm volatile("" : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]), "+v"(d[4]), "+v"(d[5]), "+v"(d[6]),
+                       "+v"(d[7]));
       }
     }
-    acc = fma(sqd[H * 128 + h], dot > 0.0 ? dot : 0.0, acc);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) dot[ug + t] = d[t];
   }
-  s2[(int64_t)b * m + c] = acc;
+  double acc = 0.0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int h = 4 * u;
+    const double x0 = quad_bcast<0>(dot[u]), x1 = quad_bcast<1>(dot[u]);
+    const double x2 = quad_bcast<2>(dot[u]), x3 = quad_bcast<3>(dot[u]);
+    if (h < H) acc = fma(sw[h], x0 > 0.0 ? x0 : 0.0, acc);
+    if (h + 1 < H) acc = fma(sw[h + 1], x1 > 0.0 ? x1 : 0.0, acc);
+    if (h + 2 < H) acc = fma(sw[h + 2], x2 > 0.0 ? x2 : 0.0, acc);
+    if (h + 3 < H) acc = fma(sw[h + 3], x3 > 0.0 ? x3 : 0.0, acc);
+  }
+  if (g == 0 && c < m) s2[(int64_t)b * m + c] = valid ? acc : -INFINITY;
 }
 
 size_t compact_ws_bytes(int B, int S, int H, int m, int k) {
@@ -130,7 +213,16 @@ size_t compact_ws_bytes(int B, int S, int H, int m, int k) {
   n += align256((size_t)B * m * 4);           // shortlist
   n += align256((size_t)B * m * 8);           // s2
   n += align256((size_t)B * 4);               // cnt
+  n += align256(topk_f64_rows_ws_bytes(B, S));  // shortlist selection
   return n;
+}
+
+static int stage1_keys_per_block(int B, int S) {
+  int per_row = (1024 + B - 1) / B;  // about four workgroups per CU in all
+  if (per_row < 1) per_row = 1;
+  int kpb = (S + per_row - 1) / per_row;
+  kpb = ((kpb + 255) / 256) * 256;
+  return kpb < 256 ? 256 : kpb;
 }
 
 hipError_t launch_compact(const uint16_t* q, const float* w, const float* P, const int8_t* ck, const float* cks,
@@ -148,21 +240,43 @@ hipError_t launch_compact(const uint16_t* q, const float* w, const float* P, con
   double* s2 = (double*)p;
   p += align256((size_t)B * m * 8);
   int32_t* cnt = (int32_t*)p;
+  p += align256((size_t)B * 4);
+  void* tk_ws = p;
   int32_t* sl = shortlist ? shortlist : sl_ws;
 
   compact_query_kernel<<<B * H, 64, 0, st>>>(q, w, P, H, q8, W);
-  compact_stage1_kernel<<<dim3((S + 255) / 256, B), 256, 0, st>>>(q8, W, ck, cks, S, H, s1);
-  hipError_t e = launch_topk_f64(s1, S, nv, nullptr, B, S, m, sl, nullptr, st);
+  const int kpb = stage1_keys_per_block(B, S);
+  const dim3 g1((S + kpb - 1) / kpb, B);
+  if (H <= 32)
+    compact_stage1_kernel<1><<<g1, 256, 0, st>>>(q8, W, ck, cks, S, H, kpb, s1);
+  else if (H <= 64)
+    compact_stage1_kernel<2><<<g1, 256, 0, st>>>(q8, W, ck, cks, S, H, kpb, s1);
+  else
+    compact_stage1_kernel<4><<<g1, 256, 0, st>>>(q8, W, ck, cks, S, H, kpb, s1);
+  hipError_t e = launch_topk_f64_rows(s1, nv, B, S, m, sl, nullptr, tk_ws, st);
   if (e != hipSuccess) return e;
-  const size_t lds = sizeof(double) * (size_t)H * 129;
   static const bool attr_set = [] {
-    // H <= 128 needs up to 132 KB of dynamic LDS (the query in fp64)
-    (void)hipFuncSetAttribute((const void*)compact_stage2_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+    // 128 heads need 130 KB of dynamic LDS (the query block in fp64)
+    (void)hipFuncSetAttribute((const void*)compact_stage2_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    (void)hipFuncSetAttribute((const void*)compact_stage2_kernel<16>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    (void)hipFuncSetAttribute((const void*)compact_stage2_kernel<32>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
     return true;
   }();
   (void)attr_set;
-  compact_stage2_kernel<<<dim3((m + 255) / 256, B), 256, lds, st>>>(q, w, kf, sl, nv, S, H, m, s2, cnt);
+  const dim3 g2((m + S2_THREADS / 4 - 1) / (S2_THREADS / 4), B);
+#define LI_STAGE2(U_)                                                                                    \
+  compact_stage2_kernel<U_><<<g2, S2_THREADS, sizeof(double) * (size_t)(4 * U_) * (S2_QROW + 1), st>>>( \
+      q, w, kf, sl, nv, S, H, m, s2, cnt)
+  if (H <= 32)
+    LI_STAGE2(8);
+  else if (H <= 64)
+    LI_STAGE2(16);
+  else
+    LI_STAGE2(32);
+#undef LI_STAGE2
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topk_f64(s2, m, cnt, sl, B, m, k, idx, val, st);

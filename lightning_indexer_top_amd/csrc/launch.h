@@ -25,6 +25,12 @@ hipError_t launch_topk_f32(const float* scores, const int32_t* nv, int R, int S,
 hipError_t launch_topk_f64(const double* scores, int64_t row_stride, const int32_t* nv, const int32_t* ids, int R,
                            int S, int k, int32_t* idx, double* val, hipStream_t st);
 
+// per-row top-k of dense fp64 scores [R, S] (ids = positions); few long rows take
+// the many-workgroups-per-row path, whose buffers ws holds
+size_t topk_f64_rows_ws_bytes(int R, int S);
+hipError_t launch_topk_f64_rows(const double* scores, const int32_t* nv, int R, int S, int k, int32_t* idx,
+                                double* val, void* ws, hipStream_t st);
+
 // two-stage compact search (workspace layout in compact.hip)
 size_t compact_ws_bytes(int B, int S, int H, int m, int k);
 hipError_t launch_compact(const uint16_t* q, const float* w, const float* P, const int8_t* ck, const float* cks,

@@ -291,21 +291,23 @@ constexpr int MB_KEEP = 8192;  // kept entries the exact final pass holds
 // the result is then the lower edge of the bucket holding the kth largest, so at
 // least kth keys are >= it.  With 4 passes *n_above receives how many valid keys
 // exceed the result.
-template <int NT, int E, int PASSES>
-__device__ __forceinline__ uint32_t block_kth8(const uint32_t (&key)[E], const bool (&valid)[E], uint32_t kth,
-                                               uint32_t* hist, uint32_t* wsum, uint32_t* res,
-                                               uint32_t* n_above = nullptr) {
+template <int NT, int E, int PASSES, typename K>
+__device__ __forceinline__ K block_kth8(const K (&key)[E], const bool (&valid)[E], uint32_t kth, uint32_t* hist,
+                                        uint32_t* wsum, uint32_t* res, uint32_t* n_above = nullptr) {
   static_assert(NT >= 256 && NT % 64 == 0, "one thread per bin");
   constexpr int NW = NT / 64;
+  constexpr int BITS = 8 * (int)sizeof(K);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  uint32_t prefix = 0u, mask = 0u, need = kth;
+  K prefix = 0, mask = 0;
+  uint32_t need = kth;
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
-    const int shift = 24 - 8 * p;
+    const int shift = BITS - 8 - 8 * p;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < E; ++e) hist_add(hist, (key[e] >> shift) & 255u, valid[e] && (key[e] & mask) == prefix);
+    for (int e = 0; e < E; ++e)
+      hist_add(hist, (uint32_t)(key[e] >> shift) & 255u, valid[e] && (key[e] & mask) == prefix);
     __syncthreads();
     // counts of digits 255, 254, ... accumulated in that order
     const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;
@@ -328,8 +330,8 @@ __device__ __forceinline__ uint32_t block_kth8(const uint32_t (&key)[E], const b
     __syncthreads();
     const uint32_t d = res[0], above = res[1];
     __syncthreads();
-    prefix |= d << shift;
-    mask |= 255u << shift;
+    prefix |= (K)d << shift;
+    mask |= (K)255 << shift;
     need -= above;
   }
   if (n_above) *n_above = kth - need;
@@ -338,9 +340,11 @@ __device__ __forceinline__ uint32_t block_kth8(const uint32_t (&key)[E], const b
 
 constexpr int MB_RUNS = 64;  // sample runs of 64 entries
 
-__global__ __launch_bounds__(TK_THREADS) void topk_thresh_kernel(const float* __restrict__ scores,
+template <typename Sc>
+__global__ __launch_bounds__(TK_THREADS) void topk_thresh_kernel(const Sc* __restrict__ scores,
                                                                 const int32_t* __restrict__ nv, int S, int k,
-                                                                uint32_t* __restrict__ tau) {
+                                                                typename ScoreTraits<Sc>::K* __restrict__ tau) {
+  typedef typename ScoreTraits<Sc>::K K;
   constexpr int NW = TK_THREADS / 64;
   constexpr int E = MB_RUNS * 64 / TK_THREADS;
   static_assert(MB_RUNS * 64 == MB_SAMPLES, "sample count");
@@ -351,28 +355,29 @@ __global__ __launch_bounds__(TK_THREADS) void topk_thresh_kernel(const float* __
   int n = S;
   if (nv) n = min(max(nv[r], 0), S);
   if (n <= k) {  // every entry is kept
-    if (tid == 0) tau[r] = 0u;
+    if (tid == 0) tau[r] = 0;
     return;
   }
-  const float* row = scores + (int64_t)r * S;
+  const Sc* row = scores + (int64_t)r * S;
   const bool runs = n >= MB_SAMPLES;
   const int m = runs ? MB_SAMPLES : n;
   const int step = runs ? (n - 64) / (MB_RUNS - 1) : 64;  // run starts: the last at most n - 64
-  uint32_t key[E];
+  K key[E];
   bool valid[E];
   // unconditional loads at clamped positions, so all of them are in flight at once
-  float x[E];
+  Sc x[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) x[e] = row[min((NW * e + wid) * step + lane, n - 1)];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     valid[e] = (NW * e + wid) * step + lane < n;
-    key[e] = valid[e] ? ord_f32(x[e]) : 0u;
+    key[e] = valid[e] ? ScoreTraits<Sc>::ord(x[e]) : (K)0;
   }
   int64_t j = ((int64_t)(2 * k + 1024) * m + n - 1) / n;
   if (j < 16) j = 16;
   if (j > m) j = m;
-  const uint32_t t = block_kth8<TK_THREADS, E, 2>(key, valid, (uint32_t)j, hist, wsum, res);
+  // the top 16 key bits of a float (sign, exponent, 7 mantissa bits), 24 of a double
+  const K t = block_kth8<TK_THREADS, E, sizeof(K) == 4 ? 2 : 3>(key, valid, (uint32_t)j, hist, wsum, res);
   if (tid == 0) tau[r] = t;
 }
 
@@ -400,11 +405,14 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* s
 // holds entries base + tid + 256 u (u < MB_BATCH), so ordering by (u, wave, lane)
 // is index order; each wave's ballots give the counts, one prefix over the
 // (u, wave) counts gives every lane its position.
-__global__ __launch_bounds__(MB_THREADS) void topk_filter_kernel(const float* __restrict__ scores,
+template <typename Sc>
+__global__ __launch_bounds__(MB_THREADS) void topk_filter_kernel(const Sc* __restrict__ scores,
                                                                 const int32_t* __restrict__ nv, int S, int k,
-                                                                int chunk, const uint32_t* __restrict__ tau,
-                                                                float* __restrict__ cval, int32_t* __restrict__ cid,
+                                                                int chunk,
+                                                                const typename ScoreTraits<Sc>::K* __restrict__ tau,
+                                                                Sc* __restrict__ cval, int32_t* __restrict__ cid,
                                                                 uint32_t* __restrict__ bcnt) {
+  typedef typename ScoreTraits<Sc>::K K;
   constexpr int NW = MB_THREADS / 64;
   __shared__ uint32_t cnt_uw[MB_BATCH * NW + 1];
   const int r = blockIdx.y, p = blockIdx.x, P = gridDim.x, tid = threadIdx.x;
@@ -415,24 +423,24 @@ __global__ __launch_bounds__(MB_THREADS) void topk_filter_kernel(const float* __
     if (tid == 0) bcnt[(int64_t)r * P + p] = 0u;
     return;
   }
-  const float* row = scores + (int64_t)r * S;
+  const Sc* row = scores + (int64_t)r * S;
   const int lo = p * chunk, hi = min(lo + chunk, n);
-  const uint32_t t = tau[r];
-  float* ov = cval + (int64_t)r * S + lo;  // this workgroup's region
+  const K t = tau[r];
+  Sc* ov = cval + (int64_t)r * S + lo;  // this workgroup's region
   int32_t* oi = cid + (int64_t)r * S + lo;
   uint32_t written = 0;
   for (int base = lo; base < hi; base += MB_THREADS * MB_BATCH) {
-    float x[MB_BATCH];
+    Sc x[MB_BATCH];
 #pragma unroll
     for (int u = 0; u < MB_BATCH; ++u) {
       const int i = base + tid + MB_THREADS * u;
-      x[u] = i < hi ? row[i] : -INFINITY;
+      x[u] = i < hi ? row[i] : (Sc)-INFINITY;
     }
     uint64_t mk[MB_BATCH];
 #pragma unroll
     for (int u = 0; u < MB_BATCH; ++u) {
       const int i = base + tid + MB_THREADS * u;
-      mk[u] = __ballot(i < hi && ord_f32(x[u]) >= t);
+      mk[u] = __ballot(i < hi && ScoreTraits<Sc>::ord(x[u]) >= t);
       if (lane == 0) cnt_uw[u * NW + wid] = (uint32_t)__popcll(mk[u]);
     }
     __syncthreads();
@@ -466,14 +474,16 @@ __global__ __launch_bounds__(MB_THREADS) void topk_filter_kernel(const float* __
 // positions from a prefix scan.  Rows whose list cannot be used take the
 // whole-row path.
 
-__global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const float* __restrict__ scores,
+template <typename Sc>
+__global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __restrict__ scores,
                                                                   const int32_t* __restrict__ nv, int S, int k,
                                                                   int P, int chunk,
                                                                   const uint32_t* __restrict__ bcnt,
-                                                                  const float* __restrict__ cval,
+                                                                  const Sc* __restrict__ cval,
                                                                   const int32_t* __restrict__ cid,
                                                                   int32_t* __restrict__ idx_out,
-                                                                  float* __restrict__ val_out) {
+                                                                  Sc* __restrict__ val_out) {
+  typedef typename ScoreTraits<Sc>::K K;
   constexpr int NW = TK_THREADS / 64;
   constexpr int E = MB_KEEP / TK_THREADS;
   __shared__ uint32_t off[257];
@@ -510,15 +520,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const float* 
   __syncthreads();
   const uint32_t c = off[P];
   int32_t* io = idx_out + (int64_t)r * k;
-  float* vo = val_out ? val_out + (int64_t)r * k : nullptr;
+  Sc* vo = val_out ? val_out + (int64_t)r * k : nullptr;
   // the list is usable when at least k entries cleared the threshold
   if (n <= k || c < (uint32_t)k || c > (uint32_t)MB_KEEP) {
-    select_block<float>(scores + (int64_t)r * S, nullptr, n, k, io, vo);
+    select_block<Sc>(scores + (int64_t)r * S, nullptr, n, k, io, vo);
     return;
   }
   // entries E*tid .. E*tid+E-1 of the concatenated regions (index order)
-  uint32_t key[E];
-  float val[E];
+  K key[E];
+  Sc val[E];
   int32_t id[E];
   bool valid[E];
   // every load is issued (entries past the list read entry 0) before any is used
@@ -537,10 +547,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const float* 
     id[e] = cid[src];
   }
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = valid[e] ? ord_f32(val[e]) : 0u;
+  for (int e = 0; e < E; ++e) key[e] = valid[e] ? ScoreTraits<Sc>::ord(val[e]) : (K)0;
   // T: the k-th best kept key; n_gt entries lie above it
   uint32_t n_gt_all;
-  const uint32_t T = block_kth8<TK_THREADS, E, 4>(key, valid, (uint32_t)k, hist, wsum8, res8, &n_gt_all);
+  const K T = block_kth8<TK_THREADS, E, (int)sizeof(K)>(key, valid, (uint32_t)k, hist, wsum8, res8, &n_gt_all);
   uint32_t ties = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) ties += valid[e] && key[e] == T ? 1u : 0u;
@@ -577,36 +587,41 @@ static int mb_chunks(int R, int S) {
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t topk_mb_ws_bytes(int R, int S, int k) {
-  (void)k;
-  return a256((size_t)R * 4) + a256((size_t)R * 256 * 4) + a256((size_t)R * S * 4) * 2;
+template <typename Sc>
+static size_t topk_mb_ws_bytes(int R, int S) {
+  return a256((size_t)R * 8) + a256((size_t)R * 256 * 4) + a256((size_t)R * S * sizeof(Sc)) + a256((size_t)R * S * 4);
 }
 
 bool topk_use_mb(int R, int S) { return R < 160 && S >= 16384; }
 
-hipError_t launch_topk_mb(const float* scores, const int32_t* nv, int R, int S, int k, int32_t* idx, float* val,
-                          void* ws, hipStream_t st) {
+template <typename Sc>
+static hipError_t launch_topk_mb(const Sc* scores, const int32_t* nv, int R, int S, int k, int32_t* idx, Sc* val,
+                                 void* ws, hipStream_t st) {
+  typedef typename ScoreTraits<Sc>::K K;
   uint8_t* p = (uint8_t*)ws;
-  uint32_t* tau = (uint32_t*)p;
-  p += a256((size_t)R * 4);
+  K* tau = (K*)p;
+  p += a256((size_t)R * 8);
   uint32_t* bcnt = (uint32_t*)p;
   p += a256((size_t)R * 256 * 4);
-  float* cval = (float*)p;
-  p += a256((size_t)R * S * 4);
+  Sc* cval = (Sc*)p;
+  p += a256((size_t)R * S * sizeof(Sc));
   int32_t* cid = (int32_t*)p;
   const int P = mb_chunks(R, S);
   const int chunk = (S + P - 1) / P;
-  topk_thresh_kernel<<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, tau);
-  topk_filter_kernel<<<dim3(P, R), MB_THREADS, 0, st>>>(scores, nv, S, k, chunk, tau, cval, cid, bcnt);
-  topk_finalize_kernel<<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val);
+  topk_thresh_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, tau);
+  topk_filter_kernel<Sc><<<dim3(P, R), MB_THREADS, 0, st>>>(scores, nv, S, k, chunk, tau, cval, cid, bcnt);
+  topk_finalize_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val);
   return hipGetLastError();
 }
 
-size_t topk_ws_bytes(int R, int S, int k) { return topk_use_mb(R, S) ? topk_mb_ws_bytes(R, S, k) : 0; }
+size_t topk_ws_bytes(int R, int S, int k) {
+  (void)k;
+  return topk_use_mb(R, S) ? topk_mb_ws_bytes<float>(R, S) : 0;
+}
 
 hipError_t launch_topk_f32(const float* scores, const int32_t* nv, int R, int S, int k, int32_t* idx, float* val,
                            void* ws, hipStream_t st) {
-  if (topk_use_mb(R, S)) return launch_topk_mb(scores, nv, R, S, k, idx, val, ws, st);
+  if (topk_use_mb(R, S)) return launch_topk_mb<float>(scores, nv, R, S, k, idx, val, ws, st);
   topk_row_kernel<float><<<R, TK_THREADS, 0, st>>>(scores, S, nv, nullptr, S, k, idx, val);
   return hipGetLastError();
 }
@@ -615,6 +630,14 @@ hipError_t launch_topk_f64(const double* scores, int64_t row_stride, const int32
                            int S, int k, int32_t* idx, double* val, hipStream_t st) {
   topk_row_kernel<double><<<R, TK_THREADS, 0, st>>>(scores, row_stride, nv, ids, S, k, idx, val);
   return hipGetLastError();
+}
+
+size_t topk_f64_rows_ws_bytes(int R, int S) { return topk_use_mb(R, S) ? topk_mb_ws_bytes<double>(R, S) : 0; }
+
+hipError_t launch_topk_f64_rows(const double* scores, const int32_t* nv, int R, int S, int k, int32_t* idx,
+                                double* val, void* ws, hipStream_t st) {
+  if (topk_use_mb(R, S)) return launch_topk_mb<double>(scores, nv, R, S, k, idx, val, ws, st);
+  return launch_topk_f64(scores, S, nv, nullptr, R, S, k, idx, val, st);
 }
 
 }  // namespace li
