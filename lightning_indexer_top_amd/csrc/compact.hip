@@ -46,27 +46,25 @@ __global__ __launch_bounds__(64) void compact_query_kernel(const uint16_t* __res
 }
 
 // Stage 1.  A wave scores 64 keys at a time: the exact int32 dots D[h][s] of the
-// int8 query block (A operand, in VGPRs) against 32 compact keys (B operand) come
-// from v_mfma_i32_32x32x32_i8, 32 heads per instruction (a query row and a
-// compact key are one K = 32 step).  The accumulator tiles go to LDS transposed
-// (key rows padded to an odd word count, so neither side conflicts), and then
-// every lane runs the fp64 head chain of one key in ascending head order.
+// int8 query block (A operand, in VGPRs) against two tiles of 32 compact keys (B
+// operand) come from v_mfma_i32_32x32x32_i8, 32 heads per instruction (a query
+// row and a compact key are one K = 32 step).  In the accumulator lane (s, half)
+// holds half of the heads of key s; one v_permlane32_swap per register pair
+// trades the second tile's low half for the first tile's high half, after which
+// lane l holds every head dot of key l of the 64, and runs that key's fp64 head
+// chain in ascending head order from registers.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 template <int HT>
-__global__ __launch_bounds__(256) void compact_stage1_kernel(const int8_t* __restrict__ q8,
-                                                             const double* __restrict__ W,
-                                                             const int8_t* __restrict__ ck,
-                                                             const float* __restrict__ cks, int S, int H, int kpb,
-                                                             double* __restrict__ s1) {
-  constexpr int RS = 32 * HT + 1;  // LDS row stride (words) of one key's head dots
-  __shared__ int32_t dt[4][64 * RS];
-  __shared__ double sW[32 * HT];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void compact_stage1_kernel(
+    const int8_t* __restrict__ q8, const double* __restrict__ W, const int8_t* __restrict__ ck,
+    const float* __restrict__ cks, int S, int H, int kpb, double* __restrict__ s1) {
+  constexpr bool WREG = HT <= 2;  // head weights in VGPRs (up to 64 heads), else LDS broadcasts
+  __shared__ __attribute__((aligned(16))) double sW[WREG ? 2 : 32 * HT];
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, col = lane & 31;
-  for (int h = tid; h < 32 * HT; h += 256) sW[h] = h < H ? W[(int64_t)b * H + h] : 0.0;
   // A operand: head ht*32 + col, query bytes [16 hf, 16 hf + 16)
   i32x4 a[HT];
 #pragma unroll
@@ -74,48 +72,87 @@ __global__ __launch_bounds__(256) void compact_stage1_kernel(const int8_t* __res
     const int h = ht * 32 + col;
     a[ht] = h < H ? *(const i32x4*)(q8 + ((int64_t)b * H + h) * DC + 16 * hf) : i32x4{0, 0, 0, 0};
   }
-  __syncthreads();
-  int32_t* dw = dt[wave];
+  double wr[WREG ? 32 * HT : 1];
+  if constexpr (WREG) {
+    // a lane-dependent zero keeps the (uniform) weights in VGPRs rather than SGPRs
+    const int z = __builtin_amdgcn_mbcnt_lo(0u, 0u);
+#pragma unroll
+    for (int h = 0; h < 32 * HT; ++h) wr[h] = h < H ? W[(int64_t)b * H + h + z] : 0.0;
+  } else {
+    for (int h = tid; h < 32 * HT; h += 256) sW[h] = h < H ? W[(int64_t)b * H + h] : 0.0;
+    __syncthreads();
+  }
   const int key0 = blockIdx.x * kpb, kend = min(key0 + kpb, S);
   const int8_t* cbase = ck + (int64_t)b * S * DC;
-  for (int kb = key0 + 64 * wave; kb < kend; kb += 256) {
-    i32x4 bc[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) bc[u] = *(const i32x4*)(cbase + (int64_t)min(kb + 32 * u + col, S - 1) * DC + 16 * hf);
-    const float csv = cks[(int64_t)b * S + min(kb + lane, S - 1)];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        const i32x16 d = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ht], bc[u], i32x16{}, 0, 0, 0);
-        // accumulator element (head i, key col): i = 8 (r >> 2) + 4 hf + (r & 3)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dw[(32 * u + col) * RS + ht * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)] = d[r];
-      }
-    }
-    // the wave's LDS operations run in order: every write above lands before the
-    // reads below, which land before the next iteration's writes
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    double acc = 0.0;
-    for (int h = 0; h < H; ++h) {
-      const int32_t dv = dw[lane * RS + h];
-      acc = fma(sW[h], (double)(dv > 0 ? dv : 0), acc);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    if (kb + lane < kend) s1[(int64_t)b * S + kb + lane] = (double)csv * acc;
+  const float* sbase = cks + (int64_t)b * S;
+  // the next 64-key tile is loaded while this one is scored (compact keys and
+  // scales in VGPRs); loads past the range read the last key and are not used
+#define LI_S1_LOAD(X, kb)                                                                      \
+  do {                                                                                         \
+    X##0 = *(const i32x4*)(cbase + (int64_t)min((kb) + col, S - 1) * DC + 16 * hf);            \
+    X##1 = *(const i32x4*)(cbase + (int64_t)min((kb) + 32 + col, S - 1) * DC + 16 * hf);       \
+    X##s = sbase[min((kb) + lane, S - 1)];                                                     \
+  } while (0)
+#define LI_S1_TILE(X, kb)                                                                                      \
+  do {                                                                                                         \
+    double acc = 0.0;                                                                                          \
+    _Pragma("unroll") for (int ht = 0; ht < HT; ++ht) {                                                        \
+      i32x16 d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ht], X##0, i32x16{}, 0, 0, 0);                       \
+      i32x16 d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ht], X##1, i32x16{}, 0, 0, 0);                       \
+      /* register r of a tile holds head 8 (r >> 2) + 4 hf + (r & 3); after the swap */                        \
+      /* d0 holds heads 8 (r >> 2) + (r & 3) and d1 heads 8 (r >> 2) + 4 + (r & 3)  */                         \
+      /* of key lane (tile 0 in lanes 0..31, tile 1 in lanes 32..63) */                                         \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                                          \
+        const auto sw2 = __builtin_amdgcn_permlane32_swap((unsigned)d0[r], (unsigned)d1[r], false, false);    \
+        d0[r] = (int)sw2[0];                                                                                    \
+        d1[r] = (int)sw2[1];                                                                                    \
+      }                                                                                                        \
+      _Pragma("unroll") for (int g4 = 0; g4 < 4; ++g4) {                                                        \
+        /* the group's dots count as depending on the running sum, so they are */                               \
+        /* widened when the chain reaches them (not all at once, ahead of it) */                                \
+        asm volatile("" : "+v"(d0[4 * g4]), "+v"(d0[4 * g4 + 1]), "+v"(d0[4 * g4 + 2]), "+v"(d0[4 * g4 + 3]),   \
+                     "+v"(d1[4 * g4]), "+v"(d1[4 * g4 + 1]), "+v"(d1[4 * g4 + 2]), "+v"(d1[4 * g4 + 3])         \
+                     : "v"(acc));                                                                              \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                                         \
+          const int h = 32 * ht + 8 * g4 + e;                                                                  \
+          const int dv = e < 4 ? d0[4 * g4 + e] : d1[4 * g4 + e - 4];                                           \
+          double wh;                                                                                           \
+          if constexpr (WREG) wh = wr[h]; else wh = sW[h];                                                      \
+          acc = fma(wh, (double)(dv > 0 ? dv : 0), acc); /* heads past H: fma(0, 0, acc) == acc */             \
+        }                                                                                                      \
+      }                                                                                                        \
+      /* the next head group's MFMAs stay after this group's chain */                                          \
+      asm volatile("" : "+v"(X##0), "+v"(X##1));                                                               \
+    }                                                                                                          \
+    if ((kb) + lane < kend) s1[(int64_t)b * S + (kb) + lane] = (double)X##s * acc;                             \
+  } while (0)
+  i32x4 A0, A1, B0, B1;
+  float As, Bs;
+  int kb = key0 + 64 * wave;
+  LI_S1_LOAD(A, kb);
+  for (; kb < kend; kb += 512) {
+    LI_S1_LOAD(B, kb + 256);
+    LI_S1_TILE(A, kb);
+    if (kb + 256 >= kend) break;
+    LI_S1_LOAD(A, kb + 512);
+    LI_S1_TILE(B, kb + 256);
   }
+#undef LI_S1_LOAD
+#undef LI_S1_TILE
 }
 
-// Stage 2.  Four lanes (a quad) per shortlisted candidate: lane g of the quad
-// computes the dots of heads g, g + 4, g + 8, ... (U per lane), eight fp64 fma
-// chains over the 128 dimensions at a time, ascending, against the query block
-// held as fp64 in LDS (rows padded to 129 doubles, so the quad's four heads sit
-// in different banks).  The candidate's bf16 key stays in VGPRs and each element
-// is widened once per eight FMAs.  The head chain then runs in ascending head
-// order in all four lanes, each step taking its dot from the owning lane with a
-// quad broadcast (DPP).
+// Stage 2.  A quad of lanes serves two shortlisted candidates: lane g computes,
+// for both, the dots of heads g, g + 4, g + 8, ..., eight heads at a time, each
+// an fp64 fma chain over the 128 dimensions in ascending order, against the
+// query block held as fp64 in LDS (rows padded to 129 doubles, so the quad's four
+// heads sit in different banks); every query operand read serves both candidates.
+// The keys stay in VGPRs as bf16 and each element is widened once per eight
+// FMAs.  After each group of eight heads per lane (32 consecutive heads) the head
+// chain advances over those heads in ascending order in all four lanes, each step
+// taking its dot from the owning lane with a quad broadcast (DPP).
 constexpr int S2_THREADS = 256;
 constexpr int S2_QROW = 129;  // LDS row stride of the query block, doubles
+constexpr int S2_CPB = S2_THREADS / 2;  // candidates per workgroup
 
 template <int G>
 __device__ __forceinline__ double quad_bcast(double v) {
@@ -125,14 +162,17 @@ __device__ __forceinline__ double quad_bcast(double v) {
   return __longlong_as_double(((int64_t)hi << 32) | (uint32_t)lo);
 }
 
+#define LI_TOUCH4(v, i)                                                                                     \
+  asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w), "+v"(v[i + 1].x), "+v"(v[i + 1].y), \
+               "+v"(v[i + 1].z), "+v"(v[i + 1].w), "+v"(v[i + 2].x), "+v"(v[i + 2].y), "+v"(v[i + 2].z),       \
+               "+v"(v[i + 2].w), "+v"(v[i + 3].x), "+v"(v[i + 3].y), "+v"(v[i + 3].z), "+v"(v[i + 3].w))
+
 template <int U>
-__global__ __launch_bounds__(S2_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void compact_stage2_kernel(const uint16_t* __restrict__ q,
-                                                                    const float* __restrict__ w,
-                                                                    const uint16_t* __restrict__ kf,
-                                                                    const int32_t* __restrict__ sl,
-                                                                    const int32_t* __restrict__ nv, int S, int H, int m,
-                                                                    double* __restrict__ s2, int32_t* __restrict__ cnt) {
-  static_assert(U % 8 == 0, "eight chains at a time");
+__global__ __launch_bounds__(S2_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void compact_stage2_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ kf,
+    const int32_t* __restrict__ sl, const int32_t* __restrict__ nv, int S, int H, int m, double* __restrict__ s2,
+    int32_t* __restrict__ cnt) {
+  static_assert(U % 8 == 0, "eight heads per lane at a time");
   extern __shared__ double sqd[];  // [4 U][S2_QROW] query as fp64 (zero past H), then [4 U] weights
   constexpr int HP = 4 * U;
   const int b = blockIdx.y;
@@ -144,65 +184,75 @@ __global__ __launch_bounds__(S2_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
   double* sw = sqd + HP * S2_QROW;
   for (int i = tid; i < HP; i += S2_THREADS) sw[i] = i < H ? (double)w[(int64_t)b * H + i] : 0.0;
   __syncthreads();
-  const int c = blockIdx.x * (S2_THREADS / 4) + (tid >> 2), g = tid & 3;
-  if (c == 0 && g == 0) {
+  const int c0 = blockIdx.x * S2_CPB + 2 * (tid >> 2), g = tid & 3;
+  if (c0 == 0 && g == 0) {
     int n = S;
     if (nv) n = min(max(nv[b], 0), S);
     cnt[b] = min(n, m);
   }
-  const int cc = min(c, m - 1);  // lanes past the shortlist recompute its last entry and store nothing
-  const int id = sl[(int64_t)b * m + cc];
-  const bool valid = id >= 0 && id < S;
-  const uint4* kp = (const uint4*)(kf + ((int64_t)b * S + (valid ? id : 0)) * 128);
-  uint4 kr[16];
+  // lanes past the shortlist recompute its last entry and store nothing
+  const int id0 = sl[(int64_t)b * m + min(c0, m - 1)], id1 = sl[(int64_t)b * m + min(c0 + 1, m - 1)];
+  const bool v0 = id0 >= 0 && id0 < S, v1 = id1 >= 0 && id1 < S;
+  const uint4* kp0 = (const uint4*)(kf + ((int64_t)b * S + (v0 ? id0 : 0)) * 128);
+  const uint4* kp1 = (const uint4*)(kf + ((int64_t)b * S + (v1 ? id1 : 0)) * 128);
+  uint4 k0[16], k1[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) kr[i] = kp[i];
-  double dot[U];
+  for (int i = 0; i < 16; ++i) {
+    k0[i] = kp0[i];
+    k1[i] = kp1[i];
+  }
+  double acc0 = 0.0, acc1 = 0.0;
 #pragma unroll
   for (int ug = 0; ug < U; ug += 8) {
-    // groups of eight heads one after the other: the packed key counts as
-    // rewritten here, so no work of this group moves into the previous one
-#pragma unroll
-    for (int i = 0; i < 16; i += 4)
-      asm volatile("" : "+v"(kr[i].x), "+v"(kr[i].y), "+v"(kr[i].z), "+v"(kr[i].w), "+v"(kr[i + 1].x),
-                   "+v"(kr[i + 1].y), "+v"(kr[i + 1].z), "+v"(kr[i + 1].w), "+v"(kr[i + 2].x), "+v"(kr[i + 2].y),
-                   "+v"(kr[i + 2].z), "+v"(kr[i + 2].w), "+v"(kr[i + 3].x), "+v"(kr[i + 3].y), "+v"(kr[i + 3].z),
-                   "+v"(kr[i + 3].w));
+    // groups of eight heads one after the other: the keys count as rewritten
+    // here, so no work of this group moves into the previous one
+    LI_TOUCH4(k0, 0); LI_TOUCH4(k0, 4); LI_TOUCH4(k0, 8); LI_TOUCH4(k0, 12);
+    LI_TOUCH4(k1, 0); LI_TOUCH4(k1, 4); LI_TOUCH4(k1, 8); LI_TOUCH4(k1, 12);
     const double* qrow = sqd + (4 * ug + g) * S2_QROW;  // head 4 (ug + t) + g is row 4 t ahead
-    double d[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    double d0[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    double d1[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint32_t wds[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+      const uint32_t w0[4] = {k0[i].x, k0[i].y, k0[i].z, k0[i].w};
+      const uint32_t w1[4] = {k1[i].x, k1[i].y, k1[i].z, k1[i].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = 8 * i + e;
-        const uint32_t bits = (e & 1) ? (wds[e >> 1] & 0xFFFF0000u) : (wds[e >> 1] << 16);
-        const double kv = (double)__uint_as_float(bits);
+        const uint32_t b0 = (e & 1) ? (w0[e >> 1] & 0xFFFF0000u) : (w0[e >> 1] << 16);
+        const uint32_t b1 = (e & 1) ? (w1[e >> 1] & 0xFFFF0000u) : (w1[e >> 1] << 16);
+        const double kv0 = (double)__uint_as_float(b0), kv1 = (double)__uint_as_float(b1);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) d[t] = fma(qrow[4 * t * S2_QROW + j], kv, d[t]);
-        // advance the chains together, four elements at a time (one after the
-        // other they would keep every widened key value and query operand live)
-        if ((e & 3) == 3)
-          asm volatile("" : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3]), "+v"(d[4]), "+v"(d[5]), "+v"(d[6]),
-                       "+v"(d[7]));
+        for (int t = 0; t < 8; ++t) {
+          const double qv = qrow[4 * t * S2_QROW + j];
+          d0[t] = fma(qv, kv0, d0[t]);
+          d1[t] = fma(qv, kv1, d1[t]);
+        }
+        // advance all chains together, two elements at a time (run one after
+        // the other they would keep every widened key value and query operand live)
+        if (e & 1)
+          asm volatile("" : "+v"(d0[0]), "+v"(d0[1]), "+v"(d0[2]), "+v"(d0[3]), "+v"(d0[4]), "+v"(d0[5]),
+                       "+v"(d0[6]), "+v"(d0[7]), "+v"(d1[0]), "+v"(d1[1]), "+v"(d1[2]), "+v"(d1[3]), "+v"(d1[4]),
+                       "+v"(d1[5]), "+v"(d1[6]), "+v"(d1[7]));
       }
     }
+    // head chain over heads 4 ug .. 4 ug + 31, ascending
 #pragma unroll
-    for (int t = 0; t < 8; ++t) dot[ug + t] = d[t];
+    for (int t = 0; t < 8; ++t) {
+      const int h = 4 * (ug + t);
+#define LI_STEP(G_)                                                             \
+  if (h + G_ < H) {                                                             \
+    const double x0 = quad_bcast<G_>(d0[t]), x1 = quad_bcast<G_>(d1[t]);       \
+    acc0 = fma(sw[h + G_], x0 > 0.0 ? x0 : 0.0, acc0);                          \
+    acc1 = fma(sw[h + G_], x1 > 0.0 ? x1 : 0.0, acc1);                          \
   }
-  double acc = 0.0;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int h = 4 * u;
-    const double x0 = quad_bcast<0>(dot[u]), x1 = quad_bcast<1>(dot[u]);
-    const double x2 = quad_bcast<2>(dot[u]), x3 = quad_bcast<3>(dot[u]);
-    if (h < H) acc = fma(sw[h], x0 > 0.0 ? x0 : 0.0, acc);
-    if (h + 1 < H) acc = fma(sw[h + 1], x1 > 0.0 ? x1 : 0.0, acc);
-    if (h + 2 < H) acc = fma(sw[h + 2], x2 > 0.0 ? x2 : 0.0, acc);
-    if (h + 3 < H) acc = fma(sw[h + 3], x3 > 0.0 ? x3 : 0.0, acc);
+      LI_STEP(0) LI_STEP(1) LI_STEP(2) LI_STEP(3)
+#undef LI_STEP
+    }
   }
-  if (g == 0 && c < m) s2[(int64_t)b * m + c] = valid ? acc : -INFINITY;
+  if (g == 0 && c0 < m) s2[(int64_t)b * m + c0] = v0 ? acc0 : -INFINITY;
+  if (g == 0 && c0 + 1 < m) s2[(int64_t)b * m + c0 + 1] = v1 ? acc1 : -INFINITY;
 }
+#undef LI_TOUCH4
 
 size_t compact_ws_bytes(int B, int S, int H, int m, int k) {
   (void)k;
@@ -266,7 +316,7 @@ hipError_t launch_compact(const uint16_t* q, const float* w, const float* P, con
     return true;
   }();
   (void)attr_set;
-  const dim3 g2((m + S2_THREADS / 4 - 1) / (S2_THREADS / 4), B);
+  const dim3 g2((m + S2_CPB - 1) / S2_CPB, B);
 #define LI_STAGE2(U_)                                                                                    \
   compact_stage2_kernel<U_><<<g2, S2_THREADS, sizeof(double) * (size_t)(4 * U_) * (S2_QROW + 1), st>>>( \
       q, w, kf, sl, nv, S, H, m, s2, cnt)
