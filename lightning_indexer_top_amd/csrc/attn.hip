@@ -24,15 +24,26 @@ constexpr int AT_DQK = 576;
 constexpr int AT_DV = 512;
 constexpr int AT_CH = 32;      // rows per chunk
 constexpr int AT_ROWB = 1168;  // LDS bytes per row (1152 + 16 padding)
+constexpr int AT_KMAX = 2048;  // selected rows per sequence at most
+constexpr int AT_GU = AT_CH * 72 / 256;  // 16-byte pieces per thread per chunk
+static_assert(AT_CH * 72 == AT_GU * 256, "whole pieces per thread");
+
+// the value of x held by the other lane half (lane l +- 32)
+__device__ __forceinline__ float other_half(float x, int hf) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(hf ? r[0] : r[1]);
+}
 
 __global__ __launch_bounds__(256) void sparse_attn_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ kv,
                                                           const int32_t* __restrict__ idx, int B, int Hq, int S, int k,
                                                           float tau, uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) uint8_t skv[AT_CH * AT_ROWB];
+  // two chunk buffers: the rows of chunk c + 1 are loaded (into VGPRs) while
+  // chunk c is computed, and stored into the other buffer after it
+  __shared__ __attribute__((aligned(16))) uint8_t skv2[2][AT_CH * AT_ROWB];
   __shared__ float spart[4][16][64];
-  __shared__ int svalid[AT_CH];
+  __shared__ int sidx[AT_KMAX];
 
   // block -> (sequence, head tile): the head tiles of one sequence land on blocks
   // 8 apart, which the dispatcher places on the same XCD, so they share its L2.
@@ -56,101 +67,137 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const uint16_t* __rest
     qb[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(qrow + 16 * g + 8 * hf));
   }
 
+  // softmax in base 2: exp(tau x - m) == 2^(tau log2(e) x - m / ln 2)
+  const float tau2 = tau * 1.4426950408889634f;
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16 o[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) o[t] = (f32x16){};
 
+  // the selected rows' indices, -1 for entries that select nothing
   const int32_t* irow = idx + (int64_t)b * k;
-  for (int c0 = 0; c0 < k; c0 += AT_CH) {
-    // gather 32 rows (72 x 16 B each) into LDS
-    for (int ci = tid; ci < AT_CH * 72; ci += 256) {
-      const int r = ci / 72, part = ci - r * 72;
-      const int id = (c0 + r < k) ? irow[c0 + r] : -1;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (id >= 0 && id < S) v = ((const uint4*)(kv + ((int64_t)b * S + id) * AT_DQK))[part];
-      *(uint4*)(skv + r * AT_ROWB + part * 16) = v;
-    }
-    if (tid < AT_CH) {
-      const int id = (c0 + tid < k) ? irow[c0 + tid] : -1;
-      svalid[tid] = (id >= 0 && id < S);
-    }
-    __syncthreads();
-
-    // partial S^T over this wave's K-steps
-    f32x16 s = {};
-#pragma unroll
-    for (int kk = 0; kk < 9; ++kk) {
-      const int g = 9 * wave + kk;
-      const bf16x8 a = __builtin_bit_cast(bf16x8, *(const uint4*)(skv + col * AT_ROWB + 2 * (16 * g + 8 * hf)));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[kk], s, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) spart[wave][r][lane] = s[r];
-    __syncthreads();
-
-    float st[16];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = (r & 3) + 8 * (r >> 2) + 4 * hf;
-      float x = spart[0][r][lane] + spart[1][r][lane] + spart[2][r][lane] + spart[3][r][lane];
-      x = svalid[row] ? x * tau : -INFINITY;
-      st[r] = x;
-      mloc = fmaxf(mloc, x);
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    float alpha, lsum = 0.0f;
-    bf16x8 pb[2];
-    if (m_new == -INFINITY) {
-      alpha = 1.0f;
-#pragma unroll
-      for (int sidx = 0; sidx < 2; ++sidx) pb[sidx] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-    } else {
-      alpha = expf(m_run - m_new);
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = expf(st[r] - m_new);
-        lsum += p[r];
-      }
-#pragma unroll
-      for (int sidx = 0; sidx < 2; ++sidx) {
-        uint32_t wds[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          wds[e] = (uint32_t)f32_to_bf16(p[8 * sidx + 2 * e]) | ((uint32_t)f32_to_bf16(p[8 * sidx + 2 * e + 1]) << 16);
-        pb[sidx] = __builtin_bit_cast(bf16x8, make_uint4(wds[0], wds[1], wds[2], wds[3]));
-      }
-    }
-    lsum += __shfl_xor(lsum, 32, 64);
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-      const int dv = (4 * wave + t) * 32 + col;
-#pragma unroll
-      for (int sidx = 0; sidx < 2; ++sidx) {
-        uint32_t wds[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int e0 = 2 * e2, e1 = 2 * e2 + 1;
-          const int r0 = (e0 & 3) + 8 * (e0 >> 2) + 4 * hf + 16 * sidx;
-          const int r1 = (e1 & 3) + 8 * (e1 >> 2) + 4 * hf + 16 * sidx;
-          const uint32_t v0 = *(const uint16_t*)(skv + r0 * AT_ROWB + 2 * dv);
-          const uint32_t v1 = *(const uint16_t*)(skv + r1 * AT_ROWB + 2 * dv);
-          wds[e2] = v0 | (v1 << 16);
-        }
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(wds[0], wds[1], wds[2], wds[3]));
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[sidx], o[t], 0, 0, 0);
-      }
-    }
-    __syncthreads();
+  for (int i = tid; i < k; i += 256) {
+    const int id = irow[i];
+    sidx[i] = (id >= 0 && id < S) ? id : -1;
   }
+  __syncthreads();
+  const uint16_t* kvb = kv + (int64_t)b * S * AT_DQK;
+  // thread tid moves the 16-byte pieces tid + 256 u (u < 9) of a chunk: row
+  // piece / 72, part piece % 72; skipped rows load row 0 and store zeros
+  // chunk c + 2 is loaded (into VGPRs) while chunk c is computed, chunk c + 1
+  // (loaded during chunk c - 1) is stored into the other LDS buffer after it:
+  // two register sets, used in turn
+  uint4 gA[AT_GU], gB[AT_GU];
+#define AT_LOAD(G, c0)                                                                      \
+  do {                                                                                      \
+    _Pragma("unroll") for (int u = 0; u < AT_GU; ++u) {                                     \
+      const int pc = tid + 256 * u, r = pc / 72, part = pc - r * 72;                        \
+      const int id = (c0) + r < k ? sidx[(c0) + r] : -1;                                    \
+      G[u] = ((const uint4*)(kvb + (int64_t)(id < 0 ? 0 : id) * AT_DQK))[part];             \
+    }                                                                                       \
+  } while (0)
+#define AT_STORE(G, c0, buf)                                                                \
+  do {                                                                                      \
+    _Pragma("unroll") for (int u = 0; u < AT_GU; ++u) {                                     \
+      const int pc = tid + 256 * u, r = pc / 72, part = pc - r * 72;                        \
+      const int id = (c0) + r < k ? sidx[(c0) + r] : -1;                                    \
+      *(uint4*)((buf) + r * AT_ROWB + part * 16) = id < 0 ? make_uint4(0, 0, 0, 0) : G[u]; \
+    }                                                                                       \
+  } while (0)
+#define AT_BODY(GL, GS)                                                                                               \
+    const uint8_t* skv = skv2[it & 1];                                                                                \
+    if (c0 + 2 * AT_CH < k) AT_LOAD(GL, c0 + 2 * AT_CH);                                                              \
+    /* rows of this chunk that select something (bit r: row c0 + r) */                                                \
+    const uint64_t vrow = __ballot(lane < AT_CH && c0 + lane < k && sidx[min(c0 + lane, k - 1)] >= 0);                \
+    /* partial S^T over this wave's K-steps: all operand reads first */                                               \
+    bf16x8 av[9];                                                                                                     \
+    _Pragma("unroll")                                                                                                 \
+    for (int kk = 0; kk < 9; ++kk)                                                                                    \
+      av[kk] = __builtin_bit_cast(bf16x8, *(const uint4*)(skv + col * AT_ROWB + 2 * (16 * (9 * wave + kk) + 8 * hf))); \
+    f32x16 s = {};                                                                                                    \
+    _Pragma("unroll")                                                                                                 \
+    for (int kk = 0; kk < 9; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk], qb[kk], s, 0, 0, 0);           \
+    _Pragma("unroll")                                                                                                 \
+    for (int r = 0; r < 16; ++r) spart[wave][r][lane] = s[r];                                                         \
+    lds_barrier();                                                                                                    \
+    /* logits in base-2 units (tau log2 e folded in), running max and sum */                                          \
+    float st[16];                                                                                                     \
+    float mloc = -INFINITY;                                                                                           \
+    _Pragma("unroll")                                                                                                 \
+    for (int r = 0; r < 16; ++r) {                                                                                    \
+      const int row = (r & 3) + 8 * (r >> 2) + 4 * hf;                                                                \
+      const float x = spart[0][r][lane] + spart[1][r][lane] + spart[2][r][lane] + spart[3][r][lane];                  \
+      st[r] = ((vrow >> row) & 1ull) ? x * tau2 : -INFINITY;                                                          \
+      mloc = fmaxf(mloc, st[r]);                                                                                      \
+    }                                                                                                                 \
+    mloc = fmaxf(mloc, other_half(mloc, hf));                                                                         \
+    const float m_new = fmaxf(m_run, mloc);                                                                           \
+    float alpha = 1.0f, lsum = 0.0f;                                                                                  \
+    bf16x8 pb[2];                                                                                                     \
+    if (m_new == -INFINITY) {                                                                                         \
+      pb[0] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));                                                     \
+      pb[1] = pb[0];                                                                                                  \
+    } else {                                                                                                          \
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);                                                                  \
+      float p[16];                                                                                                    \
+      _Pragma("unroll")                                                                                               \
+      for (int r = 0; r < 16; ++r) {                                                                                  \
+        p[r] = __builtin_amdgcn_exp2f(st[r] - m_new);                                                                 \
+        lsum += p[r];                                                                                                 \
+      }                                                                                                               \
+      _Pragma("unroll")                                                                                               \
+      for (int s2 = 0; s2 < 2; ++s2) {                                                                                \
+        bf16x8 v;                                                                                                     \
+        _Pragma("unroll")                                                                                             \
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)p[8 * s2 + e];                                                     \
+        pb[s2] = v;                                                                                                   \
+      }                                                                                                               \
+    }                                                                                                                 \
+    lsum += other_half(lsum, hf);                                                                                     \
+    l_run = l_run * alpha + lsum;                                                                                     \
+    m_run = m_new;                                                                                                    \
+    /* rescale the outputs only when some head's maximum moved */                                                     \
+    const bool rescale = __ballot(alpha != 1.0f) != 0ull;                                                             \
+    _Pragma("unroll")                                                                                                 \
+    for (int t = 0; t < 4; ++t) {                                                                                     \
+      /* V^T operands of this dv tile: 16 rows of column dv, all read first */                                        \
+      const int dv = (4 * wave + t) * 32 + col;                                                                       \
+      uint32_t vv[16];                                                                                                \
+      _Pragma("unroll")                                                                                               \
+      for (int e = 0; e < 16; ++e) {                                                                                  \
+        const int row = (e & 3) + 8 * ((e >> 2) & 1) + 4 * hf + 16 * (e >> 3);                                        \
+        vv[e] = *(const uint16_t*)(skv + row * AT_ROWB + 2 * dv);                                                     \
+      }                                                                                                               \
+      if (rescale) {                                                                                                  \
+        _Pragma("unroll")                                                                                             \
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;                                                                \
+      }                                                                                                               \
+      _Pragma("unroll")                                                                                               \
+      for (int sidx2 = 0; sidx2 < 2; ++sidx2) {                                                                       \
+        const uint32_t* w8 = vv + 8 * sidx2;                                                                          \
+        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(w8[0] | (w8[1] << 16), w8[2] | (w8[3] << 16),         \
+                                                                w8[4] | (w8[5] << 16), w8[6] | (w8[7] << 16)));       \
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[sidx2], o[t], 0, 0, 0);                                 \
+      }                                                                                                               \
+    }                                                                                                                 \
+    if (c0 + AT_CH < k) AT_STORE(GS, c0 + AT_CH, skv2[(it + 1) & 1]);                                                 \
+    lds_barrier();
+  AT_LOAD(gA, 0);
+  AT_STORE(gA, 0, skv2[0]);
+  if (AT_CH < k) AT_LOAD(gA, AT_CH);
+  lds_barrier();    
+  for (int c0 = 0, it = 0; c0 < k;) {
+    { AT_BODY(gB, gA); }
+    c0 += AT_CH;
+    ++it;
+    if (c0 >= k) break;
+    { AT_BODY(gA, gB); }
+    c0 += AT_CH;
+    ++it;
+  }
+#undef AT_BODY
+#undef AT_LOAD
+#undef AT_STORE
 
   const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
   uint16_t* orow = out + ((int64_t)b * Hq + head) * AT_DV;
@@ -162,7 +209,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const uint16_t* __rest
       orow[dv] = f32_to_bf16(o[t][r] * inv);
     }
   }
-  if (lse && wave == 0 && hf == 0) lse[(int64_t)b * Hq + head] = l_run > 0.0f ? m_run + logf(l_run) : -INFINITY;
+  if (lse && wave == 0 && hf == 0)
+    lse[(int64_t)b * Hq + head] = l_run > 0.0f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
 }
 
 size_t attn_ws_bytes(int B, int Hq, int k, int dv) {

@@ -47,6 +47,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
+// does not wait for the wave's outstanding global loads, so prefetches issued
+// before it stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sum over the 64 lanes of a wave (result in every lane).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
