@@ -88,20 +88,29 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const uint16_t* __rest
   // (loaded during chunk c - 1) is stored into the other LDS buffer after it:
   // two register sets, used in turn
   uint4 gA[AT_GU], gB[AT_GU];
+  // per-thread piece coordinates (the same for every chunk)
+  int prow[AT_GU], ppart[AT_GU];
+#pragma unroll
+  for (int u = 0; u < AT_GU; ++u) {
+    const int pc = tid + 256 * u;
+    prow[u] = pc / 72;
+    ppart[u] = pc - prow[u] * 72;
+  }
+  // index reads first (unconditional, clamped), then every row load
 #define AT_LOAD(G, c0)                                                                      \
   do {                                                                                      \
-    _Pragma("unroll") for (int u = 0; u < AT_GU; ++u) {                                     \
-      const int pc = tid + 256 * u, r = pc / 72, part = pc - r * 72;                        \
-      const int id = (c0) + r < k ? sidx[(c0) + r] : -1;                                    \
-      G[u] = ((const uint4*)(kvb + (int64_t)(id < 0 ? 0 : id) * AT_DQK))[part];             \
-    }                                                                                       \
+    int id_[AT_GU];                                                                         \
+    _Pragma("unroll") for (int u = 0; u < AT_GU; ++u) id_[u] = sidx[min((c0) + prow[u], k - 1)]; \
+    _Pragma("unroll") for (int u = 0; u < AT_GU; ++u)                                       \
+      G[u] = ((const uint4*)(kvb + (int64_t)(id_[u] < 0 ? 0 : id_[u]) * AT_DQK))[ppart[u]];  \
   } while (0)
 #define AT_STORE(G, c0, buf)                                                                \
   do {                                                                                      \
+    int id_[AT_GU];                                                                         \
+    _Pragma("unroll") for (int u = 0; u < AT_GU; ++u) id_[u] = sidx[min((c0) + prow[u], k - 1)]; \
     _Pragma("unroll") for (int u = 0; u < AT_GU; ++u) {                                     \
-      const int pc = tid + 256 * u, r = pc / 72, part = pc - r * 72;                        \
-      const int id = (c0) + r < k ? sidx[(c0) + r] : -1;                                    \
-      *(uint4*)((buf) + r * AT_ROWB + part * 16) = id < 0 ? make_uint4(0, 0, 0, 0) : G[u]; \
+      const bool live = (c0) + prow[u] < k && id_[u] >= 0;                                 \
+      *(uint4*)((buf) + prow[u] * AT_ROWB + ppart[u] * 16) = live ? G[u] : make_uint4(0, 0, 0, 0); \
     }                                                                                       \
   } while (0)
 #define AT_BODY(GL, GS)                                                                                               \
