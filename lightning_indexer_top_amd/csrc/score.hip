@@ -324,7 +324,9 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
         for (int e = 0; e < 4; ++e) part = fmaf(__int_as_float(wr[i4][e]), relu_bits(acc[4 * i4 + e]), part);
       }
     }
-    part += __shfl_xor(part, 32, 64);
+    // lanes 0..31 add the partial sum of lanes 32..63 (same key, other heads)
+    part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
+                                                             false)[1]);
     if (hf == 0 && key < key_end) out_row[key] = key < nvis ? part * sc : -INFINITY;
   }
 }

@@ -444,14 +444,18 @@ __global__ __launch_bounds__(MB_THREADS) void topk_filter_kernel(const Sc* __res
       if (lane == 0) cnt_uw[u * NW + wid] = (uint32_t)__popcll(mk[u]);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t acc = 0;
-      for (int e = 0; e < MB_BATCH * NW; ++e) {
-        const uint32_t c = cnt_uw[e];
-        cnt_uw[e] = acc;
-        acc += c;
+    // exclusive prefix of the (u, wave) counts: one wave, one entry per lane
+    static_assert(MB_BATCH * NW == 64, "one count per lane of a wave");
+    if (tid < 64) {
+      const uint32_t c = cnt_uw[tid];
+      uint32_t incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t up = __shfl_up(incl, o, 64);
+        if (tid >= o) incl += up;
       }
-      cnt_uw[MB_BATCH * NW] = acc;
+      cnt_uw[tid] = incl - c;
+      if (tid == 63) cnt_uw[64] = incl;
     }
     __syncthreads();
 #pragma unroll
@@ -578,7 +582,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
 }
 
 static int mb_chunks(int R, int S) {
-  int p = (512 + R - 1) / R;  // about two workgroups per CU over the rows
+  int p = (2048 + R - 1) / R;  // about eight workgroups per CU over the rows
   const int max_p = (S + MB_THREADS * MB_BATCH - 1) / (MB_THREADS * MB_BATCH);
   if (p > max_p) p = max_p;
   if (p > 256) p = 256;
