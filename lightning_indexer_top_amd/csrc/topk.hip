@@ -53,20 +53,12 @@ __device__ int find_cut(const uint32_t* hist, uint32_t need, uint32_t* above, ui
   uint32_t v = c0 + c1;
   // inclusive scan across the wave
   const int lane = tid & 63, wid = tid >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
+  v = wave_incl_scan(v);
   if (lane == 63) sh_scan[wid] = v;
   __syncthreads();
   if (tid < 64) {
     uint32_t x = tid < TK_THREADS / 64 ? sh_scan[tid] : 0;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      uint32_t u = __shfl_up(x, o, 64);
-      if (tid >= o) x += u;
-    }
+    x = wave_incl_scan(x);
     if (tid < TK_THREADS / 64) sh_scan[tid] = x;  // inclusive over waves
   }
   __syncthreads();
@@ -270,13 +262,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restric
 // (checked), the k best are among them.  A row whose estimate misses, or keeps
 // more entries than the final sort holds, falls back to the exact single-workgroup
 // selection over the whole row, so the result is always the exact top-k.
-//   1. one workgroup per row estimates tau as the j-th largest of m = min(n, 4096)
-//      samples (64 runs of 64 consecutive entries spread evenly over the row:
-//      16 KB read), j = max(ceil((2k + 1024) m / n), 16): about 2k + 1024 entries
-//      (at least 16 sample gaps) should clear it, with a relative spread of
-//      1/sqrt(j); the estimate needs only the top 16 key bits;
-//   2. many workgroups per row append every entry with ord >= tau to the
-//      workgroup's own region of the list (no global atomics, nothing to clear);
+//   1. tau is the j-th largest of m = min(n, 4096) samples (64 runs of 64
+//      consecutive entries spread evenly over the row: 16 KB read),
+//      j = max(ceil((2k + 1024) m / n), 16): about 2k + 1024 entries (at least 16
+//      sample gaps) should clear it, with a relative spread of 1/sqrt(j); the
+//      estimate needs only the top 16 key bits;
+//      one workgroup per row estimates it;
+//   2. many workgroups per row append every entry of their chunk with ord >= tau
+//      to their own region of the list (no global atomics, nothing to clear);
 //   3. one workgroup per row selects exactly among the kept entries, or over the
 //      whole row.
 // Both k-th searches are radix selects over LDS histograms (11-bit digits).
@@ -312,11 +305,7 @@ __device__ __forceinline__ K block_kth8(const K (&key)[E], const bool (&valid)[E
     // counts of digits 255, 254, ... accumulated in that order
     const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;
     uint32_t v = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t u = __shfl_up(v, o, 64);
-      if (lane >= o) v += u;
-    }
+    v = wave_incl_scan(v);
     if (lane == 63) wsum[wid] = v;
     __syncthreads();
     uint32_t base = 0;
@@ -340,25 +329,17 @@ __device__ __forceinline__ K block_kth8(const K (&key)[E], const bool (&valid)[E
 
 constexpr int MB_RUNS = 64;  // sample runs of 64 entries
 
-template <typename Sc>
-__global__ __launch_bounds__(TK_THREADS) void topk_thresh_kernel(const Sc* __restrict__ scores,
-                                                                const int32_t* __restrict__ nv, int S, int k,
-                                                                typename ScoreTraits<Sc>::K* __restrict__ tau) {
+// tau of row `row` (n > k entries): the j-th largest of m = min(n, MB_SAMPLES)
+// samples, 64 runs of 64 consecutive entries spread evenly over the row, by a
+// workgroup of NT threads (every one of them gets the result).
+template <typename Sc, int NT>
+__device__ __forceinline__ typename ScoreTraits<Sc>::K sample_tau(const Sc* __restrict__ row, int n, int k,
+                                                                   uint32_t* hist, uint32_t* wsum, uint32_t* res) {
   typedef typename ScoreTraits<Sc>::K K;
-  constexpr int NW = TK_THREADS / 64;
-  constexpr int E = MB_RUNS * 64 / TK_THREADS;
-  static_assert(MB_RUNS * 64 == MB_SAMPLES, "sample count");
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[NW];
-  __shared__ uint32_t res[2];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  int n = S;
-  if (nv) n = min(max(nv[r], 0), S);
-  if (n <= k) {  // every entry is kept
-    if (tid == 0) tau[r] = 0;
-    return;
-  }
-  const Sc* row = scores + (int64_t)r * S;
+  constexpr int NW = NT / 64;
+  constexpr int E = MB_RUNS * 64 / NT;
+  static_assert(MB_RUNS * 64 == MB_SAMPLES && E * NT == MB_SAMPLES, "sample count");
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const bool runs = n >= MB_SAMPLES;
   const int m = runs ? MB_SAMPLES : n;
   const int step = runs ? (n - 64) / (MB_RUNS - 1) : 64;  // run starts: the last at most n - 64
@@ -377,8 +358,26 @@ __global__ __launch_bounds__(TK_THREADS) void topk_thresh_kernel(const Sc* __res
   if (j < 16) j = 16;
   if (j > m) j = m;
   // the top 16 key bits of a float (sign, exponent, 7 mantissa bits), 24 of a double
-  const K t = block_kth8<TK_THREADS, E, sizeof(K) == 4 ? 2 : 3>(key, valid, (uint32_t)j, hist, wsum, res);
-  if (tid == 0) tau[r] = t;
+  return block_kth8<NT, E, sizeof(K) == 4 ? 2 : 3>(key, valid, (uint32_t)j, hist, wsum, res);
+}
+
+template <typename Sc>
+__global__ __launch_bounds__(TK_THREADS) void topk_thresh_kernel(const Sc* __restrict__ scores,
+                                                                const int32_t* __restrict__ nv, int S, int k,
+                                                                typename ScoreTraits<Sc>::K* __restrict__ tau) {
+  constexpr int NW = TK_THREADS / 64;
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wsum[NW];
+  __shared__ uint32_t res[2];
+  const int r = blockIdx.x;
+  int n = S;
+  if (nv) n = min(max(nv[r], 0), S);
+  if (n <= k) {  // every entry is kept
+    if (threadIdx.x == 0) tau[r] = 0;
+    return;
+  }
+  const typename ScoreTraits<Sc>::K t = sample_tau<Sc, TK_THREADS>(scores + (int64_t)r * S, n, k, hist, wsum, res);
+  if (threadIdx.x == 0) tau[r] = t;
 }
 
 // Exclusive prefix sum of x over the workgroup (blockDim.x = NW * 64), in thread
@@ -387,11 +386,7 @@ template <int NW>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* scratch) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   uint32_t incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
+  incl = wave_incl_scan(incl);
   if (lane == 63) scratch[wid] = incl;
   __syncthreads();
   uint32_t base = 0;
@@ -449,11 +444,7 @@ __global__ __launch_bounds__(MB_THREADS) void topk_filter_kernel(const Sc* __res
     if (tid < 64) {
       const uint32_t c = cnt_uw[tid];
       uint32_t incl = c;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t up = __shfl_up(incl, o, 64);
-        if (tid >= o) incl += up;
-      }
+      incl = wave_incl_scan(incl);
       cnt_uw[tid] = incl - c;
       if (tid == 63) cnt_uw[64] = incl;
     }
@@ -508,11 +499,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
       tot += c4[e];
     }
     uint32_t incl = tot;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t u = __shfl_up(incl, o, 64);
-      if (tid >= o) incl += u;
-    }
+    incl = wave_incl_scan(incl);
     uint32_t ex = incl - tot;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -535,18 +522,26 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
   Sc val[E];
   int32_t id[E];
   bool valid[E];
-  // every load is issued (entries past the list read entry 0) before any is used
+  // every load is issued (entries past the list read its last entry) before any
+  // is used; a thread's entries are consecutive, so after one binary search for
+  // the region of its first entry the later ones only step forward
+  int rg;
+  {
+    const uint32_t jf = min((uint32_t)(E * tid), c - 1u);
+    int lo2 = 0, hi2 = P - 1;  // region b with off[b] <= jf < off[b+1]
+    while (lo2 < hi2) {
+      const int mid = (lo2 + hi2 + 1) >> 1;
+      if (off[mid] <= jf) lo2 = mid; else hi2 = mid - 1;
+    }
+    rg = lo2;
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t j0 = (uint32_t)(E * tid + e);
     valid[e] = j0 < c;
-    const uint32_t j = valid[e] ? j0 : 0u;
-    int lo2 = 0, hi2 = P - 1;  // region b with off[b] <= j < off[b+1]
-    while (lo2 < hi2) {
-      const int mid = (lo2 + hi2 + 1) >> 1;
-      if (off[mid] <= j) lo2 = mid; else hi2 = mid - 1;
-    }
-    const int64_t src = (int64_t)r * S + (int64_t)lo2 * chunk + (j - off[lo2]);
+    const uint32_t j = valid[e] ? j0 : c - 1u;
+    while (rg + 1 < P && off[rg + 1] <= j) ++rg;
+    const int64_t src = (int64_t)r * S + (int64_t)rg * chunk + (j - off[rg]);
     val[e] = cval[src];
     id[e] = cid[src];
   }
