@@ -187,10 +187,26 @@ def bench_prefill(torch, li, workloads, steps, warmup):
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev[-steps:]]))
     flop = float(x["nv"].astype(np.int64).sum()) * H * FLOP_PER_KEY_PER_HEAD
     tf = flop / (ms * 1e-3) / 1e12
-    log(f"[prefill] {ms:.2f} ms -> {tf:.1f} TFLOP/s")
+    # the same contraction without selection: li_indexer_score writes all 2 GiB of scores
+    scores = torch.empty((B * T, S), dtype=torch.float32, device="cuda")
+    ev2 = []
+
+    def step2(i):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        li.indexer_score(q, w, kk, None, nv, out=scores)
+        e1.record()
+        ev2.append((e0, e1))
+
+    timed(torch, step2, max(3, steps // 2), 1, ev2)
+    ms2 = float(np.mean([a.elapsed_time(b) for a, b in ev2[-max(3, steps // 2):]]))
+    tf2 = flop / (ms2 * 1e-3) / 1e12
+    del scores
+    log(f"[prefill] fused {ms:.2f} ms -> {tf:.1f} TFLOP/s; scores only {ms2:.2f} ms -> {tf2:.1f} TFLOP/s")
     return {"workload": "prefill_chunk T=4096 S=131072 H=64 bf16 causal top-512", "ms": round(ms, 4),
             "value": round(tf, 2), "unit": "TFLOP/s", "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
-            "flop": flop}
+            "flop": flop, "unfused_score_ms": round(ms2, 4), "unfused_score_tflops": round(tf2, 2),
+            "unfused_frac_bf16_peak": round(tf2 / BF16_PEAK_TFLOPS, 4)}
 
 
 def bench_compact(torch, li, workloads, steps, warmup):

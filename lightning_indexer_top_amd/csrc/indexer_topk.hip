@@ -38,32 +38,74 @@ constexpr int PS_KMAX = 512;   // largest k the fused kernel takes (CAP - NK - k
 // max(x, 0) on the bit pattern (exact, -0 -> +0).
 __device__ __forceinline__ float relu_bits_f(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// hist[d] += 1 for every lane with valid set (one wave, LDS atomics); when all
+// such lanes share one digit a single atomic adds them.
+__device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t d, bool valid) {
+  const uint64_t act = __ballot(valid);
+  if (!act) return;
+  const int first = __ffsll((unsigned long long)act) - 1;
+  const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, first);  // first is wave-uniform
+  if (__ballot(valid && d == d0) == act) {
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[d0], (uint32_t)__popcll(act));
+  } else if (valid) {
+    atomicAdd(&hist[d], 1u);
+  }
+}
+
 // Wave-level exact compaction of a candidate list (entries [0, cnt) in index
-// order, orderable keys in sk, ids in si; every listed key is above 0) to its
-// best `keep` entries, preserving order.  Returns the orderable key T of the
-// worst kept entry.  Lane l handles entries l + 64 e, so the rank of an entry
-// among the kept ones is a ballot prefix: rows e' < e, then lanes below l.
-__device__ uint32_t ps_compact(uint32_t* sk, int32_t* si, int cnt, int keep) {
+// order, orderable keys in sk, ids in si) to its best `keep` entries, preserving
+// order.  Returns the orderable key T of the worst kept entry.  T comes from a
+// radix select (four 8-bit digits, the wave's own 256-bin histogram hw in LDS).
+// Lane l handles entries l + 64 e, so the rank of an entry among the kept ones
+// is a ballot prefix: rows e' < e, then lanes below l.
+__device__ uint32_t ps_compact(uint32_t* sk, int32_t* si, uint32_t* hw, int cnt, int keep) {
   constexpr int E = PS_CAP / 64;
   const int lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1;
   uint32_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = lane + 64 * e < cnt ? sk[lane + 64 * e] : 0u;
-  // T: the largest t with count(key >= t) >= keep (padding keys are 0)
-  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
-  while (lo < hi) {
-    const uint32_t mid = lo + (uint32_t)(((uint64_t)(hi - lo) + 1) >> 1);
-    int c = 0;
+  // T: the keep-th largest listed key, digit by digit from the top
+  uint32_t prefix = 0u, mask = 0u;
+  uint32_t need = (uint32_t)keep;
 #pragma unroll
-    for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= mid));
-    if (c >= keep) lo = mid; else hi = mid - 1;
+  for (int p = 0; p < 4; ++p) {
+    const int shift = 24 - 8 * p;
+    *(uint4*)&hw[4 * lane] = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      wave_hist_add(hw, (key[e] >> shift) & 255u, lane + 64 * e < cnt && (key[e] & mask) == prefix);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // lane l holds digits 255 - 4 l .. 252 - 4 l, counted from the top
+    const uint4 c4 = *(const uint4*)&hw[252 - 4 * lane];  // digits 252-4l .. 255-4l
+    const uint32_t cs = c4.x + c4.y + c4.z + c4.w;
+    const uint32_t incl = wave_incl_scan(cs), excl = incl - cs;
+    const uint64_t hit = __ballot(excl < need && need <= incl);
+    const int hl = __ffsll((unsigned long long)hit) - 1;
+    // inside the hit lane: digits 255-4l (c4.w) down to 252-4l (c4.x)
+    uint32_t d = 0u, above = excl;
+    if (need <= excl + c4.w) {
+      d = 255u - 4u * (uint32_t)lane;
+    } else if (need <= excl + c4.w + c4.z) {
+      d = 254u - 4u * (uint32_t)lane; above = excl + c4.w;
+    } else if (need <= excl + c4.w + c4.z + c4.y) {
+      d = 253u - 4u * (uint32_t)lane; above = excl + c4.w + c4.z;
+    } else {
+      d = 252u - 4u * (uint32_t)lane; above = excl + c4.w + c4.z + c4.y;
+    }
+    const uint32_t dd = (uint32_t)__builtin_amdgcn_readlane((int)d, hl);
+    const uint32_t ab = (uint32_t)__builtin_amdgcn_readlane((int)above, hl);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    prefix |= dd << shift;
+    mask |= 255u << shift;
+    need -= ab;
   }
-  const uint32_t T = lo;
+  const uint32_t T = prefix;
   int gt = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) gt += __popcll(__ballot(key[e] > T));
-  const int need = keep - gt;  // entries equal to T to keep, smallest index first
+  for (int e = 0; e < E; ++e) gt += __popcll(__ballot(lane + 64 * e < cnt && key[e] > T));
+  const int need_ties = keep - gt;  // entries equal to T to keep, smallest index first
   // a kept entry moves to its rank, never above its own position: the writes of
   // row e land in rows <= e, and row e is read before it is written
   int base = 0, tbase = 0;
@@ -74,7 +116,7 @@ __device__ uint32_t ps_compact(uint32_t* sk, int32_t* si, int cnt, int keep) {
     const bool valid = j < cnt;
     const bool tie = valid && key[e] == T;
     const uint64_t mt = __ballot(tie);
-    const bool sel = (valid && key[e] > T) || (tie && tbase + __popcll(mt & below) < need);
+    const bool sel = (valid && key[e] > T) || (tie && tbase + __popcll(mt & below) < need_ties);
     tbase += __popcll(mt);
     const uint64_t ms = __ballot(sel);
     const int32_t id = valid ? si[j] : 0;
@@ -89,16 +131,20 @@ __device__ uint32_t ps_compact(uint32_t* sk, int32_t* si, int cnt, int keep) {
   return T;
 }
 
-template <int HT>
+// SCORES: write every score to scores [B*T, S] (masked keys -inf) instead of
+// selecting (the same contraction for li_indexer_score at prefill shapes).
+template <int HT, bool SCORES>
 __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
                            const uint16_t* __restrict__ k, const int32_t* __restrict__ nv, int T, int S, int H,
-                           int topk, int32_t* __restrict__ idx_out, float* __restrict__ val_out) {
+                           int topk, int32_t* __restrict__ idx_out, float* __restrict__ val_out,
+                           float* __restrict__ scores) {
   // LDS: two key tiles (64 keys x 256 B, 16-byte chunks XOR-swizzled by key),
   // then per wave a candidate list (orderable keys, ids)
   __shared__ __attribute__((aligned(16))) uint8_t tiles[2][PS_NK * 256];
   __shared__ uint32_t cand_k[PS_WAVES][PS_CAP];
   __shared__ int32_t cand_i[PS_WAVES][PS_CAP];
+  __shared__ __attribute__((aligned(16))) uint32_t whist[PS_WAVES][256];  // compaction histograms
 
   const int blocks_per_seq = (T + PS_WAVES - 1) / PS_WAVES;
   const int b = blockIdx.x / blocks_per_seq;
@@ -236,6 +282,10 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
           }
         }
         const int key = kt + 32 * s + col;
+        if constexpr (SCORES) {
+          if (active && hf == 0 && key < kend) scores[r * S + key] = key < nvis ? part : -INFINITY;
+          continue;
+        }
         const uint32_t ok = ord_f32(part);
         const uint64_t mk = __ballot(hf == 0 && key < nvis && ok > theta);
         if (mk) {
@@ -248,8 +298,8 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
         }
       }
       // room for the next tile's entries
-      if (cnt > PS_CAP - PS_NK) {
-        theta = ps_compact(sk, si, cnt, topk);
+      if (!SCORES && cnt > PS_CAP - PS_NK) {
+        theta = ps_compact(sk, si, whist[wave], cnt, topk);
         cnt = topk;
       }
     }
@@ -267,8 +317,15 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
 #undef PS_LOAD
 #undef PS_STORE
   if (!active) return;
+  if constexpr (SCORES) {
+    // keys this row's tiles did not cover: the tiles from the first at or past
+    // nvis were skipped, keys past kend were not scored
+    const int from = min((nvis + PS_NK - 1) / PS_NK * PS_NK, kend);
+    for (int key = from + lane; key < S; key += 64) scores[r * S + key] = -INFINITY;
+    return;
+  }
   if (cnt > topk) {
-    ps_compact(sk, si, cnt, topk);
+    ps_compact(sk, si, whist[wave], cnt, topk);
     cnt = topk;
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -279,6 +336,25 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
     io[j] = v ? si[j] : -1;
     if (vo) vo[j] = v ? unord_f32(sk[j]) : -INFINITY;
   }
+}
+
+bool prefill_scores_apply(int q_type, int k_type, int T, int H) {
+  return q_type == DT_BF16 && k_type == DT_BF16 && T >= 2 * PS_WAVES && H <= 128;
+}
+
+hipError_t launch_prefill_scores(const uint16_t* q, const float* w, const uint16_t* k, const int32_t* nv, int B,
+                                 int T, int S, int H, float* scores, hipStream_t st) {
+  const int blocks = B * ((T + PS_WAVES - 1) / PS_WAVES);
+  if (H <= 32)
+    prefill_select_kernel<1, true><<<blocks, PS_WAVES * 64, 0, st>>>(q, w, k, nv, T, S, H, 0, nullptr, nullptr,
+                                                                    scores);
+  else if (H <= 64)
+    prefill_select_kernel<2, true><<<blocks, PS_WAVES * 64, 0, st>>>(q, w, k, nv, T, S, H, 0, nullptr, nullptr,
+                                                                    scores);
+  else
+    prefill_select_kernel<4, true><<<blocks, PS_WAVES * 64, 0, st>>>(q, w, k, nv, T, S, H, 0, nullptr, nullptr,
+                                                                    scores);
+  return hipGetLastError();
 }
 
 static bool use_fused(int q_type, int k_type, int T, int H, int topk) {
@@ -300,11 +376,14 @@ hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const 
     const uint16_t* qq = (const uint16_t*)q;
     const uint16_t* kk = (const uint16_t*)k;
     if (H <= 32)
-      prefill_select_kernel<1><<<blocks, PS_WAVES * 64, 0, st>>>(qq, w, kk, nv, T, S, H, topk, idx, val);
+      prefill_select_kernel<1, false><<<blocks, PS_WAVES * 64, 0, st>>>(qq, w, kk, nv, T, S, H, topk, idx, val,
+                                                                       nullptr);
     else if (H <= 64)
-      prefill_select_kernel<2><<<blocks, PS_WAVES * 64, 0, st>>>(qq, w, kk, nv, T, S, H, topk, idx, val);
+      prefill_select_kernel<2, false><<<blocks, PS_WAVES * 64, 0, st>>>(qq, w, kk, nv, T, S, H, topk, idx, val,
+                                                                       nullptr);
     else
-      prefill_select_kernel<4><<<blocks, PS_WAVES * 64, 0, st>>>(qq, w, kk, nv, T, S, H, topk, idx, val);
+      prefill_select_kernel<4, false><<<blocks, PS_WAVES * 64, 0, st>>>(qq, w, kk, nv, T, S, H, topk, idx, val,
+                                                                       nullptr);
     return hipGetLastError();
   }
   float* scores = (float*)ws;

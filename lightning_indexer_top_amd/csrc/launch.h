@@ -42,6 +42,12 @@ size_t attn_ws_bytes(int B, int Hq, int k, int dv);
 hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int B, int Hq, int S, int k,
                        float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t st);
 
+// scores of many query rows (prefill shapes: bf16 queries and keys, T >= 16,
+// H <= 128) by the MFMA-tiled kernel that also serves the fused selection
+bool prefill_scores_apply(int q_type, int k_type, int T, int H);
+hipError_t launch_prefill_scores(const uint16_t* q, const float* w, const uint16_t* k, const int32_t* nv, int B,
+                                 int T, int S, int H, float* scores, hipStream_t st);
+
 // fused scoring + selection for many query rows (prefill); falls back to
 // score-then-select where the fused kernel does not apply
 size_t indexer_topk_ws_bytes(int B, int T, int S, int H, int topk);

@@ -422,6 +422,8 @@ __global__ __launch_bounds__(256) void score_valu_kernel(const QT* __restrict__ 
 hipError_t launch_score(const void* q, int q_type, const float* w, const void* k, int k_type, const float* ks,
                         const int32_t* nv, int B, int T, int S, int H, float* scores, hipStream_t st) {
   const int R = B * T;
+  if (prefill_scores_apply(q_type, k_type, T, H))
+    return launch_prefill_scores((const uint16_t*)q, w, (const uint16_t*)k, nv, B, T, S, H, scores, st);
   if (q_type == DT_BF16 && (k_type == DT_FP8 || k_type == DT_BF16)) {
     const bool f8 = k_type == DT_FP8;
     const uint16_t* qq = (const uint16_t*)q;

@@ -65,6 +65,21 @@ def test_prefill_causal_small():
         assert np.isneginf(g[t, nv[t]:]).all() and np.isfinite(g[t, : nv[t]]).all()
 
 
+@pytest.mark.parametrize("B,T,S,H", [(2, 17, 1000, 64), (1, 40, 3001, 100), (3, 64, 513, 8)])
+def test_prefill_tiled_scores(B, T, S, H):
+    # many query rows (bf16): the MFMA-tiled scoring kernel, ragged row counts (rows
+    # past T in a workgroup), ragged key tails and per-row visible counts in [0, S]
+    print("prefill tiled", B, T, S, H, flush=True)
+    sp = workloads.spec("prefill_chunk", B=B, T=T, S=S, H=H, seed=0x5EED0C00 + T + S)
+    rng = np.random.default_rng(T + S)
+    nv = rng.integers(0, S + 1, B * T).astype(np.int32)
+    nv[0], nv[-1] = 0, S
+    g, o, _ = run(sp, nv=nv)
+    assert_scores_close(g, o, f"prefill tiled B={B} T={T} S={S} H={H}")
+    for r in range(B * T):
+        assert np.isneginf(g[r, nv[r]:]).all() and np.isfinite(g[r, : nv[r]]).all()
+
+
 def test_visible_count_edges():
     print("nv edges", flush=True)
     sp = workloads.spec("batched_decode", B=1, T=6, S=700, H=64, seed=0x5EED0400)
