@@ -7,12 +7,13 @@
 //
 // score_stream_kernel: bf16 queries against fp8 (or bf16) keys.  Decode is a pure
 // stream over the key cache, so each wave owns one query row's 64 x 128 query
-// block in VGPRs (the MFMA A operand, loaded once) and streams 32-key tiles
-// through v_mfma_f32_32x32x16_bf16 as the B operand.  fp8 codes are widened to
-// bf16 in registers (exact: every E4M3 value is a bf16 value); the per-key scale is
+// block in VGPRs (the MFMA A operand, loaded once) and streams 32-key tiles through
+// LDS as the B operand.  bf16 keys: v_mfma_f32_32x32x16_bf16.  fp8 keys: the block-
+// scaled fp8 MFMA with the key bytes as they arrive and the query split exactly into
+// two E4M3 halves (see QSplit below), so no key is converted.  The per-key scale is
 // positive, so it commutes with the ReLU and is applied once after the head sum.
 //
-// MFMA layout used (32x32x16, wave64): lane l supplies row/column (l & 31) of the
+// bf16 MFMA layout (32x32x16, wave64): lane l supplies row/column (l & 31) of the
 // A/B operands and 8 consecutive K elements chosen by l >> 5; the accumulator
 // element (i, j) lives in lane j + 32 * ((i / 4) & 1), register (i & 3) + 4 * (i / 8).
 // The dot product does not depend on which K positions a lane carries as long as A
@@ -23,20 +24,6 @@
 #include "launch.h"
 
 namespace li {
-
-// Widen 16 fp8 E4M3 codes (one uint4) to two 8-element bf16 MFMA operands.
-__device__ __forceinline__ void fp8x16_to_bf16(const uint4 raw, bf16x8& lo8, bf16x8& hi8) {
-  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, false);
-  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, 1.0f, true);
-  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, false);
-  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, 1.0f, true);
-  bf16x2 p4 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.z, 1.0f, false);
-  bf16x2 p5 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.z, 1.0f, true);
-  bf16x2 p6 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w, 1.0f, false);
-  bf16x2 p7 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.w, 1.0f, true);
-  lo8 = (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-  hi8 = (bf16x8){p4[0], p4[1], p5[0], p5[1], p6[0], p6[1], p7[0], p7[1]};
-}
 
 // Occupancy target (waves per SIMD) and ring depth (tiles in flight per wave) of
 // the streaming kernel, per head-tile count and key format: the VGPR budget of the
@@ -80,6 +67,7 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // One 32-key tile of one wave: K rows of ROW bytes, stored in LDS as 16-byte
 // chunks with the chunk index XOR-swizzled by the key so that the MFMA operand
@@ -191,6 +179,92 @@ __device__ __forceinline__ float lds_read_f32(uint32_t a) {
   return r;
 }
 
+// fp8 keys: the bf16 query split exactly into two E4M3 halves with power-of-two
+// scales, for the block-scaled fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4).  For each
+// run of 32 query values whose largest magnitude lies in [2^E, 2^(E+1)):
+//   hi = RNE_e4m3(q 2^-(E-7)),  lo = (q 2^-(E-7) - hi) 2^4,  q = hi 2^(E-7) + lo 2^(E-11).
+// hi keeps the top 4 significant bits (|q 2^-(E-7)| < 2^8, inside E4M3's range); the
+// remainder is a multiple of q's bf16 ulp at most 2^3 of it, so lo holds it exactly
+// for every value down to 2^-13 of the run's maximum (below that lo rounds, an error
+// under 2^-22 of the maximum).  Code x code products are exact and each lane's 32
+// codes carry one E8M0 exponent, so hi.k + lo.k is the bf16-query, fp8-key product
+// sum with fp32 accumulation, as with keys widened to bf16, but the key bytes are the
+// MFMA operand as they sit in LDS: no per-key conversion.
+//
+// Operand layout of the 32x32x64 fp8 MFMA (measured on the device): lane l supplies 32
+// codes of row/column (l & 31); A lane l pairs code by code with B lanes of the same
+// half (l >> 5).  The scale blocks of 32 codes along K are: block kb = bytes
+// [16 kb, 16 kb + 16) of both lane halves, and the scale of (row i, block kb) is the
+// byte OPSEL selects of lane i + 32 kb's scale operand.  The accumulator layout is
+// that of the other 32x32 MFMAs.  Lane half hf carries key dimensions [64 hf,
+// 64 hf + 64), 32 per MFMA (kk), the 64 bytes of its key row the LDS operand reads
+// return; so scale block (kk, kb) of a head covers dimensions 32 kk + 16 kb + [0, 16)
+// and 64 + 32 kk + 16 kb + [0, 16), and that is the run the query split works on.
+//
+// Query code layout in LDS: slot ((t * 2 + kk) * 2 + hf) * 32 + col holds the 32 codes
+// lane (hf, col) feeds MFMA kk of head tile t: hi codes, then lo codes; then per lane
+// (hf, col) a record of 2 HT scale bytes, byte t * 2 + kk = the scale of block kb = hf.
+template <int HT>
+struct QSplit {
+  static constexpr int HI = 0;
+  static constexpr int LO = HT * 4 * 32 * 32;
+  static constexpr int SC = 2 * LO;
+  static constexpr int BYTES = SC + 64 * 2 * HT;
+};
+
+// hi and lo codes of one run of 32 bf16 values (four uint4), and its scale exponent
+__device__ __forceinline__ int split_run(const uint4 (&v)[4], uint32_t (&hi)[8], uint32_t (&lo)[8]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      m = fmaxf(m, fmaxf(fabsf(__uint_as_float(u[e] << 16)), fabsf(__uint_as_float(u[e] & 0xffff0000u))));
+  }
+  const int ex = m > 0.0f ? __builtin_amdgcn_frexp_expf(m) - 1 : 0;
+  const int sh = min(max(ex - 7, -122), 120);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const float a0 = __builtin_ldexpf(__uint_as_float(u[2 * e2] << 16), -sh);
+      const float a1 = __builtin_ldexpf(__uint_as_float(u[2 * e2] & 0xffff0000u), -sh);
+      const float a2 = __builtin_ldexpf(__uint_as_float(u[2 * e2 + 1] << 16), -sh);
+      const float a3 = __builtin_ldexpf(__uint_as_float(u[2 * e2 + 1] & 0xffff0000u), -sh);
+      int hc = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+      hc = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, hc, true);
+      const float r0 = (a0 - __builtin_amdgcn_cvt_f32_fp8(hc, 0)) * 16.0f;
+      const float r1 = (a1 - __builtin_amdgcn_cvt_f32_fp8(hc, 1)) * 16.0f;
+      const float r2 = (a2 - __builtin_amdgcn_cvt_f32_fp8(hc, 2)) * 16.0f;
+      const float r3 = (a3 - __builtin_amdgcn_cvt_f32_fp8(hc, 3)) * 16.0f;
+      int lc = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false);
+      lc = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, lc, true);
+      hi[2 * j + e2] = (uint32_t)hc;
+      lo[2 * j + e2] = (uint32_t)lc;
+    }
+  }
+  return sh;
+}
+
+__device__ __forceinline__ i32x8 cat8(const i32x4 a, const i32x4 b) {
+  return (i32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// q.k over 128 dimensions for one 32-head tile on the fp8 MFMA: hi and lo codes of
+// the tile's two 32-dimension runs per lane; scale byte SEL and SEL + 1 of sh / sl
+template <int SEL>
+__device__ __forceinline__ f32x16 f8_dot(const i32x8 h0, const i32x8 h1, const i32x8 l0, const i32x8 l1,
+                                         const i32x8 b0, const i32x8 b1, int sh, int sl) {
+  f32x16 c = {};
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(h0, b0, c, 0, 0, SEL, sh, 0, 127);
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(h1, b1, c, 0, 0, SEL + 1, sh, 0, 127);
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(l0, b0, c, 0, 0, SEL, sl, 0, 127);
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(l1, b1, c, 0, 0, SEL + 1, sl, 0, 127);
+  return c;
+}
+
 template <int HT, bool FP8, int NST, int WPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ k,
@@ -198,6 +272,10 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
                          int keys_per_block, float* __restrict__ scores) {
   typedef TileGeom<FP8> G;
   static_assert(NST >= 1 && NST <= 3, "ring depth");
+  // fp8: the query codes occupy the last SPL ring stages until every wave has
+  // read its operands; those stages are filled after that
+  constexpr int SPL = FP8 ? (QSplit<HT>::BYTES + 4 * G::BYTES - 1) / (4 * G::BYTES) : 0;
+  static_assert(!FP8 || SPL <= NST, "query codes fit in the ring");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int r = blockIdx.y;
   const int b = r / T;
@@ -214,11 +292,14 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
   const int vis_end = min(key_end, nvis);
   for (int key = max(key0, vis_end) + (int)threadIdx.x; key < key_end; key += 256) out_row[key] = -INFINITY;
 
-  // LDS: the head weights (2 x HT x 16 floats), then each wave's ring of NST tiles
+  // LDS: the head weights (2 x HT x 16 floats), then the ring, stage-major: stage st
+  // of wave w at ring0 + (st * 4 + w) * BYTES
   uint8_t* ring = lds + 2 * HT * 16 * sizeof(float);
   ring = (uint8_t*)(((uintptr_t)ring + 127) & ~(uintptr_t)127);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t my_ring = lds_addr(ring) + (uint32_t)(wave_u * NST * G::BYTES);
+  const uint32_t ring0 = lds_addr(ring);
+  const uint32_t my_ring = ring0 + (uint32_t)(wave_u * G::BYTES);
+  constexpr uint32_t SSTRIDE = 4 * G::BYTES;  // bytes between a wave's stages
   const float* sbase = ks + (int64_t)b * S;
   float* sw = (float*)lds;  // [2][HT][16]
   const int first = key0 + wave_u * 32;
@@ -240,35 +321,106 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
   for (int j = 0; j < NCH; ++j) roff[j] = (uint32_t)(G::slot(col, NCH * hf + j) * 16);
   const uint32_t soff = (uint32_t)(G::KBYTES + 4 * col);
 
-  // head weights in accumulator row order per lane half (read as LDS broadcasts);
-  // written before any LDS DMA is in flight
+  // head weights in accumulator row order per lane half (read as LDS broadcasts)
   if (threadIdx.x < 2 * HT * 16) {
     const int g = threadIdx.x >> 4, i = threadIdx.x & 15;
     const int hf2 = g / HT, t = g % HT;
     const int hh = t * 32 + (i & 3) + 8 * (i >> 2) + 4 * hf2;
     sw[(hf2 * HT + t) * 16 + i] = hh < H ? w[(int64_t)r * H + hh] : 0.0f;
   }
-  __syncthreads();
 
-  // prologue: NST tiles in flight, issued before the query block is loaded so
-  // the two overlap
+  // A operand.  bf16: query heads t*32 + col, dims [64 hf, 64 hf + 64), from global.
+  // fp8: hi / lo codes and scale bytes, through the block's split in LDS.
+  bf16x8 a[FP8 ? 1 : HT][FP8 ? 1 : 8];
+  i32x8 ahi[FP8 ? HT : 1][2], alo[FP8 ? HT : 1][2];
+  int sch[(HT + 1) / 2], scl[(HT + 1) / 2];
+  if constexpr (!FP8) {
+    // weights written before any LDS DMA is in flight
+    __syncthreads();
 #pragma unroll
-  for (int st = 0; st < NST; ++st) {
-    const int t0 = first + st * step;
-    if (t0 < vis_end)
-      issue_tile<FP8>(kbase + (int64_t)t0 * G::ROW, sbase + t0, my_ring + st * G::BYTES, goff, lane, min(32, S - t0));
-  }
-
-  // A operand: query heads t*32 + col, dims [64 hf, 64 hf + 64).
-  bf16x8 a[HT][8];
+    for (int st = 0; st < NST; ++st) {
+      const int t0 = first + st * step;
+      if (t0 < vis_end)
+        issue_tile<FP8>(kbase + (int64_t)t0 * G::ROW, sbase + t0, my_ring + st * SSTRIDE, goff, lane, min(32, S - t0));
+    }
 #pragma unroll
-  for (int t = 0; t < HT; ++t) {
-    const int h = t * 32 + col;
-    const uint4* qp = (const uint4*)(q + ((int64_t)r * H + (h < H ? h : 0)) * 128 + 64 * hf);
+    for (int t = 0; t < HT; ++t) {
+      const int h = t * 32 + col;
+      const uint4* qp = (const uint4*)(q + ((int64_t)r * H + (h < H ? h : 0)) * 128 + 64 * hf);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      uint4 v = h < H ? qp[kk] : make_uint4(0, 0, 0, 0);
-      a[t][kk] = __builtin_bit_cast(bf16x8, v);
+      for (int kk = 0; kk < 8; ++kk) {
+        uint4 v = h < H ? qp[kk] : make_uint4(0, 0, 0, 0);
+        a[t][kk] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  } else {
+    // query runs (thread = head x run of 32 dimensions) loaded before the first
+    // tiles' DMA so their wait does not cover it
+    // run (kk, kb) of head h: dimensions 32 kk + 16 kb + [0, 16) and 64 + that
+    constexpr int RUNS = (HT * 128 + 255) / 256;
+    uint4 qv[RUNS][4];
+#pragma unroll
+    for (int u = 0; u < RUNS; ++u) {
+      const int id = (int)threadIdx.x + 256 * u;
+      const int h = id >> 2, run = id & 3;
+      const bool ok = id < HT * 128 && h < H;
+      const uint4* qp = (const uint4*)(q + ((int64_t)r * H + (ok ? h : 0)) * 128 + 16 * run);
+      qv[u][0] = ok ? qp[0] : make_uint4(0, 0, 0, 0);
+      qv[u][1] = ok ? qp[1] : make_uint4(0, 0, 0, 0);
+      qv[u][2] = ok ? qp[8] : make_uint4(0, 0, 0, 0);
+      qv[u][3] = ok ? qp[9] : make_uint4(0, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < NST - SPL; ++st) {
+      const int t0 = first + st * step;
+      if (t0 < vis_end)
+        issue_tile<FP8>(kbase + (int64_t)t0 * G::ROW, sbase + t0, my_ring + st * SSTRIDE, goff, lane, min(32, S - t0));
+    }
+    uint8_t* split = ring + (NST - SPL) * SSTRIDE;
+#pragma unroll
+    for (int u = 0; u < RUNS; ++u) {
+      const int id = (int)threadIdx.x + 256 * u;
+      if (id < HT * 128) {
+        const int h = id >> 2, run = id & 3;
+        const int t = h >> 5, c = h & 31, kk = run >> 1, kb = run & 1;
+        uint32_t hi[8], lo[8];
+        const int sh = split_run(qv[u], hi, lo);
+        // first 16 codes: lane (0, c); last 16: lane (1, c); bytes [16 kb, 16 kb + 16)
+        const int slot0 = ((t * 2 + kk) * 2 + 0) * 32 + c, slot1 = slot0 + 32;
+        *(uint4*)(split + QSplit<HT>::HI + slot0 * 32 + 16 * kb) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *(uint4*)(split + QSplit<HT>::HI + slot1 * 32 + 16 * kb) = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+        *(uint4*)(split + QSplit<HT>::LO + slot0 * 32 + 16 * kb) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        *(uint4*)(split + QSplit<HT>::LO + slot1 * 32 + 16 * kb) = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+        // the scale of block kb comes from lane half kb
+        split[QSplit<HT>::SC + (kb * 32 + c) * (2 * HT) + t * 2 + kk] = (uint8_t)(127 + sh);
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int t = 0; t < HT; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int slot = ((t * 2 + kk) * 2 + hf) * 32 + col;
+        const i32x4* ph = (const i32x4*)(split + QSplit<HT>::HI + slot * 32);
+        const i32x4* pl = (const i32x4*)(split + QSplit<HT>::LO + slot * 32);
+        ahi[t][kk] = cat8(ph[0], ph[1]);
+        alo[t][kk] = cat8(pl[0], pl[1]);
+      }
+    const uint8_t* psc = split + QSplit<HT>::SC + (hf * 32 + col) * (2 * HT);
+#pragma unroll
+    for (int p2 = 0; p2 < (HT + 1) / 2; ++p2) {
+      // bytes (2 p2 + t') * 2 + kk of the lane's scale record, one word per head pair;
+      // the lo scale is the hi scale / 2^4 in every byte (no byte is below 5)
+      sch[p2] = HT == 1 ? (int)*(const uint16_t*)psc : ((const int*)psc)[p2];
+      scl[p2] = sch[p2] - (HT == 1 ? 0x0404 : 0x04040404);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int st = NST - SPL; st < NST; ++st) {
+      const int t0 = first + st * step;
+      if (t0 < vis_end)
+        issue_tile<FP8>(kbase + (int64_t)t0 * G::ROW, sbase + t0, my_ring + st * SSTRIDE, goff, lane, min(32, S - t0));
     }
   }
 
@@ -281,9 +433,8 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
     const int n_after = min(NST - 1, (vis_end - 1 - tile) / step);
     wait_vmcnt(n_after * OPS + min(iter, NST));
     ++iter;
-    const uint32_t la = my_ring + (uint32_t)(stage * G::BYTES);
+    const uint32_t la = my_ring + (uint32_t)(stage * SSTRIDE);
     const int key = tile + col;
-    bf16x8 bop[8];
     float sc = 1.0f;
     i32x4 raw[NCH];
     if constexpr (FP8) {
@@ -296,23 +447,31 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
     // the stage is free again: refill it with the tile NST steps ahead
     const int tn = tile + NST * step;
     if (tn < vis_end) issue_tile<FP8>(kbase + (int64_t)tn * G::ROW, sbase + tn, la, goff, lane, min(32, S - tn));
+    stage = stage + 1 == NST ? 0 : stage + 1;
+    f32x16 acc[HT];
     if constexpr (FP8) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 u = make_uint4((uint32_t)raw[j][0], (uint32_t)raw[j][1], (uint32_t)raw[j][2], (uint32_t)raw[j][3]);
-        fp8x16_to_bf16(u, bop[2 * j], bop[2 * j + 1]);
+      const i32x8 b0 = cat8(raw[0], raw[1]), b1 = cat8(raw[2], raw[3]);
+      acc[0] = f8_dot<0>(ahi[0][0], ahi[0][1], alo[0][0], alo[0][1], b0, b1, sch[0], scl[0]);
+      if constexpr (HT >= 2) acc[1] = f8_dot<2>(ahi[1][0], ahi[1][1], alo[1][0], alo[1][1], b0, b1, sch[0], scl[0]);
+      if constexpr (HT >= 4) {
+        acc[HT - 2] = f8_dot<0>(ahi[HT - 2][0], ahi[HT - 2][1], alo[HT - 2][0], alo[HT - 2][1], b0, b1,
+                                sch[(HT - 1) / 2], scl[(HT - 1) / 2]);
+        acc[HT - 1] = f8_dot<2>(ahi[HT - 1][0], ahi[HT - 1][1], alo[HT - 1][0], alo[HT - 1][1], b0, b1,
+                                sch[(HT - 1) / 2], scl[(HT - 1) / 2]);
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) bop[kk] = __builtin_bit_cast(bf16x8, raw[kk]);
+      for (int t = 0; t < HT; ++t) {
+        f32x16 c = {};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t][kk], __builtin_bit_cast(bf16x8, raw[kk]), c, 0, 0, 0);
+        acc[t] = c;
+      }
     }
-    stage = stage + 1 == NST ? 0 : stage + 1;
     float part = 0.0f;
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t][kk], bop[kk], acc, 0, 0, 0);
       // weights via the asm read as well: a compiler-visible LDS read here would
       // be made to wait for every outstanding key load
       const uint32_t wa = lds_addr(&sw[(hf * HT + t) * 16]);
@@ -321,7 +480,7 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) part = fmaf(__int_as_float(wr[i4][e]), relu_bits(acc[4 * i4 + e]), part);
+        for (int e = 0; e < 4; ++e) part = fmaf(__int_as_float(wr[i4][e]), relu_bits(acc[t][4 * i4 + e]), part);
       }
     }
     // lanes 0..31 add the partial sum of lanes 32..63 (same key, other heads)
