@@ -46,6 +46,48 @@ def test_decode_heads_and_tail(key, H):
     assert_scores_close(g, o, f"{key} H={H}")
 
 
+@pytest.mark.parametrize("spread", [False, True])
+@pytest.mark.parametrize("H", [8, 64, 100])
+def test_fp8_keys_summation_bound(H, spread):
+    """fp8 keys against bf16 queries: the query enters the fp8 MFMA as two E4M3
+    halves that add up to it, so the products are exact and only the MFMA's sums
+    round.  The GPU score stays within 1e-4 of the absolute condition
+    scale_s * sum_h |w_h| sum_i |q_hi k_si| of the fp64 oracle (measured: 3e-6 on the
+    workload's distribution, 3e-5 with the spread below), 200 times tighter than the
+    general score tolerance; a query rounded to a single E4M3 half is off by 5e-3.
+    The halves reproduce every query value of a scale run (the 32 dimensions
+    16 j + [0, 16) and 64 + 16 j + [0, 16)) down to 2^-13 of the run's maximum m;
+    smaller values may be off by up to 2^-21 m, which the bound adds per element.
+    spread: query values scaled by powers of two over 24 binades, so that runs mix
+    magnitudes far below their maximum."""
+    print("fp8 summation bound", H, spread, flush=True)
+    sp = workloads.spec("batched_decode", B=2, S=3001, H=H, seed=0x5EED0150 + H + 7 * spread)
+    x = workloads.indexer_inputs(sp)
+    if spread:
+        rng = np.random.default_rng(0x5EED0151 + H)
+        qf = (x["q"].astype(np.uint32) << 16).view(np.float32)
+        qf = qf * np.exp2(rng.integers(-20, 5, size=qf.shape)).astype(np.float32)
+        x["q"] = (qf.view(np.uint32) >> 16).astype(np.uint16)
+    g = li.indexer_score(dev(x["q"], "bf16"), dev(x["w"]), dev(x["k"], "fp8"), dev(x["k_scale"]))
+    torch.cuda.synchronize()
+    g = g.cpu().numpy().astype(np.float64)
+    o = oracle.indexer_score(x["q"], oracle.BF16, x["w"], x["k"], oracle.FP8_E4M3, x["k_scale"])
+    lut = np.array([oracle.dec_e4m3(c) for c in range(256)])
+    kabs = np.abs(lut[x["k"]])                                   # [B, S, d]
+    qabs = np.abs((x["q"].astype(np.uint32) << 16).view(np.float32).astype(np.float64))  # [B, 1, H, d]
+    v = np.einsum("bh,bhd->bd", np.abs(x["w"][:, 0].astype(np.float64)), qabs[:, 0])
+    cond = x["k_scale"].astype(np.float64) * np.einsum("bsd,bd->bs", kabs, v)
+    qr = qabs[:, 0].reshape(qabs.shape[0], H, 2, 4, 16)           # [B, H, half, run, 16]
+    m = qr.max(axis=(2, 4), keepdims=True)
+    ex = np.floor(np.log2(np.where(m > 0, m, 1.0)))
+    e_split = np.where(qr < np.exp2(ex - 13), np.exp2(-21.0) * m, 0.0).reshape(qabs.shape[0], H, 128)
+    vs = np.einsum("bh,bhd->bd", np.abs(x["w"][:, 0].astype(np.float64)), e_split)
+    split = x["k_scale"].astype(np.float64) * np.einsum("bsd,bd->bs", kabs, vs)
+    err = np.abs(g - o)
+    bound = 1e-4 * cond + split + 1e-6 * np.abs(o)
+    assert (err <= bound).all(), f"H={H}: worst error / condition {np.max(err / np.maximum(cond, 1e-300)):.3e}"
+
+
 @pytest.mark.parametrize("combo", [("f32", "f32"), ("f32", "fp8"), ("f32", "bf16"), ("bf16", "f32")])
 def test_fp32_paths(combo):
     qt, kt = combo
