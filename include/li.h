@@ -131,10 +131,17 @@ li_status li_topk_select(const float *scores, const int32_t *nv, int R, int S, i
  * li_indexer_topk -- li_indexer_score followed by li_topk_select, with the same
  * arguments, without handing the score matrix back: for many query rows (a prefill
  * chunk) the selection runs inside the scoring kernel and the [B*T, S] scores are
- * never written to memory.
+ * never written to memory.  For few long rows (decode) the scoring kernel lists
+ * each row's candidates above a threshold taken from a sample of its own scores,
+ * and one exact pass selects among them.
  *
  *   idx [B*T, topk] int32, val [B*T, topk] fp32 or NULL (ascending key index)
- *   ws  workspace of at least li_indexer_topk_workspace_bytes(...) bytes
+ *   ws  workspace of at least li_indexer_topk_workspace_bytes(...) bytes.  Its
+ *       last B*T*1024 words hold per-row flags of the decode path, which every call
+ *       leaves at zero: a zero-filled workspace is ready for the first call.  Any
+ *       other contents give the same results, that call being slower (its rows
+ *       wait up to 200 us, then select over the whole row).  Calls that share a
+ *       workspace must not overlap.
  *
  * Requires q_type == LI_BF16 and k_type in {LI_BF16, LI_FP8_E4M3}, or the fp32
  * combinations accepted by li_indexer_score.  1 <= topk <= LI_TOPK_MAX.

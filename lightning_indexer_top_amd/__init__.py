@@ -110,7 +110,9 @@ def _workspace(nbytes, device, workspace=None):
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError(f"workspace needs {nbytes} bytes")
         return workspace, workspace.numel() * workspace.element_size()
-    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    # zero-filled: the fused decode selection keeps per-row counters there, which a
+    # zeroed workspace has ready (any contents give the same results)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
 def indexer_score(q, w, k, k_scale=None, nv=None, out=None):

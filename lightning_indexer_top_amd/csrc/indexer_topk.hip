@@ -365,7 +365,8 @@ size_t indexer_topk_ws_bytes(int B, int T, int S, int H, int topk) {
   (void)H;
   // the fused path needs no workspace; sized for the score-then-select path,
   // which any shape may take
-  return align256((size_t)B * T * S * sizeof(float)) + topk_ws_bytes(B * T, S, topk);
+  return align256((size_t)B * T * S * sizeof(float)) + topk_ws_bytes(B * T, S, topk) +
+         align256((size_t)B * T * 1024 * sizeof(uint32_t));
 }
 
 hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const void* k, int k_type, const float* ks,
@@ -387,10 +388,24 @@ hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const 
     return hipGetLastError();
   }
   float* scores = (float*)ws;
+  void* tws = (uint8_t*)ws + align256((size_t)B * T * S * sizeof(float));
+  if (select_score_apply(q_type, k_type, B * T, S, H, topk)) {
+    // few long rows: the scoring kernel lists the candidates, one finalize selects
+    uint32_t *unused, *bcnt;
+    float* cval;
+    int32_t* cid;
+    topk_mb_layout(tws, B * T, S, &unused, &bcnt, &cval, &cid);
+    // sample flags (1024 words per row) after the top-k's area
+    uint32_t* counters = (uint32_t*)((uint8_t*)tws + topk_ws_bytes(B * T, S, topk));
+    int P = 0, chunk = 0;
+    hipError_t e = launch_score_select(q, k_type, w, k, ks, nv, B, T, S, H, topk, scores, counters, bcnt, cval, cid,
+                                       &P, &chunk, st);
+    if (e != hipSuccess) return e;
+    return launch_topk_finalize_f32(scores, nv, B * T, S, topk, P, chunk, bcnt, cval, cid, idx, val, counters, st);
+  }
   hipError_t e = launch_score(q, q_type, w, k, k_type, ks, nv, B, T, S, H, scores, st);
   if (e != hipSuccess) return e;
-  return launch_topk_f32(scores, nv, B * T, S, topk, idx, val,
-                         (uint8_t*)ws + align256((size_t)B * T * S * sizeof(float)), st);
+  return launch_topk_f32(scores, nv, B * T, S, topk, idx, val, tws, st);
 }
 
 }  // namespace li

@@ -22,6 +22,7 @@
 // key row.
 #include "common.h"
 #include "launch.h"
+#include "select.h"
 
 namespace li {
 
@@ -266,11 +267,94 @@ __device__ __forceinline__ f32x16 f8_dot(const i32x8 h0, const i32x8 h1, const i
   return c;
 }
 
-template <int HT, bool FP8, int NST, int WPE>
+// Selection epilogue of the scoring kernel (decode rows, see select_score_apply):
+// after every wave of the workgroup has stored its scores, the row's threshold is
+// the j-th largest of the samples (sample_rank) and the workgroup lists its own
+// visible range's entries at or above it into its region of the candidate list.
+// Samples: the first 32-key tile of the row's waves (every stride-th wave when
+// there are more than 128 of them), stored device-coherent by their waves, which
+// raise their own flag (counters[r * SEL_FLAGS + wave of the row]) right after that
+// tile; the threshold is taken once all P * 4 flags of the row are up (waiting for
+// that, boundedly), else the region is marked unfiltered.
+// Whatever the threshold, the finalize's check (at least k listed) keeps the
+// selection exact.
+constexpr int SEL_FLAGS = 1024;  // sample flags per row: 256 workgroups x 4 waves
+
+__device__ void score_select_epilogue(const float* __restrict__ out_row, int r, int nvis, int key0, int key_end,
+                                      int kpb, int k, const uint32_t* __restrict__ counters,
+                                      uint32_t* __restrict__ bcnt, float* __restrict__ cval,
+                                      int32_t* __restrict__ cid, int S, uint8_t* lds) {
+  constexpr int SE = 16;  // samples per thread: at most 4,096
+  uint32_t* hist = (uint32_t*)lds;  // 256 bins
+  uint32_t* wsum = hist + 256;      // 4 waves
+  uint32_t* res = wsum + 4;         // 2
+  uint32_t* cnt_uw = res + 4;       // MB_BATCH * 4 + 1
+  uint32_t* s_flag = cnt_uw + 72;   // -, sample count
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int P = gridDim.x, bx = blockIdx.x;
+  uint32_t* bc = bcnt + (int64_t)r * P + bx;
+  if (nvis <= k) {  // the final pass takes the whole row
+    if (tid == 0) *bc = 0u;
+    return;
+  }
+  const int W = P * 4;  // waves of the row, one flag each
+  // Workgroups of a fast XCD can finish before a slow one's waves have stored their
+  // sample; every workgroup of the launch is resident (one per slot), so waiting a
+  // little costs nothing on the critical path.  The wait is bounded by the realtime
+  // clock (100 MHz), after which the region goes unfiltered.
+  const uint32_t* fl = counters + (int64_t)r * SEL_FLAGS;
+  const uint64_t give_up = __builtin_amdgcn_s_memrealtime() + 20000;  // 200 us
+  bool all_set = false;
+  for (;;) {
+    bool mine_set = true;
+    for (int i = tid; i < W; i += 256)
+      mine_set = mine_set && __hip_atomic_load(&fl[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1u;
+    const bool expired = tid == 0 && __builtin_amdgcn_s_memrealtime() >= give_up;
+    all_set = __syncthreads_and(mine_set);
+    // both decisions are workgroup-wide votes, so every wave leaves together
+    if (all_set || __syncthreads_or(expired)) break;
+    __builtin_amdgcn_s_sleep(127);  // about 3 us between polls
+  }
+  if (tid == 0) s_flag[1] = 0;
+  __syncthreads();
+  if (!all_set) {
+    if (tid == 0) *bc = REGION_UNFILTERED;
+    return;
+  }
+  const int stride = (W + 127) / 128;  // at most 128 sampled wave tiles
+  uint32_t key[SE];
+  bool valid[SE];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int e = 0; e < SE; ++e) {
+    const int s = e * 256 + tid;
+    const int wt = (s >> 5) * stride, bx2 = wt >> 2;
+    const int kk = bx2 * kpb + 32 * (wt & 3) + (s & 31);
+    valid[e] = wt < W && kk < min(bx2 * kpb + kpb, nvis);
+    const float x = __hip_atomic_load(&out_row[valid[e] ? kk : 0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    key[e] = valid[e] ? ord_f32(x) : 0u;
+    mine += valid[e] ? 1u : 0u;
+  }
+  mine = wave_incl_scan(mine);
+  if (lane == 63) atomicAdd(&s_flag[1], mine);
+  __syncthreads();
+  const int m = (int)s_flag[1];
+  const uint32_t tau = block_kth8<256, SE, 2>(key, valid, sample_rank(k, m, nvis), hist, wsum, res);
+  const int vis_end = min(key_end, nvis);
+  const uint32_t written = key0 < vis_end ? filter_region<float>(out_row, key0, vis_end, tau,
+                                                                  cval + (int64_t)r * S + key0,
+                                                                  cid + (int64_t)r * S + key0, cnt_uw)
+                                          : 0u;
+  if (tid == 0) *bc = written;
+  (void)wid;
+}
+
+template <int HT, bool FP8, int NST, int WPE, bool SEL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ k,
                          const float* __restrict__ ks, const int32_t* __restrict__ nv, int T, int S, int H,
-                         int keys_per_block, float* __restrict__ scores) {
+                         int keys_per_block, float* __restrict__ scores, int topk, uint32_t* __restrict__ counters,
+                         uint32_t* __restrict__ bcnt, float* __restrict__ cval, int32_t* __restrict__ cid) {
   typedef TileGeom<FP8> G;
   static_assert(NST >= 1 && NST <= 3, "ring depth");
   // fp8: the query codes occupy the last SPL ring stages until every wave has
@@ -295,8 +379,9 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
 
   // LDS: the head weights (2 x HT x 16 floats), then the ring, stage-major: stage st
   // of wave w at ring0 + (st * 4 + w) * BYTES
-  uint8_t* ring = lds + 2 * HT * 16 * sizeof(float);
-  ring = (uint8_t*)(((uintptr_t)ring + 127) & ~(uintptr_t)127);
+  // (dynamic LDS starts at offset 0: the kernel has no static LDS; aligning the
+  // offset, not the pointer, keeps every access to it an LDS instruction)
+  uint8_t* ring = lds + ((2 * HT * 16 * sizeof(float) + 127) & ~(size_t)127);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ring0 = lds_addr(ring);
   const uint32_t my_ring = ring0 + (uint32_t)(wave_u * G::BYTES);
@@ -330,6 +415,12 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
     sw[(hf2 * HT + t) * 16 + i] = hh < H ? w[(int64_t)r * H + hh] : 0.0f;
   }
 
+  // key of the tile of this wave's ring stage st in the prologue, or -1 for none
+  auto pro_tile = [&](int st) -> int {
+    const int t0 = first + st * step;
+    return t0 < vis_end ? t0 : -1;
+  };
+
   // A operand.  bf16: query heads t*32 + col, dims [64 hf, 64 hf + 64), from global.
   // fp8: hi / lo codes and scale bytes, through the block's split in LDS.
   bf16x8 a[FP8 ? 1 : HT][FP8 ? 1 : 8];
@@ -340,8 +431,8 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
     __syncthreads();
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
-      const int t0 = first + st * step;
-      if (t0 < vis_end)
+      const int t0 = pro_tile(st);
+      if (t0 >= 0)
         issue_tile<FP8>(kbase + (int64_t)t0 * G::ROW, sbase + t0, my_ring + st * SSTRIDE, goff, lane, min(32, S - t0));
     }
 #pragma unroll
@@ -374,8 +465,8 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < NST - SPL; ++st) {
-      const int t0 = first + st * step;
-      if (t0 < vis_end)
+      const int t0 = pro_tile(st);
+      if (t0 >= 0)
         issue_tile<FP8>(kbase + (int64_t)t0 * G::ROW, sbase + t0, my_ring + st * SSTRIDE, goff, lane, min(32, S - t0));
     }
     uint8_t* split = ring + (NST - SPL) * SSTRIDE;
@@ -419,12 +510,54 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
     lds_barrier();
 #pragma unroll
     for (int st = NST - SPL; st < NST; ++st) {
-      const int t0 = first + st * step;
-      if (t0 < vis_end)
+      const int t0 = pro_tile(st);
+      if (t0 >= 0)
         issue_tile<FP8>(kbase + (int64_t)t0 * G::ROW, sbase + t0, my_ring + st * SSTRIDE, goff, lane, min(32, S - t0));
     }
   }
 
+  // ReLU x weight head sum of the tile in raw[] (lanes 0..31 end with the key's total)
+#define LI_TILE_PART() \
+  do { \
+    f32x16 acc[HT]; \
+    if constexpr (FP8) { \
+      const i32x8 b0 = cat8(raw[0], raw[1]), b1 = cat8(raw[2], raw[3]); \
+      acc[0] = f8_dot<0>(ahi[0][0], ahi[0][1], alo[0][0], alo[0][1], b0, b1, sch[0], scl[0]); \
+      if constexpr (HT >= 2) acc[1] = f8_dot<2>(ahi[1][0], ahi[1][1], alo[1][0], alo[1][1], b0, b1, sch[0], scl[0]); \
+      if constexpr (HT >= 4) { \
+        acc[HT - 2] = f8_dot<0>(ahi[HT - 2][0], ahi[HT - 2][1], alo[HT - 2][0], alo[HT - 2][1], b0, b1, \
+                                sch[(HT - 1) / 2], scl[(HT - 1) / 2]); \
+        acc[HT - 1] = f8_dot<2>(ahi[HT - 1][0], ahi[HT - 1][1], alo[HT - 1][0], alo[HT - 1][1], b0, b1, \
+                                sch[(HT - 1) / 2], scl[(HT - 1) / 2]); \
+      } \
+    } else { \
+_Pragma("unroll") \
+      for (int t = 0; t < HT; ++t) { \
+        f32x16 c = {}; \
+_Pragma("unroll") \
+        for (int kk = 0; kk < 8; ++kk) \
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t][kk], __builtin_bit_cast(bf16x8, raw[kk]), c, 0, 0, 0); \
+        acc[t] = c; \
+      } \
+    } \
+    part = 0.0f; \
+_Pragma("unroll") \
+    for (int t = 0; t < HT; ++t) { \
+      /* weights via the asm read as well: a compiler-visible LDS read here would */ \
+      /* be made to wait for every outstanding key load */ \
+      const uint32_t wa = lds_addr(&sw[(hf * HT + t) * 16]); \
+      i32x4 wr[4]; \
+      lds_read4(wr[0], wr[1], wr[2], wr[3], wa, wa + 16, wa + 32, wa + 48); \
+_Pragma("unroll") \
+      for (int i4 = 0; i4 < 4; ++i4) { \
+_Pragma("unroll") \
+        for (int e = 0; e < 4; ++e) part = fmaf(__int_as_float(wr[i4][e]), relu_bits(acc[t][4 * i4 + e]), part); \
+      } \
+    } \
+    /* lanes 0..31 add the partial sum of lanes 32..63 (same key, other heads) */ \
+    part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, \
+                                                             false)[1]); \
+  } while (0)
   int stage = 0, iter = 0;
   for (int tile = first; tile < vis_end; tile += step) {
     // vmcnt counts loads and stores in issue order.  Issued after this tile's
@@ -449,46 +582,35 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
     const int tn = tile + NST * step;
     if (tn < vis_end) issue_tile<FP8>(kbase + (int64_t)tn * G::ROW, sbase + tn, la, goff, lane, min(32, S - tn));
     stage = stage + 1 == NST ? 0 : stage + 1;
-    f32x16 acc[HT];
-    if constexpr (FP8) {
-      const i32x8 b0 = cat8(raw[0], raw[1]), b1 = cat8(raw[2], raw[3]);
-      acc[0] = f8_dot<0>(ahi[0][0], ahi[0][1], alo[0][0], alo[0][1], b0, b1, sch[0], scl[0]);
-      if constexpr (HT >= 2) acc[1] = f8_dot<2>(ahi[1][0], ahi[1][1], alo[1][0], alo[1][1], b0, b1, sch[0], scl[0]);
-      if constexpr (HT >= 4) {
-        acc[HT - 2] = f8_dot<0>(ahi[HT - 2][0], ahi[HT - 2][1], alo[HT - 2][0], alo[HT - 2][1], b0, b1,
-                                sch[(HT - 1) / 2], scl[(HT - 1) / 2]);
-        acc[HT - 1] = f8_dot<2>(ahi[HT - 1][0], ahi[HT - 1][1], alo[HT - 1][0], alo[HT - 1][1], b0, b1,
-                                sch[(HT - 1) / 2], scl[(HT - 1) / 2]);
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < HT; ++t) {
-        f32x16 c = {};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t][kk], __builtin_bit_cast(bf16x8, raw[kk]), c, 0, 0, 0);
-        acc[t] = c;
-      }
+    float part;
+    LI_TILE_PART();
+    if (hf == 0 && key < key_end) {
+      const float v = key < nvis ? part * sc : -INFINITY;
+      if (SEL && iter == 1)  // the wave's sample tile: stored device-coherent
+        __hip_atomic_store(&out_row[key], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        out_row[key] = v;
     }
-    float part = 0.0f;
-#pragma unroll
-    for (int t = 0; t < HT; ++t) {
-      // weights via the asm read as well: a compiler-visible LDS read here would
-      // be made to wait for every outstanding key load
-      const uint32_t wa = lds_addr(&sw[(hf * HT + t) * 16]);
-      i32x4 wr[4];
-      lds_read4(wr[0], wr[1], wr[2], wr[3], wa, wa + 16, wa + 32, wa + 48);
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) part = fmaf(__int_as_float(wr[i4][e]), relu_bits(acc[t][4 * i4 + e]), part);
-      }
+    if (SEL && iter == 1) {
+      // publish the sample at once: wait for the store (and the loads before it;
+      // every tile later waited for is issued after this point, so the counts
+      // above stay exact), then raise the wave's own flag (a word of its own: no
+      // two waves write one address)
+      LI_WAIT_VMCNT(0);
+      if (lane == 0)
+        __hip_atomic_store(&counters[(int64_t)r * SEL_FLAGS + blockIdx.x * 4 + wave], 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
-    // lanes 0..31 add the partial sum of lanes 32..63 (same key, other heads)
-    part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false,
-                                                             false)[1]);
-    if (hf == 0 && key < key_end) out_row[key] = key < nvis ? part * sc : -INFINITY;
   }
+  if constexpr (SEL) {
+    if (iter == 0 && lane == 0)  // no tile: flagged without a sample
+      __hip_atomic_store(&counters[(int64_t)r * SEL_FLAGS + blockIdx.x * 4 + wave], 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    LI_WAIT_VMCNT(0);
+    __syncthreads();
+    score_select_epilogue(out_row, r, nvis, key0, key_end, keys_per_block, topk, counters, bcnt, cval, cid, S, lds);
+  }
+#undef LI_TILE_PART
 }
 
 template <int HT, bool FP8>
@@ -588,19 +710,19 @@ hipError_t launch_score(const void* q, int q_type, const float* w, const void* k
     const bool f8 = k_type == DT_FP8;
     const uint16_t* qq = (const uint16_t*)q;
     const uint8_t* kk = (const uint8_t*)k;
-#define LI_LAUNCH_STREAM(HT_, F8_)                                                                                  \
+#define LI_LAUNCH_STREAM(HT_, F8_)                                                                            \
   do {                                                                                                              \
     typedef StreamCfg<HT_, F8_> C;                                                                                  \
-    auto kern = score_stream_kernel<HT_, F8_, C::NST, C::WPE>;                                                      \
+    auto kern = score_stream_kernel<HT_, F8_, C::NST, C::WPE, false>;                                               \
     const size_t lds = stream_lds_bytes<HT_, F8_>();                                                                \
     const int kpb = stream_keys_per_block(R, S, C::BPC);                                                            \
     dim3 grid((S + kpb - 1) / kpb, R);                                                                              \
     static const bool attr = [&] {                                                                                  \
-      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);        \
+      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);          \
       return true;                                                                                                  \
     }();                                                                                                            \
     (void)attr;                                                                                                     \
-    kern<<<grid, 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores);                                         \
+    kern<<<grid, 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, 0, nullptr, nullptr, nullptr, nullptr);  \
   } while (0)
     if (H <= 32) {
       if (f8) LI_LAUNCH_STREAM(1, true); else LI_LAUNCH_STREAM(1, false);
@@ -636,6 +758,67 @@ hipError_t launch_score(const void* q, int q_type, const float* w, const void* k
     const uint16_t* qq = (const uint16_t*)q;
     score_valu_kernel<uint16_t, 0><<<grid, 256, lds, st>>>(qq, w, k, ks, nv, T, S, H, scores);
   }
+  return hipGetLastError();
+}
+
+// ---- scoring with the selection epilogue (few long rows) ----------------------
+template <int HT, bool F8>
+static int select_blocks_per_row(int R, int S, int* kpb_out) {
+  const int kpb = stream_keys_per_block(R, S, StreamCfg<HT, F8>::BPC);
+  if (kpb_out) *kpb_out = kpb;
+  return (S + kpb - 1) / kpb;
+}
+
+bool select_score_apply(int q_type, int k_type, int R, int S, int H, int topk) {
+  if (q_type != DT_BF16 || (k_type != DT_FP8 && k_type != DT_BF16) || H < 1 || H > 128) return false;
+  if (!topk_use_mb(R, S) || topk > 2048) return false;
+  // the finalize takes at most 256 regions per row,
+  const bool f8 = k_type == DT_FP8;
+  // and every wave streams at least eight tiles, so that the row's samples (each
+  // wave's first tile) are counted long before its workgroups finish
+  int P, kpb;
+  if (H <= 32) P = f8 ? select_blocks_per_row<1, true>(R, S, &kpb) : select_blocks_per_row<1, false>(R, S, &kpb);
+  else if (H <= 64) P = f8 ? select_blocks_per_row<2, true>(R, S, &kpb) : select_blocks_per_row<2, false>(R, S, &kpb);
+  else P = f8 ? select_blocks_per_row<4, true>(R, S, &kpb) : select_blocks_per_row<4, false>(R, S, &kpb);
+  // and all workgroups of the launch are resident at once (the epilogue may wait
+  // for the row's other workgroups to count their samples)
+  const int bpc = H <= 32 ? StreamCfg<1, true>::BPC : (H <= 64 ? StreamCfg<2, true>::BPC : StreamCfg<4, true>::BPC);
+  const int bpc_b = H <= 32 ? StreamCfg<1, false>::BPC : (H <= 64 ? StreamCfg<2, false>::BPC : StreamCfg<4, false>::BPC);
+  return P <= 256 && kpb >= 1024 && (int64_t)P * R <= (int64_t)num_cus() * (f8 ? bpc : bpc_b);
+}
+
+hipError_t launch_score_select(const void* q, int k_type, const float* w, const void* k, const float* ks,
+                               const int32_t* nv, int B, int T, int S, int H, int topk, float* scores,
+                               uint32_t* counters, uint32_t* bcnt, float* cval, int32_t* cid, int* P_out,
+                               int* chunk_out, hipStream_t st) {
+  const int R = B * T;
+  const bool f8 = k_type == DT_FP8;
+  const uint16_t* qq = (const uint16_t*)q;
+  const uint8_t* kk = (const uint8_t*)k;
+#define LI_LAUNCH_SELECT(HT_, F8_)                                                                                  \
+  do {                                                                                                              \
+    typedef StreamCfg<HT_, F8_> C;                                                                                  \
+    auto kern = score_stream_kernel<HT_, F8_, C::NST, C::WPE, true>;                                                \
+    const size_t lds = stream_lds_bytes<HT_, F8_>();                                                                \
+    int kpb;                                                                                                        \
+    const int P = select_blocks_per_row<HT_, F8_>(R, S, &kpb);                                                      \
+    static const bool attr = [&] {                                                                                  \
+      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);          \
+      return true;                                                                                                  \
+    }();                                                                                                            \
+    (void)attr;                                                                                                     \
+    *P_out = P;                                                                                                     \
+    *chunk_out = kpb;                                                                                               \
+    kern<<<dim3(P, R), 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, topk, counters, bcnt, cval, cid);   \
+  } while (0)
+  if (H <= 32) {
+    if (f8) LI_LAUNCH_SELECT(1, true); else LI_LAUNCH_SELECT(1, false);
+  } else if (H <= 64) {
+    if (f8) LI_LAUNCH_SELECT(2, true); else LI_LAUNCH_SELECT(2, false);
+  } else {
+    if (f8) LI_LAUNCH_SELECT(4, true); else LI_LAUNCH_SELECT(4, false);
+  }
+#undef LI_LAUNCH_SELECT
   return hipGetLastError();
 }
 

@@ -1,0 +1,177 @@
+// Selection building blocks shared by the top-k kernels and the scoring kernel's
+// selection epilogue (gfx950, wave64): orderable score keys, wave-aggregated LDS
+// histograms, a workgroup radix select over 8-bit digits, and the threshold filter
+// that lists a range's entries at or above a threshold in index order.
+#pragma once
+
+#include "common.h"
+
+namespace li {
+
+constexpr int MB_THREADS = 256;
+constexpr int MB_SAMPLES = 4096;
+constexpr int MB_BATCH = 16;  // loads in flight per thread
+constexpr int MB_KEEP = 8192;  // kept entries the exact final pass holds
+
+template <typename S>
+struct ScoreTraits;
+template <>
+struct ScoreTraits<float> {
+  typedef uint32_t K;
+  static constexpr int BITS = 32;
+  __device__ static K ord(float x) { return ord_f32(x); }
+};
+template <>
+struct ScoreTraits<double> {
+  typedef uint64_t K;
+  static constexpr int BITS = 64;
+  __device__ static K ord(double x) { return ord_f64(x); }
+};
+
+// hist[d] += 1 for every lane with valid set; when all such lanes of the wave
+// share one digit (scores concentrated in few bins) a single atomic adds them.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t d, bool valid) {
+  const uint64_t act = __ballot(valid);
+  if (!act) return;
+  const int first = __ffsll((unsigned long long)act) - 1;
+  const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, first);  // first is wave-uniform
+  const uint64_t same = __ballot(valid && d == d0);
+  if (same == act) {
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[d0], (uint32_t)__popcll(act));
+  } else if (valid) {
+    atomicAdd(&hist[d], 1u);
+  }
+}
+
+// The kth largest (1-based) of the valid keys held E per thread over a workgroup
+// of NT >= 256 threads, by PASSES 8-bit digits from the top (LDS histograms of
+// 256 bins).  With fewer than 4 passes the unresolved low bits come back zero:
+// the result is then the lower edge of the bucket holding the kth largest, so at
+// least kth keys are >= it.  With 4 passes *n_above receives how many valid keys
+// exceed the result.
+template <int NT, int E, int PASSES, typename K>
+__device__ __forceinline__ K block_kth8(const K (&key)[E], const bool (&valid)[E], uint32_t kth, uint32_t* hist,
+                                        uint32_t* wsum, uint32_t* res, uint32_t* n_above = nullptr) {
+  static_assert(NT >= 256 && NT % 64 == 0, "one thread per bin");
+  constexpr int NW = NT / 64;
+  constexpr int BITS = 8 * (int)sizeof(K);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  K prefix = 0, mask = 0;
+  uint32_t need = kth;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int shift = BITS - 8 - 8 * p;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      hist_add(hist, (uint32_t)(key[e] >> shift) & 255u, valid[e] && (key[e] & mask) == prefix);
+    __syncthreads();
+    // counts of digits 255, 254, ... accumulated in that order
+    const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;
+    uint32_t v = c;
+    v = wave_incl_scan(v);
+    if (lane == 63) wsum[wid] = v;
+    __syncthreads();
+    uint32_t base = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) base += w < wid ? wsum[w] : 0u;
+    const uint32_t incl = base + v, excl = incl - c;
+    if (tid < 256 && excl < need && need <= incl) {
+      res[0] = 255u - (uint32_t)tid;
+      res[1] = excl;
+    }
+    __syncthreads();
+    const uint32_t d = res[0], above = res[1];
+    __syncthreads();
+    prefix |= (K)d << shift;
+    mask |= (K)255 << shift;
+    need -= above;
+  }
+  if (n_above) *n_above = kth - need;
+  return prefix;
+}
+
+// Exclusive prefix sum of x over the workgroup (blockDim.x = NW * 64), in thread
+// order; scratch holds NW entries.
+template <int NW>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* scratch) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t incl = x;
+  incl = wave_incl_scan(incl);
+  if (lane == 63) scratch[wid] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) base += w < wid ? scratch[w] : 0u;
+  __syncthreads();
+  return base + incl - x;
+}
+
+// The entries of row[lo, hi) whose orderable key is >= t, listed in index order at
+// ov / oi (values, positions); returns how many.  A workgroup of MB_THREADS threads
+// (every thread calls it); cnt_uw holds MB_BATCH * MB_THREADS / 64 + 1 words of LDS.
+// A batch holds entries base + tid + 256 u (u < MB_BATCH), so ordering by
+// (u, wave, lane) is index order; each wave's ballots give the counts, and one
+// prefix over the (u, wave) counts gives every lane its position.
+template <typename Sc>
+__device__ __forceinline__ uint32_t filter_region(const Sc* __restrict__ row, int lo, int hi,
+                                                  typename ScoreTraits<Sc>::K t, Sc* __restrict__ ov,
+                                                  int32_t* __restrict__ oi, uint32_t* cnt_uw) {
+  constexpr int NW = MB_THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t written = 0;
+  for (int base = lo; base < hi; base += MB_THREADS * MB_BATCH) {
+    Sc x[MB_BATCH];
+#pragma unroll
+    for (int u = 0; u < MB_BATCH; ++u) {
+      const int i = base + tid + MB_THREADS * u;
+      x[u] = i < hi ? row[i] : (Sc)-INFINITY;
+    }
+    uint64_t mk[MB_BATCH];
+#pragma unroll
+    for (int u = 0; u < MB_BATCH; ++u) {
+      const int i = base + tid + MB_THREADS * u;
+      mk[u] = __ballot(i < hi && ScoreTraits<Sc>::ord(x[u]) >= t);
+      if (lane == 0) cnt_uw[u * NW + wid] = (uint32_t)__popcll(mk[u]);
+    }
+    __syncthreads();
+    // exclusive prefix of the (u, wave) counts: one wave, one entry per lane
+    static_assert(MB_BATCH * NW == 64, "one count per lane of a wave");
+    if (tid < 64) {
+      const uint32_t c = cnt_uw[tid];
+      uint32_t incl = c;
+      incl = wave_incl_scan(incl);
+      cnt_uw[tid] = incl - c;
+      if (tid == 63) cnt_uw[64] = incl;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < MB_BATCH; ++u) {
+      if ((mk[u] >> lane) & 1ull) {
+        const uint32_t pos = written + cnt_uw[u * NW + wid] + (uint32_t)__popcll(mk[u] & ((1ull << lane) - 1));
+        ov[pos] = x[u];
+        oi[pos] = base + tid + MB_THREADS * u;
+      }
+    }
+    written += cnt_uw[MB_BATCH * NW];
+    __syncthreads();
+  }
+  return written;
+}
+
+// How many of m samples of an n-entry row the threshold estimate keeps above it:
+// j = max(ceil((2k + 1024) m / n), 16), at most m.  About 2k + 1024 entries of the
+// row (at least 16 sample gaps) then clear the j-th largest sample.
+__device__ __forceinline__ uint32_t sample_rank(int k, int m, int n) {
+  int64_t j = ((int64_t)(2 * k + 1024) * m + n - 1) / n;
+  if (j < 16) j = 16;
+  if (j > m) j = m;
+  return (uint32_t)j;
+}
+
+// Region count marking a range that was not filtered (its threshold was not
+// available): the final selection then takes the whole row.
+constexpr uint32_t REGION_UNFILTERED = 0xFFFFFFFFu;
+
+}  // namespace li

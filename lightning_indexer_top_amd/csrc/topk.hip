@@ -17,26 +17,12 @@
 // One workgroup of 1024 threads handles one row.
 #include "common.h"
 #include "launch.h"
+#include "select.h"
 
 namespace li {
 
 constexpr int TK_THREADS = 1024;
 constexpr int TK_BINS = 2048;  // 11-bit digits
-
-template <typename S>
-struct ScoreTraits;
-template <>
-struct ScoreTraits<float> {
-  typedef uint32_t K;
-  static constexpr int BITS = 32;
-  __device__ static K ord(float x) { return ord_f32(x); }
-};
-template <>
-struct ScoreTraits<double> {
-  typedef uint64_t K;
-  static constexpr int BITS = 64;
-  __device__ static K ord(double x) { return ord_f64(x); }
-};
 
 // Block-wide search for the digit d such that (count of entries above d) < need
 // <= (count above d) + hist[d], scanning digits from the top.  Returns d and sets
@@ -75,21 +61,6 @@ __device__ int find_cut(const uint32_t* hist, uint32_t need, uint32_t* above, ui
   *above = (uint32_t)sh_res[1];
   __syncthreads();
   return d;
-}
-
-// hist[d] += 1 for every lane with valid set; when all such lanes of the wave
-// share one digit (scores concentrated in few bins) a single atomic adds them.
-__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t d, bool valid) {
-  const uint64_t act = __ballot(valid);
-  if (!act) return;
-  const int first = __ffsll((unsigned long long)act) - 1;
-  const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, first);  // first is wave-uniform
-  const uint64_t same = __ballot(valid && d == d0);
-  if (same == act) {
-    if ((int)(threadIdx.x & 63) == first) atomicAdd(&hist[d0], (uint32_t)__popcll(act));
-  } else if (valid) {
-    atomicAdd(&hist[d], 1u);
-  }
 }
 
 struct Sel {
@@ -273,59 +244,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restric
 //   3. one workgroup per row selects exactly among the kept entries, or over the
 //      whole row.
 // Both k-th searches are radix selects over LDS histograms (11-bit digits).
-constexpr int MB_THREADS = 256;
-constexpr int MB_SAMPLES = 4096;
-constexpr int MB_BATCH = 16;  // loads in flight per thread
-constexpr int MB_KEEP = 8192;  // kept entries the exact final pass holds
-
-// The kth largest (1-based) of the valid keys held E per thread over a workgroup
-// of NT >= 256 threads, by PASSES 8-bit digits from the top (LDS histograms of
-// 256 bins).  With fewer than 4 passes the unresolved low bits come back zero:
-// the result is then the lower edge of the bucket holding the kth largest, so at
-// least kth keys are >= it.  With 4 passes *n_above receives how many valid keys
-// exceed the result.
-template <int NT, int E, int PASSES, typename K>
-__device__ __forceinline__ K block_kth8(const K (&key)[E], const bool (&valid)[E], uint32_t kth, uint32_t* hist,
-                                        uint32_t* wsum, uint32_t* res, uint32_t* n_above = nullptr) {
-  static_assert(NT >= 256 && NT % 64 == 0, "one thread per bin");
-  constexpr int NW = NT / 64;
-  constexpr int BITS = 8 * (int)sizeof(K);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  K prefix = 0, mask = 0;
-  uint32_t need = kth;
-#pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int shift = BITS - 8 - 8 * p;
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      hist_add(hist, (uint32_t)(key[e] >> shift) & 255u, valid[e] && (key[e] & mask) == prefix);
-    __syncthreads();
-    // counts of digits 255, 254, ... accumulated in that order
-    const uint32_t c = tid < 256 ? hist[255 - tid] : 0u;
-    uint32_t v = c;
-    v = wave_incl_scan(v);
-    if (lane == 63) wsum[wid] = v;
-    __syncthreads();
-    uint32_t base = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) base += w < wid ? wsum[w] : 0u;
-    const uint32_t incl = base + v, excl = incl - c;
-    if (tid < 256 && excl < need && need <= incl) {
-      res[0] = 255u - (uint32_t)tid;
-      res[1] = excl;
-    }
-    __syncthreads();
-    const uint32_t d = res[0], above = res[1];
-    __syncthreads();
-    prefix |= (K)d << shift;
-    mask |= (K)255 << shift;
-    need -= above;
-  }
-  if (n_above) *n_above = kth - need;
-  return prefix;
-}
 
 constexpr int MB_RUNS = 64;  // sample runs of 64 entries
 
@@ -354,11 +272,8 @@ __device__ __forceinline__ typename ScoreTraits<Sc>::K sample_tau(const Sc* __re
     valid[e] = (NW * e + wid) * step + lane < n;
     key[e] = valid[e] ? ScoreTraits<Sc>::ord(x[e]) : (K)0;
   }
-  int64_t j = ((int64_t)(2 * k + 1024) * m + n - 1) / n;
-  if (j < 16) j = 16;
-  if (j > m) j = m;
   // the top 16 key bits of a float (sign, exponent, 7 mantissa bits), 24 of a double
-  return block_kth8<NT, E, sizeof(K) == 4 ? 2 : 3>(key, valid, (uint32_t)j, hist, wsum, res);
+  return block_kth8<NT, E, sizeof(K) == 4 ? 2 : 3>(key, valid, sample_rank(k, m, n), hist, wsum, res);
 }
 
 template <typename Sc>
@@ -380,22 +295,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_thresh_kernel(const Sc* __res
   if (threadIdx.x == 0) tau[r] = t;
 }
 
-// Exclusive prefix sum of x over the workgroup (blockDim.x = NW * 64), in thread
-// order; scratch holds NW entries.
-template <int NW>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* scratch) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  uint32_t incl = x;
-  incl = wave_incl_scan(incl);
-  if (lane == 63) scratch[wid] = incl;
-  __syncthreads();
-  uint32_t base = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) base += w < wid ? scratch[w] : 0u;
-  __syncthreads();
-  return base + incl - x;
-}
-
 // Kept entries go to this workgroup's region of the list in index order: a batch
 // holds entries base + tid + 256 u (u < MB_BATCH), so ordering by (u, wave, lane)
 // is index order; each wave's ballots give the counts, one prefix over the
@@ -407,59 +306,17 @@ __global__ __launch_bounds__(MB_THREADS) void topk_filter_kernel(const Sc* __res
                                                                 const typename ScoreTraits<Sc>::K* __restrict__ tau,
                                                                 Sc* __restrict__ cval, int32_t* __restrict__ cid,
                                                                 uint32_t* __restrict__ bcnt) {
-  typedef typename ScoreTraits<Sc>::K K;
-  constexpr int NW = MB_THREADS / 64;
-  __shared__ uint32_t cnt_uw[MB_BATCH * NW + 1];
+  __shared__ uint32_t cnt_uw[MB_BATCH * (MB_THREADS / 64) + 1];
   const int r = blockIdx.y, p = blockIdx.x, P = gridDim.x, tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
   int n = S;
   if (nv) n = min(max(nv[r], 0), S);
   if (n <= k) {  // the final pass takes the whole row
     if (tid == 0) bcnt[(int64_t)r * P + p] = 0u;
     return;
   }
-  const Sc* row = scores + (int64_t)r * S;
   const int lo = p * chunk, hi = min(lo + chunk, n);
-  const K t = tau[r];
-  Sc* ov = cval + (int64_t)r * S + lo;  // this workgroup's region
-  int32_t* oi = cid + (int64_t)r * S + lo;
-  uint32_t written = 0;
-  for (int base = lo; base < hi; base += MB_THREADS * MB_BATCH) {
-    Sc x[MB_BATCH];
-#pragma unroll
-    for (int u = 0; u < MB_BATCH; ++u) {
-      const int i = base + tid + MB_THREADS * u;
-      x[u] = i < hi ? row[i] : (Sc)-INFINITY;
-    }
-    uint64_t mk[MB_BATCH];
-#pragma unroll
-    for (int u = 0; u < MB_BATCH; ++u) {
-      const int i = base + tid + MB_THREADS * u;
-      mk[u] = __ballot(i < hi && ScoreTraits<Sc>::ord(x[u]) >= t);
-      if (lane == 0) cnt_uw[u * NW + wid] = (uint32_t)__popcll(mk[u]);
-    }
-    __syncthreads();
-    // exclusive prefix of the (u, wave) counts: one wave, one entry per lane
-    static_assert(MB_BATCH * NW == 64, "one count per lane of a wave");
-    if (tid < 64) {
-      const uint32_t c = cnt_uw[tid];
-      uint32_t incl = c;
-      incl = wave_incl_scan(incl);
-      cnt_uw[tid] = incl - c;
-      if (tid == 63) cnt_uw[64] = incl;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < MB_BATCH; ++u) {
-      if ((mk[u] >> lane) & 1ull) {
-        const uint32_t pos = written + cnt_uw[u * NW + wid] + (uint32_t)__popcll(mk[u] & ((1ull << lane) - 1));
-        ov[pos] = x[u];
-        oi[pos] = base + tid + MB_THREADS * u;
-      }
-    }
-    written += cnt_uw[MB_BATCH * NW];
-    __syncthreads();
-  }
+  const uint32_t written = filter_region<Sc>(scores + (int64_t)r * S, lo, hi, tau[r], cval + (int64_t)r * S + lo,
+                                             cid + (int64_t)r * S + lo, cnt_uw);
   if (tid == 0) bcnt[(int64_t)r * P + p] = written;
 }
 
@@ -477,11 +334,13 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
                                                                   const Sc* __restrict__ cval,
                                                                   const int32_t* __restrict__ cid,
                                                                   int32_t* __restrict__ idx_out,
-                                                                  Sc* __restrict__ val_out) {
+                                                                  Sc* __restrict__ val_out,
+                                                                  uint32_t* __restrict__ reset) {
   typedef typename ScoreTraits<Sc>::K K;
   constexpr int NW = TK_THREADS / 64;
   constexpr int E = MB_KEEP / TK_THREADS;
   __shared__ uint32_t off[257];
+  __shared__ int s_unfiltered;
   __shared__ uint32_t scan1[NW], scan2[NW];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wsum8[NW];
@@ -489,15 +348,24 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
   const int r = blockIdx.x, tid = threadIdx.x;
   int n = S;
   if (nv) n = min(max(nv[r], 0), S);
+  // the sample flags of a fused scoring pass (4 P per row, rows 1024 apart): clear
+  // for the next one
+  if (reset)
+    for (int i = tid; i < 4 * P; i += TK_THREADS) reset[(int64_t)r * 1024 + i] = 0u;
+  if (tid == 0) s_unfiltered = 0;
+  __syncthreads();
   // exclusive prefix of the region counts (P <= 256): one wave, four per lane
   if (tid < 64) {
     uint32_t c4[4], tot = 0;
+    bool unf = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int b = 4 * tid + e;
       c4[e] = b < P ? bcnt[(int64_t)r * P + b] : 0u;
+      unf = unf || c4[e] == REGION_UNFILTERED;
       tot += c4[e];
     }
+    if (__ballot(unf) && tid == 0) s_unfiltered = 1;
     uint32_t incl = tot;
     incl = wave_incl_scan(incl);
     uint32_t ex = incl - tot;
@@ -512,8 +380,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
   const uint32_t c = off[P];
   int32_t* io = idx_out + (int64_t)r * k;
   Sc* vo = val_out ? val_out + (int64_t)r * k : nullptr;
-  // the list is usable when at least k entries cleared the threshold
-  if (n <= k || c < (uint32_t)k || c > (uint32_t)MB_KEEP) {
+  // the list is usable when every region was filtered and at least k entries
+  // cleared the threshold
+  if (n <= k || s_unfiltered || c < (uint32_t)k || c > (uint32_t)MB_KEEP) {
     select_block<Sc>(scores + (int64_t)r * S, nullptr, n, k, io, vo);
     return;
   }
@@ -609,7 +478,26 @@ static hipError_t launch_topk_mb(const Sc* scores, const int32_t* nv, int R, int
   const int chunk = (S + P - 1) / P;
   topk_thresh_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, tau);
   topk_filter_kernel<Sc><<<dim3(P, R), MB_THREADS, 0, st>>>(scores, nv, S, k, chunk, tau, cval, cid, bcnt);
-  topk_finalize_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val);
+  topk_finalize_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val,
+                                                      nullptr);
+  return hipGetLastError();
+}
+
+void topk_mb_layout(void* ws, int R, int S, uint32_t** counters, uint32_t** bcnt, float** cval, int32_t** cid) {
+  uint8_t* p = (uint8_t*)ws;
+  *counters = (uint32_t*)p;  // the threshold area: one word per row in the fused pass
+  p += a256((size_t)R * 8);
+  *bcnt = (uint32_t*)p;
+  p += a256((size_t)R * 256 * 4);
+  *cval = (float*)p;
+  p += a256((size_t)R * S * sizeof(float));
+  *cid = (int32_t*)p;
+}
+
+hipError_t launch_topk_finalize_f32(const float* scores, const int32_t* nv, int R, int S, int k, int P, int chunk,
+                                    const uint32_t* bcnt, const float* cval, const int32_t* cid, int32_t* idx,
+                                    float* val, uint32_t* reset, hipStream_t st) {
+  topk_finalize_kernel<float><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val, reset);
   return hipGetLastError();
 }
 

@@ -90,3 +90,69 @@ def test_fused_prefill_ties_and_masks():
     nv[:5] = [0, 1, 511, 512, 513]
     x = {"q": q, "w": w, "k": kk, "nv": nv}
     _fused_check(x, None, k, "ties")
+
+
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("over,topk,nvs", [
+    (dict(B=6, S=131072), 512, None),
+    (dict(B=8, S=131072, H=8, key="bf16"), 512, None),
+    (dict(B=4, S=70001, H=100), 512, None),
+    (dict(B=6, S=140000), 512, [140000, 0, 300, 513, 139999, 70000]),
+    (dict(B=8, S=131072, H=32), 2048, None),
+    (dict(B=6, S=131072), 1, None),
+])
+def test_decode_select_fused(over, topk, nvs):
+    """Few long rows (at least 1,024 keys per scoring workgroup): li_indexer_topk runs
+    the scoring kernel with its selection epilogue (threshold from every wave's first
+    tile, per-workgroup candidate lists) and one finalize.  The result must equal
+    score-then-select bit for bit, pass the oracle band on every row, repeat on the
+    same workspace, follow other queries on that workspace, and come out the same
+    from a workspace of arbitrary bytes (whose flags send rows through the whole-row
+    selection)."""
+    print("decode select fused", over, topk, nvs, flush=True)
+    sp = workloads.spec("batched_decode", seed=0x5EED0400 + topk + over["B"], **over)
+    x, d = inputs(sp)
+    R, S, H = sp["B"], sp["S"], sp["H"]
+    nv = None
+    if nvs is not None:
+        nv = np.asarray(nvs, np.int32)
+        d["nv"] = dev(nv)
+    nb = li.indexer_topk_workspace_bytes(R, 1, S, H, topk)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    i1, v1 = li.indexer_topk(d["q"], d["w"], d["k"], topk, d["k_scale"], d["nv"], workspace=ws)
+    torch.cuda.synchronize()
+    # every row with more than k visible keys was listed by the scoring kernel: no
+    # region is marked unfiltered (regions [R][P], P of them per row), and the
+    # finalize cleared the sample flags (1024 words per row after the top-k's area)
+    off = _a256(R * S * 4)
+    bcnt = ws[off + _a256(R * 8):off + _a256(R * 8) + R * 256 * 4].view(torch.int32).cpu().numpy()
+    flags_at = off + _a256(R * 8) + _a256(R * 256 * 4) + 2 * _a256(R * S * 4)
+    flags = ws[flags_at:flags_at + R * 1024 * 4].view(torch.int32).cpu().numpy()
+    n = np.full(R, S) if nv is None else np.minimum(nv, S)
+    regions = bcnt[:R * 256]
+    assert (flags == 0).all(), "sample flags not cleared"
+    assert (regions != -1).all(), "a region was left unfiltered"
+    # other queries on the same workspace (rows reversed): every sample comes from
+    # this call, nothing from the previous one
+    qr, wr = d["q"].flip(0).contiguous(), d["w"].flip(0).contiguous()
+    i5, v5 = li.indexer_topk(qr, wr, d["k"], topk, d["k_scale"], d["nv"], workspace=ws)
+    torch.cuda.synchronize()
+    assert (ws[off + _a256(R * 8):off + _a256(R * 8) + R * 256 * 4].view(torch.int32).cpu().numpy()[:R * 256] != -1).all()
+    s5 = li.indexer_score(qr, wr, d["k"], d["k_scale"], d["nv"])
+    i6, v6 = li.topk_select(s5, topk, d["nv"])
+    assert torch.equal(i5, i6) and torch.equal(v5, v6)
+    i2, v2 = li.indexer_topk(d["q"], d["w"], d["k"], topk, d["k_scale"], d["nv"], workspace=ws)
+    ws.fill_(0xA7)
+    i3, v3 = li.indexer_topk(d["q"], d["w"], d["k"], topk, d["k_scale"], d["nv"], workspace=ws)
+    scores = li.indexer_score(d["q"], d["w"], d["k"], d["k_scale"], d["nv"])
+    i4, v4 = li.topk_select(scores, topk, d["nv"])
+    torch.cuda.synchronize()
+    for a, b in ((i1, i4), (i2, i4), (i3, i4)):
+        assert torch.equal(a, b)
+    for a, b in ((v1, v4), (v2, v4), (v3, v4)):
+        assert torch.equal(a, b)
+    o = oracle.indexer_score(x["q"], oracle.BF16, x["w"], x["k"], OT[sp["key"]], x["k_scale"], nv)
+    assert_topk_band(i1.cpu().numpy(), o, topk, nv, "fused decode select")
