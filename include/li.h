@@ -102,8 +102,12 @@ const char *li_version(void);
  *   scores  [B*T, S]      fp32 output; invisible keys get -inf
  *
  * Shapes: d == 128, 1 <= H <= 128, B, T >= 1, 1 <= S < 2^31, B*T*S < 2^40.
- * Arithmetic: bf16 x bf16 (fp8 keys are widened exactly to bf16) products with
- * fp32 accumulation; all-fp32 inputs use fp32 FMAs.
+ * Arithmetic: bf16 keys: bf16 x bf16 products, fp32 accumulation.  fp8 keys: the
+ * bf16 query is split exactly into two E4M3 halves with power-of-two run scales
+ * (exact for every value down to 2^-13 of its 32-value run's maximum) and each
+ * half meets the key codes in the block-scaled fp8 matrix core, fp32
+ * accumulation; the key scale multiplies the head sum.  All-fp32 inputs use fp32
+ * FMAs.
  * Errors: LI_ERR_NULL (q, w, k, scores; k_scale for fp8), LI_ERR_SHAPE,
  * LI_ERR_DTYPE, LI_ERR_ALIGN, LI_ERR_LAUNCH.
  */
