@@ -28,6 +28,13 @@ struct ScoreTraits<double> {
   __device__ static K ord(double x) { return ord_f64(x); }
 };
 
+// Lane exchange of a 32- or 64-bit key.
+__device__ __forceinline__ uint32_t shfl_xor_k(uint32_t x, int o) { return (uint32_t)__shfl_xor((int)x, o); }
+__device__ __forceinline__ uint64_t shfl_xor_k(uint64_t x, int o) {
+  const uint32_t l = (uint32_t)__shfl_xor((int)(uint32_t)x, o), h = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), o);
+  return ((uint64_t)h << 32) | l;
+}
+
 // hist[d] += 1 for every lane with valid set; when all such lanes of the wave
 // share one digit (scores concentrated in few bins) a single atomic adds them.
 __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t d, bool valid) {
@@ -89,6 +96,103 @@ __device__ __forceinline__ K block_kth8(const K (&key)[E], const bool (&valid)[E
     need -= above;
   }
   if (n_above) *n_above = kth - need;
+  return prefix;
+}
+
+// Digits of the wide select: 12 bits, a 4,096-bin LDS histogram.
+constexpr int KW_BITS = 12;
+constexpr int KW_BINS = 1 << KW_BITS;
+
+// The kth largest (1-based) of the valid keys held E per thread over a workgroup
+// of NT threads, exactly, with *n_above receiving how many valid keys exceed it
+// (kth <= the number of valid keys).  The bits above the highest bit in which the
+// valid keys differ are common to all of them (block minimum and maximum); the
+// rest is resolved KW_BITS bits per pass from the top.  A list of candidates
+// above a threshold spans few binades, so 32-bit keys take two or three passes
+// and 64-bit keys four or five, against four and eight 8-bit passes.
+// hist: KW_BINS words; wsum: room for 2 NT / 64 keys; res: 2 words.
+template <int NT, int E, typename K>
+__device__ __forceinline__ K block_kth_wide(const K (&key)[E], const bool (&valid)[E], uint32_t kth, uint32_t* hist,
+                                            uint32_t* wsum, uint32_t* res, uint32_t* n_above) {
+  static_assert(NT % 64 == 0 && KW_BINS % NT == 0, "whole bins per thread");
+  constexpr int NW = NT / 64;
+  constexpr int BPT = KW_BINS / NT;  // bins per thread
+  constexpr int BITS = 8 * (int)sizeof(K);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // common high bits: minimum and maximum over the valid keys
+  K mn = ~(K)0, mx = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (valid[e]) {
+      mn = key[e] < mn ? key[e] : mn;
+      mx = key[e] > mx ? key[e] : mx;
+    }
+  for (int o = 32; o > 0; o >>= 1) {
+    const K a = shfl_xor_k(mn, o), c = shfl_xor_k(mx, o);
+    mn = a < mn ? a : mn;
+    mx = c > mx ? c : mx;
+  }
+  K* wk = (K*)wsum;  // NW minima, then NW maxima
+  if (lane == 0) {
+    wk[wid] = mn;
+    wk[NW + wid] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mn = wk[w] < mn ? wk[w] : mn;
+    mx = wk[NW + w] > mx ? wk[NW + w] : mx;
+  }
+  __syncthreads();
+  const K diff = mn ^ mx;
+  // bits [0, hi] vary; the ones above are mx's
+  int hi = diff == 0 ? -1 : BITS - 1 - (sizeof(K) == 8 ? __clzll((unsigned long long)diff) : __clz((uint32_t)diff));
+  K prefix = hi + 1 >= BITS ? (K)0 : (mx >> (hi + 1)) << (hi + 1);
+  K mask = hi + 1 >= BITS ? (K)0 : ~(K)0 << (hi + 1);
+  uint32_t need = kth;
+  while (hi >= 0) {  // uniform
+    const int lo = hi - KW_BITS + 1 > 0 ? hi - KW_BITS + 1 : 0;
+    const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) hist[tid + NT * i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      hist_add(hist, (uint32_t)(key[e] >> lo) & dmask, valid[e] && (key[e] & mask) == prefix);
+    __syncthreads();
+    // thread t holds digits KW_BINS - 1 - BPT t - i, i < BPT (largest first)
+    uint32_t c[BPT], s = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      c[i] = hist[KW_BINS - 1 - BPT * tid - i];
+      s += c[i];
+    }
+    uint32_t v = wave_incl_scan(s);
+    if (lane == 63) wsum[wid] = v;
+    __syncthreads();
+    uint32_t base = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) base += w < wid ? wsum[w] : 0u;
+    uint32_t above = base + v - s;  // keys in larger digits
+    if (above < need && need <= above + s) {
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) {
+        if (above < need && need <= above + c[i]) {
+          res[0] = (uint32_t)(KW_BINS - 1 - BPT * tid - i);
+          res[1] = above;
+        }
+        above += c[i];
+      }
+    }
+    __syncthreads();
+    const uint32_t d = res[0], ab = res[1];
+    __syncthreads();
+    prefix |= (K)d << lo;
+    mask |= (K)dmask << lo;
+    need -= ab;
+    hi = lo - 1;
+  }
+  *n_above = kth - need;
   return prefix;
 }
 

@@ -342,8 +342,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
   __shared__ uint32_t off[257];
   __shared__ int s_unfiltered;
   __shared__ uint32_t scan1[NW], scan2[NW];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum8[NW];
+  __shared__ uint32_t hist[KW_BINS];
+  __shared__ uint64_t wsum8[2 * NW];  // minima and maxima of the keys, per wave
   __shared__ uint32_t res8[2];
   const int r = blockIdx.x, tid = threadIdx.x;
   int n = S;
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
   for (int e = 0; e < E; ++e) key[e] = valid[e] ? ScoreTraits<Sc>::ord(val[e]) : (K)0;
   // T: the k-th best kept key; n_gt entries lie above it
   uint32_t n_gt_all;
-  const K T = block_kth8<TK_THREADS, E, (int)sizeof(K)>(key, valid, (uint32_t)k, hist, wsum8, res8, &n_gt_all);
+  const K T = block_kth_wide<TK_THREADS, E>(key, valid, (uint32_t)k, hist, (uint32_t*)wsum8, res8, &n_gt_all);
   uint32_t ties = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) ties += valid[e] && key[e] == T ? 1u : 0u;

@@ -68,3 +68,25 @@ def test_few_long_rows_multi_workgroup_path():
     for k in (1, 64, 512, 2048):
         check(s, k, nv)
         check(s, k)
+
+
+def test_multi_workgroup_wide_select_edges():
+    # the final pass of the multi-workgroup path resolves only the bits in which its
+    # candidates differ: candidates over 60 binades of both signs, neighbours one
+    # ulp apart, a single distinct value above a sea of ties, signed zeros at the
+    # cut, and rows whose candidates straddle zero
+    print("topk wide select", flush=True)
+    rng = np.random.default_rng(9)
+    R, S = 6, 50000
+    s = np.empty((R, S), np.float32)
+    s[0] = (rng.standard_normal(S) * 10.0 ** rng.uniform(-30, 30, S)).astype(np.float32)
+    s[1] = np.float32(1.5) + np.arange(S, dtype=np.float32) * np.float32(2 ** -23)
+    s[2] = 7.0
+    s[2, rng.integers(0, S, 100)] = 7.5
+    s[3] = -np.abs(rng.standard_normal(S)).astype(np.float32)
+    s[3, :3000] = 0.0
+    s[3, 3000:6000] = -0.0
+    s[4] = rng.standard_normal(S).astype(np.float32) * 1e-3
+    s[5] = rng.integers(-3, 3, S).astype(np.float32) * np.float32(2 ** -20)
+    for k in (1, 100, 512, 2048):
+        check(s, k)
