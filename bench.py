@@ -232,20 +232,36 @@ def bench_compact(torch, li, workloads, steps, warmup):
 
     timed(torch, step, steps, warmup, ev)
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev[-steps:]]))
-    # recall@k of the two-stage result against exact scoring of the full keys (GPU)
+    # recall@k of the two-stage result against exact scoring of the full keys (GPU),
+    # and the exact scan's own time on the same data (every bf16 key read: 1.07 GB)
     q4 = d["q"].reshape(B, 1, H, 128)
     w3 = d["w"].reshape(B, 1, H)
-    ex_idx, _ = li.indexer_topk(q4, w3, d["kf"], k)
+    ex_idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    ex_ws = torch.zeros(li.lib().li_indexer_topk_workspace_bytes(B, 1, S, H, k), dtype=torch.uint8, device="cuda")
+    ev2 = []
+
+    def exact(i):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        li.indexer_topk(q4, w3, d["kf"], k, with_values=False, workspace=ex_ws, out=(ex_idx, None))
+        e1.record()
+        ev2.append((e0, e1))
+
+    timed(torch, exact, steps, warmup, ev2)
+    exact_ms = float(np.mean([a.elapsed_time(b) for a, b in ev2[-steps:]]))
     torch.cuda.synchronize()
     a, b = idx.cpu().numpy(), ex_idx.cpu().numpy()
     recall = float(np.mean([len(np.intersect1d(a[i], b[i])) / k for i in range(B)]))
     stage1_bytes = B * S * 36
     stage2_bytes = B * m * 256
     gbs = (stage1_bytes + stage2_bytes) / (ms * 1e-3) / 1e9
-    log(f"[compact] {ms * 1e3:.1f} us, {gbs:.0f} GB/s algorithmic, recall@{k} {recall:.4f}")
+    log(f"[compact] {ms * 1e3:.1f} us, {gbs:.0f} GB/s algorithmic, recall@{k} {recall:.4f}; "
+        f"exact scan {exact_ms * 1e3:.1f} us")
     return {"workload": "compact_search B=32 S=131072 int8 32-d shortlist 2048 -> top-512", "ms": round(ms, 4),
             "value": round(B * S / (ms * 1e-3), 1), "unit": "keys/s", "gbs_algorithmic": round(gbs, 1),
-            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "recall_at_512_vs_exact": round(recall, 4)}
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "recall_at_512_vs_exact": round(recall, 4),
+            "exact_scan_ms": round(exact_ms, 4),
+            "exact_scan_gbs": round(B * S * 256 / (exact_ms * 1e-3) / 1e9, 1)}
 
 
 def bench_select_attend(torch, li, workloads, steps, warmup):
@@ -366,6 +382,9 @@ def main():
                    "dim": 128, "key_format": "fp8 e4m3 + fp32 scale", "topk": 512,
                    "step": "indexer_score + topk_select", "input_replicas": dec["replicas"]},
         "roofline": dec["roofline"],
+        # the scoring kernel alone (keys scored per second over its own duration)
+        "score_keys_per_s": round(dec["keys"] / (dec["score_ms"] * 1e-3), 1),
+        "score_frac_hbm": dec["roofline"]["frac"],
     }
     if not args.no_cpu:
         log("[cpu] timing the oracle on a bounded sample")
