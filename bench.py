@@ -141,8 +141,22 @@ def bench_decode(torch, li, workloads, steps, warmup):
         traffic = round((SCORE_TRAFFIC["fetch_kib"] + SCORE_TRAFFIC["write_kib"]) * 1024)
     log(f"[decode] step {ms * 1e3:.1f} us, score kernel {score_ms * 1e3:.1f} us ({score_in_step_ms * 1e3:.1f} us "
         f"between the step's events) -> {achieved:.0f} GB/s")
+    # the same step through the fused entry point (li_indexer_topk: the scoring
+    # kernel lists candidates above a sampled threshold, one exact pass selects)
+    fws_n = L.li_indexer_topk_workspace_bytes(B, 1, S, H, k)
+    fws = torch.zeros(fws_n, dtype=torch.uint8, device="cuda")
+    fused_args = [(_p(q), li.LI_BF16, _p(w), _p(keys[r]), li.LI_FP8_E4M3, _p(scales[r]), None, B, 1, S, H, 128, k,
+                   _p(idx), _p(val), _p(fws), ctypes.c_size_t(fws_n), stream) for r in range(n_rep)]
+
+    def fstep(i):
+        if L.li_indexer_topk(*fused_args[i % n_rep]):
+            raise RuntimeError(L.li_last_error().decode())
+
+    fused_ms = timed(torch, fstep, steps, warmup) / steps
+    log(f"[decode] fused step {fused_ms * 1e3:.1f} us")
     return {
         "ms": ms, "score_ms": score_ms, "score_in_step_ms": score_in_step_ms, "keys": n_keys, "replicas": n_rep,
+        "fused_ms": fused_ms,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "score_stream_kernel (fp8 keys, 64 heads)",
@@ -385,6 +399,9 @@ def main():
         # the scoring kernel alone (keys scored per second over its own duration)
         "score_keys_per_s": round(dec["keys"] / (dec["score_ms"] * 1e-3), 1),
         "score_frac_hbm": dec["roofline"]["frac"],
+        # the same step through li_indexer_topk (scoring kernel with a selection epilogue)
+        "fused_step_ms": round(dec["fused_ms"], 5),
+        "fused_step_keys_per_s": round(dec["keys"] / (dec["fused_ms"] * 1e-3), 1),
     }
     if not args.no_cpu:
         log("[cpu] timing the oracle on a bounded sample")
