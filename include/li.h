@@ -140,12 +140,12 @@ li_status li_topk_select(const float *scores, const int32_t *nv, int R, int S, i
  * and one exact pass selects among them.
  *
  *   idx [B*T, topk] int32, val [B*T, topk] fp32 or NULL (ascending key index)
- *   ws  workspace of at least li_indexer_topk_workspace_bytes(...) bytes.  Its
- *       last B*T*1024 words hold per-row flags of the decode path, which every call
- *       leaves at zero: a zero-filled workspace is ready for the first call.  Any
- *       other contents give the same results, that call being slower (its rows
- *       wait up to 200 us, then select over the whole row).  Calls that share a
- *       workspace must not overlap.
+ *   ws  workspace of at least li_indexer_topk_workspace_bytes(...) bytes.  The
+ *       decode path keeps per-row flags there (after the score and top-k areas),
+ *       which every call leaves at zero: a zero-filled workspace is ready for the
+ *       first call.  Any other contents give the same results, that call being
+ *       slower (its rows wait up to 200 us, then select over the whole row).
+ *       Calls that share a workspace must not overlap.
  *
  * Requires q_type == LI_BF16 and k_type in {LI_BF16, LI_FP8_E4M3}, or the fp32
  * combinations accepted by li_indexer_score.  1 <= topk <= LI_TOPK_MAX.

@@ -366,7 +366,8 @@ size_t indexer_topk_ws_bytes(int B, int T, int S, int H, int topk) {
   // the fused path needs no workspace; sized for the score-then-select path,
   // which any shape may take
   return align256((size_t)B * T * S * sizeof(float)) + topk_ws_bytes(B * T, S, topk) +
-         align256((size_t)B * T * 1024 * sizeof(uint32_t));
+         align256((size_t)B * T * 1024 * sizeof(uint32_t)) + align256((size_t)B * T * 256 * sizeof(uint32_t)) +
+         align256((size_t)B * T * 128);
 }
 
 hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const void* k, int k_type, const float* ks,
@@ -395,13 +396,18 @@ hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const 
     float* cval;
     int32_t* cid;
     topk_mb_layout(tws, B * T, S, &unused, &bcnt, &cval, &cid);
-    // sample flags (1024 words per row) after the top-k's area
+    // after the top-k's area: the sample flags (1024 words per row), the threshold
+    // each region used (256 words per row), the published thresholds (one 128-byte
+    // line per row)
     uint32_t* counters = (uint32_t*)((uint8_t*)tws + topk_ws_bytes(B * T, S, topk));
+    uint32_t* tau_used = counters + align256((size_t)B * T * 1024 * sizeof(uint32_t)) / sizeof(uint32_t);
+    uint64_t* taupub = (uint64_t*)(tau_used + align256((size_t)B * T * 256 * sizeof(uint32_t)) / sizeof(uint32_t));
     int P = 0, chunk = 0;
     hipError_t e = launch_score_select(q, k_type, w, k, ks, nv, B, T, S, H, topk, scores, counters, bcnt, cval, cid,
-                                       &P, &chunk, st);
+                                       taupub, tau_used, &P, &chunk, st);
     if (e != hipSuccess) return e;
-    return launch_topk_finalize_f32(scores, nv, B * T, S, topk, P, chunk, bcnt, cval, cid, idx, val, counters, st);
+    return launch_topk_finalize_f32(scores, nv, B * T, S, topk, P, chunk, bcnt, cval, cid, idx, val, counters,
+                                    tau_used, st);
   }
   hipError_t e = launch_score(q, q_type, w, k, k_type, ks, nv, B, T, S, H, scores, st);
   if (e != hipSuccess) return e;

@@ -54,18 +54,21 @@ hipError_t launch_prefill_scores(const uint16_t* q, const float* w, const uint16
 // Its workgroups take the row's threshold from the first 32-key tile of every wave
 // (published with one flag per wave, counters[r * 1024 + wave]) and list their own
 // range's entries at or above it into the multi-workgroup top-k's regions (bcnt /
-// cval / cid, P regions of chunk keys per row); the finalize then selects exactly and
-// clears the row's flags (reset).
+// cval / cid, P regions of chunk keys per row); the first to compute a row's
+// threshold publishes it (taupub[16 r], one word per 128-byte line) for the later ones, and
+// every region records the threshold it used (tau_used[r * 256 + p]); the finalize
+// then selects exactly (if all of a row's regions used one threshold) and clears
+// the row's flags (reset).
 // select_score_apply tells whether the shape takes this path.
 bool select_score_apply(int q_type, int k_type, int R, int S, int H, int topk);
 hipError_t launch_score_select(const void* q, int k_type, const float* w, const void* k, const float* ks,
                                const int32_t* nv, int B, int T, int S, int H, int topk, float* scores,
-                               uint32_t* counters, uint32_t* bcnt, float* cval, int32_t* cid, int* P, int* chunk,
-                               hipStream_t st);
+                               uint32_t* counters, uint32_t* bcnt, float* cval, int32_t* cid, uint64_t* taupub,
+                               uint32_t* tau_used, int* P, int* chunk, hipStream_t st);
 void topk_mb_layout(void* ws, int R, int S, uint32_t** counters, uint32_t** bcnt, float** cval, int32_t** cid);
 hipError_t launch_topk_finalize_f32(const float* scores, const int32_t* nv, int R, int S, int k, int P, int chunk,
                                     const uint32_t* bcnt, const float* cval, const int32_t* cid, int32_t* idx,
-                                    float* val, uint32_t* reset, hipStream_t st);
+                                    float* val, uint32_t* reset, const uint32_t* tau_used, hipStream_t st);
 
 // fused scoring + selection for many query rows (prefill); falls back to
 // score-then-select where the fused kernel does not apply

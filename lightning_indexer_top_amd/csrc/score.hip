@@ -20,6 +20,8 @@
 // and B agree, so lane half hf carries key dimensions [64 hf, 64 hf + 64), eight
 // per K step: each lane then reads 64 (fp8) or 128 (bf16) contiguous bytes of its
 // key row.
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 #include "select.h"
@@ -283,13 +285,14 @@ constexpr int SEL_FLAGS = 1024;  // sample flags per row: 256 workgroups x 4 wav
 __device__ void score_select_epilogue(const float* __restrict__ out_row, int r, int nvis, int key0, int key_end,
                                       int kpb, int k, const uint32_t* __restrict__ counters,
                                       uint32_t* __restrict__ bcnt, float* __restrict__ cval,
-                                      int32_t* __restrict__ cid, int S, uint8_t* lds) {
+                                      int32_t* __restrict__ cid, uint64_t* __restrict__ taupub,
+                                      uint32_t* __restrict__ tau_used, uint32_t epoch, int S, uint8_t* lds) {
   constexpr int SE = 16;  // samples per thread: at most 4,096
   uint32_t* hist = (uint32_t*)lds;  // 256 bins
   uint32_t* wsum = hist + 256;      // 4 waves
   uint32_t* res = wsum + 4;         // 2
   uint32_t* cnt_uw = res + 4;       // MB_BATCH * 4 + 1
-  uint32_t* s_flag = cnt_uw + 72;   // -, sample count
+  uint32_t* s_flag = cnt_uw + 72;   // -, sample count, published-threshold found, its value
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int P = gridDim.x, bx = blockIdx.x;
   uint32_t* bc = bcnt + (int64_t)r * P + bx;
@@ -298,6 +301,22 @@ __device__ void score_select_epilogue(const float* __restrict__ out_row, int r, 
     return;
   }
   const int W = P * 4;  // waves of the row, one flag each
+  // The row's threshold, if a workgroup of this launch has already published it:
+  // one 64-bit word, epoch << 32 | threshold, stored without any ordering, alone
+  // in a 128-byte line per row (device-coherent accesses to one line shared by
+  // the rows queue behind each other).  A word from another launch carries
+  // another epoch.  Every region records the threshold
+  // it filtered with, and the final pass uses the lists only if all of a row's
+  // regions agree, so even a word that matched by accident could not change a
+  // result.
+  if (tid == 0) {
+    const uint64_t pv = __hip_atomic_load(&taupub[r * 16], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flag[2] = (uint32_t)(pv >> 32) == epoch ? 1u : 0u;
+    s_flag[3] = (uint32_t)pv;
+  }
+  __syncthreads();
+  uint32_t tau = s_flag[3];
+  if (s_flag[2] == 0u) {
   // Workgroups of a fast XCD can finish before a slow one's waves have stored their
   // sample; every workgroup of the launch is resident (one per slot), so waiting a
   // little costs nothing on the critical path.  The wait is bounded by the realtime
@@ -339,7 +358,11 @@ __device__ void score_select_epilogue(const float* __restrict__ out_row, int r, 
   if (lane == 63) atomicAdd(&s_flag[1], mine);
   __syncthreads();
   const int m = (int)s_flag[1];
-  const uint32_t tau = block_kth8<256, SE, 2>(key, valid, sample_rank(k, m, nvis), hist, wsum, res);
+  tau = block_kth8<256, SE, 2>(key, valid, sample_rank(k, m, nvis), hist, wsum, res);
+  if (tid == 0)
+    __hip_atomic_store(&taupub[r * 16], ((uint64_t)epoch << 32) | tau, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid == 0) tau_used[(int64_t)r * 256 + bx] = tau;
   const int vis_end = min(key_end, nvis);
   const uint32_t written = key0 < vis_end ? filter_region<float>(out_row, key0, vis_end, tau,
                                                                   cval + (int64_t)r * S + key0,
@@ -354,7 +377,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ k,
                          const float* __restrict__ ks, const int32_t* __restrict__ nv, int T, int S, int H,
                          int keys_per_block, float* __restrict__ scores, int topk, uint32_t* __restrict__ counters,
-                         uint32_t* __restrict__ bcnt, float* __restrict__ cval, int32_t* __restrict__ cid) {
+                         uint32_t* __restrict__ bcnt, float* __restrict__ cval, int32_t* __restrict__ cid,
+                         uint64_t* __restrict__ taupub, uint32_t* __restrict__ tau_used, uint32_t epoch) {
   typedef TileGeom<FP8> G;
   static_assert(NST >= 1 && NST <= 3, "ring depth");
   // fp8: the query codes occupy the last SPL ring stages until every wave has
@@ -608,7 +632,8 @@ _Pragma("unroll") \
                          __HIP_MEMORY_SCOPE_AGENT);
     LI_WAIT_VMCNT(0);
     __syncthreads();
-    score_select_epilogue(out_row, r, nvis, key0, key_end, keys_per_block, topk, counters, bcnt, cval, cid, S, lds);
+    score_select_epilogue(out_row, r, nvis, key0, key_end, keys_per_block, topk, counters, bcnt, cval, cid, taupub,
+                          tau_used, epoch, S, lds);
   }
 #undef LI_TILE_PART
 }
@@ -722,7 +747,8 @@ hipError_t launch_score(const void* q, int q_type, const float* w, const void* k
       return true;                                                                                                  \
     }();                                                                                                            \
     (void)attr;                                                                                                     \
-    kern<<<grid, 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, 0, nullptr, nullptr, nullptr, nullptr);  \
+    kern<<<grid, 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, 0, nullptr, nullptr, nullptr, nullptr,   \
+                                 nullptr, nullptr, 0u);                                                             \
   } while (0)
     if (H <= 32) {
       if (f8) LI_LAUNCH_STREAM(1, true); else LI_LAUNCH_STREAM(1, false);
@@ -787,11 +813,21 @@ bool select_score_apply(int q_type, int k_type, int R, int S, int H, int topk) {
   return P <= 256 && kpb >= 1024 && (int64_t)P * R <= (int64_t)num_cus() * (f8 ? bpc : bpc_b);
 }
 
+// launch epochs of the selection kernel: a published threshold carries the epoch of
+// the launch that computed it
+static uint32_t next_select_epoch() {
+  static std::atomic<uint32_t> e{0};
+  uint32_t v = e.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  if (v == 0u) v = e.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  return v;
+}
+
 hipError_t launch_score_select(const void* q, int k_type, const float* w, const void* k, const float* ks,
                                const int32_t* nv, int B, int T, int S, int H, int topk, float* scores,
-                               uint32_t* counters, uint32_t* bcnt, float* cval, int32_t* cid, int* P_out,
-                               int* chunk_out, hipStream_t st) {
+                               uint32_t* counters, uint32_t* bcnt, float* cval, int32_t* cid, uint64_t* taupub,
+                               uint32_t* tau_used, int* P_out, int* chunk_out, hipStream_t st) {
   const int R = B * T;
+  const uint32_t epoch = next_select_epoch();
   const bool f8 = k_type == DT_FP8;
   const uint16_t* qq = (const uint16_t*)q;
   const uint8_t* kk = (const uint8_t*)k;
@@ -809,7 +845,8 @@ hipError_t launch_score_select(const void* q, int k_type, const float* w, const 
     (void)attr;                                                                                                     \
     *P_out = P;                                                                                                     \
     *chunk_out = kpb;                                                                                               \
-    kern<<<dim3(P, R), 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, topk, counters, bcnt, cval, cid);   \
+    kern<<<dim3(P, R), 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, topk, counters, bcnt, cval, cid,    \
+                                       taupub, tau_used, epoch);                                                    \
   } while (0)
   if (H <= 32) {
     if (f8) LI_LAUNCH_SELECT(1, true); else LI_LAUNCH_SELECT(1, false);

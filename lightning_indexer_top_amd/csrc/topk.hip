@@ -335,7 +335,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
                                                                   const int32_t* __restrict__ cid,
                                                                   int32_t* __restrict__ idx_out,
                                                                   Sc* __restrict__ val_out,
-                                                                  uint32_t* __restrict__ reset) {
+                                                                  uint32_t* __restrict__ reset,
+                                                                  const uint32_t* __restrict__ tau_used) {
   typedef typename ScoreTraits<Sc>::K K;
   constexpr int NW = TK_THREADS / 64;
   constexpr int E = MB_KEEP / TK_THREADS;
@@ -354,15 +355,19 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
     for (int i = tid; i < 4 * P; i += TK_THREADS) reset[(int64_t)r * 1024 + i] = 0u;
   if (tid == 0) s_unfiltered = 0;
   __syncthreads();
-  // exclusive prefix of the region counts (P <= 256): one wave, four per lane
+  // exclusive prefix of the region counts (P <= 256): one wave, four per lane.  A
+  // region left unfiltered, or regions filtered with different thresholds (where
+  // they record theirs), make the lists unusable.
   if (tid < 64) {
     uint32_t c4[4], tot = 0;
     bool unf = false;
+    const uint32_t t0 = tau_used ? tau_used[(int64_t)r * 256] : 0u;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int b = 4 * tid + e;
       c4[e] = b < P ? bcnt[(int64_t)r * P + b] : 0u;
       unf = unf || c4[e] == REGION_UNFILTERED;
+      if (tau_used && b < P) unf = unf || tau_used[(int64_t)r * 256 + b] != t0;
       tot += c4[e];
     }
     if (__ballot(unf) && tid == 0) s_unfiltered = 1;
@@ -479,13 +484,13 @@ static hipError_t launch_topk_mb(const Sc* scores, const int32_t* nv, int R, int
   topk_thresh_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, tau);
   topk_filter_kernel<Sc><<<dim3(P, R), MB_THREADS, 0, st>>>(scores, nv, S, k, chunk, tau, cval, cid, bcnt);
   topk_finalize_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val,
-                                                      nullptr);
+                                                      nullptr, nullptr);
   return hipGetLastError();
 }
 
 void topk_mb_layout(void* ws, int R, int S, uint32_t** counters, uint32_t** bcnt, float** cval, int32_t** cid) {
   uint8_t* p = (uint8_t*)ws;
-  *counters = (uint32_t*)p;  // the threshold area: one word per row in the fused pass
+  *counters = (uint32_t*)p;  // the threshold area: 8 bytes per row
   p += a256((size_t)R * 8);
   *bcnt = (uint32_t*)p;
   p += a256((size_t)R * 256 * 4);
@@ -496,8 +501,9 @@ void topk_mb_layout(void* ws, int R, int S, uint32_t** counters, uint32_t** bcnt
 
 hipError_t launch_topk_finalize_f32(const float* scores, const int32_t* nv, int R, int S, int k, int P, int chunk,
                                     const uint32_t* bcnt, const float* cval, const int32_t* cid, int32_t* idx,
-                                    float* val, uint32_t* reset, hipStream_t st) {
-  topk_finalize_kernel<float><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val, reset);
+                                    float* val, uint32_t* reset, const uint32_t* tau_used, hipStream_t st) {
+  topk_finalize_kernel<float><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val, reset,
+                                                        tau_used);
   return hipGetLastError();
 }
 

@@ -135,6 +135,18 @@ def test_decode_select_fused(over, topk, nvs):
     regions = bcnt[:R * 256]
     assert (flags == 0).all(), "sample flags not cleared"
     assert (regions != -1).all(), "a region was left unfiltered"
+    # the row's threshold was published once (epoch << 32 | threshold, one 128-byte
+    # line per row) and every region of the row filtered with it (256 words per row)
+    tu_at = flags_at + _a256(R * 1024 * 4)
+    pub_at = tu_at + _a256(R * 256 * 4)
+    tu = ws[tu_at:tu_at + R * 256 * 4].view(torch.int32).cpu().numpy().view(np.uint32).reshape(R, 256)
+    pub = ws[pub_at:pub_at + R * 128].view(torch.int64).cpu().numpy().view(np.uint64).reshape(R, 16)[:, 0]
+    for r in range(R):
+        if n[r] > topk:
+            assert pub[r] >> np.uint64(32) != 0, f"row {r}: no published threshold"
+            used = tu[r][tu[r] != 0]
+            assert len(used) > 0 and (used == np.uint32(pub[r] & np.uint64(0xFFFFFFFF))).all(), \
+                f"row {r}: regions filtered with different thresholds"
     # other queries on the same workspace (rows reversed): every sample comes from
     # this call, nothing from the previous one
     qr, wr = d["q"].flip(0).contiguous(), d["w"].flip(0).contiguous()
