@@ -168,3 +168,41 @@ def test_decode_select_fused(over, topk, nvs):
         assert torch.equal(a, b)
     o = oracle.indexer_score(x["q"], oracle.BF16, x["w"], x["k"], OT[sp["key"]], x["k_scale"], nv)
     assert_topk_band(i1.cpu().numpy(), o, topk, nv, "fused decode select")
+
+
+@pytest.mark.parametrize("bogus", ["all", "none", "mid"])
+def test_decode_select_planted_threshold(bogus):
+    """A published threshold word that matches the launch by accident: each fused
+    decode launch publishes its rows' thresholds as (epoch << 32 | threshold), the
+    epoch counting launches.  Planting the next launch's epoch with a wrong
+    threshold in one row's word makes that launch's workgroups filter with it: one
+    that keeps every entry (the list overflows), one that keeps none (too short), or
+    a plausible one (the lists are used).  The result must equal score-then-select
+    bit for bit in every case."""
+    print("planted threshold", bogus, flush=True)
+    sp = workloads.spec("batched_decode", seed=0x5EED0500, B=8, S=131072)
+    x, d = inputs(sp)
+    R, S, H, topk = sp["B"], sp["S"], sp["H"], 512
+    nb = li.indexer_topk_workspace_bytes(R, 1, S, H, topk)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    li.indexer_topk(d["q"], d["w"], d["k"], topk, d["k_scale"], None, workspace=ws)
+    torch.cuda.synchronize()
+    off = _a256(R * S * 4)
+    flags_at = off + _a256(R * 8) + _a256(R * 256 * 4) + 2 * _a256(R * S * 4)
+    pub_at = flags_at + _a256(R * 1024 * 4) + _a256(R * 256 * 4)
+    pub = ws[pub_at:pub_at + R * 128].view(torch.int64).cpu().numpy().view(np.uint64).reshape(R, 16)[:, 0]
+    epoch = int(pub[0] >> np.uint64(32))
+    assert epoch != 0
+    scores = li.indexer_score(d["q"], d["w"], d["k"], d["k_scale"])
+    i_ref, v_ref = li.topk_select(scores, topk)
+    torch.cuda.synchronize()
+    row = scores[1].cpu().numpy()
+    ordk = lambda f: int(np.float32(f).view(np.uint32) | 0x80000000) if f >= 0 else int(~np.float32(f).view(np.uint32) & 0xFFFFFFFF)
+    tau = {"all": 1, "none": 0xFFFFFFFF, "mid": ordk(np.sort(row)[-1500])}[bogus]
+    word = np.array([((epoch + 1) << 32) | tau], dtype=np.uint64)
+    ws[pub_at + 128:pub_at + 136] = torch.from_numpy(word.view(np.uint8)).cuda()  # row 1
+    i1, v1 = li.indexer_topk(d["q"], d["w"], d["k"], topk, d["k_scale"], None, workspace=ws)
+    torch.cuda.synchronize()
+    pub2 = ws[pub_at:pub_at + R * 128].view(torch.int64).cpu().numpy().view(np.uint64).reshape(R, 16)[:, 0]
+    assert int(pub2[0] >> np.uint64(32)) == epoch + 1, "the launch used the planted epoch"
+    assert torch.equal(i1, i_ref) and torch.equal(v1, v_ref)
