@@ -28,6 +28,16 @@ constexpr int AT_KMAX = 2048;  // selected rows per sequence at most
 constexpr int AT_GU = AT_CH * 72 / 256;  // 16-byte pieces per thread per chunk
 static_assert(AT_CH * 72 == AT_GU * 256, "whole pieces per thread");
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Transpose read of 4 bf16 (gfx950 ds_read_b64_tr_b16): in each group of 16 lanes,
+// lane 4 a + b receives element b of the 4-element rows read by lanes a, a + 4,
+// a + 8 and a + 12.
+__device__ __forceinline__ bf16x4 ds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(__attribute__((address_space(3))) const uint8_t*)p);
+}
+
 // the value of x held by the other lane half (lane l +- 32)
 __device__ __forceinline__ float other_half(float x, int hf) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -169,13 +179,16 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const uint16_t* __rest
     const bool rescale = __ballot(alpha != 1.0f) != 0ull;                                                             \
     _Pragma("unroll")                                                                                                 \
     for (int t = 0; t < 4; ++t) {                                                                                     \
-      /* V^T operands of this dv tile: 16 rows of column dv, all read first */                                        \
-      const int dv = (4 * wave + t) * 32 + col;                                                                       \
-      uint32_t vv[16];                                                                                                \
+      /* V^T operands of this dv tile, lane (dv, hf): rows 4 hf + 0..3 and 8 + 4 hf + 0..3 of */                      \
+      /* column dv (then the same 16 rows on), by transpose reads: lane 4 a + b of a group of */                      \
+      /* 16 receives element b of the 4-element reads of lanes a, a + 4, a + 8, a + 12, so */                         \
+      /* lane i reads columns 4 (i % 4) .. + 3 of row i / 4 */                                                        \
+      const int dv0 = (4 * wave + t) * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);                                   \
+      bf16x4 vq[4];                                                                                                   \
       _Pragma("unroll")                                                                                               \
-      for (int e = 0; e < 16; ++e) {                                                                                  \
-        const int row = (e & 3) + 8 * ((e >> 2) & 1) + 4 * hf + 16 * (e >> 3);                                        \
-        vv[e] = *(const uint16_t*)(skv + row * AT_ROWB + 2 * dv);                                                     \
+      for (int e = 0; e < 4; ++e) {                                                                                   \
+        const int row = 4 * hf + 8 * (e & 1) + 16 * (e >> 1) + ((lane >> 2) & 3);                                       \
+        vq[e] = ds_read_tr16(skv + row * AT_ROWB + 2 * dv0);                                                          \
       }                                                                                                               \
       if (rescale) {                                                                                                  \
         _Pragma("unroll")                                                                                             \
@@ -183,9 +196,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(const uint16_t* __rest
       }                                                                                                               \
       _Pragma("unroll")                                                                                               \
       for (int sidx2 = 0; sidx2 < 2; ++sidx2) {                                                                       \
-        const uint32_t* w8 = vv + 8 * sidx2;                                                                          \
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(w8[0] | (w8[1] << 16), w8[2] | (w8[3] << 16),         \
-                                                                w8[4] | (w8[5] << 16), w8[6] | (w8[7] << 16)));       \
+        const bf16x8 va = __builtin_shufflevector(vq[2 * sidx2], vq[2 * sidx2 + 1], 0, 1, 2, 3, 4, 5, 6, 7);          \
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[sidx2], o[t], 0, 0, 0);                                 \
       }                                                                                                               \
     }                                                                                                                 \
