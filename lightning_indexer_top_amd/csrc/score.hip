@@ -47,29 +47,6 @@ struct StreamCfg {
   static constexpr int BPC = WPE * LI_BPC_MUL;      // workgroups of 4 waves per CU
 };
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] in [15:14]).
-#define LI_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-#define LI_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
-
-// s_waitcnt vmcnt(n) for a run-time n in [0, 23] (the count is an immediate).
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-#define LI_CASE(c) \
-  case c:          \
-    LI_WAIT_VMCNT(c); \
-    break;
-    LI_CASE(0) LI_CASE(1) LI_CASE(2) LI_CASE(3) LI_CASE(4) LI_CASE(5) LI_CASE(6) LI_CASE(7)
-    LI_CASE(8) LI_CASE(9) LI_CASE(10) LI_CASE(11) LI_CASE(12) LI_CASE(13) LI_CASE(14) LI_CASE(15)
-    LI_CASE(16) LI_CASE(17) LI_CASE(18) LI_CASE(19) LI_CASE(20) LI_CASE(21) LI_CASE(22)
-#undef LI_CASE
-    default:
-      LI_WAIT_VMCNT(23);
-      break;
-  }
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // One 32-key tile of one wave: K rows of ROW bytes, stored in LDS as 16-byte
@@ -89,10 +66,6 @@ struct TileGeom {
   // LDS chunk slot of (key n, chunk c)
   __device__ static int slot(int n, int c) { return n * CPR + (c ^ sw(n)); }
 };
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_u8*)p; }
 
 // Issue the loads of one full tile into its LDS stage.  goff[j] is this lane's
 // byte offset inside the tile for load instruction j (precomputed); a tile of fp8

@@ -53,3 +53,34 @@ def test_nothing_selected():
     idx = -np.ones((1, 40), np.int32)
     g, gl, o, ol = run(1, 32, 100, 40, seed=0x5EED0A00, idx=idx)
     assert (g == 0).all() and np.isneginf(gl).all()
+
+
+def bf16_bits(x):
+    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("pos,scale", [(40, 4.0), (300, 0.6), (509, 4.0)])
+def test_late_dominant_row(pos, scale):
+    """A selected row planted as a multiple of one query makes that head's logit jump
+    far above everything seen in the earlier chunks (and others' by less), so the
+    running softmax reference has to move mid-sequence; sequence 1 also starts with
+    two chunks of skipped entries."""
+    print("attn dominant", pos, scale, flush=True)
+    B, Hq, S, k, seed = 2, 64, 4000, 512, 0x5EED0B00 + pos
+    tau = 1 / math.sqrt(192)
+    q = synth.normal_bf16(seed, 6, (B, Hq, 576))
+    kv = synth.normal_bf16(seed, 5, (B, S, 576))
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.choice(S, k, replace=False) for _ in range(B)]).astype(np.int32)
+    idx[1, :64] = -1
+    for b, h in ((0, 5), (1, 37)):
+        row = idx[b, pos]
+        planted = (np.asarray(q[b, h], np.uint32) << 16).view(np.float32)
+        kv[b, row] = bf16_bits(planted * scale)
+    out, lse = li.sparse_attn_gather(dev(q, "bf16"), dev(kv, "bf16"), dev(idx), tau)
+    torch.cuda.synchronize()
+    o_out, o_lse = oracle.sparse_attn(q, kv, np.where((idx >= 0) & (idx < S), idx, -1), 512, tau)
+    assert_attn_close(bf16_host(out), o_out)
+    np.testing.assert_allclose(lse.cpu().numpy(), o_lse, rtol=1e-3, atol=1e-3)
