@@ -299,6 +299,8 @@ def bench_select_attend(torch, li, workloads, steps, warmup):
     idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
     out = torch.empty((B, Hq, sp["dv"]), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    sel_ws = torch.empty(max(1, li.topk_workspace_bytes(B, S, k)), dtype=torch.uint8, device="cuda")
+    sel_idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
     ev = []
 
     def step(i):
@@ -306,7 +308,7 @@ def bench_select_attend(torch, li, workloads, steps, warmup):
         e[0].record()
         li.indexer_score(q, w, kk, ks, None, out=scores)
         e[1].record()
-        li.topk_select(scores, k, with_values=False)
+        li.topk_select(scores, k, with_values=False, workspace=sel_ws, out=(sel_idx, None))
         e[2].record()
         li.sparse_attn_gather(qa, lat, idx, sp["tau"], out=(out, lse))
         e[3].record()

@@ -103,16 +103,19 @@ def _check(status, where):
         raise LIError(status, where)
 
 
-def _workspace(nbytes, device, workspace=None):
+def _workspace(nbytes, device, workspace=None, zeroed=True):
     if nbytes == 0:
         return None, 0
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError(f"workspace needs {nbytes} bytes")
         return workspace, workspace.numel() * workspace.element_size()
-    # zero-filled: the fused decode selection keeps per-row counters there, which a
-    # zeroed workspace has ready (any contents give the same results)
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device), nbytes
+    # zero-filled unless the caller says otherwise: the fused decode selection keeps
+    # per-row counters there, which a zeroed workspace has ready (any contents give
+    # the same results)
+    if zeroed:
+        return torch.zeros(nbytes, dtype=torch.uint8, device=device), nbytes
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
 def indexer_score(q, w, k, k_scale=None, nv=None, out=None):
@@ -134,6 +137,10 @@ def indexer_score(q, w, k, k_scale=None, nv=None, out=None):
     return out
 
 
+def topk_workspace_bytes(R, S, k):
+    return int(lib().li_topk_workspace_bytes(R, S, k))
+
+
 def topk_select(scores, k, nv=None, with_values=True, workspace=None, out=None):
     """(idx [R, k] int32, val [R, k] fp32 or None) of scores [R, S]."""
     _dev(scores, "scores")
@@ -143,7 +150,8 @@ def topk_select(scores, k, nv=None, with_values=True, workspace=None, out=None):
         val = torch.empty((R, k), dtype=torch.float32, device=scores.device) if with_values else None
     else:
         idx, val = out
-    ws, nb = _workspace(lib().li_topk_workspace_bytes(R, S, k), scores.device, workspace)
+    # every byte of this workspace is written before it is read
+    ws, nb = _workspace(lib().li_topk_workspace_bytes(R, S, k), scores.device, workspace, zeroed=False)
     st = lib().li_topk_select(_ptr(scores), _ptr(nv), R, S, k, _ptr(idx), _ptr(val), _ptr(ws), nb,
                               _stream(scores.device))
     _check(st, "li_topk_select")
