@@ -67,32 +67,39 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 // transpose reads (ds_read_b64_tr_b16: in each group of 16 lanes, lane 4 a + b
 // receives element b of the 4-element rows read by lanes a, a + 4, a + 8, a + 12)
 // of the value operands, v[4 t + e] at a_t(e & 1) plus 16 rows (18432 bytes) for
-// e >= 2.
-__device__ __forceinline__ void at_read_kv(i32x4 (&r)[9], i32x2 (&v)[8], uint32_t ka, uint32_t a00, uint32_t a01,
-                                           uint32_t a10, uint32_t a11) {
+// e >= 2; then six 4-byte reads of row indices (ia[i] -> id[i]) for the loads to come.
+__device__ __forceinline__ void at_read_kv(i32x4 (&r)[9], i32x2 (&v)[8], int (&id)[6], uint32_t ka, uint32_t a00,
+                                           uint32_t a01, uint32_t a10, uint32_t a11, const uint32_t (&ia)[6]) {
   asm volatile(
-      "ds_read_b128 %0, %17\n\t"
-      "ds_read_b128 %1, %17 offset:128\n\t"
-      "ds_read_b128 %2, %17 offset:256\n\t"
-      "ds_read_b128 %3, %17 offset:384\n\t"
-      "ds_read_b128 %4, %17 offset:512\n\t"
-      "ds_read_b128 %5, %17 offset:640\n\t"
-      "ds_read_b128 %6, %17 offset:768\n\t"
-      "ds_read_b128 %7, %17 offset:896\n\t"
-      "ds_read_b128 %8, %17 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %9, %18\n\t"
-      "ds_read_b64_tr_b16 %10, %19\n\t"
-      "ds_read_b64_tr_b16 %11, %18 offset:18432\n\t"
-      "ds_read_b64_tr_b16 %12, %19 offset:18432\n\t"
-      "ds_read_b64_tr_b16 %13, %20\n\t"
-      "ds_read_b64_tr_b16 %14, %21\n\t"
-      "ds_read_b64_tr_b16 %15, %20 offset:18432\n\t"
-      "ds_read_b64_tr_b16 %16, %21 offset:18432\n\t"
+      "ds_read_b128 %0, %23\n\t"
+      "ds_read_b128 %1, %23 offset:128\n\t"
+      "ds_read_b128 %2, %23 offset:256\n\t"
+      "ds_read_b128 %3, %23 offset:384\n\t"
+      "ds_read_b128 %4, %23 offset:512\n\t"
+      "ds_read_b128 %5, %23 offset:640\n\t"
+      "ds_read_b128 %6, %23 offset:768\n\t"
+      "ds_read_b128 %7, %23 offset:896\n\t"
+      "ds_read_b128 %8, %23 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %9, %24\n\t"
+      "ds_read_b64_tr_b16 %10, %25\n\t"
+      "ds_read_b64_tr_b16 %11, %24 offset:18432\n\t"
+      "ds_read_b64_tr_b16 %12, %25 offset:18432\n\t"
+      "ds_read_b64_tr_b16 %13, %26\n\t"
+      "ds_read_b64_tr_b16 %14, %27\n\t"
+      "ds_read_b64_tr_b16 %15, %26 offset:18432\n\t"
+      "ds_read_b64_tr_b16 %16, %27 offset:18432\n\t"
+      "ds_read_b32 %17, %28\n\t"
+      "ds_read_b32 %18, %29\n\t"
+      "ds_read_b32 %19, %30\n\t"
+      "ds_read_b32 %20, %31\n\t"
+      "ds_read_b32 %21, %32\n\t"
+      "ds_read_b32 %22, %33\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
         "=&v"(r[8]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
-        "=&v"(v[7])
-      : "v"(ka), "v"(a00), "v"(a01), "v"(a10), "v"(a11)
+        "=&v"(v[7]), "=&v"(id[0]), "=&v"(id[1]), "=&v"(id[2]), "=&v"(id[3]), "=&v"(id[4]), "=&v"(id[5])
+      : "v"(ka), "v"(a00), "v"(a01), "v"(a10), "v"(a11), "v"(ia[0]), "v"(ia[1]), "v"(ia[2]), "v"(ia[3]), "v"(ia[4]),
+        "v"(ia[5])
       : "memory");
 }
 
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
 #pragma unroll
     for (int u = 0; u < 5; ++u) {
       if (u < 4 || wave < 4) {
-        const uint8_t* src = kvb + (int64_t)(id[u] < 0 ? 0 : id[u]) * AT_RB + doff[u];
+        const uint8_t* src = kvb + (int64_t)max(id[u], 0) * AT_RB + doff[u];
         __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(uintptr_t)(lb + 8192u * u), 16, 0, 0);
       }
     }
@@ -253,10 +260,22 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
         if ((u < 4 || wave < 4) && !((vr >> drow[u]) & 1u)) at_write_zero(lb + 8192u * u);
     }
   };
-  // chunk c's operands: the logit rows of this wave's 9 K-steps and the V^T values
-  auto read_chunk = [&](int c, i32x4 (&ka)[9], i32x2 (&vv)[8]) {
+  // chunk c's operands: the logit rows of this wave's 9 K-steps and the V^T values,
+  // together with the row indices of chunk c + NBUF (this wave's loads, id[0..4])
+  // and of chunk c + 1 (row c + 1 + lane, id[5])
+  const uint32_t sidx_lds = lds_addr(sidx);
+  auto read_chunk = [&](int c, i32x4 (&ka)[9], i32x2 (&vv)[8], int (&id)[6]) {
     const uint32_t bufa = kv_lds + (uint32_t)((c % NBUF) * AT_CHB);
-    at_read_kv(ka, vv, bufa + koff, bufa + voff[0][0], bufa + voff[0][1], bufa + voff[1][0], bufa + voff[1][1]);
+    uint32_t ia[6];
+#pragma unroll
+    for (int u = 0; u < 5; ++u) ia[u] = sidx_lds + 4u * (uint32_t)min((c + NBUF) * AT_CH + drow[u], k - 1);
+    ia[5] = sidx_lds + 4u * (uint32_t)min((c + 1) * AT_CH + lane, k - 1);
+    at_read_kv(ka, vv, id, bufa + koff, bufa + voff[0][0], bufa + voff[0][1], bufa + voff[1][0], bufa + voff[1][1],
+               ia);
+#pragma unroll
+    for (int u = 0; u < 5; ++u)
+      if ((c + NBUF) * AT_CH + drow[u] >= k) id[u] = -1;
+    if (lane >= AT_CH || (c + 1) * AT_CH + lane >= k) id[5] = -1;
   };
   // partial logits over the 9 K-steps, two accumulation chains
   auto logit_mfma = [&](const i32x4 (&ka)[9], f32x4& s0, f32x4& s1) {
@@ -298,18 +317,19 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     f32x4 s = sown;
     const uint32_t vrow = vr_c;
     if (!kh) s += spart[tile][lane];
-    // row indices for the loads issued after barrier Y, and chunk c + 2's
-    int nid[5];
+    // (with the operands: the row indices of the loads issued after barrier Y, and
+    // chunk c + 2's)
+    int nid[6];
+    nid[5] = -1;
     const bool load_next = c + NBUF + 1 < nch;
-    if (load_next) row_ids(c + NBUF + 1, nid);
-    const int rid2 = row_index(c + 2);
     f32x4 s0, s1;
     const bool more = c + 1 < nch;
     if (more) {
       i32x4 ka[9];
-      read_chunk(c + 1, ka, vnext);
+      read_chunk(c + 1, ka, vnext, nid);
       logit_mfma(ka, s0, s1);
     }
+    const int rid2 = nid[5];
     // the tile's owner: logits of rows 16 rh + 4 g + j (j < 4), head hs
     float st[4], lsum = 0.0f;
     if (!kh) {
@@ -329,7 +349,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     if (more) sown = s0 + s1;
     at_barrier();
     // chunk c + 1 has been read by every wave: its buffer takes chunk c + NBUF + 1
-    if (load_next) issue_ids(c + NBUF + 1, nid);
+    if (load_next) issue_ids(c + NBUF + 1, *(const int(*)[5])nid);
 
     // ---- phase B: value product of chunk c, loads of chunk c + NBUF + 1
     i32x4 pp0, pp1;
@@ -409,8 +429,9 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
   at_barrier();
   {
     i32x4 ka[9];
+    int unused[6];
     f32x4 s0, s1;
-    read_chunk(0, ka, va);
+    read_chunk(0, ka, va, unused);
     logit_mfma(ka, s0, s1);
     sown = s0 + s1;
     if (kh) spart[tile][lane] = sown;
