@@ -116,6 +116,25 @@ __device__ __forceinline__ void at_read_p(i32x4& p0, i32x4& p1, int& flag, uint3
       : "memory");
 }
 
+// The nine 16-byte operands at a + 128 i (the query's, read once).
+__device__ __forceinline__ void at_read_k(i32x4 (&r)[9], uint32_t a) {
+  asm volatile(
+      "ds_read_b128 %0, %9\n\t"
+      "ds_read_b128 %1, %9 offset:128\n\t"
+      "ds_read_b128 %2, %9 offset:256\n\t"
+      "ds_read_b128 %3, %9 offset:384\n\t"
+      "ds_read_b128 %4, %9 offset:512\n\t"
+      "ds_read_b128 %5, %9 offset:640\n\t"
+      "ds_read_b128 %6, %9 offset:768\n\t"
+      "ds_read_b128 %7, %9 offset:896\n\t"
+      "ds_read_b128 %8, %9 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+        "=&v"(r[8])
+      : "v"(a)
+      : "memory");
+}
+
 // s_waitcnt vmcnt(n) for the counts the row-load pipeline uses (0 and multiples
 // of 4 or 5 up to 15); any other count waits for everything.
 __device__ __forceinline__ void at_wait_loads(int n) {
@@ -162,14 +181,8 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
   const int hf = lane >> 5, ho = lane & 31;  // 32 x 32 tile: lane half, column (= head)
   const int tile = wave & 3, rh = tile >> 1, hh = tile & 1, kh = wave >> 2;
   const int hs = 16 * hh + c16;  // head of this lane's logits
+  i32x4 qb[9];                   // Q^T operands, read from LDS in the prologue
 
-  // Q^T operand of this wave's K-steps 2 i + kh (dims 64 i + 32 kh + 8 g .. + 7)
-  i32x4 qb[9];
-  {
-    const uint16_t* qrow = q + ((int64_t)b * Hq + 32 * ht + hs) * AT_DQK + 32 * kh + 8 * g;
-#pragma unroll
-    for (int i = 0; i < 9; ++i) qb[i] = *(const i32x4*)(qrow + 64 * i);
-  }
   // the selected rows' indices, -1 for entries that select nothing
   {
     const int32_t* irow = idx + (int64_t)b * k;
@@ -179,7 +192,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     }
   }
   if (tid == 0) sflag = 0;
-  LI_WAIT_VMCNT(0);  // the query in registers before any row load is counted
+  LI_WAIT_VMCNT(0);  // no index load is left in the row-load counts
   __syncthreads();
 
   // Row loads: load instruction j (0..35) of a chunk fills slots 64 j .. 64 j + 63;
@@ -222,6 +235,19 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     int id[5];
     row_ids(c, id);
     issue_ids(c, id);
+  };
+  // the 32 heads' query rows, laid out like a chunk, into buffer NBUF - 1 (before
+  // that buffer's first chunk): the same slots, row = head
+  auto issue_q = [&]() {
+    const uint8_t* qb0 = (const uint8_t*)(q + ((int64_t)b * Hq + 32 * ht) * AT_DQK);
+    const uint32_t lb = kv_lds + (uint32_t)((NBUF - 1) * AT_CHB) + 1024u * wave;
+#pragma unroll
+    for (int u = 0; u < 5; ++u) {
+      if (u < 4 || wave < 4) {
+        const uint8_t* src = qb0 + drow[u] * AT_RB + doff[u];
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(uintptr_t)(lb + 8192u * u), 16, 0, 0);
+      }
+    }
   };
 
   // per-lane LDS offsets inside a chunk buffer
@@ -420,14 +446,24 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     at_barrier();
   };
 
-  // prologue: chunks 0 .. NBUF in flight, chunk 0's operands read
+  // prologue: chunks 0 and 1, the query rows (into buffer NBUF - 1) and chunks
+  // 2 .. NBUF - 2 in flight; once chunks 0, 1 and the query have landed, the Q^T
+  // operands and chunk 0's operands and logits; then chunks NBUF - 1 and NBUF
   i32x2 va[8], vb[8];
-  for (int c = 0; c < NBUF && c < nch; ++c) issue(c);
+  issue(0);
+  if (1 < nch) issue(1);
+  issue_q();
+  for (int c = 2; c < NBUF - 1 && c < nch; ++c) issue(c);
   vr_c = valid_rows(row_index(0));
-  at_wait_loads(nd * (min(nch - 1, NBUF - 1)));
+  vr_c1 = valid_rows(row_index(1));
+  at_wait_loads(nd * max(0, min(nch - 1, NBUF - 2) - 1));
   zero_fill(0, vr_c);
+  if (1 < nch) zero_fill(1, vr_c1);
   at_barrier();
   {
+    // Q^T operand of this wave's K-steps 2 i + kh (dims 64 i + 32 kh + 8 g .. + 7 of
+    // head hs)
+    at_read_k(qb, kv_lds + (uint32_t)((NBUF - 1) * AT_CHB) + 16u * (AT_PPR * hs + ((g ^ at_sw(hs)) ^ (4 * kh))));
     i32x4 ka[9];
     int unused[6];
     f32x4 s0, s1;
@@ -437,13 +473,9 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     if (kh) spart[tile][lane] = sown;
   }
   at_barrier();
-  if (NBUF < nch) issue(NBUF);
-  vr_c1 = valid_rows(row_index(1));
-  if (1 < nch) {
-    at_wait_loads(nd * (min(nch - 1, NBUF) - 1));
-    zero_fill(1, vr_c1);
-  }
-  at_barrier();
+  // every wave has its query operands and chunk 0's: their buffers take chunks
+  // NBUF - 1 and NBUF (chunk 1 has landed and is zero-filled already)
+  for (int c = NBUF - 1; c <= NBUF && c < nch; ++c) issue(c);
   for (int c = 0; c < nch; c += 2) {
     step(c, va, vb);
     if (c + 1 < nch) step(c + 1, vb, va);
