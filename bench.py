@@ -71,17 +71,20 @@ def _p(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-def source_sha(rel):
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(rels):
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # HBM traffic of the decode scoring kernel from rocprofv3 PMC runs of this
 # benchmark's launch configuration (FETCH_SIZE and WRITE_SIZE, KiB per dispatch,
 # each scaled by what the same counter reads for a plain 1 GiB copy: FETCH x2.0,
 # WRITE x1.0).  Valid only for the kernel source it was taken on.
-SCORE_TRAFFIC = {"source": "lightning_indexer_top_amd/csrc/score.hip", "sha256_16": "652021e38637c5b0",
-                 "fetch_kib": 136264.2 * 2.0, "write_kib": 8192.0 * 1.0}
+SCORE_TRAFFIC = {"sources": ["lightning_indexer_top_amd/csrc/score.hip", "lightning_indexer_top_amd/csrc/common.h"],
+                 "sha256_16": "fac19ee420180558", "fetch_kib": 136264.2 * 2.0, "write_kib": 8192.0 * 1.0}
 
 
 def bench_decode(torch, li, workloads, steps, warmup):
@@ -137,7 +140,7 @@ def bench_decode(torch, li, workloads, steps, warmup):
     n_keys = B * S
     achieved = n_keys * KEY_BYTES / (score_ms * 1e-3) / 1e9
     traffic = None
-    if SCORE_TRAFFIC["sha256_16"] == source_sha(SCORE_TRAFFIC["source"]) and SCORE_TRAFFIC["fetch_kib"]:
+    if SCORE_TRAFFIC["sha256_16"] == source_sha(SCORE_TRAFFIC["sources"]) and SCORE_TRAFFIC["fetch_kib"]:
         traffic = round((SCORE_TRAFFIC["fetch_kib"] + SCORE_TRAFFIC["write_kib"]) * 1024)
     log(f"[decode] step {ms * 1e3:.1f} us, score kernel {score_ms * 1e3:.1f} us ({score_in_step_ms * 1e3:.1f} us "
         f"between the step's events) -> {achieved:.0f} GB/s")
@@ -164,6 +167,27 @@ def bench_decode(torch, li, workloads, steps, warmup):
                      "kernel_us": round(score_ms * 1e3, 2), "kernel_us_in_step": round(score_in_step_ms * 1e3, 2)},
         "x": x, "sp": sp,
     }
+
+
+def copy_bandwidth_gbs(torch, nbytes=1 << 30, reps=5):
+    """Measured HBM ceiling beside the datasheet peak: a plain 1 GiB device copy
+    (bytes read plus bytes written over its time), best of a few repetitions."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3
+        best = t if best is None or t < best else best
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / best / 1e9
 
 
 def cpu_baseline_decode(x, sp):
@@ -381,6 +405,10 @@ def main():
         return
     dec = bench_decode(torch, li, workloads, args.steps, args.warmup)
     ms = dec["ms"]
+    copy_gbs = copy_bandwidth_gbs(torch)
+    dec["roofline"]["measured_copy_gbs"] = round(copy_gbs, 1)
+    dec["roofline"]["frac_of_measured_copy"] = round(dec["roofline"]["achieved"] / copy_gbs, 4)
+    log(f"[decode] plain 1 GiB device copy: {copy_gbs:.0f} GB/s (read + write)")
     result = {
         "metric": METRIC,
         "value": round(dec["keys"] / (ms * 1e-3), 1),
