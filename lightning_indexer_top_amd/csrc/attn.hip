@@ -481,8 +481,8 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     if (c + 1 < nch) step(c + 1, vb, va);
   }
 
-  // the softmax sums: the four lane groups of each tile owner, then the two row halves
-  at_barrier();
+  // the softmax sums: the four lane groups of each tile owner, then the two row
+  // halves (the last step ended with a barrier, so mx is free)
   if (!kh) {
     float l = l_s;
     l += __shfl_xor(l, 16, WAVE);
