@@ -109,8 +109,11 @@ constexpr int KW_BINS = 1 << KW_BITS;
 // valid keys differ are common to all of them (block minimum and maximum); the
 // rest is resolved KW_BITS bits per pass from the top.  A list of candidates
 // above a threshold spans few binades, so 32-bit keys take two or three passes
-// and 64-bit keys four or five, against four and eight 8-bit passes.
-// hist: KW_BINS words; wsum: room for 2 NT / 64 keys; res: 2 words.
+// and 64-bit keys four or five, against four and eight 8-bit passes; and once the
+// digit holding the kth key holds no other key, that key is the answer and the
+// remaining passes are skipped (one key per digit is the common case after the
+// first pass or two).
+// hist: KW_BINS words; wsum: room for 2 NT / 64 keys; res: 3 words.
 template <int NT, int E, typename K>
 __device__ __forceinline__ K block_kth_wide(const K (&key)[E], const bool (&valid)[E], uint32_t kth, uint32_t* hist,
                                             uint32_t* wsum, uint32_t* res, uint32_t* n_above) {
@@ -180,17 +183,28 @@ __device__ __forceinline__ K block_kth_wide(const K (&key)[E], const bool (&vali
         if (above < need && need <= above + c[i]) {
           res[0] = (uint32_t)(KW_BINS - 1 - BPT * tid - i);
           res[1] = above;
+          res[2] = c[i];
         }
         above += c[i];
       }
     }
     __syncthreads();
-    const uint32_t d = res[0], ab = res[1];
+    const uint32_t d = res[0], ab = res[1], cd = res[2];
     __syncthreads();
     prefix |= (K)d << lo;
     mask |= (K)dmask << lo;
     need -= ab;
     hi = lo - 1;
+    if (cd == 1u && hi >= 0) {  // uniform: the digit's only key is the kth
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (valid[e] && (key[e] & mask) == prefix) wk[0] = key[e];
+      __syncthreads();
+      const K kv = wk[0];
+      __syncthreads();
+      *n_above = kth - need;
+      return kv;
+    }
   }
   *n_above = kth - need;
   return prefix;

@@ -345,7 +345,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
   __shared__ uint32_t scan1[NW], scan2[NW];
   __shared__ uint32_t hist[KW_BINS];
   __shared__ uint64_t wsum8[2 * NW];  // minima and maxima of the keys, per wave
-  __shared__ uint32_t res8[2];
+  __shared__ uint32_t res8[3];
   const int r = blockIdx.x, tid = threadIdx.x;
   int n = S;
   if (nv) n = min(max(nv[r], 0), S);
