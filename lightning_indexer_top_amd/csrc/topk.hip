@@ -212,6 +212,99 @@ __device__ void select_block(const S* __restrict__ row, const int32_t* __restric
   }
 }
 
+// The k best of the valid entries held E per thread in list order (entry E tid + e,
+// a list in index order), written in that order at io / vo: T, the k-th best key,
+// by the wide radix select, then every entry above T and the first (k - count
+// above T) entries equal to T, each at its position from a prefix scan.  Every
+// thread of the TK_THREADS workgroup calls it; at least k entries are valid.
+template <typename Sc, int E>
+__device__ __forceinline__ void write_top_listed(const typename ScoreTraits<Sc>::K (&key)[E], const Sc (&val)[E],
+                                                 const int32_t (&id)[E], const bool (&valid)[E], uint32_t k,
+                                                 int32_t* __restrict__ io, Sc* __restrict__ vo, uint32_t* hist,
+                                                 uint64_t* wsum8, uint32_t* res, uint32_t* scan1, uint32_t* scan2) {
+  typedef typename ScoreTraits<Sc>::K K;
+  constexpr int NW = TK_THREADS / 64;
+  uint32_t n_gt_all;
+  const K T = block_kth_wide<TK_THREADS, E>(key, valid, k, hist, (uint32_t*)wsum8, res, &n_gt_all);
+  uint32_t ties = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) ties += valid[e] && key[e] == T ? 1u : 0u;
+  // rank of this thread's first tie in list order
+  const uint32_t tie_rank0 = block_exclusive_scan<NW>(ties, scan1);
+  const uint32_t need = k - n_gt_all;  // ties taken, first in the list first
+  bool sel[E];
+  uint32_t tr = tie_rank0, nsel = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool tie = valid[e] && key[e] == T;
+    sel[e] = (valid[e] && key[e] > T) || (tie && tr < need);
+    tr += tie ? 1u : 0u;
+    nsel += sel[e] ? 1u : 0u;
+  }
+  uint32_t pos = block_exclusive_scan<NW>(nsel, scan2);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (sel[e]) {
+      io[pos] = id[e];
+      if (vo) vo[pos] = val[e];
+      ++pos;
+    }
+  }
+}
+
+// A row of at most MB_KEEP entries whose ids ascend along the row (a row of scores
+// by position, or a list of candidates kept in index order): every entry is held
+// in registers, and the selection above writes the k best in position order, which
+// is ascending-id order, so no sort is needed.  Rows whose ids do not ascend take
+// select_block.
+template <typename S>
+__device__ void select_small(const S* __restrict__ row, const int32_t* __restrict__ idrow, int n, int k,
+                             int32_t* __restrict__ idx_out, S* __restrict__ val_out) {
+  typedef typename ScoreTraits<S>::K K;
+  constexpr int NW = TK_THREADS / 64;
+  constexpr int E = MB_KEEP / TK_THREADS;
+  __shared__ uint32_t scan1[NW], scan2[NW];
+  __shared__ uint32_t hist[KW_BINS];
+  __shared__ uint64_t wsum8[2 * NW];
+  __shared__ uint32_t res3[3];
+  const int tid = threadIdx.x;
+  K key[E];
+  S val[E];
+  int32_t id[E];
+  bool valid[E];
+  bool asc = true;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = E * tid + e;
+    valid[e] = j < n;
+    const int jc = valid[e] ? j : 0;
+    val[e] = row[jc];
+    id[e] = idrow ? idrow[jc] : jc;
+    // the id of the next entry (this thread's last one looks at the following thread's first)
+    if (idrow && j + 1 < n) asc = asc && idrow[j + 1] > id[e];
+  }
+  if (!__syncthreads_and(asc)) {
+    select_block<S>(row, idrow, n, k, idx_out, val_out);
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = valid[e] ? ScoreTraits<S>::ord(val[e]) : (K)0;
+  if (n <= k) {  // every entry, then padding
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (valid[e]) {
+        idx_out[E * tid + e] = id[e];
+        if (val_out) val_out[E * tid + e] = val[e];
+      }
+    for (int j = n + tid; j < k; j += TK_THREADS) {
+      idx_out[j] = -1;
+      if (val_out) val_out[j] = (S)-INFINITY;
+    }
+    return;
+  }
+  write_top_listed<S, E>(key, val, id, valid, (uint32_t)k, idx_out, val_out, hist, wsum8, res3, scan1, scan2);
+}
+
 template <typename S>
 __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restrict__ scores, int64_t row_stride,
                                                               const int32_t* __restrict__ nv,
@@ -220,8 +313,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restric
   const int r = blockIdx.x;
   int n = S_len;
   if (nv) n = min(max(nv[r], 0), S_len);
-  select_block<S>(scores + (int64_t)r * row_stride, ids ? ids + (int64_t)r * row_stride : nullptr, n, k,
-                  idx_out + (int64_t)r * k, val_out ? val_out + (int64_t)r * k : nullptr);
+  const S* row = scores + (int64_t)r * row_stride;
+  const int32_t* idrow = ids ? ids + (int64_t)r * row_stride : nullptr;
+  int32_t* io = idx_out + (int64_t)r * k;
+  S* vo = val_out ? val_out + (int64_t)r * k : nullptr;
+  if (n <= MB_KEEP)
+    select_small<S>(row, idrow, n, k, io, vo);
+  else
+    select_block<S>(row, idrow, n, k, io, vo);
 }
 
 // ---- many workgroups per row (few, long rows) --------------------------------
@@ -421,33 +520,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = valid[e] ? ScoreTraits<Sc>::ord(val[e]) : (K)0;
-  // T: the k-th best kept key; n_gt entries lie above it
-  uint32_t n_gt_all;
-  const K T = block_kth_wide<TK_THREADS, E>(key, valid, (uint32_t)k, hist, (uint32_t*)wsum8, res8, &n_gt_all);
-  uint32_t ties = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) ties += valid[e] && key[e] == T ? 1u : 0u;
-  // rank of this thread's first tie in index order
-  const uint32_t tie_rank0 = block_exclusive_scan<NW>(ties, scan1);
-  const uint32_t need = (uint32_t)k - n_gt_all;  // ties taken, smallest index first
-  bool sel[E];
-  uint32_t tr = tie_rank0, nsel = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const bool tie = valid[e] && key[e] == T;
-    sel[e] = (valid[e] && key[e] > T) || (tie && tr < need);
-    tr += tie ? 1u : 0u;
-    nsel += sel[e] ? 1u : 0u;
-  }
-  uint32_t pos = block_exclusive_scan<NW>(nsel, scan2);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (sel[e]) {
-      io[pos] = id[e];
-      if (vo) vo[pos] = val[e];
-      ++pos;
-    }
-  }
+  write_top_listed<Sc, E>(key, val, id, valid, (uint32_t)k, io, vo, hist, wsum8, res8, scan1, scan2);
 }
 
 static int mb_chunks(int R, int S) {
