@@ -33,7 +33,19 @@ __global__ __launch_bounds__(64) void compact_query_kernel(const uint16_t* __res
   const uint16_t* qr = q + (int64_t)bh * 128;
   double y = 0.0;
   if (i < DC) {
-    for (int j = 0; j < 128; ++j) y = fma((double)P[i * 128 + j], (double)bf16_to_f32(qr[j]), y);
+    // the chain runs in ascending j; its operands arrive 64 at a time
+#pragma unroll
+    for (int j0 = 0; j0 < 128; j0 += 64) {
+      float pv[64];
+      uint16_t qv[64];
+#pragma unroll
+      for (int j = 0; j < 64; ++j) {
+        pv[j] = P[i * 128 + j0 + j];
+        qv[j] = qr[j0 + j];
+      }
+#pragma unroll
+      for (int j = 0; j < 64; ++j) y = fma((double)pv[j], (double)bf16_to_f32(qv[j]), y);
+    }
   }
   const double amax = wave_max_d(i < DC ? fabs(y) : 0.0);
   const double s = amax > 0.0 ? amax / 127.0 : 1.0;
