@@ -121,7 +121,10 @@ li_status li_indexer_score(const void *q, li_dtype q_type, const float *w, const
  *   scores [R, S] fp32; nv [R] int32 or NULL (row r considers s < nv[r] only)
  *   idx    [R, k] int32 output (ascending key index, padded with -1)
  *   val    [R, k] fp32 output or NULL (the selected scores, padded with -inf)
- *   ws     workspace of at least li_topk_workspace_bytes(R, S, k) bytes
+ *   ws     workspace of at least li_topk_workspace_bytes(R, S, k) bytes (0 for
+ *          shapes that need none); its contents on entry do not matter (every
+ *          byte is written before it is read), and calls that share one must not
+ *          overlap
  *
  * Ties are broken towards the smaller index, so the result is unique and
  * deterministic.  Shapes: R >= 1, 1 <= S < 2^31, 1 <= k <= LI_TOPK_MAX.
