@@ -221,7 +221,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
       id[u] = row < k ? v : -1;
     }
   };
-  auto issue_ids = [&](int c, const int (&id)[5]) {
+  auto issue_ids = [&](int c, const int* id) {  // id[0..4]
     const uint32_t lb = kv_lds + (uint32_t)((c % NBUF) * AT_CHB) + 1024u * wave;
 #pragma unroll
     for (int u = 0; u < 5; ++u) {
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     if (more) sown = s0 + s1;
     at_barrier();
     // chunk c + 1 has been read by every wave: its buffer takes chunk c + NBUF + 1
-    if (load_next) issue_ids(c + NBUF + 1, *(const int(*)[5])nid);
+    if (load_next) issue_ids(c + NBUF + 1, nid);
 
     // ---- phase B: value product of chunk c, loads of chunk c + NBUF + 1
     i32x4 pp0, pp1;
