@@ -345,7 +345,7 @@ __device__ void score_select_epilogue(const float* __restrict__ out_row, int r, 
   (void)wid;
 }
 
-template <int HT, bool FP8, int NST, int WPE, bool SEL>
+template <int HT, bool FP8, int NST, int WPE, bool SEL, bool STG = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ k,
                          const float* __restrict__ ks, const int32_t* __restrict__ nv, int T, int S, int H,
@@ -354,6 +354,9 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
                          uint64_t* __restrict__ taupub, uint32_t* __restrict__ tau_used, uint32_t epoch) {
   typedef TileGeom<FP8> G;
   static_assert(NST >= 1 && NST <= 3, "ring depth");
+  // STG: the workgroup's scores are held in LDS behind the ring and written in one
+  // pass at the end (keys_per_block floats of dynamic LDS)
+  constexpr bool STAGE = STG && !SEL;
   // fp8: the query codes occupy the last SPL ring stages until every wave has
   // read its operands; those stages are filled after that
   constexpr int SPL = FP8 ? (QSplit<HT>::BYTES + 4 * G::BYTES - 1) / (4 * G::BYTES) : 0;
@@ -383,6 +386,7 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
   const uint32_t ring0 = lds_addr(ring);
   const uint32_t my_ring = ring0 + (uint32_t)(wave_u * G::BYTES);
   constexpr uint32_t SSTRIDE = 4 * G::BYTES;  // bytes between a wave's stages
+  const uint32_t stage0 = ring0 + NST * SSTRIDE;  // held scores (STAGE)
   const float* sbase = ks + (int64_t)b * S;
   float* sw = (float*)lds;  // [2][HT][16]
   const int first = key0 + wave_u * 32;
@@ -559,10 +563,11 @@ _Pragma("unroll") \
   for (int tile = first; tile < vis_end; tile += step) {
     // vmcnt counts loads and stores in issue order.  Issued after this tile's
     // loads: the loads of the n_after younger tiles (OPS instructions each) and
-    // the score stores of the last min(iter, NST) iterations (one each), so this
-    // tile has landed once no more than that many are outstanding.
+    // the score stores of the last min(iter, NST) iterations (one each; none when
+    // the scores are held in LDS), so this tile has landed once no more than that
+    // many are outstanding.
     const int n_after = min(NST - 1, (vis_end - 1 - tile) / step);
-    wait_vmcnt(n_after * OPS + min(iter, NST));
+    wait_vmcnt(n_after * OPS + (STAGE ? 0 : min(iter, NST)));
     ++iter;
     const uint32_t la = my_ring + (uint32_t)(stage * SSTRIDE);
     const int key = tile + col;
@@ -585,6 +590,8 @@ _Pragma("unroll") \
       const float v = key < nvis ? part * sc : -INFINITY;
       if (SEL && iter == 1)  // the wave's sample tile: stored device-coherent
         __hip_atomic_store(&out_row[key], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else if (STAGE)  // written out to LDS (no compiler-visible LDS access beside the ring's loads)
+        asm volatile("ds_write_b32 %0, %1" : : "v"(stage0 + 4u * (uint32_t)(key - key0)), "v"(v) : "memory");
       else
         out_row[key] = v;
     }
@@ -608,6 +615,15 @@ _Pragma("unroll") \
     score_select_epilogue(out_row, r, nvis, key0, key_end, keys_per_block, topk, counters, bcnt, cval, cid, taupub,
                           tau_used, epoch, S, lds);
   }
+  if constexpr (STAGE) {
+    // every load has landed; the held scores of keys key0 .. vis_end - 1 go out in
+    // one coalesced pass (the keys past vis_end were written -inf at the start)
+    LI_WAIT_VMCNT(0);
+    __syncthreads();
+    const float* held = (const float*)(ring + NST * SSTRIDE);
+    const int n = vis_end - key0;
+    for (int i = (int)threadIdx.x; i < n; i += 256) out_row[key0 + i] = held[i];
+  }
 #undef LI_TILE_PART
 }
 
@@ -625,6 +641,12 @@ static int num_cus() {
   }();
   return n;
 }
+
+// Keys per workgroup of the staged form (its scores are held in LDS): 16 KB.
+#ifndef LI_STAGE_KEYS
+#define LI_STAGE_KEYS 4096
+#endif
+constexpr int STAGE_KEYS = LI_STAGE_KEYS;
 
 // Keys per workgroup: a multiple of 128 (4 waves x 32 keys) chosen so the grid is
 // about `waves_per_cu` resident waves on every CU, one wave of work each.
@@ -726,7 +748,26 @@ hipError_t launch_score(const void* q, int q_type, const float* w, const void* k
     if (H <= 32) {
       if (f8) LI_LAUNCH_STREAM(1, true); else LI_LAUNCH_STREAM(1, false);
     } else if (H <= 64) {
-      if (f8) LI_LAUNCH_STREAM(2, true); else LI_LAUNCH_STREAM(2, false);
+      if (f8) {
+        // fp8 keys: the scores are held in LDS and written once per workgroup (two
+        // workgroups per CU, at most STAGE_KEYS keys each); writes interleaved with
+        // the key stream cost several times their bytes
+        typedef StreamCfg<2, true> C;
+        auto kern = score_stream_kernel<2, true, C::NST, 2, false, true>;
+        const int kpb = std::min(stream_keys_per_block(R, S, 2 * LI_BPC_MUL), STAGE_KEYS);
+        const size_t lds = stream_lds_bytes<2, true>() + (size_t)kpb * sizeof(float);
+        dim3 grid((S + kpb - 1) / kpb, R);
+        static const bool attr = [&] {
+          (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)(stream_lds_bytes<2, true>() + STAGE_KEYS * sizeof(float)));
+          return true;
+        }();
+        (void)attr;
+        kern<<<grid, 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, 0, nullptr, nullptr, nullptr, nullptr,
+                                     nullptr, nullptr, 0u);
+      } else {
+        LI_LAUNCH_STREAM(2, false);
+      }
     } else {
       if (f8) LI_LAUNCH_STREAM(4, true); else LI_LAUNCH_STREAM(4, false);
     }
