@@ -84,7 +84,7 @@ def source_sha(rels):
 # each scaled by what the same counter reads for a plain 1 GiB copy: FETCH x2.0,
 # WRITE x1.0).  Valid only for the kernel source it was taken on.
 SCORE_TRAFFIC = {"sources": ["lightning_indexer_top_amd/csrc/score.hip", "lightning_indexer_top_amd/csrc/common.h"],
-                 "sha256_16": "fac19ee420180558", "fetch_kib": 136264.2 * 2.0, "write_kib": 8192.0 * 1.0}
+                 "sha256_16": "689a15c7e3667b7b", "fetch_kib": 136262.3 * 2.0, "write_kib": 8192.0 * 1.0}
 
 
 def bench_decode(torch, li, workloads, steps, warmup):
