@@ -143,7 +143,9 @@ li_status li_topk_select(const float *scores, const int32_t *nv, int R, int S, i
  * and one exact pass selects among them.
  *
  *   idx [B*T, topk] int32, val [B*T, topk] fp32 or NULL (ascending key index)
- *   ws  workspace of at least li_indexer_topk_workspace_bytes(...) bytes.  The
+ *   ws  workspace of at least li_indexer_topk_workspace_bytes(q_type, k_type, B, T,
+ *       S, H, topk) bytes: the size of the path this shape and these dtypes take,
+ *       0 for the fused many-row path (ws may then be NULL).  The
  *       decode path keeps per-row flags there (after the score and top-k areas),
  *       which every call leaves at zero: a zero-filled workspace is ready for the
  *       first call.  Any other contents give the same results, that call being
@@ -153,7 +155,7 @@ li_status li_topk_select(const float *scores, const int32_t *nv, int R, int S, i
  * Requires q_type == LI_BF16 and k_type in {LI_BF16, LI_FP8_E4M3}, or the fp32
  * combinations accepted by li_indexer_score.  1 <= topk <= LI_TOPK_MAX.
  */
-size_t li_indexer_topk_workspace_bytes(int B, int T, int S, int H, int topk);
+size_t li_indexer_topk_workspace_bytes(li_dtype q_type, li_dtype k_type, int B, int T, int S, int H, int topk);
 li_status li_indexer_topk(const void *q, li_dtype q_type, const float *w, const void *k, li_dtype k_type,
                           const float *k_scale, const int32_t *nv, int B, int T, int S, int H, int d, int topk,
                           int32_t *idx, float *val, void *ws, size_t ws_bytes, hipStream_t stream);

@@ -54,7 +54,7 @@ def lib():
         L.li_topk_workspace_bytes.argtypes = [_I, _I, _I]
         L.li_topk_workspace_bytes.restype = _Z
         L.li_topk_select.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _Z, _P]
-        L.li_indexer_topk_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+        L.li_indexer_topk_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, _I]
         L.li_indexer_topk_workspace_bytes.restype = _Z
         L.li_indexer_topk.argtypes = [_P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P]
         L.li_compact_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
@@ -158,8 +158,9 @@ def topk_select(scores, k, nv=None, with_values=True, workspace=None, out=None):
     return idx, val
 
 
-def indexer_topk_workspace_bytes(B, T, S, H, topk):
-    return int(lib().li_indexer_topk_workspace_bytes(B, T, S, H, topk))
+def indexer_topk_workspace_bytes(q_type, k_type, B, T, S, H, topk):
+    """Workspace bytes li_indexer_topk needs for these dtype codes and shape."""
+    return int(lib().li_indexer_topk_workspace_bytes(q_type, k_type, B, T, S, H, topk))
 
 
 def indexer_topk(q, w, k, topk, k_scale=None, nv=None, with_values=True, workspace=None, out=None):
@@ -173,7 +174,8 @@ def indexer_topk(q, w, k, topk, k_scale=None, nv=None, with_values=True, workspa
         val = torch.empty((R, topk), dtype=torch.float32, device=q.device) if with_values else None
     else:
         idx, val = out
-    ws, nb = _workspace(indexer_topk_workspace_bytes(B, T, S, H, topk), q.device, workspace)
+    ws, nb = _workspace(indexer_topk_workspace_bytes(_dtype_code(q, "q"), _dtype_code(k, "k"), B, T, S, H, topk),
+                        q.device, workspace)
     st = lib().li_indexer_topk(_ptr(q), _dtype_code(q, "q"), _ptr(w), _ptr(k), _dtype_code(k, "k"), _ptr(k_scale),
                                _ptr(nv), B, T, S, H, d, topk, _ptr(idx), _ptr(val), _ptr(ws), nb, _stream(q.device))
     _check(st, "li_indexer_topk")

@@ -7,6 +7,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblightning_indexer.so")
+# roofline probes (measurement only, not part of the indexer path)
+PROBE_LIB = os.path.join(HERE, "liblightning_indexer_probe.so")
+PROBE_SRC = os.path.join(CSRC, "probe", "probe.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU ops are disabled for every HIP translation unit.
@@ -46,7 +49,21 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    cmd = [HIPCC] + FLAGS + ["-shared", PROBE_SRC, "-o", PROBE_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd))
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    text = "\n".join(l for l in p.stdout.decode(errors="replace").splitlines() if "packed-fp32-ops" not in l)
+    if p.returncode:
+        print(text, file=sys.stderr)
+        raise RuntimeError("hipcc failed for the probe library")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

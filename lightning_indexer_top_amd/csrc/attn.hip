@@ -26,11 +26,9 @@
 #include "common.h"
 #include "launch.h"
 
-#ifndef LI_ATTN_NBUF
-#define LI_ATTN_NBUF 4  // chunk buffers
-#endif
-
 namespace li {
+
+constexpr int ATTN_NBUF = 4;  // chunk buffers
 
 constexpr int AT_DQK = 576;
 constexpr int AT_DV = 512;
@@ -526,7 +524,7 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* idx
   (void)ws;
   const int nt = Hq / 32;
   const int blocks = ((B + 7) / 8) * 8 * nt;
-  sparse_attn_kernel<LI_ATTN_NBUF><<<blocks, 512, 0, st>>>(q, kv, idx, B, Hq, S, k, sm_scale, out, lse);
+  sparse_attn_kernel<ATTN_NBUF><<<blocks, 512, 0, st>>>(q, kv, idx, B, Hq, S, k, sm_scale, out, lse);
   return hipGetLastError();
 }
 

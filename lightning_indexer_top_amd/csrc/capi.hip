@@ -104,8 +104,9 @@ li_status li_topk_select(const float* scores, const int32_t* nv, int R, int S, i
   return launched(li::launch_topk_f32(scores, nv, R, S, k, idx, val, ws, stream), "li_topk_select");
 }
 
-size_t li_indexer_topk_workspace_bytes(int B, int T, int S, int H, int topk) {
-  return li::indexer_topk_ws_bytes(B, T, S, H, topk);
+size_t li_indexer_topk_workspace_bytes(li_dtype q_type, li_dtype k_type, int B, int T, int S, int H, int topk) {
+  if (B < 1 || T < 1 || S < 1 || H < 1 || topk < 1) return 0;
+  return li::indexer_topk_ws_bytes(q_type, k_type, B, T, S, H, topk);
 }
 
 li_status li_indexer_topk(const void* q, li_dtype q_type, const float* w, const void* k, li_dtype k_type,
@@ -116,7 +117,7 @@ li_status li_indexer_topk(const void* q, li_dtype q_type, const float* w, const 
   if (!idx) return fail(LI_ERR_NULL, "idx must be non-NULL");
   if (topk < 1 || topk > LI_TOPK_MAX) return fail(LI_ERR_SHAPE, "topk must be in [1, %d]", LI_TOPK_MAX);
   if (misaligned(idx) || misaligned(val)) return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
-  const size_t need = li::indexer_topk_ws_bytes(B, T, S, H, topk);
+  const size_t need = li::indexer_topk_ws_bytes(q_type, k_type, B, T, S, H, topk);
   if (need && (!ws || ws_bytes < need)) return fail(LI_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   if (misaligned(ws)) return fail(LI_ERR_ALIGN, "workspace must be 16-byte aligned");
   return launched(li::launch_indexer_topk(q, q_type, w, k, k_type, k_scale, nv, B, T, S, H, topk, idx, val, ws,

@@ -361,13 +361,17 @@ static bool use_fused(int q_type, int k_type, int T, int H, int topk) {
   return q_type == DT_BF16 && k_type == DT_BF16 && T >= 2 * PS_WAVES && topk <= PS_KMAX && H <= 128;
 }
 
-size_t indexer_topk_ws_bytes(int B, int T, int S, int H, int topk) {
-  (void)H;
-  // the fused path needs no workspace; sized for the score-then-select path,
-  // which any shape may take
-  return align256((size_t)B * T * S * sizeof(float)) + topk_ws_bytes(B * T, S, topk) +
-         align256((size_t)B * T * 1024 * sizeof(uint32_t)) + align256((size_t)B * T * 256 * sizeof(uint32_t)) +
-         align256((size_t)B * T * 128);
+size_t indexer_topk_ws_bytes(int q_type, int k_type, int B, int T, int S, int H, int topk) {
+  // the same predicates, in the same order, as launch_indexer_topk: the fused
+  // prefill kernel needs nothing; decode-shaped rows need the scores, the
+  // multi-workgroup top-k's lists and the selection flags; anything else the
+  // scores and the top-k's own workspace
+  if (use_fused(q_type, k_type, T, H, topk)) return 0;
+  const size_t base = align256((size_t)B * T * S * sizeof(float)) + topk_ws_bytes(B * T, S, topk);
+  if (select_score_apply(q_type, k_type, B * T, S, H, topk))
+    return base + align256((size_t)B * T * 1024 * sizeof(uint32_t)) + align256((size_t)B * T * 256 * sizeof(uint32_t)) +
+           align256((size_t)B * T * 128);
+  return base;
 }
 
 hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const void* k, int k_type, const float* ks,

@@ -72,7 +72,7 @@ hipError_t launch_topk_finalize_f32(const float* scores, const int32_t* nv, int 
 
 // fused scoring + selection for many query rows (prefill); falls back to
 // score-then-select where the fused kernel does not apply
-size_t indexer_topk_ws_bytes(int B, int T, int S, int H, int topk);
+size_t indexer_topk_ws_bytes(int q_type, int k_type, int B, int T, int S, int H, int topk);
 hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const void* k, int k_type, const float* ks,
                                const int32_t* nv, int B, int T, int S, int H, int topk, int32_t* idx, float* val,
                                void* ws, hipStream_t st);

@@ -31,20 +31,11 @@ namespace li {
 // Occupancy target (waves per SIMD) and ring depth (tiles in flight per wave) of
 // the streaming kernel, per head-tile count and key format: the VGPR budget of the
 // resident query block decides the first, LDS (waves x depth x tile) the second.
-#ifndef LI_FP8_WPE
-#define LI_FP8_WPE 3
-#endif
-#ifndef LI_FP8_NST
-#define LI_FP8_NST 3
-#endif
-#ifndef LI_BPC_MUL
-#define LI_BPC_MUL 1
-#endif
 template <int HT, bool FP8>
 struct StreamCfg {
-  static constexpr int WPE = HT == 1 ? 4 : (HT == 2 ? (FP8 ? LI_FP8_WPE : 2) : 1);
-  static constexpr int NST = FP8 ? LI_FP8_NST : 2;  // at most 3: the in-loop wait count stays <= 23
-  static constexpr int BPC = WPE * LI_BPC_MUL;      // workgroups of 4 waves per CU
+  static constexpr int WPE = HT == 1 ? 4 : (HT == 2 ? (FP8 ? 3 : 2) : 1);
+  static constexpr int NST = FP8 ? 3 : 2;  // at most 3: the in-loop wait count stays <= 23
+  static constexpr int BPC = WPE;          // workgroups of 4 waves per CU
 };
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -617,8 +608,11 @@ _Pragma("unroll") \
   }
   if constexpr (STAGE) {
     // every load has landed; the held scores of keys key0 .. vis_end - 1 go out in
-    // one coalesced pass (the keys past vis_end were written -inf at the start)
+    // one coalesced pass (the keys past vis_end were written -inf at the start).
+    // The held scores were written by inline ds_write, which the compiler's wait
+    // tracking does not see: wait for them here, before the barrier.
     LI_WAIT_VMCNT(0);
+    LI_WAIT_LGKM0();
     __syncthreads();
     const float* held = (const float*)(ring + NST * SSTRIDE);
     const int n = vis_end - key0;
@@ -643,10 +637,7 @@ static int num_cus() {
 }
 
 // Keys per workgroup of the staged form (its scores are held in LDS): 16 KB.
-#ifndef LI_STAGE_KEYS
-#define LI_STAGE_KEYS 4096
-#endif
-constexpr int STAGE_KEYS = LI_STAGE_KEYS;
+constexpr int STAGE_KEYS = 4096;
 
 // Keys per workgroup: a multiple of 128 (4 waves x 32 keys) chosen so the grid is
 // about `waves_per_cu` resident waves on every CU, one wave of work each.
@@ -754,7 +745,7 @@ hipError_t launch_score(const void* q, int q_type, const float* w, const void* k
         // the key stream cost several times their bytes
         typedef StreamCfg<2, true> C;
         auto kern = score_stream_kernel<2, true, C::NST, 2, false, true>;
-        const int kpb = std::min(stream_keys_per_block(R, S, 2 * LI_BPC_MUL), STAGE_KEYS);
+        const int kpb = std::min(stream_keys_per_block(R, S, 2), STAGE_KEYS);
         const size_t lds = stream_lds_bytes<2, true>() + (size_t)kpb * sizeof(float);
         dim3 grid((S + kpb - 1) / kpb, R);
         static const bool attr = [&] {

@@ -33,8 +33,6 @@ def lib():
         L.orc_indexer_score.argtypes = [_ptr, ctypes.c_int, _ptr, _ptr, ctypes.c_int, _ptr, _ptr,
                                         _i64, _i64, _i64, _i64, _i64, _ptr]
         L.orc_indexer_score.restype = None
-        L.orc_score_keys.argtypes = [_ptr, ctypes.c_int, _ptr, _ptr, ctypes.c_int, _ptr, _i64, _i64, _i64, _ptr]
-        L.orc_score_keys.restype = None
         L.orc_topk.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _ptr, _ptr]
         L.orc_topk.restype = None
         L.orc_compact_query.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr]
@@ -87,18 +85,6 @@ def indexer_score(q, q_type, w, k, k_type, k_scale=None, nv=None):
     assert nv is None or nv.size == B * T
     out = np.empty((B * T, S), np.float64)
     lib().orc_indexer_score(_p(q), q_type, _p(w), _p(k), k_type, _p(k_scale), _p(nv), B, T, S, H, d, _p(out))
-    return out
-
-
-def score_keys(q_row, q_type, w_row, keys, k_type, scales=None):
-    """Scores of one query row (q_row [H, d], w_row [H]) against keys [n, d]."""
-    q_row = _c(q_row, _DT[q_type]); w_row = _c(w_row, np.float32)
-    keys = _c(keys, _DT[k_type]); scales = _c(scales, np.float32)
-    H, d = q_row.shape
-    n = keys.shape[0]
-    assert keys.shape == (n, d) and w_row.shape == (H,)
-    out = np.empty((n,), np.float64)
-    lib().orc_score_keys(_p(q_row), q_type, _p(w_row), _p(keys), k_type, _p(scales), n, H, d, _p(out))
     return out
 
 

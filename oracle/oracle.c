@@ -184,23 +184,6 @@ void orc_indexer_score(const void *q, int q_type, const float *w, const void *k,
   for_rows(B * T, score_row, &c);
 }
 
-/* Score one row against an explicit list of key rows (used for sampled checks of
- * large workloads).  keys: [n, d] (k_type) with scales [n] or NULL. */
-void orc_score_keys(const void *q_row, int q_type, const float *w_row, const void *keys, int k_type,
-                    const float *scales, int64_t n, int64_t H, int64_t d, double *out) {
-  double *qd = (double *)malloc(sizeof(double) * H * d);
-  double *wd = (double *)malloc(sizeof(double) * H);
-  double *key = (double *)malloc(sizeof(double) * d);
-  for (int64_t i = 0; i < H * d; ++i) qd[i] = load_elem(q_row, q_type, i);
-  for (int64_t h = 0; h < H; ++h) wd[h] = (double)w_row[h];
-  for (int64_t s = 0; s < n; ++s) {
-    double sc = scales ? (double)scales[s] : 1.0;
-    for (int64_t j = 0; j < d; ++j) key[j] = load_elem(keys, k_type, s * d + j) * sc;
-    out[s] = score_one(qd, wd, key, H, d);
-  }
-  free(qd); free(wd); free(key);
-}
-
 /* ---- O2: top-k [LC "Stage 2, sparse main attention"; LSA packed-key order] ------- */
 
 typedef struct { double v; int32_t i; } pair_t;

@@ -17,8 +17,8 @@ MIS = ctypes.c_void_p(0x10004)      # misaligned
 NUL = None
 
 
-def declared():
-    text = open(HDR).read()
+def declared(hdr=HDR):
+    text = open(hdr).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(li_[a-z0-9_]+)\s*\(", text)))
 
@@ -30,6 +30,15 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert li.lib().li_version().startswith(b"lightning-indexer")
+
+
+def test_probe_library_exports_its_header():
+    from lightning_indexer_top_amd import build as b
+    L = ctypes.CDLL(b.PROBE_LIB)
+    names = declared(os.path.join(ROOT, "include", "li_probe.h"))
+    assert len(names) == 5
+    for n in names:
+        assert hasattr(L, n), n
 
 
 def test_status_strings():
@@ -73,10 +82,28 @@ def test_indexer_topk_rejects():
     assert L.li_indexer_topk(*args, 0, A, A, A, 1 << 30, None) == 2
     assert L.li_indexer_topk(*args, 2049, A, A, A, 1 << 30, None) == 2
     assert L.li_indexer_topk(*args, 16, NUL, A, A, 1 << 30, None) == 1
-    need = L.li_indexer_topk_workspace_bytes(1, 16, 1000, 64, 16)
-    if need:
-        assert L.li_indexer_topk(*args, 16, A, A, NUL, 0, None) == 5
-        assert L.li_indexer_topk(*args, 16, A, A, A, need - 1, None) == 5
+    # decode-shaped rows (fp8 keys, one row per sequence) need a workspace
+    fargs = [A, li.LI_BF16, A, A, li.LI_FP8_E4M3, A, NUL, 4, 1, 100000, 64, 128]
+    need = L.li_indexer_topk_workspace_bytes(li.LI_BF16, li.LI_FP8_E4M3, 4, 1, 100000, 64, 512)
+    assert need > 4 * 100000 * 4
+    assert L.li_indexer_topk(*fargs, 512, A, A, NUL, 0, None) == 5
+    assert L.li_indexer_topk(*fargs, 512, A, A, A, need - 1, None) == 5
+
+
+def test_indexer_topk_workspace_follows_the_path():
+    L = li.lib()
+    ws = L.li_indexer_topk_workspace_bytes
+    # the fused many-row kernel (bf16 queries and keys, T >= 16, k <= 512) needs
+    # none: the prefill chunk (4096 rows over 131072 keys) asks for 0 bytes
+    assert ws(li.LI_BF16, li.LI_BF16, 1, 4096, 131072, 64, 512) == 0
+    assert ws(li.LI_BF16, li.LI_BF16, 1, 16, 1000, 64, 16) == 0
+    # the same shape with fp8 keys scores then selects: the score matrix plus the
+    # top-k's own workspace
+    n = ws(li.LI_BF16, li.LI_FP8_E4M3, 1, 16, 1000, 64, 16)
+    assert n >= 16 * 1000 * 4 + L.li_topk_workspace_bytes(16, 1000, 16)
+    # decode rows: scores, candidate lists, flags
+    assert ws(li.LI_BF16, li.LI_FP8_E4M3, 16, 1, 131072, 64, 512) >= 16 * 131072 * 4 * 3
+    assert ws(li.LI_BF16, li.LI_BF16, 0, 16, 1000, 64, 16) == 0
 
 
 def test_compact_rejects():

@@ -30,6 +30,19 @@ def assert_valid_sets(idx, nv, S, k, what):
     assert (inc | ~live[:, 1:]).all(), f"{what}: not strictly ascending"
 
 
+def stratified_rows(T):
+    """Rows t with t mod 16 in {0, 3}, and the first and last 8 rows of the chunk."""
+    t = np.arange(T)
+    keep = (t % 16 == 0) | (t % 16 == 3) | (t < 8) | (t >= T - 8)
+    return t[keep]
+
+
+def test_stratified_rows_cover_both_phases_and_ends():
+    rows = stratified_rows(4096)
+    assert len(rows) == 512 + 6 + 8  # rows 0 and 3 of the first eight are in the 16-row pattern
+    assert {0, 3, 16, 19, 4093, 4095}.issubset(set(rows.tolist()))
+
+
 def test_batched_decode_full_size():
     sp = workloads.spec("batched_decode")
     B, S, k = sp["B"], sp["S"], sp["topk"]
@@ -66,9 +79,10 @@ def test_prefill_chunk_full_size():
     g_idx = idx.cpu().numpy()
     assert np.array_equal(g_idx, idx2.cpu().numpy())
     assert_valid_sets(g_idx, nv, S, k, "prefill_chunk")
-    # sampled rows: the first and last of the chunk, rows of every nv phase, the middle
-    rows = np.array([0, 1, 2, 3, 1000, 2047, 2048, 3333, 4092, 4093, 4094, 4095])
-    print("oracle rows", rows.tolist(), flush=True)
+    # a stratified subset: every 16th row at both ends of its group of four rows that
+    # share a visible count (t mod 16 in {0, 3}), plus the first and last 8 rows
+    rows = stratified_rows(T)
+    print("oracle rows", len(rows), flush=True)
     o = oracle.indexer_score(x["q"][:, rows], oracle.BF16, x["w"][:, rows], x["k"], oracle.BF16, None, nv[rows])
     assert_topk_band(g_idx[rows], o, k, nv[rows], "prefill_chunk top-k")
     # the unfused scoring kernel on the same rows, and the fused selection equal to
@@ -95,13 +109,13 @@ def test_compact_search_full_size():
     assert_valid_sets(sl, None, S, m, "shortlist")
     assert_valid_sets(idx, None, S, k, "final")
     assert all(np.isin(idx[b], sl[b]).all() for b in range(B))
-    for b in (0, 7, 19, 31):
-        print("oracle sequence", b, flush=True)
-        s = slice(b, b + 1)
-        o = oracle.compact_search(x["q"][s], x["w"][s], x["P"], x["c"][s], x["cs"][s], x["k_full"][s], m, k)
-        assert np.array_equal(sl[b], o["shortlist"][0])
-        assert np.array_equal(idx[b], o["idx"][0])
-        assert np.array_equal(val[b], o["val"][0])
+    # every sequence, bit for bit
+    print("oracle, all", B, "sequences", flush=True)
+    o = oracle.compact_search(x["q"], x["w"], x["P"], x["c"], x["cs"], x["k_full"], m, k)
+    for b in range(B):
+        assert np.array_equal(sl[b], o["shortlist"][b]), f"sequence {b}: shortlist"
+        assert np.array_equal(idx[b], o["idx"][b]), f"sequence {b}: final indices"
+        assert np.array_equal(val[b], o["val"][b]), f"sequence {b}: final values"
 
 
 def test_select_attend_full_size():
@@ -118,12 +132,15 @@ def test_select_attend_full_size():
     g = scores.cpu().numpy()
     r_idx, _ = oracle.topk(g.astype(np.float64), k)
     assert np.array_equal(g_idx, r_idx)
-    rows = [0, 33, 63]
-    print("oracle rows", rows, flush=True)
-    o = oracle.indexer_score(x["q"][rows], oracle.BF16, x["w"][rows], x["k"][rows], oracle.FP8_E4M3,
-                             x["k_scale"][rows])
-    assert_scores_close(g[rows], o, "select_attend scores")
-    assert_topk_band(g_idx[rows], o, k, None, "select_attend top-k")
+    # every row against the oracle, in four batches of 16 sequences
+    for b0 in range(0, B, 16):
+        rows = list(range(b0, b0 + 16))
+        print("oracle rows", rows[0], "-", rows[-1], flush=True)
+        o = oracle.indexer_score(x["q"][rows], oracle.BF16, x["w"][rows], x["k"][rows], oracle.FP8_E4M3,
+                                 x["k_scale"][rows])
+        assert_scores_close(g[rows], o, "select_attend scores")
+        assert_topk_band(g_idx[rows], o, k, None, "select_attend top-k")
+        del o
     del scores, kk, ks, x
     torch.cuda.empty_cache()
     # attention over the GPU's own selection, every sequence: the latent cache is

@@ -13,6 +13,7 @@ from helpers import assert_topk_band, dev, key_kind, q_kind
 pytestmark = pytest.mark.gpu
 
 OT = {"f32": oracle.F32, "bf16": oracle.BF16, "fp8": oracle.FP8_E4M3}
+KT = {"f32": li.LI_F32, "bf16": li.LI_BF16, "fp8": li.LI_FP8_E4M3}
 
 
 def inputs(sp):
@@ -51,7 +52,17 @@ def test_selection_matches_oracle(name, over):
 def _fused_check(x, sp, k, what):
     d = dict(q=dev(x["q"], "bf16"), w=dev(x["w"]), k=dev(x["k"], "bf16"),
              nv=dev(x["nv"]) if x["nv"] is not None else None)
-    g_idx, g_val = li.indexer_topk(d["q"], d["w"], d["k"], k, None, d["nv"])
+    B, T, H = x["q"].shape[:3]
+    S = x["k"].shape[1]
+    # the fused many-row path needs no workspace: a call with none at all
+    assert li.indexer_topk_workspace_bytes(li.LI_BF16, li.LI_BF16, B, T, S, H, k) == 0
+    g_idx = torch.empty((B * T, k), dtype=torch.int32, device="cuda")
+    g_val = torch.empty((B * T, k), dtype=torch.float32, device="cuda")
+    st = li.lib().li_indexer_topk(d["q"].data_ptr(), li.LI_BF16, d["w"].data_ptr(), d["k"].data_ptr(), li.LI_BF16,
+                                  None, None if d["nv"] is None else d["nv"].data_ptr(), B, T, S, H, 128, k,
+                                  g_idx.data_ptr(), g_val.data_ptr(), None, 0,
+                                  torch.cuda.current_stream().cuda_stream)
+    assert st == 0, li.lib().li_last_error()
     g_scores = li.indexer_score(d["q"], d["w"], d["k"], None, d["nv"])
     torch.cuda.synchronize()
     g_idx = g_idx.cpu().numpy()
@@ -120,7 +131,7 @@ def test_decode_select_fused(over, topk, nvs):
     if nvs is not None:
         nv = np.asarray(nvs, np.int32)
         d["nv"] = dev(nv)
-    nb = li.indexer_topk_workspace_bytes(R, 1, S, H, topk)
+    nb = li.indexer_topk_workspace_bytes(li.LI_BF16, KT[sp["key"]], R, 1, S, H, topk)
     ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     i1, v1 = li.indexer_topk(d["q"], d["w"], d["k"], topk, d["k_scale"], d["nv"], workspace=ws)
     torch.cuda.synchronize()
@@ -183,7 +194,7 @@ def test_decode_select_planted_threshold(bogus):
     sp = workloads.spec("batched_decode", seed=0x5EED0500, B=8, S=131072)
     x, d = inputs(sp)
     R, S, H, topk = sp["B"], sp["S"], sp["H"], 512
-    nb = li.indexer_topk_workspace_bytes(R, 1, S, H, topk)
+    nb = li.indexer_topk_workspace_bytes(li.LI_BF16, li.LI_FP8_E4M3, R, 1, S, H, topk)
     ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     li.indexer_topk(d["q"], d["w"], d["k"], topk, d["k_scale"], None, workspace=ws)
     torch.cuda.synchronize()

@@ -60,3 +60,28 @@ def test_permutation_and_skipped_entries():
     np.testing.assert_allclose(l3, lse, rtol=1e-15)
     o4, l4 = oracle.sparse_attn(q, kv, -np.ones_like(idx), dv, 0.2)
     assert (o4 == 0).all() and np.isneginf(l4).all()
+
+
+def test_pre_gathered_rows_match_dense_softmax():
+    # the entry point over rows already gathered (row i of b is kv[b, idx[b, i]]),
+    # with skipped entries (-1) given as zero rows, against numpy's dense softmax
+    # over the kept rows only
+    q, kv, idx, dv = _problem(3, k=10)
+    idx = idx.copy()
+    idx[0, [2, 7]] = -1
+    idx[1, 0] = -1
+    rows = np.zeros((q.shape[0], idx.shape[1], q.shape[2]), np.uint16)
+    for b in range(q.shape[0]):
+        for i, s in enumerate(idx[b]):
+            if s >= 0:
+                rows[b, i] = kv[b, s]
+    tau = 0.25
+    out, lse = oracle.sparse_attn_rows(q, rows, idx, dv, tau)
+    for b in range(q.shape[0]):
+        keep = idx[b] >= 0
+        K = _bf(rows[b][keep])
+        logits = tau * (_bf(q[b]) @ K.T)
+        p = np.exp(logits - logits.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        np.testing.assert_allclose(out[b], p @ K[:, :dv], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[b], logsumexp(logits, axis=1), rtol=1e-13)
