@@ -175,36 +175,48 @@ def probe_lib():
     if not os.path.exists(b.PROBE_LIB):
         raise RuntimeError(f"{b.PROBE_LIB} is missing: build it with __graft_entry__.build()")
     L = ctypes.CDLL(b.PROBE_LIB)
-    L.li_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    L.li_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_void_p]
+    L.li_probe_read_blocks.argtypes = [ctypes.c_int]
     L.li_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.li_probe_mfma_flop.argtypes = [ctypes.c_int]
     L.li_probe_mfma_flop.restype = ctypes.c_double
     return L
 
 
+READ_PROBE_CONFIGS = [(0, 4), (0, 8), (1, 4), (1, 8), (2, 2), (2, 3)]  # (access pattern, workgroups per CU)
+READ_PROBE_MODES = {0: "grid-stride register loads", 1: "contiguous range per wave, register loads",
+                    2: "contiguous range per wave, DMA into LDS"}
+
+
 def measure_probes(torch, read_bytes=1 << 30, n_buf=4, reps=3, mfma_iters=4000):
     """Read-only HBM stream over n_buf rotating buffers of read_bytes (more than the
-    MALL), best mean over reps bursts; bf16 matrix-core loop with constant and with
-    random operand bits."""
+    MALL) in each access pattern and occupancy of READ_PROBE_CONFIGS, best mean over
+    reps bursts, the best configuration taken as the measured read ceiling; bf16
+    matrix-core loop with constant and with random operand bits."""
     L = probe_lib()
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     bufs = [torch.empty(read_bytes, dtype=torch.uint8, device="cuda") for _ in range(n_buf)]
     for b in bufs:
         b.fill_(3)
-    sink = torch.empty(L.li_probe_read_blocks(), dtype=torch.int32, device="cuda")
+    sink = torch.empty(L.li_probe_read_blocks(16), dtype=torch.int32, device="cuda")
+    sweep = {}
+    for mode, bpc in READ_PROBE_CONFIGS:
+        def rd(i, mode=mode, bpc=bpc):
+            if L.li_probe_read(_p(bufs[i % n_buf]), read_bytes, _p(sink), mode, bpc, st):
+                raise RuntimeError("li_probe_read failed")
 
-    def rd(i):
-        if L.li_probe_read(_p(bufs[i % n_buf]), read_bytes, _p(sink), st):
-            raise RuntimeError("li_probe_read failed")
-
-    rd(0)
-    best = min(burst_ms(torch, rd, 2 * n_buf) for _ in range(reps))
-    read_gbs = read_bytes / (best * 1e-3) / 1e9
+        rd(0)
+        best = min(burst_ms(torch, rd, 2 * n_buf) for _ in range(reps))
+        sweep[f"{READ_PROBE_MODES[mode]}, {bpc} workgroups/CU"] = round(read_bytes / (best * 1e-3) / 1e9, 1)
     del bufs
     torch.cuda.empty_cache()
+    best_cfg = max(sweep, key=sweep.get)
+    read_gbs = sweep[best_cfg]
     msink = torch.empty(L.li_probe_mfma_blocks() * 4, dtype=torch.float32, device="cuda")
-    out = {"hbm_read_gbs": round(read_gbs, 1), "hbm_read_frac_of_peak": round(read_gbs / HBM_PEAK_GBS, 4),
-           "read_probe": f"{n_buf} x {read_bytes >> 20} MiB rotating, 16-byte loads, best of {reps} bursts"}
+    out = {"hbm_read_gbs": read_gbs, "hbm_read_frac_of_peak": round(read_gbs / HBM_PEAK_GBS, 4),
+           "read_probe": f"best of {len(sweep)} patterns: {best_cfg}; {n_buf} x {read_bytes >> 20} MiB rotating",
+           "read_probe_sweep_gbs": sweep}
     flop = L.li_probe_mfma_flop(mfma_iters)
     for random, name in ((0, "const"), (1, "random")):
         def mf(i, random=random):
@@ -215,8 +227,9 @@ def measure_probes(torch, read_bytes=1 << 30, n_buf=4, reps=3, mfma_iters=4000):
         tf = flop / (ms * 1e-3) / 1e12
         out[f"mfma_bf16_tflops_{name}"] = round(tf, 1)
         out[f"mfma_bf16_frac_of_peak_{name}"] = round(tf / BF16_PEAK_TFLOPS, 4)
-    log(f"[probes] read {out['hbm_read_gbs']} GB/s, bf16 MFMA {out['mfma_bf16_tflops_const']} TFLOP/s (constant "
-        f"operands) / {out['mfma_bf16_tflops_random']} (random)")
+    log(f"[probes] read {out['hbm_read_gbs']} GB/s ({best_cfg}), bf16 MFMA {out['mfma_bf16_tflops_const']} "
+        f"TFLOP/s (constant operands) / {out['mfma_bf16_tflops_random']} (random)")
+    log(f"[probes] read sweep {sweep}")
     return out
 
 
@@ -499,12 +512,11 @@ def bench_compact(torch, li, workloads, steps, warmup, cpu=True):
            "input_replicas": n_rep}
     if cpu:
         import oracle
-        nb = 8
-        s = slice(0, nb)
         t0 = time.perf_counter()
-        oracle.compact_search(x["q"][s], x["w"][s], x["P"], x["c"][s], x["cs"][s], x["k_full"][s], m, k)
+        oracle.compact_search(x["q"], x["w"], x["P"], x["c"], x["cs"], x["k_full"], m, k)
         dt = time.perf_counter() - t0
-        res["cpu_baseline"] = oracle_baseline(nb * S / dt, "keys/s", f"{nb} of {B} sequences, both stages", dt)
+        res["cpu_baseline"] = oracle_baseline(B * S / dt, "keys/s", f"the whole workload: {B} sequences, both "
+                                              "stages", dt)
     return res
 
 
@@ -575,7 +587,7 @@ def bench_select_attend(torch, li, workloads, steps, warmup, cpu=True):
     torch.cuda.empty_cache()
     if cpu:
         import oracle
-        rows = list(range(0, B, B // 8))[:8]
+        rows = list(range(0, B, B // 16))[:16]
         t0 = time.perf_counter()
         o = oracle.indexer_score(x["q"][rows], oracle.BF16, x["w"][rows], x["k"][rows], oracle.FP8_E4M3,
                                  x["k_scale"][rows])

@@ -20,12 +20,16 @@
 extern "C" {
 #endif
 
-/* Workgroups of the read probe; `sink` holds that many uint32 words. */
-int li_probe_read_blocks(void);
+/* Workgroups (of 256 threads) of the read probe at `blocks_per_cu` per compute
+ * unit; `sink` holds that many uint32 words. */
+int li_probe_read_blocks(int blocks_per_cu);
 
-/* Reads all `bytes` of `buf` once (16-byte loads, no stores but one word per
- * workgroup into sink).  buf 16-byte aligned, bytes a multiple of 16. */
-int li_probe_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+/* Reads all `bytes` of `buf` once with 16-byte loads, no stores but one word per
+ * workgroup into sink.  mode 0: grid-stride loads into registers, 8 in flight per
+ * lane; 1: a contiguous range per wave, 8 consecutive 1 KB wave loads in flight;
+ * 2: a contiguous range per wave by DMA into LDS, 12 in flight.  buf 16-byte
+ * aligned, bytes a multiple of 16, 1 <= blocks_per_cu <= 16. */
+int li_probe_read(const void *buf, size_t bytes, uint32_t *sink, int mode, int blocks_per_cu, hipStream_t stream);
 
 /* Workgroups of the matrix-core probe (4 waves each); `sink` holds 4 floats per
  * workgroup. */

@@ -2,9 +2,11 @@
 // ceilings reported beside the datasheet peaks.  Not part of the indexer path.
 //
 //   li_probe_read  -- a read-only HBM stream: every byte of a device buffer is read
-//                     once with 16-byte loads, the sum of the words folded into one
-//                     value per workgroup (so nothing is dead code); no stores in
-//                     the stream.
+//                     once with 16-byte loads (no stores in the stream but one word
+//                     per workgroup), in one of three access patterns: grid-stride
+//                     register loads, a contiguous range per wave into registers,
+//                     or a contiguous range per wave by DMA into LDS (the decode
+//                     scoring kernel's pattern).
 //   li_probe_mfma_bf16 -- a register-resident loop of v_mfma_f32_32x32x16_bf16:
 //                     four independent accumulator chains per wave, operands held
 //                     in VGPRs, either constant bits or pseudo-random normal-range
@@ -21,24 +23,10 @@ typedef float pf32x16 __attribute__((ext_vector_type(16)));
 namespace {
 
 constexpr int RD_THREADS = 256;
-constexpr int RD_UNROLL = 8;  // 16-byte loads in flight per thread per step
 
-__global__ __launch_bounds__(RD_THREADS) void probe_read_kernel(const uint4* __restrict__ p, int64_t n16,
-                                                                uint32_t* __restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * RD_THREADS;
-  int64_t i = (int64_t)blockIdx.x * RD_THREADS + threadIdx.x;
-  uint32_t acc = 0;
-  for (; i + (RD_UNROLL - 1) * stride < n16; i += RD_UNROLL * stride) {
-    uint4 v[RD_UNROLL];
-#pragma unroll
-    for (int u = 0; u < RD_UNROLL; ++u) v[u] = p[i + u * stride];
-#pragma unroll
-    for (int u = 0; u < RD_UNROLL; ++u) acc += v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
-  for (; i < n16; i += stride) {
-    const uint4 v = p[i];
-    acc += v.x ^ v.y ^ v.z ^ v.w;
-  }
+__device__ __forceinline__ uint32_t fold(const uint4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
+
+__device__ __forceinline__ void sink_block(uint32_t acc, uint32_t* sink) {
   __shared__ uint32_t red[RD_THREADS / 64];
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
@@ -48,6 +36,70 @@ __global__ __launch_bounds__(RD_THREADS) void probe_read_kernel(const uint4* __r
     for (int wv = 0; wv < RD_THREADS / 64; ++wv) s += red[wv];
     sink[blockIdx.x] = s;
   }
+}
+
+// Mode 0: grid-stride 16-byte loads, U in flight per thread, consumed in registers.
+template <int U>
+__global__ __launch_bounds__(RD_THREADS) void probe_read_stride(const uint4* __restrict__ p, int64_t n16,
+                                                                uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * RD_THREADS;
+  int64_t i = (int64_t)blockIdx.x * RD_THREADS + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += fold(v[u]);
+  }
+  for (; i < n16; i += stride) acc += fold(p[i]);
+  sink_block(acc, sink);
+}
+
+// Mode 1: every wave streams its own contiguous range, U consecutive 1 KB wave
+// loads in flight, consumed in registers.
+template <int U>
+__global__ __launch_bounds__(RD_THREADS) void probe_read_chunk(const uint4* __restrict__ p, int64_t n16,
+                                                               uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (RD_THREADS / 64);
+  const int64_t wid = (int64_t)blockIdx.x * (RD_THREADS / 64) + (threadIdx.x >> 6);
+  const int64_t per = ((n16 + waves - 1) / waves + 63) / 64 * 64;
+  const int64_t lo = wid * per, hi = lo + per < n16 ? lo + per : n16;
+  uint32_t acc = 0;
+  int64_t i = lo;
+  for (; i + 64 * U <= hi; i += 64 * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = p[i + 64 * u + lane];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc += fold(v[u]);
+  }
+  for (i += lane; i < hi; i += 64) acc += fold(p[i]);
+  sink_block(acc, sink);
+}
+
+// Mode 2: every wave streams its own contiguous range into LDS by DMA
+// (global_load_lds, 1 KB per wave load), U loads in flight, never read back.
+template <int U>
+__global__ __launch_bounds__(RD_THREADS) void probe_read_dma(const uint4* __restrict__ p, int64_t n16,
+                                                             uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RD_THREADS / 64][U][1024];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t waves = (int64_t)gridDim.x * (RD_THREADS / 64);
+  const int64_t wid = (int64_t)blockIdx.x * (RD_THREADS / 64) + w;
+  const int64_t per = ((n16 + waves - 1) / waves + 63) / 64 * 64;
+  const int64_t lo = wid * per, hi = lo + per < n16 ? lo + per : n16;
+  int slot = 0;
+  for (int64_t i = lo; i + 64 <= hi; i += 64) {
+    __builtin_amdgcn_global_load_lds((const void*)(p + i + lane),
+                                     (__attribute__((address_space(3))) void*)&ring[w][slot][0], 16, 0, 0);
+    slot = slot + 1 == U ? 0 : slot + 1;
+    // keep U loads in flight: the slot issued next is free once the load U back has landed
+    __builtin_amdgcn_s_waitcnt((U - 1) | (7 << 4) | (15 << 8));
+  }
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  sink_block(lane == 0 ? (uint32_t)hi : 0u, sink);
 }
 
 __device__ __forceinline__ uint32_t hash32(uint32_t x) {
@@ -109,11 +161,21 @@ int cus() {
 
 extern "C" {
 
-int li_probe_read_blocks(void) { return cus() * 8; }
+int li_probe_read_blocks(int blocks_per_cu) { return cus() * blocks_per_cu; }
 
-int li_probe_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
-  if (!buf || !sink || ((uintptr_t)buf & 15u) || (bytes & 15u)) return 1;
-  probe_read_kernel<<<li_probe_read_blocks(), RD_THREADS, 0, stream>>>((const uint4*)buf, (int64_t)(bytes / 16), sink);
+int li_probe_read(const void* buf, size_t bytes, uint32_t* sink, int mode, int blocks_per_cu, hipStream_t stream) {
+  if (!buf || !sink || ((uintptr_t)buf & 15u) || (bytes & 15u) || mode < 0 || mode > 2 || blocks_per_cu < 1 ||
+      blocks_per_cu > 16)
+    return 1;
+  const int g = li_probe_read_blocks(blocks_per_cu);
+  const uint4* p = (const uint4*)buf;
+  const int64_t n = (int64_t)(bytes / 16);
+  if (mode == 0)
+    probe_read_stride<8><<<g, RD_THREADS, 0, stream>>>(p, n, sink);
+  else if (mode == 1)
+    probe_read_chunk<8><<<g, RD_THREADS, 0, stream>>>(p, n, sink);
+  else
+    probe_read_dma<12><<<g, RD_THREADS, 0, stream>>>(p, n, sink);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
