@@ -135,6 +135,28 @@ li_status li_topk_select(const float *scores, const int32_t *nv, int R, int S, i
                          void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * li_topk_select_noalloc -- li_topk_select without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, results and
+ * errors as li_topk_select; the scratch the few-long-rows path needs lives in a
+ * static device array of LI_TOPK_NOALLOC_SCRATCH_BYTES per GPU, held from the
+ * library's first use on that GPU until the process ends.  The call allocates
+ * nothing.
+ *
+ * Limit: li_topk_workspace_bytes(R, S, k) <= LI_TOPK_NOALLOC_SCRATCH_BYTES, i.e.
+ * R * S <= 4,194,304 scores for the shapes that use the scratch (R < 160 rows of
+ * at least 16,384 scores); other shapes need none and have no limit.  Larger
+ * shapes return LI_ERR_WORKSPACE.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one GPU
+ * (on different streams, or from different threads) race and must not be issued;
+ * the scratch keeps the last call's contents, none of which a later call reads
+ * before writing.
+ */
+#define LI_TOPK_NOALLOC_SCRATCH_BYTES ((size_t)33816576) /* 32 MiB + 256 KiB */
+li_status li_topk_select_noalloc(const float *scores, const int32_t *nv, int R, int S, int k, int32_t *idx,
+                                 float *val, hipStream_t stream);
+
+/*
  * li_indexer_topk -- li_indexer_score followed by li_topk_select, with the same
  * arguments, without handing the score matrix back: for many query rows (a prefill
  * chunk) the selection runs inside the scoring kernel and the [B*T, S] scores are

@@ -54,6 +54,7 @@ def lib():
         L.li_topk_workspace_bytes.argtypes = [_I, _I, _I]
         L.li_topk_workspace_bytes.restype = _Z
         L.li_topk_select.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _Z, _P]
+        L.li_topk_select_noalloc.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P]
         L.li_indexer_topk_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, _I]
         L.li_indexer_topk_workspace_bytes.restype = _Z
         L.li_indexer_topk.argtypes = [_P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P]
@@ -63,7 +64,7 @@ def lib():
         L.li_sparse_attn_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.li_sparse_attn_workspace_bytes.restype = _Z
         L.li_sparse_attn_gather.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _Z, _P]
-        for name in ("li_indexer_score", "li_topk_select", "li_indexer_topk", "li_compact_search_rerank",
+        for name in ("li_indexer_score", "li_topk_select", "li_topk_select_noalloc", "li_indexer_topk", "li_compact_search_rerank",
                      "li_sparse_attn_gather"):
             getattr(L, name).restype = _I
         _LIB = L
@@ -155,6 +156,22 @@ def topk_select(scores, k, nv=None, with_values=True, workspace=None, out=None):
     st = lib().li_topk_select(_ptr(scores), _ptr(nv), R, S, k, _ptr(idx), _ptr(val), _ptr(ws), nb,
                               _stream(scores.device))
     _check(st, "li_topk_select")
+    return idx, val
+
+
+def topk_select_noalloc(scores, k, nv=None, with_values=True, out=None):
+    """topk_select without a workspace: the library's static per-GPU scratch serves
+    the few-long-rows path (li_topk_select_noalloc; calls on one GPU must not
+    overlap)."""
+    _dev(scores, "scores")
+    R, S = scores.shape
+    if out is None:
+        idx = torch.empty((R, k), dtype=torch.int32, device=scores.device)
+        val = torch.empty((R, k), dtype=torch.float32, device=scores.device) if with_values else None
+    else:
+        idx, val = out
+    st = lib().li_topk_select_noalloc(_ptr(scores), _ptr(nv), R, S, k, _ptr(idx), _ptr(val), _stream(scores.device))
+    _check(st, "li_topk_select_noalloc")
     return idx, val
 
 

@@ -8,6 +8,8 @@
 #include "../../include/li.h"
 #include "launch.h"
 
+static_assert(LI_TOPK_NOALLOC_SCRATCH_BYTES == li::NOALLOC_SCRATCH_BYTES, "header and library agree");
+
 namespace {
 
 thread_local char g_err[256] = "";
@@ -102,6 +104,26 @@ li_status li_topk_select(const float* scores, const int32_t* nv, int R, int S, i
   if (need && (!ws || ws_bytes < need)) return fail(LI_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   if (misaligned(ws)) return fail(LI_ERR_ALIGN, "workspace must be 16-byte aligned");
   return launched(li::launch_topk_f32(scores, nv, R, S, k, idx, val, ws, stream), "li_topk_select");
+}
+
+li_status li_topk_select_noalloc(const float* scores, const int32_t* nv, int R, int S, int k, int32_t* idx,
+                                 float* val, hipStream_t stream) {
+  if (!scores || !idx) return fail(LI_ERR_NULL, "scores and idx must be non-NULL");
+  if (R < 1 || S < 1) return fail(LI_ERR_SHAPE, "R and S must be >= 1");
+  if (k < 1 || k > LI_TOPK_MAX) return fail(LI_ERR_SHAPE, "k must be in [1, %d] (got %d)", LI_TOPK_MAX, k);
+  if ((int64_t)R * S >= (1ll << 40)) return fail(LI_ERR_SHAPE, "R*S too large");
+  if (misaligned(scores) || misaligned(nv) || misaligned(idx) || misaligned(val))
+    return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = li_topk_workspace_bytes(R, S, k);
+  if (need > li::NOALLOC_SCRATCH_BYTES)
+    return fail(LI_ERR_WORKSPACE, "this shape needs %zu bytes of scratch, more than the %zu of the static scratch",
+                need, (size_t)li::NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need) {
+    const hipError_t e = li::noalloc_scratch(&ws);
+    if (e != hipSuccess) return fail(LI_ERR_LAUNCH, "static scratch lookup: %s", hipGetErrorString(e));
+  }
+  return launched(li::launch_topk_f32(scores, nv, R, S, k, idx, val, ws, stream), "li_topk_select_noalloc");
 }
 
 size_t li_indexer_topk_workspace_bytes(li_dtype q_type, li_dtype k_type, int B, int T, int S, int H, int topk) {

@@ -17,6 +17,11 @@ hipError_t launch_score(const void* q, int q_type, const float* w, const void* k
 
 // per-row top-k of fp32 scores [R, S]; ws holds topk_ws_bytes(R, S, k) bytes
 size_t topk_ws_bytes(int R, int S, int k);
+
+// Size of the per-device static scratch of li_topk_select_noalloc, and its device
+// address on the current device (looked up on first use, then kept).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (32u << 20) + (256u << 10);
+hipError_t noalloc_scratch(void** ptr);
 // whether rows of this shape take the multi-workgroup top-k (few, long rows)
 bool topk_use_mb(int R, int S);
 hipError_t launch_topk_f32(const float* scores, const int32_t* nv, int R, int S, int k, int32_t* idx, float* val,

@@ -15,6 +15,8 @@
 //      order, and ascending ids keep the later gather sequential), and they are
 //      written out.
 // One workgroup of 1024 threads handles one row.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 #include "select.h"
@@ -604,6 +606,34 @@ hipError_t launch_topk_f64_rows(const double* scores, const int32_t* nv, int R, 
                                 double* val, void* ws, hipStream_t st) {
   if (topk_use_mb(R, S)) return launch_topk_mb<double>(scores, nv, R, S, k, idx, val, ws, st);
   return launch_topk_f64(scores, S, nv, nullptr, R, S, k, idx, val, st);
+}
+
+// ---- static scratch for callers that cannot allocate ---------------------------
+// The multi-workgroup selection's buffers (thresholds, region counts, candidate
+// lists) in one file-scope device array per GPU.  Its name is a host-side stand-in
+// in host code: the device address comes from hipGetSymbolAddress, looked up once
+// per device and kept.  Every call on a device shares that device's array, which
+// keeps the last call's contents (the kernels write every byte they read).
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEV] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace li

@@ -137,3 +137,20 @@ def test_sparse_attn_rejects():
     assert call(Hq=48) == 2 and call(Hq=256) == 2 and call(dqk=512) == 2 and call(dv=576) == 2
     assert call(k=0) == 2 and call(k=4096) == 2
     assert call(lse=MIS) == 4
+
+
+def test_topk_noalloc_rejects():
+    # validation runs before anything touches the device: fake pointers are safe
+    L = li.lib()
+    assert L.li_topk_select_noalloc(NUL, NUL, 4, 100, 8, A, A, None) == 1
+    assert L.li_topk_select_noalloc(A, NUL, 4, 100, 0, A, A, None) == 2
+    assert L.li_topk_select_noalloc(A, NUL, 4, 100, 2049, A, A, None) == 2
+    assert L.li_topk_select_noalloc(A, NUL, 0, 100, 8, A, A, None) == 2
+    assert L.li_topk_select_noalloc(A, NUL, 4, 100, 8, MIS, A, None) == 4
+    # a shape whose selection needs more than the static scratch
+    assert L.li_topk_workspace_bytes(64, 262144, 512) > 33816576
+    assert L.li_topk_select_noalloc(A, NUL, 64, 262144, 512, A, A, None) == 5
+    assert b"static scratch" in L.li_last_error()
+    # the largest decode shape it takes
+    assert L.li_topk_workspace_bytes(16, 262144, 512) <= 33816576
+    assert L.li_topk_workspace_bytes(159, 26379, 512) <= 33816576
