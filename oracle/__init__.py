@@ -45,6 +45,13 @@ def lib():
         L.orc_sparse_attn.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_double,
                                       _ptr, _ptr]
         L.orc_sparse_attn.restype = None
+        L.orc_e4m3_rne.argtypes = [ctypes.c_float]
+        L.orc_e4m3_rne.restype = ctypes.c_uint8
+        L.orc_pool_keys.argtypes = [_ptr, _i64, _i64, _i64, _i64, _ptr, _ptr]
+        L.orc_pool_keys.restype = None
+        L.orc_pooled_select.argtypes = [_ptr, ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64,
+                                        _i64, _i64, _ptr, _ptr]
+        L.orc_pooled_select.restype = None
         _LIB = L
     return _LIB
 
@@ -153,3 +160,38 @@ def sparse_attn(q, kv, idx, dv, tau):
     lse = np.empty((B, Hq), np.float64)
     lib().orc_sparse_attn(_p(q), _p(kv), _p(idx), B, Hq, S, k, dqk, dv, tau, _p(out), _p(lse))
     return out, lse
+
+
+def e4m3_rne(x: float) -> int:
+    """OCP E4M3FN code nearest the fp32 value x (ties to even, saturating)."""
+    return int(lib().orc_e4m3_rne(float(x)))
+
+
+def pool_keys(k, pool):
+    """Pooled fp8 keys of bf16 token keys k [B, L, d] (uint16): (codes uint8
+    [B, L // pool, d], scales float32 [B, L // pool])."""
+    k = _c(k, np.uint16)
+    B, L, d = k.shape
+    Sp = L // pool
+    codes = np.empty((B, Sp, d), np.uint8)
+    scales = np.empty((B, Sp), np.float32)
+    lib().orc_pool_keys(_p(k), B, L, d, pool, _p(codes), _p(scales))
+    return codes, scales
+
+
+def pooled_select(q, q_type, w, codes, scales, pool, k, nv_tokens=None):
+    """(idx_tokens int32 [B*T, k * pool], val_blocks fp64 [B*T, k]): the top-k pooled
+    blocks of q [B, T, H, d], w [B, T, H] over codes [B, Sp, d] + scales [B, Sp],
+    each expanded to its pool tokens."""
+    q = _c(q, _DT[q_type]); w = _c(w, np.float32); codes = _c(codes, np.uint8); scales = _c(scales, np.float32)
+    nv_tokens = _c(nv_tokens, np.int32)
+    B, T, H, d = q.shape
+    Sp = codes.shape[1]
+    assert codes.shape == (B, Sp, d) and scales.shape == (B, Sp) and w.shape == (B, T, H)
+    assert nv_tokens is None or nv_tokens.size == B * T
+    idx = np.empty((B * T, k * pool), np.int32)
+    val = np.empty((B * T, k), np.float64)
+    lib().orc_pooled_select(_p(q), q_type, _p(w), _p(codes), _p(scales), _p(nv_tokens), B, T, Sp, H, d, pool, k,
+                            _p(idx), _p(val))
+    return idx, val
+

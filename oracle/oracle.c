@@ -391,3 +391,85 @@ void orc_sparse_attn(const uint16_t *q, const uint16_t *kv, const int32_t *idx, 
   orc_sparse_attn_rows(q, rows, idx, B, Hq, k, dqk, dv, tau, out, lse);
   free(rows);
 }
+
+/* ---- O6: pooled indexer keys (IndexPool) ["Long context", section "The 2025-2026
+ * Hybrid Turn: Linear Attention Returns", GLM-5.3-Flash: four indexer keys pooled
+ * into one, index_kpool = 4; "Latent Sparse Attention", section "Where the time
+ * goes": 32 heads x 128 dims scoring keys pooled four at a time, top-512 blocks] --- */
+
+/* Nearest OCP E4M3FN value to x (finite), ties to the even code, saturating at
+ * +-448: plain search over the 127 non-negative finite codes. */
+uint8_t orc_e4m3_rne(float x) {
+  double a = fabs((double)x);
+  uint8_t best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double d = fabs(orc_dec_e4m3((uint8_t)c) - a);
+    /* codes ascend with value, so an equal distance means a tie between two
+     * neighbours: the even code wins */
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best_d = d;
+      best = (uint8_t)c;
+    }
+  }
+  if (a > 448.0) best = 0x7E;
+  return (uint8_t)(best | (signbit(x) ? 0x80 : 0x00));
+}
+
+/* Pool `pool` consecutive bf16 token keys into one fp8 key with an fp32 scale (the
+ * pooled cache is written when a block of `pool` tokens completes; an incomplete
+ * last block is not pooled).  The pooled value is the mean: m_j = (((k_0 + k_1) +
+ * k_2) + ...) * (1 / pool) in fp32 (pool a power of two, so the scaling is exact);
+ * scale = max_j |m_j| / 448 (fp32, 1 if all are zero); code_j = e4m3_rne(m_j /
+ * scale) (fp32 division).  These steps decide integer codes, so they are taken in
+ * the fp32 arithmetic the kernel uses, in this order.
+ * k: [B, L, d] bf16 -> codes [B, L / pool, d], scales [B, L / pool]. */
+void orc_pool_keys(const uint16_t *k, int64_t B, int64_t L, int64_t d, int64_t pool, uint8_t *codes,
+                   float *scales) {
+  int64_t Sp = L / pool;
+  float *m = (float *)malloc(sizeof(float) * (d > 0 ? d : 1));
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t j = 0; j < Sp; ++j) {
+      float amax = 0.0f;
+      for (int64_t i = 0; i < d; ++i) {
+        float s = (float)orc_dec_bf16(k[(b * L + j * pool) * d + i]);
+        for (int64_t t = 1; t < pool; ++t) s = s + (float)orc_dec_bf16(k[(b * L + j * pool + t) * d + i]);
+        m[i] = s * (1.0f / (float)pool);
+        if (fabsf(m[i]) > amax) amax = fabsf(m[i]);
+      }
+      float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+      scales[b * Sp + j] = sc;
+      for (int64_t i = 0; i < d; ++i) codes[(b * Sp + j) * d + i] = orc_e4m3_rne(m[i] / sc);
+    }
+  free(m);
+}
+
+/* Selection over pooled keys, expanded to tokens: score every complete visible
+ * block (nv_tokens[r] / pool of them, at most Sp) with the indexer score (O1 on
+ * the fp8 pooled keys), take the top-k blocks (O2), and list each selected block
+ * j as its tokens pool * j .. pool * j + pool - 1; a padded block (-1) gives pool
+ * entries of -1.  idx_tokens: [B*T, k * pool] in ascending token order; val_blocks:
+ * [B*T, k] or NULL, the selected blocks' scores.  nv_tokens NULL = every block. */
+void orc_pooled_select(const void *q, int q_type, const float *w, const uint8_t *codes, const float *scales,
+                       const int32_t *nv_tokens, int64_t B, int64_t T, int64_t Sp, int64_t H, int64_t d,
+                       int64_t pool, int64_t k, int32_t *idx_tokens, double *val_blocks) {
+  int64_t R = B * T;
+  int32_t *nvb = (int32_t *)malloc(sizeof(int32_t) * (R > 0 ? R : 1));
+  for (int64_t r = 0; r < R; ++r) {
+    int64_t n = nv_tokens ? (int64_t)nv_tokens[r] / pool : Sp;
+    if (nv_tokens && nv_tokens[r] < 0) n = 0;
+    nvb[r] = (int32_t)(n < Sp ? n : Sp);
+  }
+  double *sc = (double *)malloc(sizeof(double) * (R * Sp > 0 ? R * Sp : 1));
+  orc_indexer_score(q, q_type, w, codes, ORC_FP8_E4M3, scales, nvb, B, T, Sp, H, d, sc);
+  int32_t *blk = (int32_t *)malloc(sizeof(int32_t) * (R * k > 0 ? R * k : 1));
+  orc_topk(sc, nvb, R, Sp, k, blk, val_blocks);
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t j = 0; j < k; ++j)
+      for (int64_t t = 0; t < pool; ++t) {
+        int32_t bj = blk[r * k + j];
+        idx_tokens[(r * k + j) * pool + t] = bj < 0 ? -1 : (int32_t)(bj * pool + t);
+      }
+  free(nvb); free(sc); free(blk);
+}
+

@@ -30,6 +30,12 @@ void orc_sparse_attn_rows(const uint16_t *q, const uint16_t *rows, const int32_t
 void orc_sparse_attn(const uint16_t *q, const uint16_t *kv, const int32_t *idx, int64_t B, int64_t Hq, int64_t S,
                      int64_t k, int64_t dqk, int64_t dv, double tau, double *out, double *lse);
 
+uint8_t orc_e4m3_rne(float x);
+void orc_pool_keys(const uint16_t *k, int64_t B, int64_t L, int64_t d, int64_t pool, uint8_t *codes, float *scales);
+void orc_pooled_select(const void *q, int q_type, const float *w, const uint8_t *codes, const float *scales,
+                       const int32_t *nv_tokens, int64_t B, int64_t T, int64_t Sp, int64_t H, int64_t d,
+                       int64_t pool, int64_t k, int32_t *idx_tokens, double *val_blocks);
+
 /* synth/gen.c */
 uint64_t synth_stream_base(uint64_t seed, uint64_t tid);
 uint16_t synth_bf16_rne(double v);
@@ -146,6 +152,20 @@ int main(void) {
   uint16_t *gathered = xmalloc(sizeof(uint16_t) * B * ka * dqk);
   memset(gathered, 0, sizeof(uint16_t) * B * ka * dqk);
   orc_sparse_attn_rows(qa, gathered, ia, B, Hq, ka, dqk, dv, 0.2, out, lse);
+
+  /* pooled keys: an incomplete last block, visible counts below one block */
+  for (int c = -500; c <= 500; c += 3) (void)orc_e4m3_rne((float)c * 0.917f);
+  const int64_t pool = 4, Sp = S / pool, kp = 5;
+  uint8_t *pc = xmalloc((size_t)(B * Sp * d));
+  float *ps = xmalloc(sizeof(float) * B * Sp);
+  orc_pool_keys(kb, B, S, d, pool, pc, ps);
+  int32_t pnv[6] = {0, 3, 4, 97, 1000, 23};
+  int32_t *pidx = xmalloc(sizeof(int32_t) * B * T * kp * pool);
+  double *pval = xmalloc(sizeof(double) * B * T * kp);
+  orc_pooled_select(qb, BF16, w, pc, ps, pnv, B, T, Sp, H, d, pool, kp, pidx, pval);
+  int32_t *pidx2 = xmalloc(sizeof(int32_t) * B * T * 40 * pool); /* k above the block count */
+  orc_pooled_select(qb, BF16, w, pc, ps, NULL, B, T, Sp, H, d, pool, 40, pidx2, NULL);
+  free(pc); free(ps); free(pidx); free(pval); free(pidx2);
 
   free(f64); free(f32); free(qb); free(w); free(k8); free(ks); free(kb); free(rb); free(P); free(ck); free(cks);
   free(sc); free(qc); free(wc); free(q8); free(qs); free(W); free(qa); free(kv); free(out); free(lse);
