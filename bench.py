@@ -616,8 +616,65 @@ def _latent_rows_of(sp, b, sel):
     return r
 
 
+def bench_pooled(torch, li, workloads, steps, warmup, cpu=True):
+    """Pooled-key indexer: 16 sequences x 524288 bf16 token keys pooled four at a
+    time on write (li_pool_keys), then the 32-head selection over the 131072 pooled
+    fp8 keys with the top-512 blocks expanded to tokens (li_pooled_indexer_topk)."""
+    sp = workloads.spec("pooled_decode")
+    B, L, pool, H, k = sp["B"], sp["L"], sp["pool"], sp["H"], sp["topk"]
+    Sp = L // pool
+    log(f"[pooled] generating inputs B={B} L={L} tokens, pool {pool}")
+    x = workloads.pooled_inputs(sp)
+    q, w = to_dev(torch, x["q"], "bf16"), to_dev(torch, x["w"])
+    ktok = to_dev(torch, x["k_tokens"], "bf16")
+    codes, scales = li.pool_keys(ktok, pool)
+    # pooling on write: every token key read once, the pooled keys written once
+    pool_ms = burst_ms(torch, lambda i: li.pool_keys(ktok, pool, out=(codes, scales)), max(steps, 10))
+    pool_bytes = B * L * FULL_KEY_BYTES_BF16 + B * Sp * KEY_BYTES
+    del ktok
+    torch.cuda.empty_cache()
+    n_rep = max(2, int(math.ceil(1.1e9 / (B * Sp * KEY_BYTES))))
+    reps = [(codes, scales)] + [(codes.clone(), scales.clone()) for _ in range(n_rep - 1)]
+    nb = li.pooled_indexer_topk_workspace_bytes(B, 1, Sp, H, k)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, k * pool), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B, Sp), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        c, s = reps[i % n_rep]
+        li.pooled_indexer_topk(q, w, c, s, pool, k, with_values=False, workspace=ws, out=(idx, None))
+
+    for i in range(warmup):
+        step(i)
+    ms = burst_ms(torch, lambda i: step(warmup + i), max(steps, 20))
+    score_ms = burst_ms(torch, lambda i: li.indexer_score(q, w, reps[i % n_rep][0], reps[i % n_rep][1], out=sc),
+                        max(steps, 20))
+    alg = decode_bytes(B, Sp)
+    log(f"[pooled] pooling {pool_ms * 1e3:.1f} us ({pool_bytes / (pool_ms * 1e-3) / 1e9:.0f} GB/s); select step "
+        f"{ms * 1e3:.1f} us, scoring {score_ms * 1e3:.1f} us ({alg / (score_ms * 1e-3) / 1e9:.0f} GB/s)")
+    res = {"workload": "pooled_decode B=16 L=524288 tokens pooled 4 -> 131072 fp8 keys, H=32, top-512 blocks -> "
+                       "2048 tokens",
+           "ms": round(ms, 4), "value": round(B * Sp / (ms * 1e-3), 1), "unit": "pooled keys/s (select step)",
+           "step_frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "score_ms": round(score_ms, 4), "score_gbs": round(alg / (score_ms * 1e-3) / 1e9, 1),
+           "score_frac_hbm": round(alg / (score_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "pool_ms": round(pool_ms, 4), "pool_gbs": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
+           "pool_frac_hbm": round(pool_bytes / (pool_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "input_replicas": n_rep}
+    if cpu:
+        import oracle
+        rows = [0, 5, 10, 15]
+        t0 = time.perf_counter()
+        oc, os_ = oracle.pool_keys(x["k_tokens"][rows], pool)
+        oracle.pooled_select(x["q"][rows], oracle.BF16, x["w"][rows], oc, os_, pool, k)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = oracle_baseline(len(rows) * Sp / dt, "pooled keys/s (pooling + select)",
+                                              f"{len(rows)} of {B} sequences: pooling and selection", dt)
+    return res
+
+
 SECONDARY = {"tiny_decode": bench_tiny, "prefill_chunk": bench_prefill, "compact_search": bench_compact,
-             "select_attend": bench_select_attend}
+             "select_attend": bench_select_attend, "pooled_decode": bench_pooled}
 
 
 def main():

@@ -183,6 +183,53 @@ li_status li_indexer_topk(const void *q, li_dtype q_type, const float *w, const 
                           int32_t *idx, float *val, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * li_pool_keys -- pooled indexer keys, written once a block of `pool` token keys
+ * is complete ("Long context", section "The 2025-2026 Hybrid Turn: Linear
+ * Attention Returns": IndexPool, four indexer keys pooled into one, index_kpool =
+ * 4, quartering the indexer cache).
+ *
+ *   k       [B, L, d]        bf16 token keys (k_type == LI_BF16)
+ *   codes   [B, L/pool, d]   output: fp8 E4M3FN codes of the pooled keys
+ *   scales  [B, L/pool]      output: fp32 scale per pooled key (key = code * scale)
+ *
+ * Pooled key j is the mean of tokens pool*j .. pool*j + pool - 1; an incomplete
+ * last block is not pooled.  In fp32: m = (((k_0 + k_1) + k_2) + ...) * (1/pool),
+ * scale = max|m| / 448 (1 when m is all zero), code = E4M3 nearest to m / scale
+ * (ties to even, saturating).  Shapes: d == 128, pool in {1, 2, 4, 8}, B >= 1,
+ * L >= 0; with L < pool nothing is written and the pointers may be NULL.
+ * Errors: LI_ERR_NULL, LI_ERR_DTYPE, LI_ERR_SHAPE, LI_ERR_ALIGN, LI_ERR_LAUNCH.
+ */
+li_status li_pool_keys(const void *k, li_dtype k_type, int B, int L, int d, int pool, uint8_t *codes,
+                       float *scales, hipStream_t stream);
+
+/*
+ * li_pooled_indexer_topk -- selection over pooled keys, expanded to tokens
+ * ("Latent Sparse Attention", section "Where the time goes": an indexer of 32
+ * heads x 128 dims scoring keys pooled four at a time and keeping its top-512
+ * blocks).
+ *
+ *   q, w        as li_indexer_score (q_type == LI_BF16), one row per (b, t)
+ *   codes       [B, Sp, d] fp8 pooled keys, scales [B, Sp] (li_pool_keys output)
+ *   nv_tokens   [B*T] int32 visible tokens per row, or NULL (every block): row r
+ *               considers the complete blocks j < nv_tokens[r] / pool (at most Sp)
+ *   idx_tokens  [B*T, topk * pool] int32 output: the topk best blocks (ties to the
+ *               smaller block), each listed as its pool tokens, ascending; a row
+ *               with fewer than topk visible blocks pads with -1
+ *   val_blocks  [B*T, topk] fp32 output or NULL: the selected blocks' scores
+ *   ws          workspace of at least li_pooled_indexer_topk_workspace_bytes(B, T,
+ *               Sp, H, topk) bytes (the scoring and selection of li_indexer_topk
+ *               run inside it on the pooled keys)
+ *
+ * Shapes: d == 128, 1 <= H <= 128, pool in {1, 2, 4, 8}, 1 <= topk <= LI_TOPK_MAX,
+ * Sp * pool < 2^31.  Errors as li_indexer_topk.
+ */
+size_t li_pooled_indexer_topk_workspace_bytes(int B, int T, int Sp, int H, int topk);
+li_status li_pooled_indexer_topk(const void *q, li_dtype q_type, const float *w, const uint8_t *codes,
+                                 const float *scales, const int32_t *nv_tokens, int B, int T, int Sp, int H, int d,
+                                 int pool, int topk, int32_t *idx_tokens, float *val_blocks, void *ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/*
  * li_compact_search_rerank -- two-stage decode search over compact keys.
  *
  *   q        [B, H, d]   bf16 query heads (one decode row per sequence)

@@ -64,7 +64,12 @@ def lib():
         L.li_sparse_attn_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.li_sparse_attn_workspace_bytes.restype = _Z
         L.li_sparse_attn_gather.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P, _Z, _P]
-        for name in ("li_indexer_score", "li_topk_select", "li_topk_select_noalloc", "li_indexer_topk", "li_compact_search_rerank",
+        L.li_pool_keys.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _P]
+        L.li_pooled_indexer_topk_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+        L.li_pooled_indexer_topk_workspace_bytes.restype = _Z
+        L.li_pooled_indexer_topk.argtypes = [_P, _I, _P, _P, _P, _P] + [_I] * 7 + [_P, _P, _P, _Z, _P]
+        for name in ("li_indexer_score", "li_topk_select", "li_topk_select_noalloc", "li_indexer_topk",
+                     "li_pool_keys", "li_pooled_indexer_topk", "li_compact_search_rerank",
                      "li_sparse_attn_gather"):
             getattr(L, name).restype = _I
         _LIB = L
@@ -196,6 +201,48 @@ def indexer_topk(q, w, k, topk, k_scale=None, nv=None, with_values=True, workspa
     st = lib().li_indexer_topk(_ptr(q), _dtype_code(q, "q"), _ptr(w), _ptr(k), _dtype_code(k, "k"), _ptr(k_scale),
                                _ptr(nv), B, T, S, H, d, topk, _ptr(idx), _ptr(val), _ptr(ws), nb, _stream(q.device))
     _check(st, "li_indexer_topk")
+    return idx, val
+
+
+def pool_keys(k, pool, out=None):
+    """Pooled fp8 keys of bf16 token keys k [B, L, 128]: (codes float8_e4m3fn
+    [B, L // pool, 128], scales fp32 [B, L // pool])."""
+    _dev(k, "k")
+    B, L, d = k.shape
+    Sp = L // pool
+    if out is None:
+        codes = torch.empty((B, Sp, d), dtype=torch.float8_e4m3fn, device=k.device)
+        scales = torch.empty((B, Sp), dtype=torch.float32, device=k.device)
+    else:
+        codes, scales = out
+    st = lib().li_pool_keys(_ptr(k), _dtype_code(k, "k"), B, L, d, pool, _ptr(codes), _ptr(scales), _stream(k.device))
+    _check(st, "li_pool_keys")
+    return codes, scales
+
+
+def pooled_indexer_topk_workspace_bytes(B, T, Sp, H, topk):
+    return int(lib().li_pooled_indexer_topk_workspace_bytes(B, T, Sp, H, topk))
+
+
+def pooled_indexer_topk(q, w, codes, scales, pool, topk, nv_tokens=None, with_values=True, workspace=None,
+                        out=None):
+    """(idx_tokens [B*T, topk*pool] int32, val_blocks [B*T, topk] fp32 or None): the top
+    pooled blocks of q [B, T, H, 128] (bf16), w [B, T, H] over codes [B, Sp, 128]
+    (float8_e4m3fn) + scales [B, Sp], expanded to token indices."""
+    _dev(q, "q"); _dev(w, "w"); _dev(codes, "codes"); _dev(scales, "scales")
+    B, T, H, d = q.shape
+    Sp = codes.shape[1]
+    R = B * T
+    if out is None:
+        idx = torch.empty((R, topk * pool), dtype=torch.int32, device=q.device)
+        val = torch.empty((R, topk), dtype=torch.float32, device=q.device) if with_values else None
+    else:
+        idx, val = out
+    ws, nb = _workspace(pooled_indexer_topk_workspace_bytes(B, T, Sp, H, topk), q.device, workspace)
+    st = lib().li_pooled_indexer_topk(_ptr(q), _dtype_code(q, "q"), _ptr(w), _ptr(codes), _ptr(scales),
+                                      _ptr(nv_tokens), B, T, Sp, H, d, pool, topk, _ptr(idx), _ptr(val), _ptr(ws), nb,
+                                      _stream(q.device))
+    _check(st, "li_pooled_indexer_topk")
     return idx, val
 
 

@@ -147,6 +147,45 @@ li_status li_indexer_topk(const void* q, li_dtype q_type, const float* w, const 
                   "li_indexer_topk");
 }
 
+li_status li_pool_keys(const void* k, li_dtype k_type, int B, int L, int d, int pool, uint8_t* codes,
+                       float* scales, hipStream_t stream) {
+  if (k_type != LI_BF16) return fail(LI_ERR_DTYPE, "token keys must be LI_BF16");
+  if (d != LI_INDEX_DIM) return fail(LI_ERR_SHAPE, "d must be %d", LI_INDEX_DIM);
+  if (pool != 1 && pool != 2 && pool != 4 && pool != 8) return fail(LI_ERR_SHAPE, "pool must be 1, 2, 4 or 8");
+  if (B < 1 || L < 0) return fail(LI_ERR_SHAPE, "need B >= 1 and L >= 0");
+  if ((int64_t)B * L >= (1ll << 40)) return fail(LI_ERR_SHAPE, "B*L too large");
+  if (L / pool == 0) return ok();  // no complete block: nothing to write
+  if (!k || !codes || !scales) return fail(LI_ERR_NULL, "k, codes and scales must be non-NULL");
+  if (misaligned(k) || misaligned(codes) || misaligned(scales))
+    return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  return launched(li::launch_pool_keys((const uint16_t*)k, B, L, pool, codes, scales, stream), "li_pool_keys");
+}
+
+size_t li_pooled_indexer_topk_workspace_bytes(int B, int T, int Sp, int H, int topk) {
+  if (B < 1 || T < 1 || Sp < 1 || H < 1 || topk < 1) return 0;
+  return li::pooled_topk_ws_bytes(B, T, Sp, H, topk);
+}
+
+li_status li_pooled_indexer_topk(const void* q, li_dtype q_type, const float* w, const uint8_t* codes,
+                                 const float* scales, const int32_t* nv_tokens, int B, int T, int Sp, int H, int d,
+                                 int pool, int topk, int32_t* idx_tokens, float* val_blocks, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  if (q_type != LI_BF16) return fail(LI_ERR_DTYPE, "q_type must be LI_BF16");
+  li_status s = check_score_args(q, q_type, w, codes, LI_FP8_E4M3, scales, nv_tokens, B, T, Sp, H, d);
+  if (s != LI_OK) return s;
+  if (!idx_tokens) return fail(LI_ERR_NULL, "idx_tokens must be non-NULL");
+  if (pool != 1 && pool != 2 && pool != 4 && pool != 8) return fail(LI_ERR_SHAPE, "pool must be 1, 2, 4 or 8");
+  if (topk < 1 || topk > LI_TOPK_MAX) return fail(LI_ERR_SHAPE, "topk must be in [1, %d]", LI_TOPK_MAX);
+  if ((int64_t)Sp * pool >= (1ll << 31)) return fail(LI_ERR_SHAPE, "Sp * pool must fit in int32");
+  if (misaligned(idx_tokens) || misaligned(val_blocks) || misaligned(ws))
+    return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = li::pooled_topk_ws_bytes(B, T, Sp, H, topk);
+  if (!ws || ws_bytes < need) return fail(LI_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  return launched(li::launch_pooled_topk((const uint16_t*)q, w, codes, scales, nv_tokens, B, T, Sp, H, pool, topk,
+                                         idx_tokens, val_blocks, ws, stream),
+                  "li_pooled_indexer_topk");
+}
+
 size_t li_compact_workspace_bytes(int B, int S, int H, int m, int k) {
   if (B < 1 || S < 1 || H < 1 || m < 1) return 0;
   return li::compact_ws_bytes(B, S, H, m, k);

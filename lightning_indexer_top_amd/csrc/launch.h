@@ -82,4 +82,14 @@ hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const 
                                const int32_t* nv, int B, int T, int S, int H, int topk, int32_t* idx, float* val,
                                void* ws, hipStream_t st);
 
+// pooled indexer keys (pooled.hip): pool bf16 token keys [B, L, 128] into fp8
+// codes [B, L / pool, 128] + scales; score the pooled keys, select the top blocks
+// and expand them to token indices
+hipError_t launch_pool_keys(const uint16_t* k, int B, int L, int pool, uint8_t* codes, float* scales,
+                            hipStream_t st);
+size_t pooled_topk_ws_bytes(int B, int T, int Sp, int H, int topk);
+hipError_t launch_pooled_topk(const uint16_t* q, const float* w, const uint8_t* codes, const float* scales,
+                              const int32_t* nv_tokens, int B, int T, int Sp, int H, int pool, int topk,
+                              int32_t* idx_tokens, float* val_blocks, void* ws, hipStream_t st);
+
 }  // namespace li

@@ -398,21 +398,23 @@ void orc_sparse_attn(const uint16_t *q, const uint16_t *kv, const int32_t *idx, 
  * goes": 32 heads x 128 dims scoring keys pooled four at a time, top-512 blocks] --- */
 
 /* Nearest OCP E4M3FN value to x (finite), ties to the even code, saturating at
- * +-448: plain search over the 127 non-negative finite codes. */
+ * +-448: the non-negative finite codes 0x00..0x7E decode to ascending values, so
+ * a binary search finds the two codes around |x| and the nearer one wins, the
+ * even one on a tie. */
 uint8_t orc_e4m3_rne(float x) {
   double a = fabs((double)x);
-  uint8_t best = 0;
-  double best_d = INFINITY;
-  for (int c = 0; c <= 0x7E; ++c) {
-    double d = fabs(orc_dec_e4m3((uint8_t)c) - a);
-    /* codes ascend with value, so an equal distance means a tie between two
-     * neighbours: the even code wins */
-    if (d < best_d || (d == best_d && (c & 1) == 0)) {
-      best_d = d;
-      best = (uint8_t)c;
+  uint8_t best;
+  if (a >= 448.0) {
+    best = 0x7E;
+  } else {
+    int lo = 0, hi = 0x7E; /* invariant: value(lo) <= a < value(hi) */
+    while (hi - lo > 1) {
+      int mid = (lo + hi) / 2;
+      if (orc_dec_e4m3((uint8_t)mid) <= a) lo = mid; else hi = mid;
     }
+    double dl = a - orc_dec_e4m3((uint8_t)lo), dh = orc_dec_e4m3((uint8_t)hi) - a;
+    best = (uint8_t)(dl < dh ? lo : dh < dl ? hi : ((lo & 1) == 0 ? lo : hi));
   }
-  if (a > 448.0) best = 0x7E;
   return (uint8_t)(best | (signbit(x) ? 0x80 : 0x00));
 }
 

@@ -35,6 +35,11 @@ WORKLOADS = {
     "select_attend": dict(B=64, T=1, S=262144, H=64, d=128, topk=512, key="fp8", q="bf16", q_scale=1.0,
                           w="normal", causal=False, Hq=128, dqk=576, dv=512, tau=1 / math.sqrt(192),
                           seed=SEED_BASE + 5),
+    # 16 sequences x 524288 bf16 token keys pooled four at a time on write (131072
+    # fp8 pooled keys each), a 32-head indexer over the pooled keys, top-512 blocks
+    # expanded to 2048 tokens
+    "pooled_decode": dict(B=16, T=1, L=524288, pool=4, S=131072, H=32, d=128, topk=512, key="bf16", q="bf16",
+                          q_scale=1 / math.sqrt(128), w="uniform", causal=False, seed=SEED_BASE + 6),
 }
 
 
@@ -117,3 +122,14 @@ def latent_rows(sp, idx):
     rows = normal_bf16_rows(sp["seed"], TID_LATENT, flat, dqk, 1.0).reshape(B, k, dqk)
     rows[idx < 0] = 0
     return rows
+
+
+def pooled_inputs(sp):
+    """q [B, T, H, d] bf16, w [B, T, H], token keys [B, L, d] bf16 N(0, 1) (the
+    pooled cache is written from these)."""
+    B, T, L, H, d, seed = sp["B"], sp["T"], sp["L"], sp["H"], sp["d"], sp["seed"]
+    q = normal_bf16(seed, TID_Q, (B, T, H, d), sp["q_scale"])
+    w = uniform_f32(seed, TID_W, (B, T, H), 0.0, 1.0)
+    k = normal_bf16(seed, TID_K, (B, L, d), 1.0)
+    return {"q": q, "w": w, "k_tokens": k}
+

@@ -154,3 +154,29 @@ def test_topk_noalloc_rejects():
     # the largest decode shape it takes
     assert L.li_topk_workspace_bytes(16, 262144, 512) <= 33816576
     assert L.li_topk_workspace_bytes(159, 26379, 512) <= 33816576
+
+
+def test_pooled_rejects():
+    L = li.lib()
+    assert L.li_pool_keys(NUL, li.LI_BF16, 2, 100, 128, 4, A, A, None) == 1
+    assert L.li_pool_keys(A, li.LI_FP8_E4M3, 2, 100, 128, 4, A, A, None) == 3
+    assert L.li_pool_keys(A, li.LI_BF16, 2, 100, 64, 4, A, A, None) == 2
+    assert L.li_pool_keys(A, li.LI_BF16, 2, 100, 128, 3, A, A, None) == 2
+    assert L.li_pool_keys(A, li.LI_BF16, 2, 100, 128, 4, MIS, A, None) == 4
+    assert L.li_pool_keys(NUL, li.LI_BF16, 2, 3, 128, 4, NUL, NUL, None) == 0  # no complete block
+    need = L.li_pooled_indexer_topk_workspace_bytes(16, 1, 131072, 32, 512)
+    assert need > 16 * 131072 * 4
+
+    def call(**kw):
+        a = dict(q=A, qt=li.LI_BF16, w=A, c=A, s=A, nv=NUL, B=16, T=1, Sp=131072, H=32, d=128, pool=4, k=512,
+                 idx=A, val=A, ws=A2, nb=need)
+        a.update(kw)
+        return L.li_pooled_indexer_topk(a["q"], a["qt"], a["w"], a["c"], a["s"], a["nv"], a["B"], a["T"], a["Sp"],
+                                        a["H"], a["d"], a["pool"], a["k"], a["idx"], a["val"], a["ws"], a["nb"],
+                                        None)
+    assert call(q=NUL) == 1 and call(s=NUL) == 1 and call(idx=NUL) == 1
+    assert call(qt=li.LI_F32) == 3
+    assert call(pool=5) == 2 and call(k=0) == 2 and call(k=4096) == 2 and call(H=0) == 2
+    assert call(Sp=1 << 29, pool=8) == 2
+    assert call(ws=NUL) == 5 and call(nb=need - 1) == 5
+    assert call(idx=MIS) == 4
