@@ -78,7 +78,7 @@ def check_pooled(sp, nv_tokens=None):
     R = sp["B"] * sp["T"]
     # blocks: every pool-th token, the rest its expansion
     blocks = idx[:, ::pool]
-    exp = np.where(blocks[:, :, None] >= 0, blocks[:, :, None] * pool + np.arange(pool), -1).reshape(R, -1)
+    exp = np.where(blocks[:, :, None] >= 0, blocks[:, :, None] + np.arange(pool), -1).reshape(R, -1)
     assert np.array_equal(idx, exp), "tokens are not the expansion of the blocks"
     assert np.all((blocks == -1) | (blocks % pool == 0))
     blk = np.where(blocks >= 0, blocks // pool, -1)
