@@ -565,6 +565,15 @@ def bench_select_attend(torch, li, workloads, steps, warmup, cpu=True):
     # the attention kernel alone over a burst
     attn_burst_ms = burst_ms(torch, lambda i: li.sparse_attn_gather(qa, lat, idx, sp["tau"], out=(out, lse)),
                              max(steps, 20))
+    # the same attention through a slot table (page size 1): the latent buffer read as a
+    # pool of B * S rows, every token at a random slot (timing only: the rows read
+    # are other tokens' rows, the access pattern is what counts)
+    perm = torch.randperm(B * S, generator=torch.Generator().manual_seed(0x5EED0E01)).to(torch.int32)
+    slot_table = perm.reshape(B, S).cuda()
+    pool = lat.view(B * S, sp["dqk"])
+    paged_ms = burst_ms(torch, lambda i: li.sparse_attn_gather_paged(qa, pool, slot_table, S, idx, sp["tau"],
+                                                                     out=(out, lse)), max(steps, 20))
+    del slot_table, perm
     gb = attn_bytes(B, Hq, k)
     af = attn_flop(B, Hq, k)
     res = {
@@ -580,6 +589,8 @@ def bench_select_attend(torch, li, workloads, steps, warmup, cpu=True):
         "attn_frac_hbm": round(gb / (attn_burst_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "attn_tflops": round(af / (attn_burst_ms * 1e-3) / 1e12, 2),
         "attn_bytes": gb, "attn_flop": af,
+        "paged_attn_ms": round(paged_ms, 4),
+        "paged_attn_gbs": round(gb / (paged_ms * 1e-3) / 1e9, 1),
     }
     log(f"[select_attend] score {score_ms * 1e3:.1f} us, select {sel_ms * 1e3:.1f} us, attn {attn_ms * 1e3:.1f} us "
         f"({attn_burst_ms * 1e3:.1f} us over a burst)")
@@ -673,8 +684,70 @@ def bench_pooled(torch, li, workloads, steps, warmup, cpu=True):
     return res
 
 
+def bench_paged(torch, li, workloads, steps, warmup, cpu=True):
+    """The batched decode over a paged fp8 key cache: every sequence's 2048 pages of
+    64 keys scattered in a random order over a shared pool (with spare pages), read
+    through page tables (li_indexer_score_paged + li_topk_select)."""
+    sp = workloads.spec("batched_decode")
+    B, S, H, k = sp["B"], sp["S"], sp["H"], sp["topk"]
+    P = S // li.PAGE
+    log(f"[paged] generating inputs B={B} S={S} in pages of {li.PAGE}")
+    x = workloads.indexer_inputs(sp)
+    q, w = to_dev(torch, x["q"], "bf16"), to_dev(torch, x["w"])
+    rng = np.random.default_rng(0x5EED0E00)
+    num = B * P + 4096
+    perm = rng.permutation(num)[:B * P].reshape(B, P).astype(np.int32)
+    table = to_dev(torch, perm)
+    kc = to_dev(torch, x["k"].reshape(B * P, li.PAGE, 128), "fp8")
+    ks = to_dev(torch, x["k_scale"].reshape(B * P, li.PAGE))
+    flat = torch.from_numpy(perm.reshape(-1).astype(np.int64)).cuda()
+    n_rep = max(2, int(math.ceil(1.1e9 / (num * li.PAGE * KEY_BYTES))))
+    pools = []
+    for _ in range(n_rep):
+        kp = torch.zeros((num, li.PAGE, 128), dtype=torch.uint8, device="cuda")
+        spool = torch.ones((num, li.PAGE), dtype=torch.float32, device="cuda")
+        kp[flat] = kc.view(torch.uint8)
+        spool[flat] = ks
+        pools.append((kp.view(torch.float8_e4m3fn), spool))
+    del kc, ks
+    scores = torch.empty((B, S), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(li.topk_workspace_bytes(B, S, k), 256), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        kp, spool = pools[i % n_rep]
+        li.indexer_score_paged(q, w, kp, spool, table, S, out=scores)
+        li.topk_select(scores, k, with_values=False, workspace=ws, out=(idx, None))
+
+    for i in range(warmup):
+        step(i)
+    ms = burst_ms(torch, lambda i: step(warmup + i), max(steps, 20))
+    score_ms = burst_ms(torch, lambda i: li.indexer_score_paged(q, w, pools[i % n_rep][0], pools[i % n_rep][1], table,
+                                                                 S, out=scores), max(steps, 20))
+    alg = decode_bytes(B, S)
+    log(f"[paged] step {ms * 1e3:.1f} us, paged scoring {score_ms * 1e3:.1f} us "
+        f"({alg / (score_ms * 1e-3) / 1e9:.0f} GB/s)")
+    res = {"workload": "paged batched_decode: 16 x 131072 fp8 keys in 2048 random pages of 64 each, top-512",
+           "ms": round(ms, 4), "value": round(B * S / (ms * 1e-3), 1), "unit": "keys/s",
+           "score_ms": round(score_ms, 4), "score_gbs": round(alg / (score_ms * 1e-3) / 1e9, 1),
+           "score_frac_hbm": round(alg / (score_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "input_replicas": n_rep}
+    if cpu:
+        import oracle
+        rows = [0, 7, 15]
+        kpool = x["k"].reshape(B * P, li.PAGE, 128)
+        spool_h = x["k_scale"].reshape(B * P, li.PAGE)
+        tab = (np.arange(B * P, dtype=np.int32).reshape(B, P))[rows]
+        t0 = time.perf_counter()
+        sc = oracle.indexer_score_paged(x["q"][rows], oracle.BF16, x["w"][rows], kpool, spool_h, tab, S)
+        oracle.topk(sc, k)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = oracle_baseline(len(rows) * S / dt, "keys/s", f"{len(rows)} of {B} sequences read "
+                                              "through their page tables (score + top-512)", dt)
+    return res
+
+
 SECONDARY = {"tiny_decode": bench_tiny, "prefill_chunk": bench_prefill, "compact_search": bench_compact,
-             "select_attend": bench_select_attend, "pooled_decode": bench_pooled}
+             "select_attend": bench_select_attend, "pooled_decode": bench_pooled, "paged_decode": bench_paged}
 
 
 def main():

@@ -72,6 +72,8 @@ typedef enum li_dtype {
   LI_I8 = 3        /* signed 8-bit integer                                           */
 } li_dtype;
 
+/* Keys per page of the paged indexer key cache. */
+#define LI_INDEX_PAGE 64
 /* Largest k any selection supports (the engine-side fused top-k cap of 2,048). */
 #define LI_TOPK_MAX 2048
 /* Indexer key width and compact key width the kernels are specialised for. */
@@ -278,6 +280,53 @@ size_t li_sparse_attn_workspace_bytes(int B, int Hq, int k, int dv);
 li_status li_sparse_attn_gather(const void *q, const void *kv, const int32_t *idx, int B, int Hq, int S, int k,
                                 int dqk, int dv, float sm_scale, void *out, float *lse, void *ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/*
+ * Paged caches ("Long context", section "Sparsity Is a Systems Feature: The Blast
+ * Radius", paragraph "KV-cache management": the indexer key cache and its scales
+ * are separate buffers read in pages of 64 keys, while the token-level sparse read
+ * of the latent cache uses pages of one token).  Sequences then own no contiguous
+ * key range: their keys sit in pool pages named by a page table.
+ *
+ * li_indexer_score_paged / li_indexer_topk_paged -- li_indexer_score /
+ * li_indexer_topk over a paged fp8 key cache (q_type == LI_BF16):
+ *   k_pool        [num_pages, 64, d]  fp8 E4M3FN codes
+ *   k_scale_pool  [num_pages, 64]     fp32 scales
+ *   page_table    [B, max_pages] int32: page p of sequence b (keys 64 p .. 64 p + 63)
+ *                 is pool page page_table[b * max_pages + p]; only the entries
+ *                 covering keys < S are read.  Entries outside [0, num_pages) are
+ *                 clamped into it (the scores are then unspecified, no access leaves
+ *                 the pool).
+ *   page_size     must be LI_INDEX_PAGE; max_pages * 64 >= S; 1 <= num_pages < 2^25
+ *   other arguments and outputs as the unpaged calls (scores in logical key order);
+ *   the results equal the unpaged calls' on the same logical keys, bit for bit.
+ *   ws: at least li_indexer_topk_paged_workspace_bytes(B, T, S, H, topk) bytes, with
+ *   the unpaged call's contract.
+ */
+li_status li_indexer_score_paged(const void *q, li_dtype q_type, const float *w, const uint8_t *k_pool,
+                                 const float *k_scale_pool, const int32_t *page_table, int page_size, int max_pages,
+                                 int num_pages, const int32_t *nv, int B, int T, int S, int H, int d, float *scores,
+                                 hipStream_t stream);
+size_t li_indexer_topk_paged_workspace_bytes(int B, int T, int S, int H, int topk);
+li_status li_indexer_topk_paged(const void *q, li_dtype q_type, const float *w, const uint8_t *k_pool,
+                                const float *k_scale_pool, const int32_t *page_table, int page_size, int max_pages,
+                                int num_pages, const int32_t *nv, int B, int T, int S, int H, int d, int topk,
+                                int32_t *idx, float *val, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * li_sparse_attn_gather_paged -- li_sparse_attn_gather over a latent pool read at
+ * page size 1:
+ *   kv_pool     [num_slots, dqk] bf16 latent rows
+ *   slot_table  [B, max_slots] int32: token s of sequence b is pool row
+ *               slot_table[b * max_slots + s]; only the entries named by valid
+ *               indices (0 <= idx < S) are read; slots outside [0, num_slots) are
+ *               clamped into it.  max_slots >= S.
+ *   other arguments and outputs as li_sparse_attn_gather (which needs no workspace);
+ *   the results equal the unpaged call's on the same logical rows, bit for bit.
+ */
+li_status li_sparse_attn_gather_paged(const void *q, const void *kv_pool, const int32_t *slot_table, int max_slots,
+                                      int num_slots, const int32_t *idx, int B, int Hq, int S, int k, int dqk, int dv,
+                                      float sm_scale, void *out, float *lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -68,8 +68,15 @@ def lib():
         L.li_pooled_indexer_topk_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.li_pooled_indexer_topk_workspace_bytes.restype = _Z
         L.li_pooled_indexer_topk.argtypes = [_P, _I, _P, _P, _P, _P] + [_I] * 7 + [_P, _P, _P, _Z, _P]
+        L.li_indexer_score_paged.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P] + [_I] * 5 + [_P, _P]
+        L.li_indexer_topk_paged_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+        L.li_indexer_topk_paged_workspace_bytes.restype = _Z
+        L.li_indexer_topk_paged.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P] + [_I] * 6 + [_P, _P, _P, _Z, _P]
+        L.li_sparse_attn_gather_paged.argtypes = [_P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P,
+                                                  _P, _P]
         for name in ("li_indexer_score", "li_topk_select", "li_topk_select_noalloc", "li_indexer_topk",
-                     "li_pool_keys", "li_pooled_indexer_topk", "li_compact_search_rerank",
+                     "li_pool_keys", "li_pooled_indexer_topk", "li_indexer_score_paged", "li_indexer_topk_paged",
+                     "li_sparse_attn_gather_paged", "li_compact_search_rerank",
                      "li_sparse_attn_gather"):
             getattr(L, name).restype = _I
         _LIB = L
@@ -291,3 +298,70 @@ def sparse_attn_gather(q, kv, idx, sm_scale, with_lse=True, workspace=None, out=
                                      _ptr(lse), _ptr(ws), nb, _stream(q.device))
     _check(st, "li_sparse_attn_gather")
     return o, lse
+
+
+PAGE = 64  # keys per page of the paged indexer key cache
+
+
+def indexer_score_paged(q, w, k_pool, k_scale_pool, page_table, S, nv=None, out=None):
+    """Scores [B*T, S] of q [B, T, H, 128] (bf16), w [B, T, H] over a paged fp8 key
+    cache: k_pool [num_pages, 64, 128] float8_e4m3fn, k_scale_pool [num_pages, 64],
+    page_table [B, max_pages] int32 (pool page of keys 64 p .. 64 p + 63)."""
+    for t, n in ((q, "q"), (w, "w"), (k_pool, "k_pool"), (k_scale_pool, "k_scale_pool"), (page_table, "page_table")):
+        _dev(t, n)
+    B, T, H, d = q.shape
+    num_pages = k_pool.shape[0]
+    max_pages = page_table.shape[1]
+    if out is None:
+        out = torch.empty((B * T, S), dtype=torch.float32, device=q.device)
+    st = lib().li_indexer_score_paged(_ptr(q), _dtype_code(q, "q"), _ptr(w), _ptr(k_pool), _ptr(k_scale_pool),
+                                      _ptr(page_table), PAGE, max_pages, num_pages, _ptr(nv), B, T, S, H, d,
+                                      _ptr(out), _stream(q.device))
+    _check(st, "li_indexer_score_paged")
+    return out
+
+
+def indexer_topk_paged_workspace_bytes(B, T, S, H, topk):
+    return int(lib().li_indexer_topk_paged_workspace_bytes(B, T, S, H, topk))
+
+
+def indexer_topk_paged(q, w, k_pool, k_scale_pool, page_table, S, topk, nv=None, with_values=True, workspace=None,
+                       out=None):
+    """(idx [B*T, topk], val [B*T, topk] or None) over a paged fp8 key cache (see
+    indexer_score_paged)."""
+    for t, n in ((q, "q"), (w, "w"), (k_pool, "k_pool"), (k_scale_pool, "k_scale_pool"), (page_table, "page_table")):
+        _dev(t, n)
+    B, T, H, d = q.shape
+    R = B * T
+    if out is None:
+        idx = torch.empty((R, topk), dtype=torch.int32, device=q.device)
+        val = torch.empty((R, topk), dtype=torch.float32, device=q.device) if with_values else None
+    else:
+        idx, val = out
+    ws, nb = _workspace(indexer_topk_paged_workspace_bytes(B, T, S, H, topk), q.device, workspace)
+    st = lib().li_indexer_topk_paged(_ptr(q), _dtype_code(q, "q"), _ptr(w), _ptr(k_pool), _ptr(k_scale_pool),
+                                     _ptr(page_table), PAGE, page_table.shape[1], k_pool.shape[0], _ptr(nv), B, T, S,
+                                     H, d, topk, _ptr(idx), _ptr(val), _ptr(ws), nb, _stream(q.device))
+    _check(st, "li_indexer_topk_paged")
+    return idx, val
+
+
+def sparse_attn_gather_paged(q, kv_pool, slot_table, S, idx, sm_scale, with_lse=True, out=None):
+    """q [B, Hq, 576] bf16, kv_pool [num_slots, 576] bf16, slot_table [B, max_slots]
+    int32 (pool row of token s of b), idx [B, k] -> (out [B, Hq, 512], lse)."""
+    for t, n in ((q, "q"), (kv_pool, "kv_pool"), (slot_table, "slot_table"), (idx, "idx")):
+        _dev(t, n)
+    B, Hq, dqk = q.shape
+    k = idx.shape[1]
+    dv = 512
+    if out is None:
+        o = torch.empty((B, Hq, dv), dtype=torch.bfloat16, device=q.device)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if with_lse else None
+    else:
+        o, lse = out
+    st = lib().li_sparse_attn_gather_paged(_ptr(q), _ptr(kv_pool), _ptr(slot_table), slot_table.shape[1],
+                                           kv_pool.shape[0], _ptr(idx), B, Hq, S, k, dqk, dv, float(sm_scale),
+                                           _ptr(o), _ptr(lse), _stream(q.device))
+    _check(st, "li_sparse_attn_gather_paged")
+    return o, lse
+

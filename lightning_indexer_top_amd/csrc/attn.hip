@@ -152,12 +152,19 @@ __device__ __forceinline__ void at_write_zero(uint32_t a) {
   asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(z) : "memory");
 }
 
-template <int NBUF>
+// PAGED: the latent rows live in a pool read at page size 1 ("Long context",
+// section "Sparsity Is a Systems Feature: The Blast Radius", paragraph "KV-cache
+// management": the token-level sparse read takes pages of one token);
+// slot_table[b * max_slots + s] is the pool row of token s of sequence b.  Slots
+// outside [0, num_slots) are clamped into it.
+template <int NBUF, bool PAGED>
 __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ kv,
                                                           const int32_t* __restrict__ idx, int B, int Hq, int S, int k,
                                                           float tau, uint16_t* __restrict__ out,
-                                                          float* __restrict__ lse) {
+                                                          float* __restrict__ lse,
+                                                          const int32_t* __restrict__ slot_table, int max_slots,
+                                                          int num_slots) {
   __shared__ __attribute__((aligned(1024))) uint8_t kvbuf[NBUF * AT_CHB];
   __shared__ int sidx[AT_KMAX];
   __shared__ f32x4 spart[4][64];
@@ -186,7 +193,11 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     const int32_t* irow = idx + (int64_t)b * k;
     for (int i = tid; i < k; i += 512) {
       const int id = irow[i];
-      sidx[i] = (id >= 0 && id < S) ? id : -1;
+      int v = (id >= 0 && id < S) ? id : -1;
+      if constexpr (PAGED) {
+        if (v >= 0) v = min(max(slot_table[(int64_t)b * max_slots + v], 0), num_slots - 1);
+      }
+      sidx[i] = v;
     }
   }
   if (tid == 0) sflag = 0;
@@ -206,7 +217,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     drow[u] = r;
     doff[u] = 16 * ((ps & ~7) | ((ps ^ at_sw(r)) & 7));
   }
-  const uint8_t* kvb = (const uint8_t*)(kv + (int64_t)b * S * AT_DQK);
+  const uint8_t* kvb = (const uint8_t*)(kv + (PAGED ? 0 : (int64_t)b * S * AT_DQK));
   const uint32_t kv_lds = lds_addr(kvbuf);
   const int nch = (k + AT_CH - 1) / AT_CH;
   // the row indices of this wave's loads of chunk c (LDS reads), then the loads
@@ -524,7 +535,18 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* idx
   (void)ws;
   const int nt = Hq / 32;
   const int blocks = ((B + 7) / 8) * 8 * nt;
-  sparse_attn_kernel<ATTN_NBUF><<<blocks, 512, 0, st>>>(q, kv, idx, B, Hq, S, k, sm_scale, out, lse);
+  sparse_attn_kernel<ATTN_NBUF, false><<<blocks, 512, 0, st>>>(q, kv, idx, B, Hq, S, k, sm_scale, out, lse, nullptr, 0,
+                                                               0);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_paged(const uint16_t* q, const uint16_t* kv_pool, const int32_t* slot_table, int max_slots,
+                             int num_slots, const int32_t* idx, int B, int Hq, int S, int k, float sm_scale,
+                             uint16_t* out, float* lse, hipStream_t st) {
+  const int nt = Hq / 32;
+  const int blocks = ((B + 7) / 8) * 8 * nt;
+  sparse_attn_kernel<ATTN_NBUF, true><<<blocks, 512, 0, st>>>(q, kv_pool, idx, B, Hq, S, k, sm_scale, out, lse,
+                                                              slot_table, max_slots, num_slots);
   return hipGetLastError();
 }
 

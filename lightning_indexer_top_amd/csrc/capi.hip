@@ -186,6 +186,79 @@ li_status li_pooled_indexer_topk(const void* q, li_dtype q_type, const float* w,
                   "li_pooled_indexer_topk");
 }
 
+namespace {
+li_status check_paged_args(const int32_t* page_table, int page_size, int max_pages, int num_pages, int S) {
+  if (!page_table) return fail(LI_ERR_NULL, "page_table must be non-NULL");
+  if (page_size != LI_INDEX_PAGE) return fail(LI_ERR_SHAPE, "page_size must be %d", LI_INDEX_PAGE);
+  if (num_pages < 1 || (int64_t)num_pages * LI_INDEX_PAGE >= (1ll << 31))
+    return fail(LI_ERR_SHAPE, "num_pages must be in [1, 2^31 / %d)", LI_INDEX_PAGE);
+  if ((int64_t)max_pages * LI_INDEX_PAGE < S) return fail(LI_ERR_SHAPE, "max_pages * %d must cover S", LI_INDEX_PAGE);
+  if (misaligned(page_table)) return fail(LI_ERR_ALIGN, "page_table must be 16-byte aligned");
+  return LI_OK;
+}
+}  // namespace
+
+li_status li_indexer_score_paged(const void* q, li_dtype q_type, const float* w, const uint8_t* k_pool,
+                                 const float* k_scale_pool, const int32_t* page_table, int page_size, int max_pages,
+                                 int num_pages, const int32_t* nv, int B, int T, int S, int H, int d, float* scores,
+                                 hipStream_t stream) {
+  if (q_type != LI_BF16) return fail(LI_ERR_DTYPE, "q_type must be LI_BF16");
+  li_status s = check_score_args(q, q_type, w, k_pool, LI_FP8_E4M3, k_scale_pool, nv, B, T, S, H, d);
+  if (s != LI_OK) return s;
+  s = check_paged_args(page_table, page_size, max_pages, num_pages, S);
+  if (s != LI_OK) return s;
+  if (!scores) return fail(LI_ERR_NULL, "scores must be non-NULL");
+  if (misaligned(scores)) return fail(LI_ERR_ALIGN, "scores must be 16-byte aligned");
+  return launched(li::launch_score_paged((const uint16_t*)q, w, k_pool, k_scale_pool, page_table, max_pages,
+                                         num_pages, nv, B, T, S, H, scores, stream),
+                  "li_indexer_score_paged");
+}
+
+size_t li_indexer_topk_paged_workspace_bytes(int B, int T, int S, int H, int topk) {
+  if (B < 1 || T < 1 || S < 1 || H < 1 || topk < 1) return 0;
+  return li::indexer_topk_paged_ws_bytes(B, T, S, H, topk);
+}
+
+li_status li_indexer_topk_paged(const void* q, li_dtype q_type, const float* w, const uint8_t* k_pool,
+                                const float* k_scale_pool, const int32_t* page_table, int page_size, int max_pages,
+                                int num_pages, const int32_t* nv, int B, int T, int S, int H, int d, int topk,
+                                int32_t* idx, float* val, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (q_type != LI_BF16) return fail(LI_ERR_DTYPE, "q_type must be LI_BF16");
+  li_status s = check_score_args(q, q_type, w, k_pool, LI_FP8_E4M3, k_scale_pool, nv, B, T, S, H, d);
+  if (s != LI_OK) return s;
+  s = check_paged_args(page_table, page_size, max_pages, num_pages, S);
+  if (s != LI_OK) return s;
+  if (!idx) return fail(LI_ERR_NULL, "idx must be non-NULL");
+  if (topk < 1 || topk > LI_TOPK_MAX) return fail(LI_ERR_SHAPE, "topk must be in [1, %d]", LI_TOPK_MAX);
+  if (misaligned(idx) || misaligned(val) || misaligned(ws))
+    return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = li::indexer_topk_paged_ws_bytes(B, T, S, H, topk);
+  if (!ws || ws_bytes < need) return fail(LI_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  return launched(li::launch_indexer_topk_paged((const uint16_t*)q, w, k_pool, k_scale_pool, page_table, max_pages,
+                                                num_pages, nv, B, T, S, H, topk, idx, val, ws, stream),
+                  "li_indexer_topk_paged");
+}
+
+li_status li_sparse_attn_gather_paged(const void* q, const void* kv_pool, const int32_t* slot_table, int max_slots,
+                                      int num_slots, const int32_t* idx, int B, int Hq, int S, int k, int dqk, int dv,
+                                      float sm_scale, void* out, float* lse, hipStream_t stream) {
+  if (!q || !kv_pool || !slot_table || !idx || !out)
+    return fail(LI_ERR_NULL, "q, kv_pool, slot_table, idx and out must be non-NULL");
+  if (dqk != 576 || dv != 512) return fail(LI_ERR_SHAPE, "dqk must be 576 and dv 512");
+  if (Hq < 1 || Hq > 128 || Hq % 32) return fail(LI_ERR_SHAPE, "Hq must be a multiple of 32 in [32, 128]");
+  if (B < 1 || S < 1 || k < 1 || k > LI_TOPK_MAX)
+    return fail(LI_ERR_SHAPE, "need B, S >= 1 and 1 <= k <= %d", LI_TOPK_MAX);
+  if (max_slots < S) return fail(LI_ERR_SHAPE, "max_slots must cover S");
+  if (num_slots < 1) return fail(LI_ERR_SHAPE, "num_slots must be >= 1");
+  if ((int64_t)B * max_slots >= (1ll << 40)) return fail(LI_ERR_SHAPE, "B*max_slots too large");
+  if (misaligned(q) || misaligned(kv_pool) || misaligned(slot_table) || misaligned(idx) || misaligned(out) ||
+      misaligned(lse))
+    return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  return launched(li::launch_attn_paged((const uint16_t*)q, (const uint16_t*)kv_pool, slot_table, max_slots,
+                                        num_slots, idx, B, Hq, S, k, sm_scale, (uint16_t*)out, lse, stream),
+                  "li_sparse_attn_gather_paged");
+}
+
 size_t li_compact_workspace_bytes(int B, int S, int H, int m, int k) {
   if (B < 1 || S < 1 || H < 1 || m < 1) return 0;
   return li::compact_ws_bytes(B, S, H, m, k);

@@ -418,4 +418,40 @@ hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const 
   return launch_topk_f32(scores, nv, B * T, S, topk, idx, val, tws, st);
 }
 
+size_t indexer_topk_paged_ws_bytes(int B, int T, int S, int H, int topk) {
+  (void)H;
+  // scores, the top-k's lists and the selection flags (either path fits)
+  return align256((size_t)B * T * S * sizeof(float)) + topk_ws_bytes(B * T, S, topk) +
+         align256((size_t)B * T * 1024 * sizeof(uint32_t)) + align256((size_t)B * T * 256 * sizeof(uint32_t)) +
+         align256((size_t)B * T * 128);
+}
+
+hipError_t launch_indexer_topk_paged(const uint16_t* q, const float* w, const uint8_t* k_pool, const float* ks_pool,
+                                     const int32_t* page_table, int max_pages, int num_pages, const int32_t* nv,
+                                     int B, int T, int S, int H, int topk, int32_t* idx, float* val, void* ws,
+                                     hipStream_t st) {
+  const int R = B * T;
+  float* scores = (float*)ws;
+  void* tws = (uint8_t*)ws + align256((size_t)R * S * sizeof(float));
+  if (select_score_apply_paged(R, S, H, topk)) {
+    uint32_t *unused, *bcnt;
+    float* cval;
+    int32_t* cid;
+    topk_mb_layout(tws, R, S, &unused, &bcnt, &cval, &cid);
+    uint32_t* counters = (uint32_t*)((uint8_t*)tws + topk_ws_bytes(R, S, topk));
+    uint32_t* tau_used = counters + align256((size_t)R * 1024 * sizeof(uint32_t)) / sizeof(uint32_t);
+    uint64_t* taupub = (uint64_t*)(tau_used + align256((size_t)R * 256 * sizeof(uint32_t)) / sizeof(uint32_t));
+    int P = 0, chunk = 0;
+    hipError_t e = launch_score_select(q, DT_FP8, w, k_pool, ks_pool, nv, B, T, S, H, topk, scores, counters, bcnt,
+                                       cval, cid, taupub, tau_used, &P, &chunk, st, page_table, max_pages, num_pages);
+    if (e != hipSuccess) return e;
+    return launch_topk_finalize_f32(scores, nv, R, S, topk, P, chunk, bcnt, cval, cid, idx, val, counters, tau_used,
+                                    st);
+  }
+  hipError_t e = launch_score_paged(q, w, k_pool, ks_pool, page_table, max_pages, num_pages, nv, B, T, S, H, scores,
+                                    st);
+  if (e != hipSuccess) return e;
+  return launch_topk_f32(scores, nv, R, S, topk, idx, val, tws, st);
+}
+
 }  // namespace li

@@ -66,10 +66,28 @@ hipError_t launch_prefill_scores(const uint16_t* q, const float* w, const uint16
 // the row's flags (reset).
 // select_score_apply tells whether the shape takes this path.
 bool select_score_apply(int q_type, int k_type, int R, int S, int H, int topk);
+// (page_table non-NULL: fp8 keys in pool pages of 64, see launch_score_paged)
 hipError_t launch_score_select(const void* q, int k_type, const float* w, const void* k, const float* ks,
                                const int32_t* nv, int B, int T, int S, int H, int topk, float* scores,
                                uint32_t* counters, uint32_t* bcnt, float* cval, int32_t* cid, uint64_t* taupub,
-                               uint32_t* tau_used, int* P, int* chunk, hipStream_t st);
+                               uint32_t* tau_used, int* P, int* chunk, hipStream_t st,
+                               const int32_t* page_table = nullptr, int max_pages = 0, int num_pages = 0);
+bool select_score_apply_paged(int R, int S, int H, int topk);
+
+// Paged fp8 keys: k_pool [num_pages, 64, 128] codes, ks_pool [num_pages, 64]
+// scales, page_table [B, max_pages] (pool page of keys 64 p .. 64 p + 63 of b).
+hipError_t launch_score_paged(const uint16_t* q, const float* w, const uint8_t* k_pool, const float* ks_pool,
+                              const int32_t* page_table, int max_pages, int num_pages, const int32_t* nv, int B,
+                              int T, int S, int H, float* scores, hipStream_t st);
+size_t indexer_topk_paged_ws_bytes(int B, int T, int S, int H, int topk);
+hipError_t launch_indexer_topk_paged(const uint16_t* q, const float* w, const uint8_t* k_pool, const float* ks_pool,
+                                     const int32_t* page_table, int max_pages, int num_pages, const int32_t* nv,
+                                     int B, int T, int S, int H, int topk, int32_t* idx, float* val, void* ws,
+                                     hipStream_t st);
+// Paged latent rows (page size 1): kv_pool [num_slots, 576], slot_table [B, max_slots]
+hipError_t launch_attn_paged(const uint16_t* q, const uint16_t* kv_pool, const int32_t* slot_table, int max_slots,
+                             int num_slots, const int32_t* idx, int B, int Hq, int S, int k, float sm_scale,
+                             uint16_t* out, float* lse, hipStream_t st);
 void topk_mb_layout(void* ws, int R, int S, uint32_t** counters, uint32_t** bcnt, float** cval, int32_t** cid);
 hipError_t launch_topk_finalize_f32(const float* scores, const int32_t* nv, int R, int S, int k, int P, int chunk,
                                     const uint32_t* bcnt, const float* cval, const int32_t* cid, int32_t* idx,

@@ -7,7 +7,8 @@
 // cache; "Latent Sparse Attention", section "Where the time goes": 32 heads x 128
 // dims over keys pooled four at a time, top-512 blocks).
 //
-// pool_keys_kernel: one wave per pooled key.  Lane l owns dimensions 2l and 2l+1
+// pool_keys_kernel: one wave per four pooled keys (all their token loads in
+// flight before the first is used).  Lane l owns dimensions 2l and 2l+1
 // (one 32-bit word of each bf16 token row, so every token row is read as one
 // coalesced 256-byte wave load); the mean is summed in fp32 in token order and
 // scaled by 1/pool (a power of two: exact), the wave's largest magnitude sets the
@@ -40,31 +41,43 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
   return sign | ((uint32_t)(e + 7) << 3) | m;
 }
 
+constexpr int POOL_KPW = 4;  // pooled keys per wave: all their token loads are issued before any is used
+
 __global__ __launch_bounds__(256) void pool_keys_kernel(const uint32_t* __restrict__ k, int64_t L, int64_t Sp,
                                                         int pool, float inv_pool, int64_t n_keys,
                                                         uint16_t* __restrict__ codes, float* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
-  const int64_t key = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (key >= n_keys) return;
-  const int64_t b = key / Sp, j = key - b * Sp;
-  const uint32_t* row = k + ((b * L + j * pool) * 64) + lane;
-  uint32_t v[8];
+  const int64_t key0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * POOL_KPW;
+  if (key0 >= n_keys) return;
+  uint32_t v[POOL_KPW][8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) v[t] = t < pool ? row[(int64_t)t * 64] : 0u;
-  float s0 = __uint_as_float(v[0] << 16), s1 = __uint_as_float(v[0] & 0xFFFF0000u);
+  for (int u = 0; u < POOL_KPW; ++u) {
+    const int64_t key = key0 + u < n_keys ? key0 + u : n_keys - 1;
+    const int64_t b = key / Sp, j = key - b * Sp;
+    const uint32_t* row = k + ((b * L + j * pool) * 64) + lane;
 #pragma unroll
-  for (int t = 1; t < 8; ++t) {
-    if (t < pool) {
-      s0 = s0 + __uint_as_float(v[t] << 16);
-      s1 = s1 + __uint_as_float(v[t] & 0xFFFF0000u);
+    for (int t = 0; t < 8; ++t) v[u][t] = t < pool ? row[(int64_t)t * 64] : 0u;
+  }
+#pragma unroll
+  for (int u = 0; u < POOL_KPW; ++u) {
+    const int64_t key = key0 + u;
+    float s0 = __uint_as_float(v[u][0] << 16), s1 = __uint_as_float(v[u][0] & 0xFFFF0000u);
+#pragma unroll
+    for (int t = 1; t < 8; ++t) {
+      if (t < pool) {
+        s0 = s0 + __uint_as_float(v[u][t] << 16);
+        s1 = s1 + __uint_as_float(v[u][t] & 0xFFFF0000u);
+      }
+    }
+    const float m0 = s0 * inv_pool, m1 = s1 * inv_pool;
+    const float amax = wave_max(fmaxf(fabsf(m0), fabsf(m1)));
+    const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+    const uint32_t c0 = e4m3_code(m0 / sc), c1 = e4m3_code(m1 / sc);
+    if (key < n_keys) {
+      codes[key * 64 + lane] = (uint16_t)(c0 | (c1 << 8));
+      if (lane == 0) scales[key] = sc;
     }
   }
-  const float m0 = s0 * inv_pool, m1 = s1 * inv_pool;
-  const float amax = wave_max(fmaxf(fabsf(m0), fabsf(m1)));
-  const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-  const uint32_t c0 = e4m3_code(m0 / sc), c1 = e4m3_code(m1 / sc);
-  codes[key * 64 + lane] = (uint16_t)(c0 | (c1 << 8));
-  if (lane == 0) scales[key] = sc;
 }
 
 hipError_t launch_pool_keys(const uint16_t* k, int B, int L, int pool, uint8_t* codes, float* scales,
@@ -72,7 +85,8 @@ hipError_t launch_pool_keys(const uint16_t* k, int B, int L, int pool, uint8_t* 
   const int64_t Sp = L / pool;
   const int64_t n = (int64_t)B * Sp;
   if (n == 0) return hipSuccess;
-  const int64_t blocks = (n + 3) / 4;
+  const int64_t waves = (n + POOL_KPW - 1) / POOL_KPW;
+  const int64_t blocks = (waves + 3) / 4;
   pool_keys_kernel<<<(unsigned)blocks, 256, 0, st>>>((const uint32_t*)k, L, Sp, pool, 1.0f / (float)pool, n,
                                                      (uint16_t*)codes, scales);
   return hipGetLastError();

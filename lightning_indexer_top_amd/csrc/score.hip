@@ -336,13 +336,26 @@ __device__ void score_select_epilogue(const float* __restrict__ out_row, int r, 
   (void)wid;
 }
 
-template <int HT, bool FP8, int NST, int WPE, bool SEL, bool STG = false>
+// PAGED: the keys (and scales) of every sequence live in pages of PAGE keys of a
+// shared pool; page_table[b * max_pages + p] is the pool page holding keys
+// PAGE p .. PAGE p + PAGE - 1 of sequence b ("Long context", section "Sparsity Is
+// a Systems Feature: The Blast Radius", paragraph "KV-cache management": the
+// indexer kernel reads its cache in pages of 64 keys).  A workgroup covers at most
+// 64 pages: lane l holds the pool page of the workgroup's l-th page and each tile
+// (32 keys, inside one page) takes its page by a lane read.  Page ids outside
+// [0, num_pages) read page num_pages - 1 or 0 (clamped; no access leaves the pool).
+constexpr int PAGE = 64;
+constexpr int PAGED_MAX_KPB = 64 * PAGE;
+
+template <int HT, bool FP8, int NST, int WPE, bool SEL, bool STG = false, bool PAGED = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ k,
                          const float* __restrict__ ks, const int32_t* __restrict__ nv, int T, int S, int H,
                          int keys_per_block, float* __restrict__ scores, int topk, uint32_t* __restrict__ counters,
                          uint32_t* __restrict__ bcnt, float* __restrict__ cval, int32_t* __restrict__ cid,
-                         uint64_t* __restrict__ taupub, uint32_t* __restrict__ tau_used, uint32_t epoch) {
+                         uint64_t* __restrict__ taupub, uint32_t* __restrict__ tau_used, uint32_t epoch,
+                         const int32_t* __restrict__ page_table, int max_pages, int num_pages) {
+  static_assert(!PAGED || FP8, "paged keys are fp8");
   typedef TileGeom<FP8> G;
   static_assert(NST >= 1 && NST <= 3, "ring depth");
   // STG: the workgroup's scores are held in LDS behind the ring and written in one
@@ -364,7 +377,7 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
   const int key_end = min(key0 + keys_per_block, S);
   float* out_row = scores + (int64_t)r * S;
 
-  const uint8_t* kbase = k + (int64_t)b * S * G::ROW;
+  const uint8_t* kbase = k + (PAGED ? 0 : (int64_t)b * S * G::ROW);
   const int vis_end = min(key_end, nvis);
   for (int key = max(key0, vis_end) + (int)threadIdx.x; key < key_end; key += 256) out_row[key] = -INFINITY;
 
@@ -378,7 +391,32 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
   const uint32_t my_ring = ring0 + (uint32_t)(wave_u * G::BYTES);
   constexpr uint32_t SSTRIDE = 4 * G::BYTES;  // bytes between a wave's stages
   const uint32_t stage0 = ring0 + NST * SSTRIDE;  // held scores (STAGE)
-  const float* sbase = ks + (int64_t)b * S;
+  const float* sbase = ks + (PAGED ? 0 : (int64_t)b * S);
+  // pool page of the workgroup's page `lane` (paged keys)
+  int my_page = 0;
+  if constexpr (PAGED) {
+    const int pi = (key0 / PAGE) + lane;
+    const int npg = min(max_pages, (S + PAGE - 1) / PAGE);
+    const int v = pi < npg ? page_table[(int64_t)b * max_pages + pi] : 0;
+    my_page = min(max(v, 0), num_pages - 1);
+  }
+  // key row and scale of the tile starting at key t
+  auto tile_k = [&](int t) -> const uint8_t* {
+    if constexpr (PAGED) {
+      const int pg = __builtin_amdgcn_readlane(my_page, (t - key0) / PAGE);
+      return kbase + ((int64_t)pg * PAGE + (t % PAGE)) * G::ROW;
+    } else {
+      return kbase + (int64_t)t * G::ROW;
+    }
+  };
+  auto tile_s = [&](int t) -> const float* {
+    if constexpr (PAGED) {
+      const int pg = __builtin_amdgcn_readlane(my_page, (t - key0) / PAGE);
+      return sbase + (int64_t)pg * PAGE + (t % PAGE);
+    } else {
+      return sbase + t;
+    }
+  };
   float* sw = (float*)lds;  // [2][HT][16]
   const int first = key0 + wave_u * 32;
   const int step = 4 * 32;
@@ -425,7 +463,7 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
     for (int st = 0; st < NST; ++st) {
       const int t0 = pro_tile(st);
       if (t0 >= 0)
-        issue_tile<FP8>(kbase + (int64_t)t0 * G::ROW, sbase + t0, my_ring + st * SSTRIDE, goff, lane, min(32, S - t0));
+        issue_tile<FP8>(tile_k(t0), tile_s(t0), my_ring + st * SSTRIDE, goff, lane, min(32, S - t0));
     }
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
@@ -459,7 +497,7 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
     for (int st = 0; st < NST - SPL; ++st) {
       const int t0 = pro_tile(st);
       if (t0 >= 0)
-        issue_tile<FP8>(kbase + (int64_t)t0 * G::ROW, sbase + t0, my_ring + st * SSTRIDE, goff, lane, min(32, S - t0));
+        issue_tile<FP8>(tile_k(t0), tile_s(t0), my_ring + st * SSTRIDE, goff, lane, min(32, S - t0));
     }
     uint8_t* split = ring + (NST - SPL) * SSTRIDE;
 #pragma unroll
@@ -504,7 +542,7 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
     for (int st = NST - SPL; st < NST; ++st) {
       const int t0 = pro_tile(st);
       if (t0 >= 0)
-        issue_tile<FP8>(kbase + (int64_t)t0 * G::ROW, sbase + t0, my_ring + st * SSTRIDE, goff, lane, min(32, S - t0));
+        issue_tile<FP8>(tile_k(t0), tile_s(t0), my_ring + st * SSTRIDE, goff, lane, min(32, S - t0));
     }
   }
 
@@ -573,7 +611,7 @@ _Pragma("unroll") \
     }
     // the stage is free again: refill it with the tile NST steps ahead
     const int tn = tile + NST * step;
-    if (tn < vis_end) issue_tile<FP8>(kbase + (int64_t)tn * G::ROW, sbase + tn, la, goff, lane, min(32, S - tn));
+    if (tn < vis_end) issue_tile<FP8>(tile_k(tn), tile_s(tn), la, goff, lane, min(32, S - tn));
     stage = stage + 1 == NST ? 0 : stage + 1;
     float part;
     LI_TILE_PART();
@@ -712,58 +750,66 @@ __global__ __launch_bounds__(256) void score_valu_kernel(const QT* __restrict__ 
   scores[(int64_t)r * S + s] = acc;
 }
 
+// One launch of the streaming kernel.  STG: scores held in LDS (two workgroups per
+// CU, at most STAGE_KEYS keys each); PAGED: keys in pool pages (at most
+// PAGED_MAX_KPB keys per workgroup).
+template <int HT, bool F8, bool STG, bool PAGED>
+static hipError_t launch_stream(const uint16_t* qq, const float* w, const uint8_t* kk, const float* ks,
+                                const int32_t* nv, int R, int T, int S, int H, float* scores,
+                                const int32_t* page_table, int max_pages, int num_pages, hipStream_t st) {
+  typedef StreamCfg<HT, F8> C;
+  auto kern = score_stream_kernel<HT, F8, C::NST, STG ? 2 : C::WPE, false, STG, PAGED>;
+  int kpb = stream_keys_per_block(R, S, STG ? 2 : C::BPC);
+  if (STG) kpb = std::min(kpb, STAGE_KEYS);
+  if (PAGED) kpb = std::min(kpb, PAGED_MAX_KPB);
+  const size_t lds = stream_lds_bytes<HT, F8>() + (STG ? (size_t)kpb * sizeof(float) : 0);
+  static const bool attr = [&] {
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)(stream_lds_bytes<HT, F8>() + (STG ? STAGE_KEYS * sizeof(float) : 0)));
+    return true;
+  }();
+  (void)attr;
+  dim3 grid((S + kpb - 1) / kpb, R);
+  kern<<<grid, 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, 0, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, nullptr, 0u, page_table, max_pages, num_pages);
+  return hipGetLastError();
+}
+
+// fp8 keys at 33-64 heads hold their scores in LDS and write them once per
+// workgroup: writes interleaved with the key stream cost several times their bytes
+template <bool PAGED>
+static hipError_t launch_stream_fp8(const uint16_t* qq, const float* w, const uint8_t* kk, const float* ks,
+                                    const int32_t* nv, int R, int T, int S, int H, float* scores,
+                                    const int32_t* page_table, int max_pages, int num_pages, hipStream_t st) {
+  if (H <= 32)
+    return launch_stream<1, true, false, PAGED>(qq, w, kk, ks, nv, R, T, S, H, scores, page_table, max_pages,
+                                                num_pages, st);
+  if (H <= 64)
+    return launch_stream<2, true, true, PAGED>(qq, w, kk, ks, nv, R, T, S, H, scores, page_table, max_pages,
+                                               num_pages, st);
+  return launch_stream<4, true, false, PAGED>(qq, w, kk, ks, nv, R, T, S, H, scores, page_table, max_pages,
+                                              num_pages, st);
+}
+
+hipError_t launch_score_paged(const uint16_t* q, const float* w, const uint8_t* k_pool, const float* ks_pool,
+                              const int32_t* page_table, int max_pages, int num_pages, const int32_t* nv, int B,
+                              int T, int S, int H, float* scores, hipStream_t st) {
+  return launch_stream_fp8<true>(q, w, k_pool, ks_pool, nv, B * T, T, S, H, scores, page_table, max_pages,
+                                 num_pages, st);
+}
+
 hipError_t launch_score(const void* q, int q_type, const float* w, const void* k, int k_type, const float* ks,
                         const int32_t* nv, int B, int T, int S, int H, float* scores, hipStream_t st) {
   const int R = B * T;
   if (prefill_scores_apply(q_type, k_type, T, H))
     return launch_prefill_scores((const uint16_t*)q, w, (const uint16_t*)k, nv, B, T, S, H, scores, st);
   if (q_type == DT_BF16 && (k_type == DT_FP8 || k_type == DT_BF16)) {
-    const bool f8 = k_type == DT_FP8;
     const uint16_t* qq = (const uint16_t*)q;
     const uint8_t* kk = (const uint8_t*)k;
-#define LI_LAUNCH_STREAM(HT_, F8_)                                                                            \
-  do {                                                                                                              \
-    typedef StreamCfg<HT_, F8_> C;                                                                                  \
-    auto kern = score_stream_kernel<HT_, F8_, C::NST, C::WPE, false>;                                               \
-    const size_t lds = stream_lds_bytes<HT_, F8_>();                                                                \
-    const int kpb = stream_keys_per_block(R, S, C::BPC);                                                            \
-    dim3 grid((S + kpb - 1) / kpb, R);                                                                              \
-    static const bool attr = [&] {                                                                                  \
-      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);          \
-      return true;                                                                                                  \
-    }();                                                                                                            \
-    (void)attr;                                                                                                     \
-    kern<<<grid, 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, 0, nullptr, nullptr, nullptr, nullptr,   \
-                                 nullptr, nullptr, 0u);                                                             \
-  } while (0)
-    if (H <= 32) {
-      if (f8) LI_LAUNCH_STREAM(1, true); else LI_LAUNCH_STREAM(1, false);
-    } else if (H <= 64) {
-      if (f8) {
-        // fp8 keys: the scores are held in LDS and written once per workgroup (two
-        // workgroups per CU, at most STAGE_KEYS keys each); writes interleaved with
-        // the key stream cost several times their bytes
-        typedef StreamCfg<2, true> C;
-        auto kern = score_stream_kernel<2, true, C::NST, 2, false, true>;
-        const int kpb = std::min(stream_keys_per_block(R, S, 2), STAGE_KEYS);
-        const size_t lds = stream_lds_bytes<2, true>() + (size_t)kpb * sizeof(float);
-        dim3 grid((S + kpb - 1) / kpb, R);
-        static const bool attr = [&] {
-          (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)(stream_lds_bytes<2, true>() + STAGE_KEYS * sizeof(float)));
-          return true;
-        }();
-        (void)attr;
-        kern<<<grid, 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, 0, nullptr, nullptr, nullptr, nullptr,
-                                     nullptr, nullptr, 0u);
-      } else {
-        LI_LAUNCH_STREAM(2, false);
-      }
-    } else {
-      if (f8) LI_LAUNCH_STREAM(4, true); else LI_LAUNCH_STREAM(4, false);
-    }
-#undef LI_LAUNCH_STREAM
-    return hipGetLastError();
+    if (k_type == DT_FP8) return launch_stream_fp8<false>(qq, w, kk, ks, nv, R, T, S, H, scores, nullptr, 0, 0, st);
+    if (H <= 32) return launch_stream<1, false, false, false>(qq, w, kk, ks, nv, R, T, S, H, scores, nullptr, 0, 0, st);
+    if (H <= 64) return launch_stream<2, false, false, false>(qq, w, kk, ks, nv, R, T, S, H, scores, nullptr, 0, 0, st);
+    return launch_stream<4, false, false, false>(qq, w, kk, ks, nv, R, T, S, H, scores, nullptr, 0, 0, st);
   }
   dim3 grid((S + 255) / 256, R);
   const size_t lds = sizeof(float) * (size_t)H * 129;
@@ -794,29 +840,36 @@ hipError_t launch_score(const void* q, int q_type, const float* w, const void* k
 
 // ---- scoring with the selection epilogue (few long rows) ----------------------
 template <int HT, bool F8>
-static int select_blocks_per_row(int R, int S, int* kpb_out) {
-  const int kpb = stream_keys_per_block(R, S, StreamCfg<HT, F8>::BPC);
+static int select_blocks_per_row(int R, int S, bool paged, int* kpb_out) {
+  int kpb = stream_keys_per_block(R, S, StreamCfg<HT, F8>::BPC);
+  if (paged) kpb = std::min(kpb, PAGED_MAX_KPB);
   if (kpb_out) *kpb_out = kpb;
   return (S + kpb - 1) / kpb;
 }
 
-bool select_score_apply(int q_type, int k_type, int R, int S, int H, int topk) {
-  if (q_type != DT_BF16 || (k_type != DT_FP8 && k_type != DT_BF16) || H < 1 || H > 128) return false;
+static bool select_score_shape(int k_type, int R, int S, int H, int topk, bool paged) {
+  if ((k_type != DT_FP8 && k_type != DT_BF16) || H < 1 || H > 128) return false;
   if (!topk_use_mb(R, S) || topk > 2048) return false;
   // the finalize takes at most 256 regions per row,
   const bool f8 = k_type == DT_FP8;
   // and every wave streams at least eight tiles, so that the row's samples (each
   // wave's first tile) are counted long before its workgroups finish
   int P, kpb;
-  if (H <= 32) P = f8 ? select_blocks_per_row<1, true>(R, S, &kpb) : select_blocks_per_row<1, false>(R, S, &kpb);
-  else if (H <= 64) P = f8 ? select_blocks_per_row<2, true>(R, S, &kpb) : select_blocks_per_row<2, false>(R, S, &kpb);
-  else P = f8 ? select_blocks_per_row<4, true>(R, S, &kpb) : select_blocks_per_row<4, false>(R, S, &kpb);
+  if (H <= 32) P = f8 ? select_blocks_per_row<1, true>(R, S, paged, &kpb) : select_blocks_per_row<1, false>(R, S, paged, &kpb);
+  else if (H <= 64) P = f8 ? select_blocks_per_row<2, true>(R, S, paged, &kpb) : select_blocks_per_row<2, false>(R, S, paged, &kpb);
+  else P = f8 ? select_blocks_per_row<4, true>(R, S, paged, &kpb) : select_blocks_per_row<4, false>(R, S, paged, &kpb);
   // and all workgroups of the launch are resident at once (the epilogue may wait
   // for the row's other workgroups to count their samples)
   const int bpc = H <= 32 ? StreamCfg<1, true>::BPC : (H <= 64 ? StreamCfg<2, true>::BPC : StreamCfg<4, true>::BPC);
   const int bpc_b = H <= 32 ? StreamCfg<1, false>::BPC : (H <= 64 ? StreamCfg<2, false>::BPC : StreamCfg<4, false>::BPC);
   return P <= 256 && kpb >= 1024 && (int64_t)P * R <= (int64_t)num_cus() * (f8 ? bpc : bpc_b);
 }
+
+bool select_score_apply(int q_type, int k_type, int R, int S, int H, int topk) {
+  return q_type == DT_BF16 && select_score_shape(k_type, R, S, H, topk, false);
+}
+
+bool select_score_apply_paged(int R, int S, int H, int topk) { return select_score_shape(DT_FP8, R, S, H, topk, true); }
 
 // launch epochs of the selection kernel: a published threshold carries the epoch of
 // the launch that computed it
@@ -830,19 +883,21 @@ static uint32_t next_select_epoch() {
 hipError_t launch_score_select(const void* q, int k_type, const float* w, const void* k, const float* ks,
                                const int32_t* nv, int B, int T, int S, int H, int topk, float* scores,
                                uint32_t* counters, uint32_t* bcnt, float* cval, int32_t* cid, uint64_t* taupub,
-                               uint32_t* tau_used, int* P_out, int* chunk_out, hipStream_t st) {
+                               uint32_t* tau_used, int* P_out, int* chunk_out, hipStream_t st,
+                               const int32_t* page_table, int max_pages, int num_pages) {
   const int R = B * T;
   const uint32_t epoch = next_select_epoch();
   const bool f8 = k_type == DT_FP8;
+  const bool paged = page_table != nullptr;
   const uint16_t* qq = (const uint16_t*)q;
   const uint8_t* kk = (const uint8_t*)k;
-#define LI_LAUNCH_SELECT(HT_, F8_)                                                                                  \
+#define LI_LAUNCH_SELECT(HT_, F8_, PG_)                                                                             \
   do {                                                                                                              \
     typedef StreamCfg<HT_, F8_> C;                                                                                  \
-    auto kern = score_stream_kernel<HT_, F8_, C::NST, C::WPE, true>;                                                \
+    auto kern = score_stream_kernel<HT_, F8_, C::NST, C::WPE, true, false, PG_>;                                   \
     const size_t lds = stream_lds_bytes<HT_, F8_>();                                                                \
     int kpb;                                                                                                        \
-    const int P = select_blocks_per_row<HT_, F8_>(R, S, &kpb);                                                      \
+    const int P = select_blocks_per_row<HT_, F8_>(R, S, PG_, &kpb);                                                 \
     static const bool attr = [&] {                                                                                  \
       (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);          \
       return true;                                                                                                  \
@@ -851,14 +906,18 @@ hipError_t launch_score_select(const void* q, int k_type, const float* w, const 
     *P_out = P;                                                                                                     \
     *chunk_out = kpb;                                                                                               \
     kern<<<dim3(P, R), 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, topk, counters, bcnt, cval, cid,    \
-                                       taupub, tau_used, epoch);                                                    \
+                                       taupub, tau_used, epoch, page_table, max_pages, num_pages);                  \
   } while (0)
-  if (H <= 32) {
-    if (f8) LI_LAUNCH_SELECT(1, true); else LI_LAUNCH_SELECT(1, false);
+  if (paged) {
+    if (H <= 32) LI_LAUNCH_SELECT(1, true, true);
+    else if (H <= 64) LI_LAUNCH_SELECT(2, true, true);
+    else LI_LAUNCH_SELECT(4, true, true);
+  } else if (H <= 32) {
+    if (f8) LI_LAUNCH_SELECT(1, true, false); else LI_LAUNCH_SELECT(1, false, false);
   } else if (H <= 64) {
-    if (f8) LI_LAUNCH_SELECT(2, true); else LI_LAUNCH_SELECT(2, false);
+    if (f8) LI_LAUNCH_SELECT(2, true, false); else LI_LAUNCH_SELECT(2, false, false);
   } else {
-    if (f8) LI_LAUNCH_SELECT(4, true); else LI_LAUNCH_SELECT(4, false);
+    if (f8) LI_LAUNCH_SELECT(4, true, false); else LI_LAUNCH_SELECT(4, false, false);
   }
 #undef LI_LAUNCH_SELECT
   return hipGetLastError();

@@ -195,3 +195,36 @@ def pooled_select(q, q_type, w, codes, scales, pool, k, nv_tokens=None):
                             _p(idx), _p(val))
     return idx, val
 
+
+# ---- paged caches ("Long context", section "Sparsity Is a Systems Feature: The
+# Blast Radius", paragraph "KV-cache management": indexer keys and their scales in
+# separate buffers read in pages of 64, the latent read at page size 1) --------
+
+def unpage(pool, table, S):
+    """Logical rows [B, S, ...] of a paged pool [num_pages, page, ...]: row s of
+    sequence b is pool[table[b, s // page], s % page]."""
+    pool = np.asarray(pool)
+    table = np.asarray(table, np.int64)
+    page = pool.shape[1]
+    s = np.arange(S, dtype=np.int64)
+    return pool[table[:, s // page], s % page]
+
+
+def indexer_score_paged(q, q_type, w, k_pool, k_scale_pool, page_table, S, nv=None):
+    """O1 over paged fp8 keys: the keys gathered through the page table, then scored."""
+    return indexer_score(q, q_type, w, unpage(k_pool, page_table, S), FP8_E4M3,
+                         unpage(k_scale_pool, page_table, S), nv)
+
+
+def sparse_attn_paged(q, kv_pool, slot_table, idx, dv, tau):
+    """O4 over a latent pool read at page size 1: row idx[b, i] of sequence b is
+    kv_pool[slot_table[b, idx[b, i]]]; entries outside [0, S) select nothing."""
+    idx = np.asarray(idx, np.int64)
+    slot_table = np.asarray(slot_table, np.int64)
+    S = slot_table.shape[1]
+    ok = (idx >= 0) & (idx < S)
+    slots = np.where(ok, np.take_along_axis(slot_table, np.where(ok, idx, 0), axis=1), 0)
+    rows = np.asarray(kv_pool)[slots]
+    rows[~ok] = 0
+    return sparse_attn_rows(q, rows, np.where(ok, idx, -1).astype(np.int32), dv, tau)
+

@@ -180,3 +180,37 @@ def test_pooled_rejects():
     assert call(Sp=1 << 29, pool=8) == 2
     assert call(ws=NUL) == 5 and call(nb=need - 1) == 5
     assert call(idx=MIS) == 4
+
+
+def test_paged_rejects():
+    L = li.lib()
+
+    def score(**kw):
+        a = dict(q=A, qt=li.LI_BF16, w=A, k=A, s=A, pt=A, ps=64, mp=2048, npg=40000, nv=NUL, B=16, T=1, S=131072,
+                 H=64, d=128, out=A)
+        a.update(kw)
+        return L.li_indexer_score_paged(a["q"], a["qt"], a["w"], a["k"], a["s"], a["pt"], a["ps"], a["mp"],
+                                        a["npg"], a["nv"], a["B"], a["T"], a["S"], a["H"], a["d"], a["out"], None)
+    assert score(pt=NUL) == 1 and score(s=NUL) == 1 and score(out=NUL) == 1
+    assert score(qt=li.LI_F32) == 3
+    assert score(ps=32) == 2 and score(mp=2047) == 2 and score(npg=0) == 2 and score(npg=1 << 25) == 2
+    assert score(pt=MIS) == 4
+    need = L.li_indexer_topk_paged_workspace_bytes(16, 1, 131072, 64, 512)
+    assert need >= L.li_indexer_topk_workspace_bytes(li.LI_BF16, li.LI_FP8_E4M3, 16, 1, 131072, 64, 512)
+
+    def topk(**kw):
+        a = dict(pt=A, mp=2048, k=512, ws=A2, nb=need)
+        a.update(kw)
+        return L.li_indexer_topk_paged(A, li.LI_BF16, A, A, A, a["pt"], 64, a["mp"], 40000, NUL, 16, 1, 131072, 64,
+                                       128, a["k"], A, A, a["ws"], a["nb"], None)
+    assert topk(pt=NUL) == 1 and topk(mp=100) == 2 and topk(k=0) == 2 and topk(nb=need - 1) == 5
+    assert topk(ws=NUL) == 5
+
+    def attn(**kw):
+        a = dict(q=A, kv=A, st=A, ms=1000, ns=5000, idx=A, B=2, Hq=128, S=1000, k=64, out=A)
+        a.update(kw)
+        return L.li_sparse_attn_gather_paged(a["q"], a["kv"], a["st"], a["ms"], a["ns"], a["idx"], a["B"], a["Hq"],
+                                             a["S"], a["k"], 576, 512, 0.07, a["out"], NUL, None)
+    assert attn(st=NUL) == 1 and attn(kv=NUL) == 1
+    assert attn(ms=999) == 2 and attn(ns=0) == 2 and attn(Hq=40) == 2 and attn(k=0) == 2
+    assert attn(st=MIS) == 4
