@@ -45,6 +45,10 @@ def lib():
         L.orc_sparse_attn.argtypes = [_ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_double,
                                       _ptr, _ptr]
         L.orc_sparse_attn.restype = None
+        L.orc_pq_query.argtypes = [_ptr, _ptr, ctypes.c_double, _i64, _i64, _i64, _ptr, _ptr]
+        L.orc_pq_query.restype = None
+        L.orc_pq_search.argtypes = [_ptr, _ptr, _ptr, ctypes.c_double, _ptr, _ptr, _ptr] + [_i64] * 6 + [_ptr] * 4
+        L.orc_pq_search.restype = None
         L.orc_e4m3_rne.argtypes = [ctypes.c_float]
         L.orc_e4m3_rne.restype = ctypes.c_uint8
         L.orc_pool_keys.argtypes = [_ptr, _i64, _i64, _i64, _i64, _ptr, _ptr]
@@ -227,4 +231,33 @@ def sparse_attn_paged(q, kv_pool, slot_table, idx, dv, tau):
     rows = np.asarray(kv_pool)[slots]
     rows[~ok] = 0
     return sparse_attn_rows(q, rows, np.where(ok, idx, -1).astype(np.int32), dv, tau)
+
+
+def pq_query(q, w, sigma):
+    """(q8 [B, H, d] int8, W [B, H] fp64): the int8 query codes of the product-
+    quantised search and the head weights W = (w * qs) * sigma."""
+    q = _c(q, np.uint16); w = _c(w, np.float32)
+    B, H, d = q.shape
+    q8 = np.empty((B, H, d), np.int8)
+    W = np.empty((B, H), np.float64)
+    lib().orc_pq_query(_p(q), _p(w), float(sigma), B, H, d, _p(q8), _p(W))
+    return q8, W
+
+
+def pq_search(q, w, cb, sigma, codes, k_full, m, k, nv=None, want_s1=False):
+    """Two-stage search over product-quantised keys -> dict(shortlist [B, m],
+    idx [B, k], val [B, k], s1 [B, S] or None).  cb [d/4, 256, 4] int8 codebook,
+    sigma its scale, codes [B, S, d/4] uint8, k_full [B, S, d] bf16."""
+    q = _c(q, np.uint16); w = _c(w, np.float32); cb = _c(cb, np.int8); codes = _c(codes, np.uint8)
+    k_full = _c(k_full, np.uint16); nv = _c(nv, np.int32)
+    B, H, d = q.shape
+    S = codes.shape[1]
+    assert cb.shape == (d // 4, 256, 4) and codes.shape == (B, S, d // 4) and k_full.shape == (B, S, d)
+    sl = np.empty((B, m), np.int32)
+    idx = np.empty((B, k), np.int32)
+    val = np.empty((B, k), np.float64)
+    s1 = np.empty((B, S), np.float64) if want_s1 else None
+    lib().orc_pq_search(_p(q), _p(w), _p(cb), float(sigma), _p(codes), _p(k_full), _p(nv), B, S, H, d, m, k,
+                        _p(sl), _p(idx), _p(val), _p(s1))
+    return {"shortlist": sl, "idx": idx, "val": val, "s1": s1}
 

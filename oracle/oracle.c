@@ -475,3 +475,107 @@ void orc_pooled_select(const void *q, int q_type, const float *w, const uint8_t 
   free(nvb); free(sc); free(blk);
 }
 
+/* ---- O7: product-quantised compact keys [LS 07:12-08:00: each 128-d key split
+ * into 32 four-dimension pieces, each piece a one-byte index into a 256-entry
+ * codebook trained offline; a coarse pass over the codes keeps 2,048 candidates,
+ * their original keys are reranked exactly to 512] ----------------------------- */
+
+/* Query side for one (b, h): q8 = rint(q / qs) clamped to [-127, 127] with
+ * qs = max|q| / 127 (1 if zero), W = (w * qs) * sigma, all in fp64. */
+static void pq_query_one(const uint16_t *q, float w, double sigma, int64_t d, int8_t *q8, double *W) {
+  double amax = 0.0;
+  for (int64_t i = 0; i < d; ++i) {
+    double v = fabs(orc_dec_bf16(q[i]));
+    if (v > amax) amax = v;
+  }
+  double qs = amax > 0.0 ? amax / 127.0 : 1.0;
+  for (int64_t i = 0; i < d; ++i) {
+    double t = rint(orc_dec_bf16(q[i]) / qs);
+    if (t > 127.0) t = 127.0;
+    if (t < -127.0) t = -127.0;
+    q8[i] = (int8_t)t;
+  }
+  *W = ((double)w * qs) * sigma;
+}
+
+/* q: [B, H, d] bf16 -> q8 [B, H, d] int8, W [B, H] fp64. */
+void orc_pq_query(const uint16_t *q, const float *w, double sigma, int64_t B, int64_t H, int64_t d, int8_t *q8,
+                  double *W) {
+  for (int64_t r = 0; r < B * H; ++r) pq_query_one(q + r * d, w[r], sigma, d, q8 + r * d, W + r);
+}
+
+/* Stage-1 score of one key from its codes: the key is decoded piece by piece from
+ * the codebook, D_h = q8_h . decoded key (exact integers), and
+ * s1 = chain_h(W_h, max(D_h, 0)) (fp64 fma chain, h ascending). */
+static double pq_stage1_one(const int8_t *q8, const double *W, const uint8_t *code, const int8_t *cb, int64_t H,
+                            int64_t d) {
+  int64_t np = d / 4;
+  double acc = 0.0;
+  for (int64_t h = 0; h < H; ++h) {
+    int64_t D = 0;
+    for (int64_t j = 0; j < np; ++j) {
+      const int8_t *c = cb + (j * 256 + code[j]) * 4;
+      for (int64_t i = 0; i < 4; ++i) D += (int64_t)q8[h * d + 4 * j + i] * (int64_t)c[i];
+    }
+    acc = fma(W[h], (double)(D > 0 ? D : 0), acc);
+  }
+  return acc;
+}
+
+typedef struct {
+  const uint16_t *q; const float *w; const int8_t *cb; double sigma; const uint8_t *codes;
+  const uint16_t *kf; const int32_t *nv; int64_t S, H, d, m, k;
+  int32_t *shortlist; int32_t *idx; double *val; double *s1_out;
+} pq_ctx;
+
+static void pq_row(void *p, int64_t b) {
+  pq_ctx *c = (pq_ctx *)p;
+  int64_t S = c->S, H = c->H, d = c->d, m = c->m, k = c->k, np = d / 4;
+  int8_t *q8 = (int8_t *)malloc((size_t)(H * d));
+  double *W = (double *)malloc(sizeof(double) * H);
+  for (int64_t h = 0; h < H; ++h)
+    pq_query_one(c->q + (b * H + h) * d, c->w[b * H + h], c->sigma, d, q8 + h * d, W + h);
+  int64_t nv = c->nv ? c->nv[b] : S;
+  if (nv > S) nv = S;
+  if (nv < 0) nv = 0;
+  double *s1 = (double *)malloc(sizeof(double) * (nv > 0 ? nv : 1));
+  for (int64_t s = 0; s < nv; ++s) s1[s] = pq_stage1_one(q8, W, c->codes + (b * S + s) * np, c->cb, H, d);
+  if (c->s1_out)
+    for (int64_t s = 0; s < S; ++s) c->s1_out[b * S + s] = s < nv ? s1[s] : -INFINITY;
+  int32_t *sl = c->shortlist + b * m;
+  topk_one(s1, nv, m, sl, NULL);
+  /* stage 2: the exact score of the shortlisted original keys, keep the top k */
+  double *qd = (double *)malloc(sizeof(double) * H * d);
+  double *wd = (double *)malloc(sizeof(double) * H);
+  double *key = (double *)malloc(sizeof(double) * d);
+  for (int64_t i = 0; i < H * d; ++i) qd[i] = orc_dec_bf16(c->q[b * H * d + i]);
+  for (int64_t h = 0; h < H; ++h) wd[h] = (double)c->w[b * H + h];
+  int64_t nm = nv < m ? nv : m;
+  pair_t *pr = (pair_t *)malloc(sizeof(pair_t) * (nm > 0 ? nm : 1));
+  for (int64_t i = 0; i < nm; ++i) {
+    int64_t s = sl[i];
+    for (int64_t j = 0; j < d; ++j) key[j] = orc_dec_bf16(c->kf[(b * S + s) * d + j]);
+    pr[i].v = score_one(qd, wd, key, H, d);
+    pr[i].i = (int32_t)s;
+  }
+  qsort(pr, (size_t)nm, sizeof(pair_t), cmp_desc);
+  qsort(pr, (size_t)(nm < k ? nm : k), sizeof(pair_t), cmp_index);
+  for (int64_t j = 0; j < k; ++j) {
+    if (j < nm) { c->idx[b * k + j] = pr[j].i; if (c->val) c->val[b * k + j] = pr[j].v; }
+    else { c->idx[b * k + j] = -1; if (c->val) c->val[b * k + j] = -INFINITY; }
+  }
+  free(q8); free(W); free(s1); free(qd); free(wd); free(key); free(pr);
+}
+
+/* Two-stage search over product-quantised keys.  q: [B, H, d] bf16; w: [B, H];
+ * cb: [d / 4, 256, 4] int8 codebook entries (piece j of code c is
+ * sigma * cb[j, c, :]); codes: [B, S, d / 4] uint8; k_full: [B, S, d] bf16;
+ * nv: [B] or NULL.  Outputs shortlist [B, m], idx [B, k], val [B, k] (ascending
+ * index order), s1 [B, S] or NULL. */
+void orc_pq_search(const uint16_t *q, const float *w, const int8_t *cb, double sigma, const uint8_t *codes,
+                   const uint16_t *k_full, const int32_t *nv, int64_t B, int64_t S, int64_t H, int64_t d, int64_t m,
+                   int64_t k, int32_t *shortlist, int32_t *idx, double *val, double *s1) {
+  pq_ctx ctx = {q, w, cb, sigma, codes, k_full, nv, S, H, d, m, k, shortlist, idx, val, s1};
+  for_rows(B, pq_row, &ctx);
+}
+

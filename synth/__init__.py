@@ -36,6 +36,10 @@ def lib():
         L.synth_fp8_rows.restype = None
         L.synth_compact_keys.argtypes = [_ptr, _u64, _u64, _ptr, _u64, _ptr, _ptr]
         L.synth_compact_keys.restype = None
+        L.synth_pq_codebook.argtypes = [_ptr, _u64, _u64, _u64, ctypes.c_int, _ptr, _ptr]
+        L.synth_pq_codebook.restype = None
+        L.synth_pq_encode.argtypes = [_ptr, _u64, _u64, _ptr, ctypes.c_float, _ptr]
+        L.synth_pq_encode.restype = None
         L.synth_bf16_rne.argtypes = [_dbl]
         L.synth_bf16_rne.restype = ctypes.c_uint16
         L.synth_e4m3_rne.argtypes = [_dbl]
@@ -120,6 +124,31 @@ def compact_keys(k_bf16, P):
     cs = np.empty(k_bf16.shape[:-1], np.float32)
     lib().synth_compact_keys(_p(k_bf16), rows, d, _p(P), dc, _p(c), _p(cs))
     return c, cs
+
+
+def pq_codebook(k_bf16, seed, iters=8):
+    """(cb int8 [d/4, 256, 4], sigma float): k-means codebooks of the 4-dim pieces of
+    bf16 keys [n, d] (Lloyd iterations from seeded sample points), stored as int8
+    entries with one scale."""
+    k_bf16 = np.ascontiguousarray(k_bf16, dtype=np.uint16)
+    d = k_bf16.shape[-1]
+    n = k_bf16.size // d
+    cb = np.empty((d // 4, 256, 4), np.int8)
+    sg = ctypes.c_float(0.0)
+    lib().synth_pq_codebook(_p(k_bf16), n, d, seed, iters, _p(cb), ctypes.byref(sg))
+    return cb, float(sg.value)
+
+
+def pq_encode(k_bf16, cb, sigma):
+    """Codes uint8 [..., d/4] of bf16 keys [..., d]: the nearest entry of each
+    piece's codebook."""
+    k_bf16 = np.ascontiguousarray(k_bf16, dtype=np.uint16)
+    cb = np.ascontiguousarray(cb, dtype=np.int8)
+    d = k_bf16.shape[-1]
+    rows = k_bf16.size // d
+    codes = np.empty(k_bf16.shape[:-1] + (d // 4,), np.uint8)
+    lib().synth_pq_encode(_p(k_bf16), rows, d, _p(cb), sigma, _p(codes))
+    return codes
 
 
 def bf16_rne(x: float) -> int:

@@ -328,4 +328,112 @@ void synth_compact_keys(const uint16_t *k_bf16, uint64_t rows, uint64_t d, const
   parallel_for(rows, 256, compact_range, &ctx);
 }
 
+/* ---- product-quantisation codebooks and codes ------------------------------
+ * The storage format of product-quantised indexer keys: each key's d dims split
+ * into d / 4 pieces of 4, each piece stored as the one-byte index of an entry of
+ * its piece's 256-entry codebook, the codebooks trained offline (k-means) and kept
+ * as int8 entries with one fp32 scale for all of them.  Like the fp8 and int8
+ * encoders above this only prepares input bytes: nothing here scores or selects. */
+
+typedef struct { const uint16_t *k; uint64_t n, d, seed; int iters; double *cent; } pqtrain_ctx;
+
+static void pqtrain_range(void *p, uint64_t lo, uint64_t hi) {
+  pqtrain_ctx *c = (pqtrain_ctx *)p;
+  uint64_t n = c->n, d = c->d;
+  uint32_t *asg = (uint32_t *)malloc(sizeof(uint32_t) * (n ? n : 1));
+  double *sum = (double *)malloc(sizeof(double) * 256 * 4);
+  uint64_t *cnt = (uint64_t *)malloc(sizeof(uint64_t) * 256);
+  for (uint64_t j = lo; j < hi; ++j) {
+    double *cent = c->cent + j * 256 * 4;
+    /* initial centroids: 256 sample points chosen by the seeded stream */
+    uint64_t base = synth_stream_base(c->seed, 100 + j);
+    for (int e = 0; e < 256; ++e) {
+      uint64_t r = draw(base, (uint64_t)e) % n;
+      for (int i = 0; i < 4; ++i) cent[e * 4 + i] = bf16_value(c->k[r * d + 4 * j + i]);
+    }
+    for (int it = 0; it < c->iters; ++it) {
+      for (uint64_t x = 0; x < n; ++x) {
+        double v[4];
+        for (int i = 0; i < 4; ++i) v[i] = bf16_value(c->k[x * d + 4 * j + i]);
+        double best = INFINITY;
+        uint32_t bi = 0;
+        for (uint32_t e = 0; e < 256; ++e) {
+          double dd = 0.0;
+          for (int i = 0; i < 4; ++i) {
+            double t = v[i] - cent[e * 4 + i];
+            dd += t * t;
+          }
+          if (dd < best) { best = dd; bi = e; }
+        }
+        asg[x] = bi;
+      }
+      memset(sum, 0, sizeof(double) * 256 * 4);
+      memset(cnt, 0, sizeof(uint64_t) * 256);
+      for (uint64_t x = 0; x < n; ++x) {
+        cnt[asg[x]] += 1;
+        for (int i = 0; i < 4; ++i) sum[asg[x] * 4 + i] += bf16_value(c->k[x * d + 4 * j + i]);
+      }
+      for (int e = 0; e < 256; ++e)
+        if (cnt[e])
+          for (int i = 0; i < 4; ++i) cent[e * 4 + i] = sum[e * 4 + i] / (double)cnt[e];
+    }
+  }
+  free(asg); free(sum); free(cnt);
+}
+
+/* Codebooks from n bf16 keys [n, d]: `iters` Lloyd iterations per piece from 256
+ * seeded sample points (an entry left empty keeps its place), then one scale
+ * sigma = max |entry| / 127 and int8 entries rint(entry / sigma).
+ * cb: [d / 4, 256, 4] int8. */
+void synth_pq_codebook(const uint16_t *k, uint64_t n, uint64_t d, uint64_t seed, int iters, int8_t *cb,
+                       float *sigma) {
+  uint64_t np = d / 4;
+  double *cent = (double *)malloc(sizeof(double) * np * 256 * 4);
+  pqtrain_ctx c = {k, n, d, seed, iters, cent};
+  parallel_for(np, 1, pqtrain_range, &c);
+  double amax = 0.0;
+  for (uint64_t i = 0; i < np * 256 * 4; ++i)
+    if (fabs(cent[i]) > amax) amax = fabs(cent[i]);
+  float sg = amax > 0.0 ? (float)(amax / 127.0) : 1.0f;
+  for (uint64_t i = 0; i < np * 256 * 4; ++i) {
+    double t = rint(cent[i] / (double)sg);
+    if (t > 127.0) t = 127.0;
+    if (t < -127.0) t = -127.0;
+    cb[i] = (int8_t)t;
+  }
+  *sigma = sg;
+  free(cent);
+}
+
+typedef struct { const uint16_t *k; uint64_t d; const int8_t *cb; double sigma; uint8_t *codes; } pqenc_ctx;
+
+static void pqenc_range(void *p, uint64_t lo, uint64_t hi) {
+  pqenc_ctx *c = (pqenc_ctx *)p;
+  uint64_t d = c->d, np = d / 4;
+  for (uint64_t r = lo; r < hi; ++r)
+    for (uint64_t j = 0; j < np; ++j) {
+      double v[4];
+      for (int i = 0; i < 4; ++i) v[i] = bf16_value(c->k[r * d + 4 * j + i]);
+      const int8_t *e0 = c->cb + j * 256 * 4;
+      double best = INFINITY;
+      int bi = 0;
+      for (int e = 0; e < 256; ++e) {
+        double dd = 0.0;
+        for (int i = 0; i < 4; ++i) {
+          double t = v[i] - c->sigma * (double)e0[e * 4 + i];
+          dd += t * t;
+        }
+        if (dd < best) { best = dd; bi = e; }
+      }
+      c->codes[r * np + j] = (uint8_t)bi;
+    }
+}
+
+/* Codes of bf16 keys [rows, d]: per piece the entry nearest (squared distance in
+ * fp64, ties to the smaller index) among sigma * cb. codes: [rows, d / 4]. */
+void synth_pq_encode(const uint16_t *k, uint64_t rows, uint64_t d, const int8_t *cb, float sigma, uint8_t *codes) {
+  pqenc_ctx c = {k, d, cb, (double)sigma, codes};
+  parallel_for(rows, 256, pqenc_range, &c);
+}
+
 int synth_threads(void) { return n_threads(); }

@@ -10,7 +10,7 @@ import math
 
 import numpy as np
 
-from . import compact_keys, fp8_rows, normal_bf16, normal_bf16_rows, normal_f32, uniform_f32
+from . import compact_keys, fp8_rows, normal_bf16, normal_bf16_rows, normal_f32, pq_codebook, pq_encode, uniform_f32
 
 SEED_BASE = 0x5EED0000
 
@@ -35,6 +35,12 @@ WORKLOADS = {
     "select_attend": dict(B=64, T=1, S=262144, H=64, d=128, topk=512, key="fp8", q="bf16", q_scale=1.0,
                           w="normal", causal=False, Hq=128, dqk=576, dv=512, tau=1 / math.sqrt(192),
                           seed=SEED_BASE + 5),
+    # 32 sequences x 131072 keys: product-quantised codes (32 pieces of 4 dims, one
+    # byte each into a 256-entry k-means codebook per piece) -> 2048 shortlist ->
+    # exact top-512 over the bf16 keys
+    "pq_search": dict(B=32, T=1, S=131072, H=64, d=128, m=2048, topk=512, key="bf16", q="bf16",
+                      q_scale=1 / math.sqrt(128), w="uniform", causal=False, pq_train_stride=64, pq_iters=8,
+                      seed=SEED_BASE + 7),
     # 16 sequences x 524288 bf16 token keys pooled four at a time on write (131072
     # fp8 pooled keys each), a 32-head indexer over the pooled keys, top-512 blocks
     # expanded to 2048 tokens
@@ -132,4 +138,18 @@ def pooled_inputs(sp):
     w = uniform_f32(seed, TID_W, (B, T, H), 0.0, 1.0)
     k = normal_bf16(seed, TID_K, (B, L, d), 1.0)
     return {"q": q, "w": w, "k_tokens": k}
+
+
+def pq_inputs(sp):
+    """q [B, H, d] bf16, w [B, H], full keys [B, S, d] bf16 N(0, 1), the codebook cb
+    [d/4, 256, 4] int8 + sigma trained on every pq_train_stride-th key of the
+    workload, and the keys' codes [B, S, d/4]."""
+    B, S, H, d, seed = sp["B"], sp["S"], sp["H"], sp["d"], sp["seed"]
+    q = normal_bf16(seed, TID_Q, (B, H, d), sp["q_scale"])
+    w = uniform_f32(seed, TID_W, (B, H), 0.0, 1.0)
+    k_full = normal_bf16(seed, TID_K, (B, S, d), 1.0)
+    sample = np.ascontiguousarray(k_full.reshape(-1, d)[::sp.get("pq_train_stride", 64)])
+    cb, sigma = pq_codebook(sample, seed, sp.get("pq_iters", 8))
+    codes = pq_encode(k_full, cb, sigma)
+    return {"q": q, "w": w, "k_full": k_full, "cb": cb, "sigma": sigma, "codes": codes}
 

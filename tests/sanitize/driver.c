@@ -36,6 +36,12 @@ void orc_pooled_select(const void *q, int q_type, const float *w, const uint8_t 
                        const int32_t *nv_tokens, int64_t B, int64_t T, int64_t Sp, int64_t H, int64_t d,
                        int64_t pool, int64_t k, int32_t *idx_tokens, double *val_blocks);
 
+void orc_pq_query(const uint16_t *q, const float *w, double sigma, int64_t B, int64_t H, int64_t d, int8_t *q8,
+                  double *W);
+void orc_pq_search(const uint16_t *q, const float *w, const int8_t *cb, double sigma, const uint8_t *codes,
+                   const uint16_t *k_full, const int32_t *nv, int64_t B, int64_t S, int64_t H, int64_t d, int64_t m,
+                   int64_t k, int32_t *shortlist, int32_t *idx, double *val, double *s1);
+
 /* synth/gen.c */
 uint64_t synth_stream_base(uint64_t seed, uint64_t tid);
 uint16_t synth_bf16_rne(double v);
@@ -52,6 +58,9 @@ void synth_fp8_rows(uint64_t seed, uint64_t tid, uint64_t row_off, uint64_t rows
 void synth_compact_keys(const uint16_t *k_bf16, uint64_t rows, uint64_t d, const float *P, uint64_t dc, int8_t *c,
                         float *cs);
 int synth_threads(void);
+void synth_pq_codebook(const uint16_t *k, uint64_t n, uint64_t d, uint64_t seed, int iters, int8_t *cb,
+                       float *sigma);
+void synth_pq_encode(const uint16_t *k, uint64_t rows, uint64_t d, const int8_t *cb, float sigma, uint8_t *codes);
 
 enum { F32 = 0, BF16 = 1, FP8 = 2 };
 
@@ -166,6 +175,25 @@ int main(void) {
   int32_t *pidx2 = xmalloc(sizeof(int32_t) * B * T * 40 * pool); /* k above the block count */
   orc_pooled_select(qb, BF16, w, pc, ps, NULL, B, T, Sp, H, d, pool, 40, pidx2, NULL);
   free(pc); free(ps); free(pidx); free(pval); free(pidx2);
+
+  /* product-quantised keys: codebooks from fewer keys than entries, codes, search */
+  int8_t *cb = xmalloc(32 * 256 * 4);
+  float sigma = 0.0f;
+  synth_pq_codebook(kb, (uint64_t)(B * S), (uint64_t)d, 7, 3, cb, &sigma);
+  uint8_t *pqc = xmalloc((size_t)(B * S * 32));
+  synth_pq_encode(kb, (uint64_t)(B * S), (uint64_t)d, cb, sigma, pqc);
+  int8_t *pq8 = xmalloc((size_t)(B * H * d));
+  double *pW = xmalloc(sizeof(double) * B * H);
+  orc_pq_query(qc, wc, sigma, B, H, d, pq8, pW);
+  for (size_t i = 0; i < 3; ++i) {
+    int64_t m = mk[i][0], kk = mk[i][1];
+    int32_t *sl = xmalloc(sizeof(int32_t) * B * m), *fi = xmalloc(sizeof(int32_t) * B * kk);
+    double *fv = xmalloc(sizeof(double) * B * kk), *s1 = xmalloc(sizeof(double) * B * S);
+    orc_pq_search(qc, wc, cb, sigma, pqc, kb, cnv, B, S, H, d, m, kk, sl, fi, fv, s1);
+    orc_pq_search(qc, wc, cb, sigma, pqc, kb, NULL, B, S, H, d, m, kk, sl, fi, NULL, NULL);
+    free(sl); free(fi); free(fv); free(s1);
+  }
+  free(cb); free(pqc); free(pq8); free(pW);
 
   free(f64); free(f32); free(qb); free(w); free(k8); free(ks); free(kb); free(rb); free(P); free(ck); free(cks);
   free(sc); free(qc); free(wc); free(q8); free(qs); free(W); free(qa); free(kv); free(out); free(lse);

@@ -17,7 +17,7 @@ WRAPPER = {
     "orc_indexer_score": "indexer_score", "orc_topk": "topk", "orc_compact_query": "compact_query",
     "orc_compact_search": "compact_search", "orc_sparse_attn_rows": "sparse_attn_rows",
     "orc_sparse_attn": "sparse_attn", "orc_e4m3_rne": "e4m3_rne", "orc_pool_keys": "pool_keys",
-    "orc_pooled_select": "pooled_select",
+    "orc_pooled_select": "pooled_select", "orc_pq_query": "pq_query", "orc_pq_search": "pq_search",
 }
 
 
