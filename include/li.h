@@ -260,6 +260,35 @@ li_status li_compact_search_rerank(const void *q, const float *w, const float *P
                                    double *val, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * li_pq_search_rerank -- two-stage decode search over product-quantised keys
+ * (LeanSparse podcast transcript, cues 07:12-08:00: each 128-d key split into 32
+ * four-dimension pieces, each a one-byte index into a 256-entry codebook trained
+ * offline; a coarse pass over the codes keeps the shortlist, whose original keys
+ * are reranked exactly).
+ *
+ *   q         [B, H, d]       bf16 query heads (one decode row per sequence)
+ *   w         [B, H]          fp32 head weights
+ *   codebook  [d/4, 256, 4]   int8: piece j of code c decodes to sigma * codebook[j][c]
+ *   sigma     fp32 > 0        the codebook scale (host value)
+ *   codes     [B, S, d/4]     uint8 codes of every key
+ *   k_full    [B, S, d]       bf16 original keys
+ *   nv, shortlist, idx, val   as li_compact_search_rerank
+ *
+ * Stage 1 quantises each query head to int8 (qs = max|q| / 127, q8 = rint(q / qs)
+ * clamped to [-127, 127]), sets W = (w * qs) * sigma (fp64), takes exact int32 dots
+ * D of q8 with every key decoded from its codes (the sums a per-piece lookup table
+ * gives) and scores s1 = sum_h W[h] max(D[h], 0) (fp64 fma chain over h
+ * ascending); the m best s1 form the shortlist.  Stage 2 is that of
+ * li_compact_search_rerank.  Results are bit-identical to a CPU evaluation of the
+ * same steps.  Shapes: d == 128, 1 <= H <= 128, 1 <= k <= m <= LI_TOPK_MAX.
+ */
+size_t li_pq_workspace_bytes(int B, int S, int H, int m, int k);
+li_status li_pq_search_rerank(const void *q, const float *w, const int8_t *codebook, float sigma,
+                              const uint8_t *codes, const void *k_full, const int32_t *nv, int B, int S, int H, int d,
+                              int m, int k, int32_t *shortlist, int32_t *idx, double *val, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/*
  * li_sparse_attn_gather -- attention of every query head over only the selected
  * latent rows (MQA: one row serves all heads).
  *

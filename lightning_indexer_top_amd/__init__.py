@@ -68,6 +68,9 @@ def lib():
         L.li_pooled_indexer_topk_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.li_pooled_indexer_topk_workspace_bytes.restype = _Z
         L.li_pooled_indexer_topk.argtypes = [_P, _I, _P, _P, _P, _P] + [_I] * 7 + [_P, _P, _P, _Z, _P]
+        L.li_pq_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+        L.li_pq_workspace_bytes.restype = _Z
+        L.li_pq_search_rerank.argtypes = [_P, _P, _P, ctypes.c_float, _P, _P, _P] + [_I] * 6 + [_P] * 4 + [_Z, _P]
         L.li_indexer_score_paged.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P] + [_I] * 5 + [_P, _P]
         L.li_indexer_topk_paged_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.li_indexer_topk_paged_workspace_bytes.restype = _Z
@@ -76,7 +79,7 @@ def lib():
                                                   _P, _P]
         for name in ("li_indexer_score", "li_topk_select", "li_topk_select_noalloc", "li_indexer_topk",
                      "li_pool_keys", "li_pooled_indexer_topk", "li_indexer_score_paged", "li_indexer_topk_paged",
-                     "li_sparse_attn_gather_paged", "li_compact_search_rerank",
+                     "li_sparse_attn_gather_paged", "li_pq_search_rerank", "li_compact_search_rerank",
                      "li_sparse_attn_gather"):
             getattr(L, name).restype = _I
         _LIB = L
@@ -277,6 +280,33 @@ def compact_search_rerank(q, w, P, ck, ck_scale, k_full, m, k, nv=None, want_sho
                                         B, S, H, d, dc, m, k, _ptr(sl), _ptr(idx), _ptr(val), _ptr(ws), nb,
                                         _stream(q.device))
     _check(st, "li_compact_search_rerank")
+    return sl, idx, val
+
+
+def pq_workspace_bytes(B, S, H, m, k):
+    return int(lib().li_pq_workspace_bytes(B, S, H, m, k))
+
+
+def pq_search_rerank(q, w, codebook, sigma, codes, k_full, m, k, nv=None, want_shortlist=True, workspace=None,
+                     out=None):
+    """Two-stage search over product-quantised keys.  q [B, H, 128] bf16, w [B, H],
+    codebook [32, 256, 4] int8 (scale sigma), codes [B, S, 32] uint8, k_full
+    [B, S, 128] bf16 -> (shortlist [B, m] or None, idx [B, k], val [B, k] fp64)."""
+    for t, n in ((q, "q"), (w, "w"), (codebook, "codebook"), (codes, "codes"), (k_full, "k_full")):
+        _dev(t, n)
+    B, H, d = q.shape
+    S = codes.shape[1]
+    if out is None:
+        sl = torch.empty((B, m), dtype=torch.int32, device=q.device) if want_shortlist else None
+        idx = torch.empty((B, k), dtype=torch.int32, device=q.device)
+        val = torch.empty((B, k), dtype=torch.float64, device=q.device)
+    else:
+        sl, idx, val = out
+    ws, nb = _workspace(pq_workspace_bytes(B, S, H, m, k), q.device, workspace)
+    st = lib().li_pq_search_rerank(_ptr(q), _ptr(w), _ptr(codebook), float(sigma), _ptr(codes), _ptr(k_full),
+                                   _ptr(nv), B, S, H, d, m, k, _ptr(sl), _ptr(idx), _ptr(val), _ptr(ws), nb,
+                                   _stream(q.device))
+    _check(st, "li_pq_search_rerank")
     return sl, idx, val
 
 

@@ -287,6 +287,33 @@ li_status li_compact_search_rerank(const void* q, const float* w, const float* P
                   "li_compact_search_rerank");
 }
 
+size_t li_pq_workspace_bytes(int B, int S, int H, int m, int k) {
+  if (B < 1 || S < 1 || H < 1 || m < 1) return 0;
+  return li::pq_ws_bytes(B, S, H, m, k);
+}
+
+li_status li_pq_search_rerank(const void* q, const float* w, const int8_t* codebook, float sigma,
+                              const uint8_t* codes, const void* k_full, const int32_t* nv, int B, int S, int H, int d,
+                              int m, int k, int32_t* shortlist, int32_t* idx, double* val, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (!q || !w || !codebook || !codes || !k_full || !idx)
+    return fail(LI_ERR_NULL, "q, w, codebook, codes, k_full and idx must be non-NULL");
+  if (d != LI_INDEX_DIM) return fail(LI_ERR_SHAPE, "d must be %d", LI_INDEX_DIM);
+  if (H < 1 || H > 128) return fail(LI_ERR_SHAPE, "H must be in [1, 128]");
+  if (B < 1 || S < 1) return fail(LI_ERR_SHAPE, "B and S must be >= 1");
+  if (k < 1 || m < k || m > LI_TOPK_MAX) return fail(LI_ERR_SHAPE, "need 1 <= k <= m <= %d", LI_TOPK_MAX);
+  if ((int64_t)B * S >= (1ll << 40)) return fail(LI_ERR_SHAPE, "B*S too large");
+  if (!(sigma > 0.0f) || !(sigma < 3.0e38f)) return fail(LI_ERR_SHAPE, "sigma must be positive and finite");
+  if (misaligned(q) || misaligned(w) || misaligned(codebook) || misaligned(codes) || misaligned(k_full) ||
+      misaligned(nv) || misaligned(shortlist) || misaligned(idx) || misaligned(val) || misaligned(ws))
+    return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = li::pq_ws_bytes(B, S, H, m, k);
+  if (!ws || ws_bytes < need) return fail(LI_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  return launched(li::launch_pq((const uint16_t*)q, w, codebook, sigma, codes, (const uint16_t*)k_full, nv, B, S, H,
+                                m, k, shortlist, idx, val, ws, stream),
+                  "li_pq_search_rerank");
+}
+
 size_t li_sparse_attn_workspace_bytes(int B, int Hq, int k, int dv) { return li::attn_ws_bytes(B, Hq, k, dv); }
 
 li_status li_sparse_attn_gather(const void* q, const void* kv, const int32_t* idx, int B, int Hq, int S, int k,

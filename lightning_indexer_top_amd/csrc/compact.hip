@@ -266,6 +266,20 @@ __global__ __launch_bounds__(S2_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 }
 #undef LI_TOUCH4
 
+// 128 heads need 130 KB of dynamic LDS in stage 2 (the query block in fp64)
+static void stage2_attrs() {
+  static const bool set = [] {
+    (void)hipFuncSetAttribute((const void*)compact_stage2_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    (void)hipFuncSetAttribute((const void*)compact_stage2_kernel<16>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    (void)hipFuncSetAttribute((const void*)compact_stage2_kernel<32>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    return true;
+  }();
+  (void)set;
+}
+
 size_t compact_ws_bytes(int B, int S, int H, int m, int k) {
   (void)k;
   size_t n = 0;
@@ -317,17 +331,199 @@ hipError_t launch_compact(const uint16_t* q, const float* w, const float* P, con
     compact_stage1_kernel<4><<<g1, 256, 0, st>>>(q8, W, ck, cks, S, H, kpb, s1);
   hipError_t e = launch_topk_f64_rows(s1, nv, B, S, m, sl, nullptr, tk_ws, st);
   if (e != hipSuccess) return e;
-  static const bool attr_set = [] {
-    // 128 heads need 130 KB of dynamic LDS (the query block in fp64)
-    (void)hipFuncSetAttribute((const void*)compact_stage2_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
-    (void)hipFuncSetAttribute((const void*)compact_stage2_kernel<16>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
-    (void)hipFuncSetAttribute((const void*)compact_stage2_kernel<32>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
-    return true;
-  }();
-  (void)attr_set;
+  stage2_attrs();
+  const dim3 g2((m + S2_CPB - 1) / S2_CPB, B);
+#define LI_STAGE2(U_)                                                                                    \
+  compact_stage2_kernel<U_><<<g2, S2_THREADS, sizeof(double) * (size_t)(4 * U_) * (S2_QROW + 1), st>>>( \
+      q, w, kf, sl, nv, S, H, m, s2, cnt)
+  if (H <= 32)
+    LI_STAGE2(8);
+  else if (H <= 64)
+    LI_STAGE2(16);
+  else
+    LI_STAGE2(32);
+#undef LI_STAGE2
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topk_f64(s2, m, cnt, sl, B, m, k, idx, val, st);
+}
+
+// ---- product-quantised compact keys ----------------------------------------
+// LeanSparse podcast transcript, cues 07:12-07:34: each 128-d key is split into 32
+// four-dimension pieces, each stored as a one-byte index into that piece's
+// 256-entry codebook.  The coarse score is the asymmetric distance (the query is
+// not quantised by the codebook): per head the dot of the query with the decoded
+// key, computed exactly from int8 parts:
+//   query   qs_h = max|q_h| / 127 (1 if zero), q8_h = rint(q_h / qs_h) clamped to
+//           [-127, 127], W_h = (w_h * qs_h) * sigma (fp64);
+//   stage 1 D_h = sum over pieces j of q8_h[4j..4j+3] . cb[j][code_j] (exact
+//           int32), s1 = chain_h(W_h, max(D_h, 0)) (fp64 fma chain, h ascending);
+// then the same shortlist, exact rerank and final selection as above.
+//
+// The per-head lookup tables of a classic scan would hold 64 x 32 x 256 sums per
+// query (1 MiB at 64 heads), far past LDS; the codebook itself is 32 KiB (one
+// 32-bit word per entry), so the stage-1 kernel keeps the codebook in LDS, decodes
+// each key's 32 codes into its 128 int8 values with 32 LDS reads, and lets the int8
+// matrix core form every head's dot (the same sums the tables would give).
+constexpr int PQ_PIECES = 32;
+
+// One wave per (b, h); lane l owns dimensions 2 l and 2 l + 1.
+__global__ __launch_bounds__(64) void pq_query_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                                                      double sigma, int8_t* __restrict__ q8,
+                                                      double* __restrict__ W) {
+  const int bh = blockIdx.x, l = threadIdx.x;
+  const uint32_t two = ((const uint32_t*)(q + (int64_t)bh * 128))[l];
+  const double v0 = (double)__uint_as_float(two << 16), v1 = (double)__uint_as_float(two & 0xFFFF0000u);
+  const double amax = wave_max_d(fmax(fabs(v0), fabs(v1)));
+  const double qs = amax > 0.0 ? amax / 127.0 : 1.0;
+  const double t0 = fmin(fmax(rint(v0 / qs), -127.0), 127.0), t1 = fmin(fmax(rint(v1 / qs), -127.0), 127.0);
+  ((uint16_t*)(q8 + (int64_t)bh * 128))[l] = (uint16_t)(((int)t0 & 0xFF) | (((int)t1 & 0xFF) << 8));
+  if (l == 0) W[bh] = ((double)w[bh] * qs) * sigma;
+}
+
+// Stage 1.  A wave scores 64 keys per step, as compact_stage1_kernel, with K = 128:
+// in K step ks lane half hf carries dimensions 64 hf + 16 ks .. + 15 (pieces
+// 16 hf + 4 ks .. + 3) of both the query (A operand) and the key (B operand), so a
+// lane's 16 code bytes (one 16-byte load per key) give its four B operands through
+// 16 codebook reads.  Four v_mfma_i32_32x32x32_i8 per 32 heads and 32 keys.
+template <int HT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pq_stage1_kernel(
+    const int8_t* __restrict__ q8, const double* __restrict__ W, const uint32_t* __restrict__ cb,
+    const uint8_t* __restrict__ codes, int S, int H, int kpb, double* __restrict__ s1) {
+  constexpr bool WREG = HT <= 1;  // head weights in VGPRs up to 32 heads (64 would spill), else LDS broadcasts
+  __shared__ __attribute__((aligned(16))) uint32_t scb[PQ_PIECES * 256];
+  __shared__ __attribute__((aligned(16))) double sW[WREG ? 2 : 32 * HT];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hf = lane >> 5, col = lane & 31;
+  for (int i = tid; i < PQ_PIECES * 256 / 4; i += 256) ((uint4*)scb)[i] = ((const uint4*)cb)[i];
+  i32x4 a[HT][4];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int h = ht * 32 + col;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      a[ht][ks] = h < H ? *(const i32x4*)(q8 + ((int64_t)b * H + h) * 128 + 64 * hf + 16 * ks) : i32x4{0, 0, 0, 0};
+  }
+  double wr[WREG ? 32 * HT : 1];
+  if constexpr (WREG) {
+    const int z = __builtin_amdgcn_mbcnt_lo(0u, 0u);
+#pragma unroll
+    for (int h = 0; h < 32 * HT; ++h) wr[h] = h < H ? W[(int64_t)b * H + h + z] : 0.0;
+  } else {
+    for (int h = tid; h < 32 * HT; h += 256) sW[h] = h < H ? W[(int64_t)b * H + h] : 0.0;
+  }
+  __syncthreads();
+  const int key0 = blockIdx.x * kpb, kend = min(key0 + kpb, S);
+  const uint8_t* cbase = codes + (int64_t)b * S * PQ_PIECES;
+  const uint32_t cbl = lds_addr(scb) + (uint32_t)(16 * hf * 256 * 4);  // this lane half's first piece
+  // B operands of K step ks from the 16 code bytes X (pieces 16 hf + 4 ks + e)
+  auto decode = [&](const i32x4 X, i32x4 (&bo)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t code = ((uint32_t)X[ks] >> (8 * e)) & 0xFFu;
+        const uint32_t addr = cbl + (uint32_t)(((4 * ks + e) * 256) * 4) + 4u * code;
+        bo[ks][e] = *(const __attribute__((address_space(3))) int*)(uintptr_t)addr;
+      }
+  };
+#define LI_PQ_LOAD(X, kb)                                                                           \
+  do {                                                                                              \
+    X##0 = *(const i32x4*)(cbase + (int64_t)min((kb) + col, S - 1) * PQ_PIECES + 16 * hf);         \
+    X##1 = *(const i32x4*)(cbase + (int64_t)min((kb) + 32 + col, S - 1) * PQ_PIECES + 16 * hf);    \
+  } while (0)
+#define LI_PQ_TILE(X, kb)                                                                                      \
+  do {                                                                                                         \
+    i32x4 b0[4], b1[4];                                                                                        \
+    decode(X##0, b0);                                                                                          \
+    decode(X##1, b1);                                                                                          \
+    double acc = 0.0;                                                                                          \
+    _Pragma("unroll") for (int ht = 0; ht < HT; ++ht) {                                                        \
+      i32x16 d0 = {}, d1 = {};                                                                                 \
+      _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) {                                                       \
+        d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ht][ks], b0[ks], d0, 0, 0, 0);                            \
+        d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ht][ks], b1[ks], d1, 0, 0, 0);                            \
+      }                                                                                                        \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                                          \
+        const auto sw2 = __builtin_amdgcn_permlane32_swap((unsigned)d0[r], (unsigned)d1[r], false, false);    \
+        d0[r] = (int)sw2[0];                                                                                    \
+        d1[r] = (int)sw2[1];                                                                                    \
+      }                                                                                                        \
+      _Pragma("unroll") for (int g4 = 0; g4 < 4; ++g4) {                                                        \
+        asm volatile("" : "+v"(d0[4 * g4]), "+v"(d0[4 * g4 + 1]), "+v"(d0[4 * g4 + 2]), "+v"(d0[4 * g4 + 3]),   \
+                     "+v"(d1[4 * g4]), "+v"(d1[4 * g4 + 1]), "+v"(d1[4 * g4 + 2]), "+v"(d1[4 * g4 + 3])         \
+                     : "v"(acc));                                                                              \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                                         \
+          const int h = 32 * ht + 8 * g4 + e;                                                                  \
+          const int dv = e < 4 ? d0[4 * g4 + e] : d1[4 * g4 + e - 4];                                           \
+          double wh;                                                                                           \
+          if constexpr (WREG) wh = wr[h]; else wh = sW[h];                                                      \
+          acc = fma(wh, (double)(dv > 0 ? dv : 0), acc);                                                       \
+        }                                                                                                      \
+      }                                                                                                        \
+    }                                                                                                          \
+    if ((kb) + lane < kend) s1[(int64_t)b * S + (kb) + lane] = acc;                                            \
+  } while (0)
+  i32x4 A0, A1, B0, B1;
+  int kb = key0 + 64 * wave;
+  LI_PQ_LOAD(A, kb);
+  for (; kb < kend; kb += 512) {
+    LI_PQ_LOAD(B, kb + 256);
+    LI_PQ_TILE(A, kb);
+    if (kb + 256 >= kend) break;
+    LI_PQ_LOAD(A, kb + 512);
+    LI_PQ_TILE(B, kb + 256);
+  }
+#undef LI_PQ_LOAD
+#undef LI_PQ_TILE
+}
+
+size_t pq_ws_bytes(int B, int S, int H, int m, int k) {
+  (void)k;
+  size_t n = 0;
+  n += align256((size_t)B * H * 128);         // q8
+  n += align256((size_t)B * H * 8);           // W
+  n += align256((size_t)B * S * 8);           // s1
+  n += align256((size_t)B * m * 4);           // shortlist
+  n += align256((size_t)B * m * 8);           // s2
+  n += align256((size_t)B * 4);               // cnt
+  n += align256(topk_f64_rows_ws_bytes(B, S));  // shortlist selection
+  return n;
+}
+
+hipError_t launch_pq(const uint16_t* q, const float* w, const int8_t* cb, float sigma, const uint8_t* codes,
+                     const uint16_t* kf, const int32_t* nv, int B, int S, int H, int m, int k, int32_t* shortlist,
+                     int32_t* idx, double* val, void* ws, hipStream_t st) {
+  uint8_t* p = (uint8_t*)ws;
+  int8_t* q8 = (int8_t*)p;
+  p += align256((size_t)B * H * 128);
+  double* W = (double*)p;
+  p += align256((size_t)B * H * 8);
+  double* s1 = (double*)p;
+  p += align256((size_t)B * S * 8);
+  int32_t* sl_ws = (int32_t*)p;
+  p += align256((size_t)B * m * 4);
+  double* s2 = (double*)p;
+  p += align256((size_t)B * m * 8);
+  int32_t* cnt = (int32_t*)p;
+  p += align256((size_t)B * 4);
+  void* tk_ws = p;
+  int32_t* sl = shortlist ? shortlist : sl_ws;
+
+  pq_query_kernel<<<B * H, 64, 0, st>>>(q, w, (double)sigma, q8, W);
+  const int kpb = stage1_keys_per_block(B, S);
+  const dim3 g1((S + kpb - 1) / kpb, B);
+  const uint32_t* cbw = (const uint32_t*)cb;
+  if (H <= 32)
+    pq_stage1_kernel<1><<<g1, 256, 0, st>>>(q8, W, cbw, codes, S, H, kpb, s1);
+  else if (H <= 64)
+    pq_stage1_kernel<2><<<g1, 256, 0, st>>>(q8, W, cbw, codes, S, H, kpb, s1);
+  else
+    pq_stage1_kernel<4><<<g1, 256, 0, st>>>(q8, W, cbw, codes, S, H, kpb, s1);
+  hipError_t e = launch_topk_f64_rows(s1, nv, B, S, m, sl, nullptr, tk_ws, st);
+  if (e != hipSuccess) return e;
+  stage2_attrs();
   const dim3 g2((m + S2_CPB - 1) / S2_CPB, B);
 #define LI_STAGE2(U_)                                                                                    \
   compact_stage2_kernel<U_><<<g2, S2_THREADS, sizeof(double) * (size_t)(4 * U_) * (S2_QROW + 1), st>>>( \

@@ -44,6 +44,12 @@ hipError_t launch_compact(const uint16_t* q, const float* w, const float* P, con
                           const uint16_t* kf, const int32_t* nv, int B, int S, int H, int m, int k,
                           int32_t* shortlist, int32_t* idx, double* val, void* ws, hipStream_t st);
 
+// two-stage search over product-quantised keys (compact.hip)
+size_t pq_ws_bytes(int B, int S, int H, int m, int k);
+hipError_t launch_pq(const uint16_t* q, const float* w, const int8_t* cb, float sigma, const uint8_t* codes,
+                     const uint16_t* kf, const int32_t* nv, int B, int S, int H, int m, int k, int32_t* shortlist,
+                     int32_t* idx, double* val, void* ws, hipStream_t st);
+
 // sparse attention over selected rows (workspace layout in attn.hip)
 size_t attn_ws_bytes(int B, int Hq, int k, int dv);
 hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* idx, int B, int Hq, int S, int k,

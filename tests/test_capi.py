@@ -214,3 +214,22 @@ def test_paged_rejects():
     assert attn(st=NUL) == 1 and attn(kv=NUL) == 1
     assert attn(ms=999) == 2 and attn(ns=0) == 2 and attn(Hq=40) == 2 and attn(k=0) == 2
     assert attn(st=MIS) == 4
+
+
+def test_pq_rejects():
+    L = li.lib()
+    need = L.li_pq_workspace_bytes(2, 1000, 64, 256, 64)
+    assert need > 0
+
+    def call(**kw):
+        a = dict(q=A, w=A, cb=A, sg=0.03, c=A, kf=A, nv=NUL, B=2, S=1000, H=64, d=128, m=256, k=64, sl=A, idx=A,
+                 val=A, ws=A2, nb=need)
+        a.update(kw)
+        return L.li_pq_search_rerank(a["q"], a["w"], a["cb"], a["sg"], a["c"], a["kf"], a["nv"], a["B"], a["S"],
+                                     a["H"], a["d"], a["m"], a["k"], a["sl"], a["idx"], a["val"], a["ws"], a["nb"],
+                                     None)
+    assert call(q=NUL) == 1 and call(cb=NUL) == 1 and call(c=NUL) == 1 and call(idx=NUL) == 1
+    assert call(d=64) == 2 and call(m=32) == 2 and call(m=4096, k=64) == 2 and call(k=0) == 2 and call(H=200) == 2
+    assert call(sg=0.0) == 2 and call(sg=-1.0) == 2 and call(sg=float("inf")) == 2
+    assert call(ws=NUL) == 5 and call(nb=need - 1) == 5
+    assert call(c=MIS) == 4
