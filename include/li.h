@@ -311,6 +311,47 @@ li_status li_sparse_attn_gather(const void *q, const void *kv, const int32_t *id
                                 hipStream_t stream);
 
 /*
+ * li_layer_stream_prefill -- a prefill chunk through L layers with only two layers'
+ * history on the GPU (LeanSparse podcast transcript, cues 05:36-07:09: every
+ * layer's indexer keys and compressed KV sit in host memory; one GPU buffer serves
+ * the current layer while the other loads the next layer's history, the full
+ * compressed KV included because the picks are not known ahead; the chunk's new
+ * state goes back to the host).  Per layer l the fused prefill scoring + selection
+ * of li_indexer_topk runs on the compute stream over the keys in the buffer that
+ * holds layer l, while the copy stream writes the previous layer's new rows back
+ * and loads layer l + 1 into the other buffer.
+ *
+ *   q              [L, T, H, d] bf16 (device): each layer's chunk queries
+ *   w              [L, T, H] fp32 (device)
+ *   nv             [T] int32 (device) or NULL: visible keys per query row (every layer)
+ *   host_keys      [L, S, d] bf16 HOST memory, pinned (page-locked): indexer keys
+ *   host_kv        [L, S, kv_row_bytes] HOST memory, pinned: compressed KV rows,
+ *                  moved with the keys (NULL when kv_row_bytes == 0)
+ *   host_new_keys  [L, new_rows, d] bf16 HOST pinned or NULL, host_new_kv
+ *                  [L, new_rows, kv_row_bytes] HOST pinned or NULL: receive the last
+ *                  new_rows key and KV rows of every layer (the chunk's own rows)
+ *   buf0, buf1     device buffers of at least li_layer_stream_buffer_bytes(S,
+ *                  kv_row_bytes) bytes each (buf_bytes)
+ *   idx            [L, T, topk] int32 output (device): each layer's selection, as
+ *                  li_indexer_topk gives it for that layer's keys
+ *   compute, copy  two streams (different ones for overlap); events: four events
+ *                  created by the caller (hipEventDisableTiming recommended)
+ *
+ * Shapes: d == 128, 1 <= H <= 128, T >= 16, 1 <= topk <= 512 (the fused prefill
+ * selection), 0 <= new_rows <= S.  Nothing is allocated and the host does not
+ * wait: the call returns once everything is enqueued; the output idx is complete
+ * when the compute stream reaches its end, the host copies when the copy stream
+ * does.  Errors: LI_ERR_NULL, LI_ERR_SHAPE, LI_ERR_WORKSPACE, LI_ERR_ALIGN,
+ * LI_ERR_LAUNCH (a copy or launch the runtime refused).
+ */
+size_t li_layer_stream_buffer_bytes(int S, size_t kv_row_bytes);
+li_status li_layer_stream_prefill(const void *q, const float *w, const int32_t *nv, const void *host_keys,
+                                  const void *host_kv, size_t kv_row_bytes, void *host_new_keys, void *host_new_kv,
+                                  int new_rows, void *buf0, void *buf1, size_t buf_bytes, int L, int T, int S, int H,
+                                  int d, int topk, int32_t *idx, hipStream_t compute, hipStream_t copy,
+                                  hipEvent_t *events);
+
+/*
  * Paged caches ("Long context", section "Sparsity Is a Systems Feature: The Blast
  * Radius", paragraph "KV-cache management": the indexer key cache and its scales
  * are separate buffers read in pages of 64 keys, while the token-level sparse read

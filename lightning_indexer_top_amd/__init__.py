@@ -68,6 +68,10 @@ def lib():
         L.li_pooled_indexer_topk_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.li_pooled_indexer_topk_workspace_bytes.restype = _Z
         L.li_pooled_indexer_topk.argtypes = [_P, _I, _P, _P, _P, _P] + [_I] * 7 + [_P, _P, _P, _Z, _P]
+        L.li_layer_stream_buffer_bytes.argtypes = [_I, _Z]
+        L.li_layer_stream_buffer_bytes.restype = _Z
+        L.li_layer_stream_prefill.argtypes = [_P, _P, _P, _P, _P, _Z, _P, _P, _I, _P, _P, _Z] + [_I] * 6 + [_P, _P, _P,
+                                                                                                         _P]
         L.li_pq_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.li_pq_workspace_bytes.restype = _Z
         L.li_pq_search_rerank.argtypes = [_P, _P, _P, ctypes.c_float, _P, _P, _P] + [_I] * 6 + [_P] * 4 + [_Z, _P]
@@ -79,7 +83,7 @@ def lib():
                                                   _P, _P]
         for name in ("li_indexer_score", "li_topk_select", "li_topk_select_noalloc", "li_indexer_topk",
                      "li_pool_keys", "li_pooled_indexer_topk", "li_indexer_score_paged", "li_indexer_topk_paged",
-                     "li_sparse_attn_gather_paged", "li_pq_search_rerank", "li_compact_search_rerank",
+                     "li_sparse_attn_gather_paged", "li_pq_search_rerank", "li_layer_stream_prefill", "li_compact_search_rerank",
                      "li_sparse_attn_gather"):
             getattr(L, name).restype = _I
         _LIB = L
@@ -394,4 +398,45 @@ def sparse_attn_gather_paged(q, kv_pool, slot_table, S, idx, sm_scale, with_lse=
                                            _ptr(o), _ptr(lse), _stream(q.device))
     _check(st, "li_sparse_attn_gather_paged")
     return o, lse
+
+
+def layer_stream_buffer_bytes(S, kv_row_bytes):
+    return int(lib().li_layer_stream_buffer_bytes(S, kv_row_bytes))
+
+
+def layer_stream_prefill(q, w, host_keys, topk, nv=None, host_kv=None, new_rows=0, host_new_keys=None,
+                         host_new_kv=None, bufs=None, idx=None, compute=None, copy=None, events=None):
+    """Streams L layers of history through two device buffers while each layer's
+    chunk is scored and selected (li_layer_stream_prefill).  q [L, T, H, 128] bf16 and
+    w [L, T, H] on the device; host_keys [L, S, 128] bf16 and host_kv [L, S, kv_row]
+    uint8 in pinned host memory; returns idx [L, T, topk].  compute and copy are
+    torch streams (default: the current stream and a new one); events four
+    torch.cuda.Event objects (created here if None)."""
+    _dev(q, "q"); _dev(w, "w")
+    for t, n in ((host_keys, "host_keys"), (host_kv, "host_kv"), (host_new_keys, "host_new_keys"),
+                 (host_new_kv, "host_new_kv")):
+        if t is not None and not (isinstance(t, torch.Tensor) and not t.is_cuda and t.is_pinned()
+                                  and t.is_contiguous()):
+            raise TypeError(f"{n} must be a contiguous pinned host tensor")
+    L, T, H, d = q.shape
+    S = host_keys.shape[1]
+    kv_row = host_kv.shape[2] if host_kv is not None else 0
+    nb = layer_stream_buffer_bytes(S, kv_row)
+    if bufs is None:
+        bufs = [torch.empty(nb, dtype=torch.uint8, device=q.device) for _ in range(2)]
+    if idx is None:
+        idx = torch.empty((L, T, topk), dtype=torch.int32, device=q.device)
+    compute = compute or torch.cuda.current_stream(q.device)
+    copy = copy or torch.cuda.Stream(device=q.device)
+    if events is None:
+        events = [torch.cuda.Event() for _ in range(4)]
+    for e in events:  # the raw event exists once recorded
+        e.record(compute)
+    evs = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+    st = lib().li_layer_stream_prefill(_ptr(q), _ptr(w), _ptr(nv), _ptr(host_keys), _ptr(host_kv), kv_row,
+                                       _ptr(host_new_keys), _ptr(host_new_kv), new_rows, _ptr(bufs[0]), _ptr(bufs[1]),
+                                       min(b.numel() for b in bufs), L, T, S, H, d, topk, _ptr(idx),
+                                       ctypes.c_void_p(compute.cuda_stream), ctypes.c_void_p(copy.cuda_stream), evs)
+    _check(st, "li_layer_stream_prefill")
+    return idx
 

@@ -259,6 +259,40 @@ li_status li_sparse_attn_gather_paged(const void* q, const void* kv_pool, const 
                   "li_sparse_attn_gather_paged");
 }
 
+size_t li_layer_stream_buffer_bytes(int S, size_t kv_row_bytes) {
+  if (S < 1) return 0;
+  return li::layer_stream_buffer_bytes(S, kv_row_bytes);
+}
+
+li_status li_layer_stream_prefill(const void* q, const float* w, const int32_t* nv, const void* host_keys,
+                                  const void* host_kv, size_t kv_row_bytes, void* host_new_keys, void* host_new_kv,
+                                  int new_rows, void* buf0, void* buf1, size_t buf_bytes, int L, int T, int S, int H,
+                                  int d, int topk, int32_t* idx, hipStream_t compute, hipStream_t copy,
+                                  hipEvent_t* events) {
+  if (!q || !w || !host_keys || !buf0 || !buf1 || !idx || !events)
+    return fail(LI_ERR_NULL, "q, w, host_keys, buf0, buf1, idx and events must be non-NULL");
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return fail(LI_ERR_NULL, "events must hold four events");
+  if (kv_row_bytes && !host_kv) return fail(LI_ERR_NULL, "host_kv must be non-NULL when kv_row_bytes > 0");
+  if (d != LI_INDEX_DIM) return fail(LI_ERR_SHAPE, "d must be %d", LI_INDEX_DIM);
+  if (L < 1 || T < 1 || S < 1 || H < 1 || H > 128) return fail(LI_ERR_SHAPE, "need L, T, S >= 1 and H in [1, 128]");
+  if ((int64_t)L * T * S >= (1ll << 40)) return fail(LI_ERR_SHAPE, "L*T*S too large");
+  if (new_rows < 0 || new_rows > S) return fail(LI_ERR_SHAPE, "new_rows must be in [0, S]");
+  if (topk < 1 || topk > LI_TOPK_MAX) return fail(LI_ERR_SHAPE, "topk must be in [1, %d]", LI_TOPK_MAX);
+  if (!li::prefill_fused_apply(LI_BF16, LI_BF16, T, H, topk))
+    return fail(LI_ERR_SHAPE, "the streamed layers run the fused prefill selection: T >= 16 and topk <= 512");
+  if (buf_bytes < li::layer_stream_buffer_bytes(S, kv_row_bytes))
+    return fail(LI_ERR_WORKSPACE, "each buffer needs %zu bytes", li::layer_stream_buffer_bytes(S, kv_row_bytes));
+  if (misaligned(q) || misaligned(w) || misaligned(nv) || misaligned(buf0) || misaligned(buf1) || misaligned(idx))
+    return fail(LI_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  uint8_t* const bufs[2] = {(uint8_t*)buf0, (uint8_t*)buf1};
+  return launched(li::launch_layer_stream((const uint16_t*)q, w, nv, (const uint8_t*)host_keys,
+                                          (const uint8_t*)host_kv, kv_row_bytes, (uint8_t*)host_new_keys,
+                                          (uint8_t*)host_new_kv, new_rows, bufs, L, T, S, H, topk, idx, compute, copy,
+                                          events),
+                  "li_layer_stream_prefill");
+}
+
 size_t li_compact_workspace_bytes(int B, int S, int H, int m, int k) {
   if (B < 1 || S < 1 || H < 1 || m < 1) return 0;
   return li::compact_ws_bytes(B, S, H, m, k);

@@ -361,6 +361,10 @@ static bool use_fused(int q_type, int k_type, int T, int H, int topk) {
   return q_type == DT_BF16 && k_type == DT_BF16 && T >= 2 * PS_WAVES && topk <= PS_KMAX && H <= 128;
 }
 
+bool prefill_fused_apply(int q_type, int k_type, int T, int H, int topk) {
+  return use_fused(q_type, k_type, T, H, topk);
+}
+
 size_t indexer_topk_ws_bytes(int q_type, int k_type, int B, int T, int S, int H, int topk) {
   // the same predicates, in the same order, as launch_indexer_topk: the fused
   // prefill kernel needs nothing; decode-shaped rows need the scores, the

@@ -116,4 +116,12 @@ hipError_t launch_pooled_topk(const uint16_t* q, const float* w, const uint8_t* 
                               const int32_t* nv_tokens, int B, int T, int Sp, int H, int pool, int topk,
                               int32_t* idx_tokens, float* val_blocks, void* ws, hipStream_t st);
 
+// layer-streamed prefill (stream.hip)
+size_t layer_stream_buffer_bytes(int S, size_t kv_row_bytes);
+hipError_t launch_layer_stream(const uint16_t* q, const float* w, const int32_t* nv, const uint8_t* host_keys,
+                               const uint8_t* host_kv, size_t kv_row_bytes, uint8_t* host_new_keys,
+                               uint8_t* host_new_kv, int new_rows, uint8_t* const buf[2], int L, int T, int S, int H,
+                               int topk, int32_t* idx, hipStream_t compute, hipStream_t copy, hipEvent_t const ev[4]);
+bool prefill_fused_apply(int q_type, int k_type, int T, int H, int topk);
+
 }  // namespace li

@@ -41,6 +41,11 @@ WORKLOADS = {
     "pq_search": dict(B=32, T=1, S=131072, H=64, d=128, m=2048, topk=512, key="bf16", q="bf16",
                       q_scale=1 / math.sqrt(128), w="uniform", causal=False, pq_train_stride=64, pq_iters=8,
                       seed=SEED_BASE + 7),
+    # a 4096-query prefill chunk through 8 layers whose history (131072 bf16 indexer
+    # keys and 131072 compressed KV rows of 576 bytes per layer) lives in host
+    # memory and is streamed through two GPU buffers; causal, 64 heads, top-512
+    "layer_stream": dict(B=1, T=4096, S=131072, H=64, d=128, topk=512, L=8, kv_row=576, key="bf16", q="bf16",
+                         q_scale=1.0, w="uniform", causal=True, seed=SEED_BASE + 8),
     # 16 sequences x 524288 bf16 token keys pooled four at a time on write (131072
     # fp8 pooled keys each), a 32-head indexer over the pooled keys, top-512 blocks
     # expanded to 2048 tokens
@@ -152,4 +157,20 @@ def pq_inputs(sp):
     cb, sigma = pq_codebook(sample, seed, sp.get("pq_iters", 8))
     codes = pq_encode(k_full, cb, sigma)
     return {"q": q, "w": w, "k_full": k_full, "cb": cb, "sigma": sigma, "codes": codes}
+
+
+def layer_stream_inputs(sp, out_keys=None, out_kv=None):
+    """Per-layer chunk queries q [L, T, H, d] bf16 and weights w [L, T, H], the
+    layers' indexer keys [L, S, d] bf16 N(0, 1) and compressed KV rows [L, S, kv_row]
+    (opaque bytes on this path: seeded uniform bytes), and nv [T] (causal).
+    out_keys / out_kv: preallocated (e.g. pinned) arrays to fill."""
+    L, T, S, H, d, seed = sp["L"], sp["T"], sp["S"], sp["H"], sp["d"], sp["seed"]
+    q = normal_bf16(seed, TID_Q, (L, T, H, d), sp["q_scale"])
+    w = uniform_f32(seed, TID_W, (L, T, H), 0.0, 1.0)
+    keys = normal_bf16(seed, TID_K, (L, S, d), 1.0, out=out_keys)
+    kv = out_kv if out_kv is not None else np.empty((L, S, sp["kv_row"]), np.uint8)
+    rng = np.random.default_rng(seed)
+    for l in range(L):
+        kv[l] = rng.integers(0, 256, (S, sp["kv_row"]), dtype=np.uint8)
+    return {"q": q, "w": w, "keys": keys, "kv": kv, "nv": causal_nv(S, T)}
 
