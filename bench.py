@@ -148,6 +148,23 @@ def _p(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def capi_call(li, name, *args):
+    """A C-ABI call with its arguments converted once (tensors to device pointers,
+    None to NULL): a few microseconds of host time per call, so bursts of short
+    kernels keep the GPU queue full and the events bracket kernels only."""
+    f = getattr(li.lib(), name)
+    conv = tuple(ctypes.c_void_p(a.data_ptr()) if hasattr(a, "data_ptr") else a for a in args)
+
+    def call(*_):
+        if f(*conv):
+            raise RuntimeError(f"{name}: {li.lib().li_last_error().decode()}")
+    return call
+
+
+def cur_stream(torch):
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
 def source_sha(rels):
     h = hashlib.sha256()
     for rel in rels:
@@ -475,9 +492,12 @@ def bench_compact(torch, li, workloads, steps, warmup, cpu=True):
     idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
     val = torch.empty((B, k), dtype=torch.float64, device="cuda")
 
+    st = cur_stream(torch)
+    calls = [capi_call(li, "li_compact_search_rerank", q, w, P, c, cs, kf, None, B, S, H, 128, 32, m, k, sl, idx, val,
+                       ws, ws.numel(), st) for c, cs, kf in reps]
+
     def step(i):
-        c, cs, kf = reps[i % n_rep]
-        li.compact_search_rerank(q, w, P, c, cs, kf, m, k, workspace=ws, out=(sl, idx, val))
+        calls[i % n_rep]()
 
     for i in range(warmup):
         step(i)
@@ -490,8 +510,11 @@ def bench_compact(torch, li, workloads, steps, warmup, cpu=True):
     ex_ws = torch.zeros(li.indexer_topk_workspace_bytes(li.LI_BF16, li.LI_BF16, B, 1, S, H, k), dtype=torch.uint8,
                         device="cuda")
 
+    ex_calls = [capi_call(li, "li_indexer_topk", q4, li.LI_BF16, w3, r[2], li.LI_BF16, None, None, B, 1, S, H, 128, k,
+                          ex_idx, None, ex_ws, ex_ws.numel(), st) for r in reps]
+
     def exact(i):
-        li.indexer_topk(q4, w3, reps[i % n_rep][2], k, with_values=False, workspace=ex_ws, out=(ex_idx, None))
+        ex_calls[i % n_rep]()
 
     for i in range(warmup):
         exact(i)
@@ -537,9 +560,12 @@ def bench_pq(torch, li, workloads, steps, warmup, cpu=True):
     idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
     val = torch.empty((B, k), dtype=torch.float64, device="cuda")
 
+    st = cur_stream(torch)
+    calls = [capi_call(li, "li_pq_search_rerank", q, w, cb, x["sigma"], c, kf, None, B, S, H, 128, m, k, sl, idx, val,
+                       ws, ws.numel(), st) for c, kf in reps]
+
     def step(i):
-        c, kf = reps[i % n_rep]
-        li.pq_search_rerank(q, w, cb, x["sigma"], c, kf, m, k, workspace=ws, out=(sl, idx, val))
+        calls[i % n_rep]()
 
     for i in range(warmup):
         step(i)
@@ -610,8 +636,10 @@ def bench_stream(torch, li, workloads, steps, warmup, cpu=True):
     stream_ms = (time.perf_counter() - t0) * 1e3 / reps / L
     # the selection alone, keys resident
     kd = to_dev(torch, x["keys"][0:1], "bf16")
-    sel_ms = burst_ms(torch, lambda i: li.indexer_topk(q[i % L:i % L + 1], w[i % L:i % L + 1], kd, k, None, nv,
-                                                        with_values=False, out=(idx[0].view(T, k), None)), 2 * L) 
+    st = cur_stream(torch)
+    sel_calls = [capi_call(li, "li_indexer_topk", q[l:l + 1], li.LI_BF16, w[l:l + 1], kd, li.LI_BF16, None, nv, 1, T,
+                           S, H, 128, k, idx[0], None, None, 0, st) for l in range(L)]
+    sel_ms = burst_ms(torch, lambda i: sel_calls[i % L](), 2 * L)
     # the copies alone (one layer's keys and KV rows, host to device)
     layer_bytes = S * 256 + S * kvr
 
@@ -676,14 +704,21 @@ def bench_select_attend(torch, li, workloads, steps, warmup, cpu=True):
     sel_idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
     ev = []
 
+    st = cur_stream(torch)
+    score_call = capi_call(li, "li_indexer_score", q, li.LI_BF16, w, kk, li.LI_FP8_E4M3, ks, None, B, 1, S, H, 128,
+                           scores, st)
+    sel_call = capi_call(li, "li_topk_select", scores, None, B, S, k, sel_idx, None, sel_ws, sel_ws.numel(), st)
+    attn_step_call = capi_call(li, "li_sparse_attn_gather", qa, lat, idx, B, Hq, S, k, sp["dqk"], sp["dv"],
+                               sp["tau"], out, lse, None, 0, st)
+
     def step(i):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         e[0].record()
-        li.indexer_score(q, w, kk, ks, None, out=scores)
+        score_call()
         e[1].record()
-        li.topk_select(scores, k, with_values=False, workspace=sel_ws, out=(sel_idx, None))
+        sel_call()
         e[2].record()
-        li.sparse_attn_gather(qa, lat, idx, sp["tau"], out=(out, lse))
+        attn_step_call()
         e[3].record()
         ev.append(e)
 
@@ -694,16 +729,19 @@ def bench_select_attend(torch, li, workloads, steps, warmup, cpu=True):
     t = np.array([[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in ev[-steps:]]).mean(0)
     score_ms, sel_ms, attn_ms = [float(v) for v in t]
     # the attention kernel alone over a burst
-    attn_burst_ms = burst_ms(torch, lambda i: li.sparse_attn_gather(qa, lat, idx, sp["tau"], out=(out, lse)),
-                             max(steps, 20))
+    st = cur_stream(torch)
+    attn_call = capi_call(li, "li_sparse_attn_gather", qa, lat, idx, B, Hq, S, k, sp["dqk"], sp["dv"], sp["tau"], out,
+                          lse, None, 0, st)
+    attn_burst_ms = burst_ms(torch, attn_call, max(steps, 20))
     # the same attention through a slot table (page size 1): the latent buffer read as a
     # pool of B * S rows, every token at a random slot (timing only: the rows read
     # are other tokens' rows, the access pattern is what counts)
     perm = torch.randperm(B * S, generator=torch.Generator().manual_seed(0x5EED0E01)).to(torch.int32)
     slot_table = perm.reshape(B, S).cuda()
     pool = lat.view(B * S, sp["dqk"])
-    paged_ms = burst_ms(torch, lambda i: li.sparse_attn_gather_paged(qa, pool, slot_table, S, idx, sp["tau"],
-                                                                     out=(out, lse)), max(steps, 20))
+    paged_call = capi_call(li, "li_sparse_attn_gather_paged", qa, pool, slot_table, S, B * S, idx, B, Hq, S, k,
+                           sp["dqk"], sp["dv"], sp["tau"], out, lse, st)
+    paged_ms = burst_ms(torch, paged_call, max(steps, 20))
     del slot_table, perm
     gb = attn_bytes(B, Hq, k)
     af = attn_flop(B, Hq, k)
@@ -771,7 +809,9 @@ def bench_pooled(torch, li, workloads, steps, warmup, cpu=True):
     ktok = to_dev(torch, x["k_tokens"], "bf16")
     codes, scales = li.pool_keys(ktok, pool)
     # pooling on write: every token key read once, the pooled keys written once
-    pool_ms = burst_ms(torch, lambda i: li.pool_keys(ktok, pool, out=(codes, scales)), max(steps, 10))
+    st = cur_stream(torch)
+    pool_ms = burst_ms(torch, capi_call(li, "li_pool_keys", ktok, li.LI_BF16, B, L, 128, pool, codes, scales, st),
+                       max(steps, 10))
     pool_bytes = B * L * FULL_KEY_BYTES_BF16 + B * Sp * KEY_BYTES
     del ktok
     torch.cuda.empty_cache()
@@ -782,15 +822,18 @@ def bench_pooled(torch, li, workloads, steps, warmup, cpu=True):
     idx = torch.empty((B, k * pool), dtype=torch.int32, device="cuda")
     sc = torch.empty((B, Sp), dtype=torch.float32, device="cuda")
 
+    calls = [capi_call(li, "li_pooled_indexer_topk", q, li.LI_BF16, w, c, s, None, B, 1, Sp, H, 128, pool, k, idx,
+                       None, ws, nb, st) for c, s in reps]
+    score_calls = [capi_call(li, "li_indexer_score", q, li.LI_BF16, w, c, li.LI_FP8_E4M3, s, None, B, 1, Sp, H, 128,
+                             sc, st) for c, s in reps]
+
     def step(i):
-        c, s = reps[i % n_rep]
-        li.pooled_indexer_topk(q, w, c, s, pool, k, with_values=False, workspace=ws, out=(idx, None))
+        calls[i % n_rep]()
 
     for i in range(warmup):
         step(i)
     ms = burst_ms(torch, lambda i: step(warmup + i), max(steps, 20))
-    score_ms = burst_ms(torch, lambda i: li.indexer_score(q, w, reps[i % n_rep][0], reps[i % n_rep][1], out=sc),
-                        max(steps, 20))
+    score_ms = burst_ms(torch, lambda i: score_calls[i % n_rep](), max(steps, 20))
     alg = decode_bytes(B, Sp)
     log(f"[pooled] pooling {pool_ms * 1e3:.1f} us ({pool_bytes / (pool_ms * 1e-3) / 1e9:.0f} GB/s); select step "
         f"{ms * 1e3:.1f} us, scoring {score_ms * 1e3:.1f} us ({alg / (score_ms * 1e-3) / 1e9:.0f} GB/s)")
@@ -845,16 +888,19 @@ def bench_paged(torch, li, workloads, steps, warmup, cpu=True):
     idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
     ws = torch.empty(max(li.topk_workspace_bytes(B, S, k), 256), dtype=torch.uint8, device="cuda")
 
+    st = cur_stream(torch)
+    score_calls = [capi_call(li, "li_indexer_score_paged", q, li.LI_BF16, w, kp, spool, table, li.PAGE, P, num, None,
+                             B, 1, S, H, 128, scores, st) for kp, spool in pools]
+    topk_call = capi_call(li, "li_topk_select", scores, None, B, S, k, idx, None, ws, ws.numel(), st)
+
     def step(i):
-        kp, spool = pools[i % n_rep]
-        li.indexer_score_paged(q, w, kp, spool, table, S, out=scores)
-        li.topk_select(scores, k, with_values=False, workspace=ws, out=(idx, None))
+        score_calls[i % n_rep]()
+        topk_call()
 
     for i in range(warmup):
         step(i)
     ms = burst_ms(torch, lambda i: step(warmup + i), max(steps, 20))
-    score_ms = burst_ms(torch, lambda i: li.indexer_score_paged(q, w, pools[i % n_rep][0], pools[i % n_rep][1], table,
-                                                                 S, out=scores), max(steps, 20))
+    score_ms = burst_ms(torch, lambda i: score_calls[i % n_rep](), max(steps, 20))
     alg = decode_bytes(B, S)
     log(f"[paged] step {ms * 1e3:.1f} us, paged scoring {score_ms * 1e3:.1f} us "
         f"({alg / (score_ms * 1e-3) / 1e9:.0f} GB/s)")

@@ -372,7 +372,7 @@ size_t indexer_topk_ws_bytes(int q_type, int k_type, int B, int T, int S, int H,
   // scores and the top-k's own workspace
   if (use_fused(q_type, k_type, T, H, topk)) return 0;
   const size_t base = align256((size_t)B * T * S * sizeof(float)) + topk_ws_bytes(B * T, S, topk);
-  if (select_score_apply(q_type, k_type, B * T, S, H, topk))
+  if (held_select_apply(q_type, k_type, B * T, S, H, topk) || select_score_apply(q_type, k_type, B * T, S, H, topk))
     return base + align256((size_t)B * T * 1024 * sizeof(uint32_t)) + align256((size_t)B * T * 256 * sizeof(uint32_t)) +
            align256((size_t)B * T * 128);
   return base;
@@ -398,6 +398,22 @@ hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const 
   }
   float* scores = (float*)ws;
   void* tws = (uint8_t*)ws + align256((size_t)B * T * S * sizeof(float));
+  if (held_select_apply(q_type, k_type, B * T, S, H, topk)) {
+    // few long rows, fp8 keys, 33-64 heads: each scoring workgroup lists its own
+    // entries above a threshold of its own, one finalize selects
+    uint32_t *unused, *bcnt;
+    float* cval;
+    int32_t* cid;
+    topk_mb_layout(tws, B * T, S, &unused, &bcnt, &cval, &cid);
+    uint32_t* counters = (uint32_t*)((uint8_t*)tws + topk_ws_bytes(B * T, S, topk));
+    uint32_t* tau_used = counters + align256((size_t)B * T * 1024 * sizeof(uint32_t)) / sizeof(uint32_t);
+    int P = 0, chunk = 0;
+    hipError_t e = launch_score_held_select(q, w, k, ks, nv, B, T, S, H, topk, scores, bcnt, cval, cid, tau_used, &P,
+                                            &chunk, st);
+    if (e != hipSuccess) return e;
+    return launch_topk_finalize_f32(scores, nv, B * T, S, topk, P, chunk, bcnt, cval, cid, idx, val, nullptr,
+                                    tau_used, st, true);
+  }
   if (select_score_apply(q_type, k_type, B * T, S, H, topk)) {
     // few long rows: the scoring kernel lists the candidates, one finalize selects
     uint32_t *unused, *bcnt;
@@ -437,6 +453,20 @@ hipError_t launch_indexer_topk_paged(const uint16_t* q, const float* w, const ui
   const int R = B * T;
   float* scores = (float*)ws;
   void* tws = (uint8_t*)ws + align256((size_t)R * S * sizeof(float));
+  if (held_select_apply(DT_BF16, DT_FP8, R, S, H, topk)) {
+    uint32_t *unused, *bcnt;
+    float* cval;
+    int32_t* cid;
+    topk_mb_layout(tws, R, S, &unused, &bcnt, &cval, &cid);
+    uint32_t* counters = (uint32_t*)((uint8_t*)tws + topk_ws_bytes(R, S, topk));
+    uint32_t* tau_used = counters + align256((size_t)R * 1024 * sizeof(uint32_t)) / sizeof(uint32_t);
+    int P = 0, chunk = 0;
+    hipError_t e = launch_score_held_select(q, w, k_pool, ks_pool, nv, B, T, S, H, topk, scores, bcnt, cval, cid,
+                                            tau_used, &P, &chunk, st, page_table, max_pages, num_pages);
+    if (e != hipSuccess) return e;
+    return launch_topk_finalize_f32(scores, nv, R, S, topk, P, chunk, bcnt, cval, cid, idx, val, nullptr, tau_used,
+                                    st, true);
+  }
   if (select_score_apply_paged(R, S, H, topk)) {
     uint32_t *unused, *bcnt;
     float* cval;

@@ -79,6 +79,14 @@ hipError_t launch_score_select(const void* q, int k_type, const float* w, const 
                                uint32_t* tau_used, int* P, int* chunk, hipStream_t st,
                                const int32_t* page_table = nullptr, int max_pages = 0, int num_pages = 0);
 bool select_score_apply_paged(int R, int S, int H, int topk);
+// Few long rows, fp8 keys, 33-64 heads: the held-scores kernel lists each
+// workgroup's entries above a threshold of its own (no waiting), the finalize
+// (local_tau) selects exactly or over the whole row.
+bool held_select_apply(int q_type, int k_type, int R, int S, int H, int topk);
+hipError_t launch_score_held_select(const void* q, const float* w, const void* k, const float* ks, const int32_t* nv,
+                                    int B, int T, int S, int H, int topk, float* scores, uint32_t* bcnt, float* cval,
+                                    int32_t* cid, uint32_t* tau_used, int* P, int* chunk, hipStream_t st,
+                                    const int32_t* page_table = nullptr, int max_pages = 0, int num_pages = 0);
 
 // Paged fp8 keys: k_pool [num_pages, 64, 128] codes, ks_pool [num_pages, 64]
 // scales, page_table [B, max_pages] (pool page of keys 64 p .. 64 p + 63 of b).
@@ -97,7 +105,8 @@ hipError_t launch_attn_paged(const uint16_t* q, const uint16_t* kv_pool, const i
 void topk_mb_layout(void* ws, int R, int S, uint32_t** counters, uint32_t** bcnt, float** cval, int32_t** cid);
 hipError_t launch_topk_finalize_f32(const float* scores, const int32_t* nv, int R, int S, int k, int P, int chunk,
                                     const uint32_t* bcnt, const float* cval, const int32_t* cid, int32_t* idx,
-                                    float* val, uint32_t* reset, const uint32_t* tau_used, hipStream_t st);
+                                    float* val, uint32_t* reset, const uint32_t* tau_used, hipStream_t st,
+                                    bool local_tau = false);
 
 // fused scoring + selection for many query rows (prefill); falls back to
 // score-then-select where the fused kernel does not apply

@@ -336,6 +336,70 @@ __device__ void score_select_epilogue(const float* __restrict__ out_row, int r, 
   (void)wid;
 }
 
+// Selection epilogue of the held-scores form (few long rows): after [LSA] "What the
+// kernels do about the top-p" (a threshold, then a list of the entries above it),
+// with the threshold taken by each workgroup from its own scores, so no workgroup
+// waits for another.  held: the scores of keys key0 .. key0 + n - 1 in LDS;
+// the workgroup's threshold is the lower edge of the 16-bit key bucket holding its
+// j-th largest score, j = max(ceil(3 k / P), 16) over P workgroups of the row (all
+// n entries when n <= j), and it lists its entries at or above it, in index order,
+// into its region of the candidate list (cval / cid at r S + key0), recording the
+// count (bcnt) and the threshold (tau_used).  A row's top k lies among the lists
+// whenever its kth listed value reaches every region's threshold: the finalize
+// checks that and otherwise selects over the whole row.
+constexpr int HELD_E = 16;  // held scores per thread: at most 4,096 per workgroup
+
+__device__ void held_select_epilogue(const float* held, int n, int r, int key0, int k, uint32_t* __restrict__ bcnt,
+                                     float* __restrict__ cval, int32_t* __restrict__ cid,
+                                     uint32_t* __restrict__ tau_used, int S, uint8_t* scratch) {
+  uint32_t* hist = (uint32_t*)scratch;  // 256 bins
+  uint32_t* wsum = hist + 256;          // 4 waves
+  uint32_t* res = wsum + 4;             // 4
+  uint32_t* cnt = res + 4;              // 16 x 4 counts + total
+  const int P = gridDim.x, bx = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t key[HELD_E];
+  bool valid[HELD_E];
+#pragma unroll
+  for (int e = 0; e < HELD_E; ++e) {
+    const int i = e * 256 + tid;
+    valid[e] = i < n;
+    key[e] = valid[e] ? ord_f32(held[i]) : 0u;
+  }
+  const uint32_t j = (uint32_t)max((3 * k + P - 1) / P, 16);
+  uint32_t tau = 0u;
+  if ((uint32_t)n > j) tau = block_kth8<256, HELD_E, 2>(key, valid, j, hist, wsum, res);
+  // entries e * 256 + tid: ordering by (e, wave, lane) is index order
+  uint64_t mk[HELD_E];
+#pragma unroll
+  for (int e = 0; e < HELD_E; ++e) {
+    mk[e] = __ballot(valid[e] && key[e] >= tau);
+    if (lane == 0) cnt[e * 4 + wid] = (uint32_t)__popcll(mk[e]);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const uint32_t c = cnt[tid];
+    const uint32_t incl = wave_incl_scan(c);
+    cnt[tid] = incl - c;
+    if (tid == 63) cnt[64] = incl;
+  }
+  __syncthreads();
+  float* ov = cval + (int64_t)r * S + key0;
+  int32_t* oi = cid + (int64_t)r * S + key0;
+#pragma unroll
+  for (int e = 0; e < HELD_E; ++e) {
+    if ((mk[e] >> lane) & 1ull) {
+      const uint32_t pos = cnt[e * 4 + wid] + (uint32_t)__popcll(mk[e] & ((1ull << lane) - 1));
+      const int i = e * 256 + tid;
+      ov[pos] = held[i];
+      oi[pos] = key0 + i;
+    }
+  }
+  if (tid == 0) {
+    bcnt[(int64_t)r * P + bx] = cnt[64];
+    tau_used[(int64_t)r * 256 + bx] = tau;
+  }
+}
+
 // PAGED: the keys (and scales) of every sequence live in pages of PAGE keys of a
 // shared pool; page_table[b * max_pages + p] is the pool page holding keys
 // PAGE p .. PAGE p + PAGE - 1 of sequence b ("Long context", section "Sparsity Is
@@ -347,7 +411,7 @@ __device__ void score_select_epilogue(const float* __restrict__ out_row, int r, 
 constexpr int PAGE = 64;
 constexpr int PAGED_MAX_KPB = 64 * PAGE;
 
-template <int HT, bool FP8, int NST, int WPE, bool SEL, bool STG = false, bool PAGED = false>
+template <int HT, bool FP8, int NST, int WPE, bool SEL, bool STG = false, bool PAGED = false, bool LSEL = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ k,
                          const float* __restrict__ ks, const int32_t* __restrict__ nv, int T, int S, int H,
@@ -356,6 +420,7 @@ void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict
                          uint64_t* __restrict__ taupub, uint32_t* __restrict__ tau_used, uint32_t epoch,
                          const int32_t* __restrict__ page_table, int max_pages, int num_pages) {
   static_assert(!PAGED || FP8, "paged keys are fp8");
+  static_assert(!LSEL || (STG && !SEL), "the local selection runs on the held scores");
   typedef TileGeom<FP8> G;
   static_assert(NST >= 1 && NST <= 3, "ring depth");
   // STG: the workgroup's scores are held in LDS behind the ring and written in one
@@ -655,6 +720,8 @@ _Pragma("unroll") \
     const float* held = (const float*)(ring + NST * SSTRIDE);
     const int n = vis_end - key0;
     for (int i = (int)threadIdx.x; i < n; i += 256) out_row[key0 + i] = held[i];
+    // the ring is free: its LDS holds the selection's histograms and counts
+    if constexpr (LSEL) held_select_epilogue(held, max(n, 0), r, key0, topk, bcnt, cval, cid, tau_used, S, ring);
   }
 #undef LI_TILE_PART
 }
@@ -870,6 +937,52 @@ bool select_score_apply(int q_type, int k_type, int R, int S, int H, int topk) {
 }
 
 bool select_score_apply_paged(int R, int S, int H, int topk) { return select_score_shape(DT_FP8, R, S, H, topk, true); }
+
+// Few long rows with fp8 keys and 33-64 heads: the held-scores kernel with the
+// workgroup-local selection epilogue, then the finalize.
+bool held_select_apply(int q_type, int k_type, int R, int S, int H, int topk) {
+  if (q_type != DT_BF16 || k_type != DT_FP8 || H <= 32 || H > 64) return false;
+  if (!topk_use_mb(R, S) || topk > 2048) return false;
+  const int kpb = std::min(stream_keys_per_block(R, S, 2), STAGE_KEYS);
+  const int P = (S + kpb - 1) / kpb;
+  return P <= 256 && kpb >= 1024 && kpb <= HELD_E * 256;
+}
+
+template <bool PAGED>
+static hipError_t launch_held_select(const uint16_t* qq, const float* w, const uint8_t* kk, const float* ks,
+                                     const int32_t* nv, int R, int T, int S, int H, int topk, float* scores,
+                                     uint32_t* bcnt, float* cval, int32_t* cid, uint32_t* tau_used, int* P_out,
+                                     int* chunk_out, const int32_t* page_table, int max_pages, int num_pages,
+                                     hipStream_t st) {
+  typedef StreamCfg<2, true> C;
+  auto kern = score_stream_kernel<2, true, C::NST, 2, false, true, PAGED, true>;
+  const int kpb = std::min(stream_keys_per_block(R, S, 2), STAGE_KEYS);
+  const size_t lds = stream_lds_bytes<2, true>() + (size_t)kpb * sizeof(float);
+  static const bool attr = [&] {
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)(stream_lds_bytes<2, true>() + STAGE_KEYS * sizeof(float)));
+    return true;
+  }();
+  (void)attr;
+  const int P = (S + kpb - 1) / kpb;
+  *P_out = P;
+  *chunk_out = kpb;
+  kern<<<dim3(P, R), 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, topk, nullptr, bcnt, cval, cid, nullptr,
+                                     tau_used, 0u, page_table, max_pages, num_pages);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_held_select(const void* q, const float* w, const void* k, const float* ks, const int32_t* nv,
+                                    int B, int T, int S, int H, int topk, float* scores, uint32_t* bcnt, float* cval,
+                                    int32_t* cid, uint32_t* tau_used, int* P_out, int* chunk_out, hipStream_t st,
+                                    const int32_t* page_table, int max_pages, int num_pages) {
+  if (page_table)
+    return launch_held_select<true>((const uint16_t*)q, w, (const uint8_t*)k, ks, nv, B * T, T, S, H, topk, scores,
+                                    bcnt, cval, cid, tau_used, P_out, chunk_out, page_table, max_pages, num_pages,
+                                    st);
+  return launch_held_select<false>((const uint16_t*)q, w, (const uint8_t*)k, ks, nv, B * T, T, S, H, topk, scores,
+                                   bcnt, cval, cid, tau_used, P_out, chunk_out, nullptr, 0, 0, st);
+}
 
 // launch epochs of the selection kernel: a published threshold carries the epoch of
 // the launch that computed it

@@ -219,15 +219,19 @@ __device__ void select_block(const S* __restrict__ row, const int32_t* __restric
 // by the wide radix select, then every entry above T and the first (k - count
 // above T) entries equal to T, each at its position from a prefix scan.  Every
 // thread of the TK_THREADS workgroup calls it; at least k entries are valid.
+// With a floor: when the kth value T lies below it nothing is written and false
+// comes back (T is the same in every thread, so all of them return together).
 template <typename Sc, int E>
-__device__ __forceinline__ void write_top_listed(const typename ScoreTraits<Sc>::K (&key)[E], const Sc (&val)[E],
+__device__ __forceinline__ bool write_top_listed(const typename ScoreTraits<Sc>::K (&key)[E], const Sc (&val)[E],
                                                  const int32_t (&id)[E], const bool (&valid)[E], uint32_t k,
                                                  int32_t* __restrict__ io, Sc* __restrict__ vo, uint32_t* hist,
-                                                 uint64_t* wsum8, uint32_t* res, uint32_t* scan1, uint32_t* scan2) {
+                                                 uint64_t* wsum8, uint32_t* res, uint32_t* scan1, uint32_t* scan2,
+                                                 typename ScoreTraits<Sc>::K floor = 0) {
   typedef typename ScoreTraits<Sc>::K K;
   constexpr int NW = TK_THREADS / 64;
   uint32_t n_gt_all;
   const K T = block_kth_wide<TK_THREADS, E>(key, valid, k, hist, (uint32_t*)wsum8, res, &n_gt_all);
+  if (T < floor) return false;
   uint32_t ties = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) ties += valid[e] && key[e] == T ? 1u : 0u;
@@ -252,6 +256,7 @@ __device__ __forceinline__ void write_top_listed(const typename ScoreTraits<Sc>:
       ++pos;
     }
   }
+  return true;
 }
 
 // A row of at most MB_KEEP entries whose ids ascend along the row (a row of scores
@@ -437,12 +442,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
                                                                   int32_t* __restrict__ idx_out,
                                                                   Sc* __restrict__ val_out,
                                                                   uint32_t* __restrict__ reset,
-                                                                  const uint32_t* __restrict__ tau_used) {
+                                                                  const uint32_t* __restrict__ tau_used,
+                                                                  bool local_tau) {
   typedef typename ScoreTraits<Sc>::K K;
   constexpr int NW = TK_THREADS / 64;
   constexpr int E = MB_KEEP / TK_THREADS;
   __shared__ uint32_t off[257];
   __shared__ int s_unfiltered;
+  __shared__ uint32_t s_floor;
   __shared__ uint32_t scan1[NW], scan2[NW];
   __shared__ uint32_t hist[KW_BINS];
   __shared__ uint64_t wsum8[2 * NW];  // minima and maxima of the keys, per wave
@@ -458,9 +465,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
   __syncthreads();
   // exclusive prefix of the region counts (P <= 256): one wave, four per lane.  A
   // region left unfiltered, or regions filtered with different thresholds (where
-  // they record theirs), make the lists unusable.
+  // they record theirs and should share one), make the lists unusable.  Regions
+  // that filtered with thresholds of their own (local_tau) leave the largest of
+  // them as the floor the selected kth value must reach.
   if (tid < 64) {
-    uint32_t c4[4], tot = 0;
+    uint32_t c4[4], tot = 0, fl = 0;
     bool unf = false;
     const uint32_t t0 = tau_used ? tau_used[(int64_t)r * 256] : 0u;
 #pragma unroll
@@ -468,10 +477,19 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
       const int b = 4 * tid + e;
       c4[e] = b < P ? bcnt[(int64_t)r * P + b] : 0u;
       unf = unf || c4[e] == REGION_UNFILTERED;
-      if (tau_used && b < P) unf = unf || tau_used[(int64_t)r * 256 + b] != t0;
+      if (tau_used && b < P) {
+        const uint32_t t = tau_used[(int64_t)r * 256 + b];
+        if (local_tau)
+          fl = max(fl, t);
+        else
+          unf = unf || t != t0;
+      }
       tot += c4[e];
     }
     if (__ballot(unf) && tid == 0) s_unfiltered = 1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) fl = max(fl, (uint32_t)__shfl_xor((int)fl, o));
+    if (tid == 0) s_floor = fl;
     uint32_t incl = tot;
     incl = wave_incl_scan(incl);
     uint32_t ex = incl - tot;
@@ -522,7 +540,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = valid[e] ? ScoreTraits<Sc>::ord(val[e]) : (K)0;
-  write_top_listed<Sc, E>(key, val, id, valid, (uint32_t)k, io, vo, hist, wsum8, res8, scan1, scan2);
+  // every unlisted entry of a region lies below its threshold; when the kth listed
+  // value reaches the largest threshold no unlisted entry can enter the top k
+  if (!write_top_listed<Sc, E>(key, val, id, valid, (uint32_t)k, io, vo, hist, wsum8, res8, scan1, scan2,
+                               (K)s_floor))
+    select_block<Sc>(scores + (int64_t)r * S, nullptr, n, k, io, vo);
 }
 
 static int mb_chunks(int R, int S) {
@@ -559,7 +581,7 @@ static hipError_t launch_topk_mb(const Sc* scores, const int32_t* nv, int R, int
   topk_thresh_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, tau);
   topk_filter_kernel<Sc><<<dim3(P, R), MB_THREADS, 0, st>>>(scores, nv, S, k, chunk, tau, cval, cid, bcnt);
   topk_finalize_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val,
-                                                      nullptr, nullptr);
+                                                      nullptr, nullptr, false);
   return hipGetLastError();
 }
 
@@ -576,9 +598,10 @@ void topk_mb_layout(void* ws, int R, int S, uint32_t** counters, uint32_t** bcnt
 
 hipError_t launch_topk_finalize_f32(const float* scores, const int32_t* nv, int R, int S, int k, int P, int chunk,
                                     const uint32_t* bcnt, const float* cval, const int32_t* cid, int32_t* idx,
-                                    float* val, uint32_t* reset, const uint32_t* tau_used, hipStream_t st) {
+                                    float* val, uint32_t* reset, const uint32_t* tau_used, hipStream_t st,
+                                    bool local_tau) {
   topk_finalize_kernel<float><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val, reset,
-                                                        tau_used);
+                                                        tau_used, local_tau);
   return hipGetLastError();
 }
 

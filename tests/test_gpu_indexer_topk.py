@@ -135,6 +135,9 @@ def test_decode_select_fused(over, topk, nvs):
     ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     i1, v1 = li.indexer_topk(d["q"], d["w"], d["k"], topk, d["k_scale"], d["nv"], workspace=ws)
     torch.cuda.synchronize()
+    if sp["key"] == "fp8" and 32 < H <= 64:
+        check_local_thresholds(ws, R, S, topk, nv, v1, d, sp, x, i1)
+        return
     # every row with more than k visible keys was listed by the scoring kernel: no
     # region is marked unfiltered (regions [R][P], P of them per row), and the
     # finalize cleared the sample flags (1024 words per row after the top-k's area)
@@ -181,6 +184,74 @@ def test_decode_select_fused(over, topk, nvs):
     assert_topk_band(i1.cpu().numpy(), o, topk, nv, "fused decode select")
 
 
+def ordk(f):
+    """Orderable unsigned image of an fp32 value (larger value, larger image)."""
+    u = int(np.float32(f).view(np.uint32))
+    return (u | 0x80000000) if u < 0x80000000 else (~u & 0xFFFFFFFF)
+
+
+def check_local_thresholds(ws, R, S, topk, nv, v1, d, sp, x, i1):
+    """fp8 keys at 33-64 heads: every scoring workgroup listed its entries above a
+    threshold of its own (per-region counts and thresholds in the workspace), the
+    finalize used the lists (the kth value reaches every threshold) or selected over
+    the whole row; either way the result equals score-then-select bit for bit, on
+    repeated calls, other queries and a workspace of arbitrary bytes."""
+    off = _a256(R * S * 4)
+    bc_at = off + _a256(R * 8)
+    flags_at = bc_at + _a256(R * 256 * 4) + 2 * _a256(R * S * 4)
+    tu_at = flags_at + _a256(R * 1024 * 4)
+    tu = ws[tu_at:tu_at + R * 256 * 4].view(torch.int32).cpu().numpy().view(np.uint32).reshape(R, 256)
+    n = np.full(R, S) if nv is None else np.minimum(nv, S)
+    scores = li.indexer_score(d["q"], d["w"], d["k"], d["k_scale"], d["nv"])
+    i4, v4 = li.topk_select(scores, topk, d["nv"])
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i4) and torch.equal(v1, v4)
+    vals = v1.cpu().numpy()
+    for r in range(R):
+        if n[r] >= 64 * topk:
+            # a long row of unstructured scores: its best keys spread over the
+            # workgroups, so every threshold lies below the kth value and the lists
+            # were used
+            kth = min(ordk(v) for v in vals[r])
+            assert tu[r].max() <= kth, f"row {r}: a region's threshold lies above the kth value"
+    # other queries on the same workspace, then a workspace of arbitrary bytes
+    qr, wr = d["q"].flip(0).contiguous(), d["w"].flip(0).contiguous()
+    i5, v5 = li.indexer_topk(qr, wr, d["k"], topk, d["k_scale"], d["nv"], workspace=ws)
+    s5 = li.indexer_score(qr, wr, d["k"], d["k_scale"], d["nv"])
+    i6, v6 = li.topk_select(s5, topk, d["nv"])
+    ws.fill_(0xA7)
+    i3, v3 = li.indexer_topk(d["q"], d["w"], d["k"], topk, d["k_scale"], d["nv"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(i5, i6) and torch.equal(v5, v6)
+    assert torch.equal(i3, i4) and torch.equal(v3, v4)
+    o = oracle.indexer_score(x["q"], oracle.BF16, x["w"], x["k"], OT[sp["key"]], x["k_scale"], nv)
+    assert_topk_band(i1.cpu().numpy(), o, topk, nv, "fused decode select (local thresholds)")
+
+
+def test_local_thresholds_concentrated_row():
+    """A row whose best keys all sit in one scoring workgroup's range: that
+    workgroup's own threshold lies above the row's kth value, so the lists cannot
+    be trusted and the finalize selects over the whole row; the result stays exact."""
+    print("local thresholds, concentrated row", flush=True)
+    sp = workloads.spec("batched_decode", seed=0x5EED0510, B=4, S=131072)
+    x = workloads.indexer_inputs(sp)
+    ks = x["k_scale"].copy()
+    ks[1, 1000:1800] *= 50.0   # row 1: 800 keys far above the rest, inside one workgroup
+    ks[2, 5000:5100] *= 50.0   # row 2: 100 of them (below k)
+    d = dict(q=dev(x["q"], "bf16"), w=dev(x["w"]), k=dev(x["k"], "fp8"), k_scale=dev(ks))
+    R, S, H, topk = sp["B"], sp["S"], sp["H"], 512
+    ws = torch.zeros(li.indexer_topk_workspace_bytes(li.LI_BF16, li.LI_FP8_E4M3, R, 1, S, H, topk), dtype=torch.uint8,
+                     device="cuda")
+    i1, v1 = li.indexer_topk(d["q"], d["w"], d["k"], topk, d["k_scale"], None, workspace=ws)
+    scores = li.indexer_score(d["q"], d["w"], d["k"], d["k_scale"])
+    i4, v4 = li.topk_select(scores, topk)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i4) and torch.equal(v1, v4)
+    sel = i1.cpu().numpy()
+    assert np.isin(np.arange(1000, 1800), sel[1]).sum() >= 500  # row 1's picks come from the boosted range
+    assert np.isin(np.arange(5000, 5100), sel[2]).all()
+
+
 @pytest.mark.parametrize("bogus", ["all", "none", "mid"])
 def test_decode_select_planted_threshold(bogus):
     """A published threshold word that matches the launch by accident: each fused
@@ -191,10 +262,10 @@ def test_decode_select_planted_threshold(bogus):
     a plausible one (the lists are used).  The result must equal score-then-select
     bit for bit in every case."""
     print("planted threshold", bogus, flush=True)
-    sp = workloads.spec("batched_decode", seed=0x5EED0500, B=8, S=131072)
+    sp = workloads.spec("batched_decode", seed=0x5EED0500, B=8, S=131072, key="bf16")  # the shared-threshold path
     x, d = inputs(sp)
     R, S, H, topk = sp["B"], sp["S"], sp["H"], 512
-    nb = li.indexer_topk_workspace_bytes(li.LI_BF16, li.LI_FP8_E4M3, R, 1, S, H, topk)
+    nb = li.indexer_topk_workspace_bytes(li.LI_BF16, li.LI_BF16, R, 1, S, H, topk)
     ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     li.indexer_topk(d["q"], d["w"], d["k"], topk, d["k_scale"], None, workspace=ws)
     torch.cuda.synchronize()
@@ -204,11 +275,10 @@ def test_decode_select_planted_threshold(bogus):
     pub = ws[pub_at:pub_at + R * 128].view(torch.int64).cpu().numpy().view(np.uint64).reshape(R, 16)[:, 0]
     epoch = int(pub[0] >> np.uint64(32))
     assert epoch != 0
-    scores = li.indexer_score(d["q"], d["w"], d["k"], d["k_scale"])
+    scores = li.indexer_score(d["q"], d["w"], d["k"], None)
     i_ref, v_ref = li.topk_select(scores, topk)
     torch.cuda.synchronize()
     row = scores[1].cpu().numpy()
-    ordk = lambda f: int(np.float32(f).view(np.uint32) | 0x80000000) if f >= 0 else int(~np.float32(f).view(np.uint32) & 0xFFFFFFFF)
     tau = {"all": 1, "none": 0xFFFFFFFF, "mid": ordk(np.sort(row)[-1500])}[bogus]
     word = np.array([((epoch + 1) << 32) | tau], dtype=np.uint64)
     ws[pub_at + 128:pub_at + 136] = torch.from_numpy(word.view(np.uint8)).cuda()  # row 1
