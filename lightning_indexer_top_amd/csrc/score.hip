@@ -246,7 +246,7 @@ __device__ __forceinline__ f32x16 f8_dot(const i32x8 h0, const i32x8 h1, const i
 // selection exact.
 constexpr int SEL_FLAGS = 1024;  // sample flags per row: 256 workgroups x 4 waves
 
-__device__ void score_select_epilogue(const float* __restrict__ out_row, int r, int nvis, int key0, int key_end,
+__device__ __forceinline__ void score_select_epilogue(const float* __restrict__ out_row, int r, int nvis, int key0, int key_end,
                                       int kpb, int k, const uint32_t* __restrict__ counters,
                                       uint32_t* __restrict__ bcnt, float* __restrict__ cval,
                                       int32_t* __restrict__ cid, uint64_t* __restrict__ taupub,
@@ -339,64 +339,90 @@ __device__ void score_select_epilogue(const float* __restrict__ out_row, int r, 
 // Selection epilogue of the held-scores form (few long rows): after [LSA] "What the
 // kernels do about the top-p" (a threshold, then a list of the entries above it),
 // with the threshold taken by each workgroup from its own scores, so no workgroup
-// waits for another.  held: the scores of keys key0 .. key0 + n - 1 in LDS;
-// the workgroup's threshold is the lower edge of the 16-bit key bucket holding its
-// j-th largest score, j = max(ceil(3 k / P), 16) over P workgroups of the row (all
-// n entries when n <= j), and it lists its entries at or above it, in index order,
-// into its region of the candidate list (cval / cid at r S + key0), recording the
-// count (bcnt) and the threshold (tau_used).  A row's top k lies among the lists
-// whenever its kth listed value reaches every region's threshold: the finalize
-// checks that and otherwise selects over the whole row.
+// waits for another.  held: the scores of keys key0 .. key0 + n - 1 in LDS, 16 per
+// thread (entry e * 256 + tid); they also go to out_row from registers here.
+// With j = max(ceil(3 k / P), 16) over the P workgroups of the row, each wave finds
+// the c-th largest of its 64 per-thread maxima, c = ceil(j / 4), by a binary search
+// on the 32-bit ordered key (one compare and one ballot count per bit), and the
+// workgroup's threshold is the smallest of its four waves': every wave holds at
+// least c entries at or above it, so at least j are listed (all of a wave's entries
+// when fewer than c of its threads hold any).  It lists its entries at or above the
+// threshold, in index order, into its region of the candidate list (cval / cid at
+// r S + key0), recording the count (bcnt) and the threshold (tau_used).  A row's
+// top k lies among the lists whenever its kth listed value reaches every region's
+// threshold: the finalize checks that and otherwise selects over the whole row.
+// Both barriers order LDS only, so the score stores stay in flight across them.
 constexpr int HELD_E = 16;  // held scores per thread: at most 4,096 per workgroup
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
-__device__ void held_select_epilogue(const float* held, int n, int r, int key0, int k, uint32_t* __restrict__ bcnt,
-                                     float* __restrict__ cval, int32_t* __restrict__ cid,
-                                     uint32_t* __restrict__ tau_used, int S, uint8_t* scratch) {
-  uint32_t* hist = (uint32_t*)scratch;  // 256 bins
-  uint32_t* wsum = hist + 256;          // 4 waves
-  uint32_t* res = wsum + 4;             // 4
-  uint32_t* cnt = res + 4;              // 16 x 4 counts + total
-  const int P = gridDim.x, bx = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+__device__ __forceinline__ void held_select_epilogue(const float* held_g, int n, int r, int key0, int k,
+                                                     float* __restrict__ out_row, uint32_t* __restrict__ bcnt,
+                                                     float* __restrict__ cval, int32_t* __restrict__ cid,
+                                                     uint32_t* __restrict__ tau_used, int S, uint8_t* scratch) {
+  const lds_f32* held = (const lds_f32*)(uintptr_t)lds_addr(held_g);
+  lds_u32* wt = (lds_u32*)(uintptr_t)lds_addr(scratch);  // 4 wave thresholds
+  lds_u32* cnt = wt + 4;                                   // 4 waves x 16 byte counts
+  const int P = gridDim.x, tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float v[HELD_E];
   uint32_t key[HELD_E];
-  bool valid[HELD_E];
+  uint32_t m = 0u;  // entries past n hold the smallest key, 0
 #pragma unroll
   for (int e = 0; e < HELD_E; ++e) {
     const int i = e * 256 + tid;
-    valid[e] = i < n;
-    key[e] = valid[e] ? ord_f32(held[i]) : 0u;
+    v[e] = held[i];
+    key[e] = i < n ? ord_f32(v[e]) : 0u;
+    m = max(m, key[e]);
   }
-  const uint32_t j = (uint32_t)max((3 * k + P - 1) / P, 16);
-  uint32_t tau = 0u;
-  if ((uint32_t)n > j) tau = block_kth8<256, HELD_E, 2>(key, valid, j, hist, wsum, res);
-  // entries e * 256 + tid: ordering by (e, wave, lane) is index order
-  uint64_t mk[HELD_E];
+  const uint32_t c = ((uint32_t)max((3 * k + P - 1) / P, 16) + 3u) / 4u;
+  uint32_t t = 0u;  // the largest t with at least c maxima >= t
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    if ((uint32_t)__popcll(__ballot(m >= cand)) >= c) t = cand;
+  }
+  if (lane == 0) wt[wid] = t;
 #pragma unroll
   for (int e = 0; e < HELD_E; ++e) {
-    mk[e] = __ballot(valid[e] && key[e] >= tau);
-    if (lane == 0) cnt[e * 4 + wid] = (uint32_t)__popcll(mk[e]);
+    const int i = e * 256 + tid;
+    if (i < n) out_row[key0 + i] = v[e];
   }
-  __syncthreads();
-  if (tid < 64) {
-    const uint32_t c = cnt[tid];
-    const uint32_t incl = wave_incl_scan(c);
-    cnt[tid] = incl - c;
-    if (tid == 63) cnt[64] = incl;
+  lds_barrier();
+  const uint32_t tau = min(min(wt[0], wt[1]), min(wt[2], wt[3]));
+  // entries e * 256 + tid: ordering by (e, wave, lane) is index order.  The wave's
+  // 16 counts (each at most 64) go to LDS as bytes, four to a word, in one write
+  uint64_t mk[HELD_E];
+  uint32_t pk[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < HELD_E; ++e) {
+    mk[e] = __ballot(e * 256 + tid < n && key[e] >= tau);
+    pk[e >> 2] |= (uint32_t)__popcll(mk[e]) << (8 * (e & 3));
   }
-  __syncthreads();
+  if (lane == 0) *(lds_u32x4*)(cnt + 4 * wid) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+  lds_barrier();
+  // lane l takes the count of slot l = 4 e + w (entry slot e of wave w)
+  const int le = lane >> 2, lw = lane & 3;
+  const uint32_t cl = (cnt[4 * lw + (le >> 2)] >> (8 * (le & 3))) & 0xFFu;
+  const uint32_t incl = wave_incl_scan(cl);
+  const uint32_t excl = incl - cl;
   float* ov = cval + (int64_t)r * S + key0;
   int32_t* oi = cid + (int64_t)r * S + key0;
 #pragma unroll
   for (int e = 0; e < HELD_E; ++e) {
+    const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)excl, e * 4 + wid);
     if ((mk[e] >> lane) & 1ull) {
-      const uint32_t pos = cnt[e * 4 + wid] + (uint32_t)__popcll(mk[e] & ((1ull << lane) - 1));
-      const int i = e * 256 + tid;
-      ov[pos] = held[i];
-      oi[pos] = key0 + i;
+      const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[e] >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mk[e], 0u));
+      ov[pos] = v[e];
+      oi[pos] = key0 + e * 256 + tid;
     }
   }
   if (tid == 0) {
-    bcnt[(int64_t)r * P + bx] = cnt[64];
-    tau_used[(int64_t)r * 256 + bx] = tau;
+    bcnt[(int64_t)r * P + blockIdx.x] = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    tau_used[(int64_t)r * 256 + blockIdx.x] = tau;
   }
 }
 
@@ -719,9 +745,12 @@ _Pragma("unroll") \
     __syncthreads();
     const float* held = (const float*)(ring + NST * SSTRIDE);
     const int n = vis_end - key0;
-    for (int i = (int)threadIdx.x; i < n; i += 256) out_row[key0 + i] = held[i];
-    // the ring is free: its LDS holds the selection's histograms and counts
-    if constexpr (LSEL) held_select_epilogue(held, max(n, 0), r, key0, topk, bcnt, cval, cid, tau_used, S, ring);
+    if constexpr (LSEL) {
+      // the ring is free: its LDS holds the selection's thresholds and counts
+      held_select_epilogue(held, max(n, 0), r, key0, topk, out_row, bcnt, cval, cid, tau_used, S, ring);
+    } else {
+      for (int i = (int)threadIdx.x; i < n; i += 256) out_row[key0 + i] = held[i];
+    }
   }
 #undef LI_TILE_PART
 }
