@@ -348,7 +348,8 @@ __device__ __forceinline__ void score_select_epilogue(const float* __restrict__ 
 // least c entries at or above it, so at least j are listed (all of a wave's entries
 // when fewer than c of its threads hold any).  It lists its entries at or above the
 // threshold, in index order, into its region of the candidate list (cval / cid at
-// r S + key0), recording the count (bcnt) and the threshold (tau_used).  A row's
+// r S + key0), recording the count (bcnt), the threshold (tau_used) and, with at
+// most 128 workgroups per row, its largest key (tau_used at 128 + block).  A row's
 // top k lies among the lists whenever its kth listed value reaches every region's
 // threshold: the finalize checks that and otherwise selects over the whole row.
 // Both barriers order LDS only, so the score stores stay in flight across them.
@@ -363,8 +364,8 @@ __device__ __forceinline__ void held_select_epilogue(const float* held_g, int n,
                                                      float* __restrict__ cval, int32_t* __restrict__ cid,
                                                      uint32_t* __restrict__ tau_used, int S, uint8_t* scratch) {
   const lds_f32* held = (const lds_f32*)(uintptr_t)lds_addr(held_g);
-  lds_u32* wt = (lds_u32*)(uintptr_t)lds_addr(scratch);  // 4 wave thresholds
-  lds_u32* cnt = wt + 4;                                   // 4 waves x 16 byte counts
+  lds_u32* wt = (lds_u32*)(uintptr_t)lds_addr(scratch);  // 4 wave thresholds, 4 wave maxima
+  lds_u32* cnt = wt + 8;                                   // 4 waves x 16 byte counts
   const int P = gridDim.x, tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   float v[HELD_E];
@@ -384,7 +385,13 @@ __device__ __forceinline__ void held_select_epilogue(const float* held_g, int n,
     const uint32_t cand = t | (1u << bit);
     if ((uint32_t)__popcll(__ballot(m >= cand)) >= c) t = cand;
   }
-  if (lane == 0) wt[wid] = t;
+  uint32_t mx = m;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  if (lane == 0) {
+    wt[wid] = t;
+    wt[4 + wid] = mx;
+  }
 #pragma unroll
   for (int e = 0; e < HELD_E; ++e) {
     const int i = e * 256 + tid;
@@ -423,6 +430,9 @@ __device__ __forceinline__ void held_select_epilogue(const float* held_g, int n,
   if (tid == 0) {
     bcnt[(int64_t)r * P + blockIdx.x] = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
     tau_used[(int64_t)r * 256 + blockIdx.x] = tau;
+    // the largest key the workgroup holds (it is always listed): the finalize
+    // bounds its search by it
+    if (P <= 128) tau_used[(int64_t)r * 256 + 128 + blockIdx.x] = max(max(wt[4], wt[5]), max(wt[6], wt[7]));
   }
 }
 
@@ -772,6 +782,7 @@ static int num_cus() {
 
 // Keys per workgroup of the staged form (its scores are held in LDS): 16 KB.
 constexpr int STAGE_KEYS = 4096;
+static_assert(STAGE_KEYS == HELD_E * 256, "the held-scores selection covers the whole staged block");
 
 // Keys per workgroup: a multiple of 128 (4 waves x 32 keys) chosen so the grid is
 // about `waves_per_cu` resident waves on every CU, one wave of work each.
@@ -986,10 +997,11 @@ static hipError_t launch_held_select(const uint16_t* qq, const float* w, const u
   typedef StreamCfg<2, true> C;
   auto kern = score_stream_kernel<2, true, C::NST, 2, false, true, PAGED, true>;
   const int kpb = std::min(stream_keys_per_block(R, S, 2), STAGE_KEYS);
-  const size_t lds = stream_lds_bytes<2, true>() + (size_t)kpb * sizeof(float);
+  // the epilogue reads all HELD_E * 256 held slots (those past the block's keys
+  // are masked), so the held area is always allocated whole
+  const size_t lds = stream_lds_bytes<2, true>() + (size_t)HELD_E * 256 * sizeof(float);
   static const bool attr = [&] {
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)(stream_lds_bytes<2, true>() + STAGE_KEYS * sizeof(float)));
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     return true;
   }();
   (void)attr;

@@ -433,17 +433,11 @@ __global__ __launch_bounds__(MB_THREADS) void topk_filter_kernel(const Sc* __res
 // whole-row path.
 
 template <typename Sc>
-__global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __restrict__ scores,
-                                                                  const int32_t* __restrict__ nv, int S, int k,
-                                                                  int P, int chunk,
-                                                                  const uint32_t* __restrict__ bcnt,
-                                                                  const Sc* __restrict__ cval,
-                                                                  const int32_t* __restrict__ cid,
-                                                                  int32_t* __restrict__ idx_out,
-                                                                  Sc* __restrict__ val_out,
-                                                                  uint32_t* __restrict__ reset,
-                                                                  const uint32_t* __restrict__ tau_used,
-                                                                  bool local_tau) {
+__device__ void finalize_lists(int r, const Sc* __restrict__ scores, const int32_t* __restrict__ nv, int S, int k,
+                               int P, int chunk, const uint32_t* __restrict__ bcnt, const Sc* __restrict__ cval,
+                               const int32_t* __restrict__ cid, int32_t* __restrict__ idx_out,
+                               Sc* __restrict__ val_out, uint32_t* __restrict__ reset,
+                               const uint32_t* __restrict__ tau_used, bool local_tau) {
   typedef typename ScoreTraits<Sc>::K K;
   constexpr int NW = TK_THREADS / 64;
   constexpr int E = MB_KEEP / TK_THREADS;
@@ -454,7 +448,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
   __shared__ uint32_t hist[KW_BINS];
   __shared__ uint64_t wsum8[2 * NW];  // minima and maxima of the keys, per wave
   __shared__ uint32_t res8[3];
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   int n = S;
   if (nv) n = min(max(nv[r], 0), S);
   // the sample flags of a fused scoring pass (4 P per row, rows 1024 apart): clear
@@ -547,6 +541,252 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
     select_block<Sc>(scores + (int64_t)r * S, nullptr, n, k, io, vo);
 }
 
+template <typename Sc>
+__global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __restrict__ scores,
+                                                                  const int32_t* __restrict__ nv, int S, int k,
+                                                                  int P, int chunk,
+                                                                  const uint32_t* __restrict__ bcnt,
+                                                                  const Sc* __restrict__ cval,
+                                                                  const int32_t* __restrict__ cid,
+                                                                  int32_t* __restrict__ idx_out,
+                                                                  Sc* __restrict__ val_out,
+                                                                  uint32_t* __restrict__ reset,
+                                                                  const uint32_t* __restrict__ tau_used,
+                                                                  bool local_tau) {
+  finalize_lists<Sc>(blockIdx.x, scores, nv, S, k, P, chunk, bcnt, cval, cid, idx_out, val_out, reset, tau_used,
+                     local_tau);
+}
+
+// The finalize of lists filtered with thresholds of their own (at most LF_MAXP
+// regions): the first M = LF_SLOTS / P entries of every region are loaded in the
+// same round trip as the region counts and thresholds, before either is known
+// (thread t holds slots 4 t .. 4 t + 3; slot s is entry s % M of region s / M, so
+// thread order is index order), and the exact selection runs over them with the
+// entries past each count masked off.  A row with a region that listed more than
+// M entries takes finalize_lists; one whose kth value falls below the largest
+// threshold, or that listed fewer than k, takes the whole row.
+constexpr int LF_MAXP = 64;
+constexpr int LF_E = 4;
+constexpr int LF_SLOTS = LF_E * TK_THREADS;
+
+// The kth largest T (1-based) of the valid keys that are >= lo_key, all of them at
+// most hi_key, by 12-bit digits from the highest bit in which lo_key and hi_key
+// differ; false when fewer than kth valid keys reach lo_key.  *n_above receives
+// how many valid keys exceed T, *ties_all whether every key equal to T is among
+// the kth.  The two histograms alternate between passes (the next one is cleared
+// while the current one is scanned) and every bin keeps the largest key it
+// counted, so a bin holding only the kth key gives it at once: three barriers a
+// pass.  histA (with bmaxA) must be zero on entry.
+template <int NT, int E>
+__device__ __forceinline__ bool block_kth_bounded(const uint32_t (&key)[E], const bool (&valid)[E], uint32_t kth,
+                                                  uint32_t lo_key, uint32_t hi_key, uint32_t* histA,
+                                                  uint32_t* histB, uint32_t* bmaxA, uint32_t* bmaxB,
+                                                  uint32_t* wsum, uint32_t* res, uint32_t* T_out,
+                                                  uint32_t* n_above, bool* ties_all) {
+  constexpr int NW = NT / 64;
+  constexpr int BPT = KW_BINS / NT;
+  static_assert(BPT * NT == KW_BINS, "whole bins per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const uint32_t diff = lo_key ^ hi_key;
+  int hi = diff == 0u ? -1 : 31 - __clz(diff);
+  uint32_t prefix = hi >= 31 ? 0u : (hi_key >> (hi + 1)) << (hi + 1);
+  uint32_t mask = hi >= 31 ? 0u : ~0u << (hi + 1);
+  uint32_t need = kth;
+  bool first = true;
+  for (int pass = 0;; ++pass) {  // uniform
+    uint32_t* hist = (pass & 1) ? histB : histA;
+    uint32_t* bmax = (pass & 1) ? bmaxB : bmaxA;
+    uint32_t* nhist = (pass & 1) ? histA : histB;
+    uint32_t* nbmax = (pass & 1) ? bmaxA : bmaxB;
+    const int lo = hi - KW_BITS + 1 > 0 ? hi - KW_BITS + 1 : 0;
+    const uint32_t dmask = hi >= 0 ? (uint32_t)((1ull << (hi - lo + 1)) - 1ull) : 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (valid[e] && key[e] >= lo_key && (key[e] & mask) == prefix) {
+        const uint32_t d = hi >= 0 ? (key[e] >> lo) & dmask : 0u;
+        atomicAdd(&hist[d], 1u);
+        atomicMax(&bmax[d], key[e]);
+      }
+    }
+    __syncthreads();
+    // thread t holds digits KW_BINS - 1 - BPT t - i, i < BPT (largest first), and
+    // clears its bins of the other histogram for the next pass
+    uint32_t c[BPT], sum = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int b = KW_BINS - 1 - BPT * tid - i;
+      c[i] = hist[b];
+      sum += c[i];
+      nhist[b] = 0u;
+      nbmax[b] = 0u;
+    }
+    const uint32_t v = wave_incl_scan(sum);
+    if (lane == 63) wsum[wid] = v;
+    __syncthreads();
+    uint32_t base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t x = wsum[w];
+      base += w < wid ? x : 0u;
+      total += x;
+    }
+    if (first && total < kth) return false;  // uniform
+    first = false;
+    uint32_t above = base + v - sum;  // keys in larger digits
+    if (above < need && need <= above + sum) {
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) {
+        if (above < need && need <= above + c[i]) {
+          const int b = KW_BINS - 1 - BPT * tid - i;
+          res[0] = (uint32_t)b;
+          res[1] = above;
+          res[2] = c[i];
+          res[3] = bmax[b];
+        }
+        above += c[i];
+      }
+    }
+    __syncthreads();
+    const uint32_t d = res[0], ab = res[1], cd = res[2], bm = res[3];
+    need -= ab;
+    if (hi < 0 || cd == 1u || lo == 0) {
+      // resolved: the bin's only key, or every bit fixed (all cd keys equal T)
+      const uint32_t T = (cd == 1u) ? bm : (prefix | (hi >= 0 ? d << lo : 0u));
+      *T_out = T;
+      *n_above = kth - need;
+      *ties_all = need == cd;
+      return true;
+    }
+    prefix |= d << lo;
+    mask |= dmask << lo;
+    hi = lo - 1;
+  }
+}
+
+__global__ __launch_bounds__(TK_THREADS) void topk_finalize_local_kernel(const float* __restrict__ scores,
+                                                                        const int32_t* __restrict__ nv, int S,
+                                                                        int k, int P, int chunk,
+                                                                        const uint32_t* __restrict__ bcnt,
+                                                                        const float* __restrict__ cval,
+                                                                        const int32_t* __restrict__ cid,
+                                                                        int32_t* __restrict__ idx_out,
+                                                                        float* __restrict__ val_out,
+                                                                        const uint32_t* __restrict__ tau_used) {
+  constexpr int NW = TK_THREADS / 64;
+  __shared__ uint32_t cnt[LF_MAXP];
+  __shared__ uint32_t s_state[4];  // total, floor, overflow, largest key
+  __shared__ uint32_t scan1[NW], scan2[NW];
+  __shared__ uint32_t histA[KW_BINS], histB[KW_BINS], bmaxA[KW_BINS], bmaxB[KW_BINS];
+  __shared__ uint32_t wsum[NW];
+  __shared__ uint32_t res4[4];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  // the first pass's histogram starts at zero
+#pragma unroll
+  for (int i = 0; i < KW_BINS / TK_THREADS; ++i) {
+    histA[tid + TK_THREADS * i] = 0u;
+    bmaxA[tid + TK_THREADS * i] = 0u;
+  }
+  const int M = LF_SLOTS / P;
+  float val[LF_E];
+  int32_t id[LF_E];
+  int rg[LF_E], pos[LF_E];
+  const int64_t rb = (int64_t)r * S;
+#pragma unroll
+  for (int e = 0; e < LF_E; ++e) {
+    const int sl = LF_E * tid + e;
+    rg[e] = sl / M;
+    pos[e] = sl - rg[e] * M;
+    const int64_t at = (int64_t)rg[e] * chunk + pos[e];
+    const bool in = rg[e] < P && at < S;
+    val[e] = in ? cval[rb + at] : 0.0f;
+    id[e] = in ? cid[rb + at] : 0;
+  }
+  int n = S;
+  if (nv) n = min(max(nv[r], 0), S);
+  if (tid < 64) {
+    const uint32_t c = tid < P ? bcnt[(int64_t)r * P + tid] : 0u;
+    uint32_t fl = tid < P ? tau_used[(int64_t)r * 256 + tid] : 0u;
+    uint32_t mk = tid < P ? tau_used[(int64_t)r * 256 + 128 + tid] : 0u;
+    uint32_t tot = c;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      fl = max(fl, (uint32_t)__shfl_xor((int)fl, o));
+      mk = max(mk, (uint32_t)__shfl_xor((int)mk, o));
+      tot += (uint32_t)__shfl_xor((int)tot, o);
+    }
+    const bool over = __ballot(tid < P && c > (uint32_t)M) != 0ull;
+    if (tid < P) cnt[tid] = c;
+    if (tid == 0) {
+      s_state[0] = tot;
+      s_state[1] = fl;
+      s_state[2] = over ? 1u : 0u;
+      s_state[3] = mk;
+    }
+  }
+  __syncthreads();
+  const uint32_t total = s_state[0], floor_key = s_state[1], max_key = s_state[3];
+  int32_t* io = idx_out + (int64_t)r * k;
+  float* vo = val_out ? val_out + (int64_t)r * k : nullptr;
+  if (n <= k || total < (uint32_t)k) {
+    select_block<float>(scores + rb, nullptr, n, k, io, vo);
+    return;
+  }
+  if (s_state[2]) {
+    finalize_lists<float>(r, scores, nv, S, k, P, chunk, bcnt, cval, cid, idx_out, val_out, nullptr, tau_used, true);
+    return;
+  }
+  uint32_t key[LF_E];
+  bool valid[LF_E];
+#pragma unroll
+  for (int e = 0; e < LF_E; ++e) {
+    valid[e] = rg[e] < P && (uint32_t)pos[e] < cnt[min(rg[e], P - 1)];
+    key[e] = valid[e] ? ord_f32(val[e]) : 0u;
+  }
+  // every unlisted entry of a region lies below its threshold, so the top k lies
+  // among the lists exactly when at least k listed keys reach the largest
+  // threshold; T is then the kth of those, and at most max_key
+  uint32_t T, n_above;
+  bool ties_all;
+  if (floor_key > max_key ||
+      !block_kth_bounded<TK_THREADS, LF_E>(key, valid, (uint32_t)k, floor_key, max_key, histA, histB, bmaxA, bmaxB,
+                                           wsum, res4, &T, &n_above, &ties_all)) {
+    select_block<float>(scores + rb, nullptr, n, k, io, vo);
+    return;
+  }
+  // every key above T, and the first (k - n_above) equal to T in list order
+  bool sel[LF_E];
+  uint32_t nsel = 0;
+  if (ties_all) {
+#pragma unroll
+    for (int e = 0; e < LF_E; ++e) {
+      sel[e] = valid[e] && key[e] >= T;
+      nsel += sel[e] ? 1u : 0u;
+    }
+  } else {
+    uint32_t ties = 0;
+#pragma unroll
+    for (int e = 0; e < LF_E; ++e) ties += valid[e] && key[e] == T ? 1u : 0u;
+    uint32_t tr = block_exclusive_scan<NW>(ties, scan1);
+    const uint32_t need = (uint32_t)k - n_above;
+#pragma unroll
+    for (int e = 0; e < LF_E; ++e) {
+      const bool tie = valid[e] && key[e] == T;
+      sel[e] = (valid[e] && key[e] > T) || (tie && tr < need);
+      tr += tie ? 1u : 0u;
+      nsel += sel[e] ? 1u : 0u;
+    }
+  }
+  uint32_t at = block_exclusive_scan<NW>(nsel, scan2);
+#pragma unroll
+  for (int e = 0; e < LF_E; ++e) {
+    if (sel[e]) {
+      io[at] = id[e];
+      if (vo) vo[at] = val[e];
+      ++at;
+    }
+  }
+}
+
 static int mb_chunks(int R, int S) {
   int p = (2048 + R - 1) / R;  // about eight workgroups per CU over the rows
   const int max_p = (S + MB_THREADS * MB_BATCH - 1) / (MB_THREADS * MB_BATCH);
@@ -600,6 +840,11 @@ hipError_t launch_topk_finalize_f32(const float* scores, const int32_t* nv, int 
                                     const uint32_t* bcnt, const float* cval, const int32_t* cid, int32_t* idx,
                                     float* val, uint32_t* reset, const uint32_t* tau_used, hipStream_t st,
                                     bool local_tau) {
+  if (local_tau && tau_used && !reset && P >= 1 && P <= LF_MAXP) {
+    topk_finalize_local_kernel<<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val,
+                                                         tau_used);
+    return hipGetLastError();
+  }
   topk_finalize_kernel<float><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val, reset,
                                                         tau_used, local_tau);
   return hipGetLastError();

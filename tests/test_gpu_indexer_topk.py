@@ -208,12 +208,17 @@ def check_local_thresholds(ws, R, S, topk, nv, v1, d, sp, x, i1):
     assert torch.equal(i1, i4) and torch.equal(v1, v4)
     vals = v1.cpu().numpy()
     for r in range(R):
+        # words 0..127: the regions' thresholds; 128..255: the largest key of each
+        # region (written with at most 128 regions a row), so the largest of them is
+        # the row's best score
+        if n[r] > 0 and tu[r, 128:].any():
+            assert tu[r, 128:].max() == ordk(vals[r].max()), f"row {r}: largest listed key"
         if n[r] >= 64 * topk:
             # a long row of unstructured scores: its best keys spread over the
             # workgroups, so every threshold lies below the kth value and the lists
             # were used
             kth = min(ordk(v) for v in vals[r])
-            assert tu[r].max() <= kth, f"row {r}: a region's threshold lies above the kth value"
+            assert tu[r, :128].max() <= kth, f"row {r}: a region's threshold lies above the kth value"
     # other queries on the same workspace, then a workspace of arbitrary bytes
     qr, wr = d["q"].flip(0).contiguous(), d["w"].flip(0).contiguous()
     i5, v5 = li.indexer_topk(qr, wr, d["k"], topk, d["k_scale"], d["nv"], workspace=ws)
