@@ -154,7 +154,7 @@ li_status li_topk_select(const float *scores, const int32_t *nv, int R, int S, i
  * the scratch keeps the last call's contents, none of which a later call reads
  * before writing.
  */
-#define LI_TOPK_NOALLOC_SCRATCH_BYTES ((size_t)33816576) /* 32 MiB + 256 KiB */
+#define LI_TOPK_NOALLOC_SCRATCH_BYTES ((size_t)34078720) /* 32 MiB + 512 KiB */
 li_status li_topk_select_noalloc(const float *scores, const int32_t *nv, int R, int S, int k, int32_t *idx,
                                  float *val, hipStream_t stream);
 

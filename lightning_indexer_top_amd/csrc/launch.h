@@ -20,7 +20,7 @@ size_t topk_ws_bytes(int R, int S, int k);
 
 // Size of the per-device static scratch of li_topk_select_noalloc, and its device
 // address on the current device (looked up on first use, then kept).
-constexpr size_t NOALLOC_SCRATCH_BYTES = (32u << 20) + (256u << 10);
+constexpr size_t NOALLOC_SCRATCH_BYTES = (32u << 20) + (512u << 10);
 hipError_t noalloc_scratch(void** ptr);
 // whether rows of this shape take the multi-workgroup top-k (few, long rows)
 bool topk_use_mb(int R, int S);

@@ -336,104 +336,30 @@ __device__ __forceinline__ void score_select_epilogue(const float* __restrict__ 
   (void)wid;
 }
 
-// Selection epilogue of the held-scores form (few long rows): after [LSA] "What the
-// kernels do about the top-p" (a threshold, then a list of the entries above it),
-// with the threshold taken by each workgroup from its own scores, so no workgroup
-// waits for another.  held: the scores of keys key0 .. key0 + n - 1 in LDS, 16 per
-// thread (entry e * 256 + tid); they also go to out_row from registers here.
-// With j = max(ceil(3 k / P), 16) over the P workgroups of the row, each wave finds
-// the c-th largest of its 64 per-thread maxima, c = ceil(j / 4), by a binary search
-// on the 32-bit ordered key (one compare and one ballot count per bit), and the
-// workgroup's threshold is the smallest of its four waves': every wave holds at
-// least c entries at or above it, so at least j are listed (all of a wave's entries
-// when fewer than c of its threads hold any).  It lists its entries at or above the
-// threshold, in index order, into its region of the candidate list (cval / cid at
-// r S + key0), recording the count (bcnt), the threshold (tau_used) and, with at
-// most 128 workgroups per row, its largest key (tau_used at 128 + block).  A row's
-// top k lies among the lists whenever its kth listed value reaches every region's
-// threshold: the finalize checks that and otherwise selects over the whole row.
-// Both barriers order LDS only, so the score stores stay in flight across them.
-constexpr int HELD_E = 16;  // held scores per thread: at most 4,096 per workgroup
+// Selection epilogue of the held-scores form (few long rows): the workgroup's
+// scores (keys key0 .. key0 + n - 1, 16 per thread, entry e * 256 + tid) come from
+// LDS into registers, go out to the score row, and are listed above a threshold of
+// the workgroup's own (list_above_local_threshold) into its region of the candidate
+// list (cval / cid at r S + key0), with its count, threshold and largest key.
+constexpr int HELD_E = LT_E;  // held scores per thread: at most 4,096 per workgroup
 typedef __attribute__((address_space(3))) float lds_f32;
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 __device__ __forceinline__ void held_select_epilogue(const float* held_g, int n, int r, int key0, int k,
                                                      float* __restrict__ out_row, uint32_t* __restrict__ bcnt,
                                                      float* __restrict__ cval, int32_t* __restrict__ cid,
                                                      uint32_t* __restrict__ tau_used, int S, uint8_t* scratch) {
   const lds_f32* held = (const lds_f32*)(uintptr_t)lds_addr(held_g);
-  lds_u32* wt = (lds_u32*)(uintptr_t)lds_addr(scratch);  // 4 wave thresholds, 4 wave maxima
-  lds_u32* cnt = wt + 8;                                   // 4 waves x 16 byte counts
-  const int P = gridDim.x, tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = gridDim.x, tid = threadIdx.x;
   float v[HELD_E];
-  uint32_t key[HELD_E];
-  uint32_t m = 0u;  // entries past n hold the smallest key, 0
 #pragma unroll
-  for (int e = 0; e < HELD_E; ++e) {
-    const int i = e * 256 + tid;
-    v[e] = held[i];
-    key[e] = i < n ? ord_f32(v[e]) : 0u;
-    m = max(m, key[e]);
-  }
-  const uint32_t c = ((uint32_t)max((3 * k + P - 1) / P, 16) + 3u) / 4u;
-  uint32_t t = 0u;  // the largest t with at least c maxima >= t
-#pragma unroll
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = t | (1u << bit);
-    if ((uint32_t)__popcll(__ballot(m >= cand)) >= c) t = cand;
-  }
-  uint32_t mx = m;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-  if (lane == 0) {
-    wt[wid] = t;
-    wt[4 + wid] = mx;
-  }
+  for (int e = 0; e < HELD_E; ++e) v[e] = held[e * 256 + tid];
 #pragma unroll
   for (int e = 0; e < HELD_E; ++e) {
     const int i = e * 256 + tid;
     if (i < n) out_row[key0 + i] = v[e];
   }
-  lds_barrier();
-  const uint32_t tau = min(min(wt[0], wt[1]), min(wt[2], wt[3]));
-  // entries e * 256 + tid: ordering by (e, wave, lane) is index order.  The wave's
-  // 16 counts (each at most 64) go to LDS as bytes, four to a word, in one write
-  uint64_t mk[HELD_E];
-  uint32_t pk[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int e = 0; e < HELD_E; ++e) {
-    mk[e] = __ballot(e * 256 + tid < n && key[e] >= tau);
-    pk[e >> 2] |= (uint32_t)__popcll(mk[e]) << (8 * (e & 3));
-  }
-  if (lane == 0) *(lds_u32x4*)(cnt + 4 * wid) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
-  lds_barrier();
-  // lane l takes the count of slot l = 4 e + w (entry slot e of wave w)
-  const int le = lane >> 2, lw = lane & 3;
-  const uint32_t cl = (cnt[4 * lw + (le >> 2)] >> (8 * (le & 3))) & 0xFFu;
-  const uint32_t incl = wave_incl_scan(cl);
-  const uint32_t excl = incl - cl;
-  float* ov = cval + (int64_t)r * S + key0;
-  int32_t* oi = cid + (int64_t)r * S + key0;
-#pragma unroll
-  for (int e = 0; e < HELD_E; ++e) {
-    const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)excl, e * 4 + wid);
-    if ((mk[e] >> lane) & 1ull) {
-      const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[e] >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mk[e], 0u));
-      ov[pos] = v[e];
-      oi[pos] = key0 + e * 256 + tid;
-    }
-  }
-  if (tid == 0) {
-    bcnt[(int64_t)r * P + blockIdx.x] = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-    tau_used[(int64_t)r * 256 + blockIdx.x] = tau;
-    // the largest key the workgroup holds (it is always listed): the finalize
-    // bounds its search by it
-    if (P <= 128) tau_used[(int64_t)r * 256 + 128 + blockIdx.x] = max(max(wt[4], wt[5]), max(wt[6], wt[7]));
-  }
+  list_above_local_threshold(v, n, k, P, (int)blockIdx.x, cval + (int64_t)r * S + key0, cid + (int64_t)r * S + key0,
+                             key0, bcnt + (int64_t)r * P + blockIdx.x, tau_used + (int64_t)r * 256, scratch);
 }
 
 // PAGED: the keys (and scales) of every sequence live in pages of PAGE keys of a

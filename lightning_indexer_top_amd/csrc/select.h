@@ -292,4 +292,90 @@ __device__ __forceinline__ uint32_t sample_rank(int k, int m, int n) {
 // available): the final selection then takes the whole row.
 constexpr uint32_t REGION_UNFILTERED = 0xFFFFFFFFu;
 
+// ---- lists above a threshold of the region's own ------------------------------
+// After [LSA] "What the kernels do about the top-p" (a threshold, then a list of
+// the entries above it), with the threshold taken by each of the P regions of a
+// row from its own scores, so that no workgroup waits for another.  A workgroup of
+// 256 threads holds the n <= 4096 scores of its region, 16 per thread (entry
+// e * 256 + tid in v[e]).  With j = max(ceil(3 k / P), 16), each wave finds the
+// c-th largest of its 64 per-thread maxima, c = ceil(j / 4), by a binary search on
+// the 32-bit ordered key (one compare and one ballot count per bit), and the
+// region's threshold is the smallest of its four waves': every wave holds at least
+// c entries at or above it, so at least j are listed (all of a wave's entries when
+// fewer than c of its threads hold any).  The entries at or above the threshold
+// go to ov / oi (values, ids id0 + entry) in index order; the region records its
+// count (*bc), its threshold (tu_row[region]) and, with at most 128 regions a row,
+// its largest key (tu_row[128 + region]; it is always listed).  A row's top k lies
+// among the lists whenever its kth listed value reaches every region's threshold:
+// the finalize checks that and otherwise selects over the whole row.  scratch:
+// 96 bytes of LDS (16-byte aligned); both barriers order LDS only.
+constexpr int LT_E = 16;  // entries per thread: regions of at most 4,096 scores
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+
+__device__ __forceinline__ void list_above_local_threshold(const float (&v)[LT_E], int n, int k, int P, int region,
+                                                           float* __restrict__ ov, int32_t* __restrict__ oi,
+                                                           int id0, uint32_t* __restrict__ bc,
+                                                           uint32_t* __restrict__ tu_row, void* scratch) {
+  lds_u32* wt = (lds_u32*)(uintptr_t)lds_addr(scratch);  // 4 wave thresholds, 4 wave maxima
+  lds_u32* cnt = wt + 8;                                   // 4 waves x 16 byte counts
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t key[LT_E];
+  uint32_t m = 0u;  // entries past n hold the smallest key, 0
+#pragma unroll
+  for (int e = 0; e < LT_E; ++e) {
+    key[e] = e * 256 + tid < n ? ord_f32(v[e]) : 0u;
+    m = max(m, key[e]);
+  }
+  const uint32_t c = ((uint32_t)max((3 * k + P - 1) / P, 16) + 3u) / 4u;
+  uint32_t t = 0u;  // the largest t with at least c maxima >= t
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    if ((uint32_t)__popcll(__ballot(m >= cand)) >= c) t = cand;
+  }
+  uint32_t mx = m;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  if (lane == 0) {
+    wt[wid] = t;
+    wt[4 + wid] = mx;
+  }
+  lds_barrier();
+  const uint32_t tau = min(min(wt[0], wt[1]), min(wt[2], wt[3]));
+  // entries e * 256 + tid: ordering by (e, wave, lane) is index order.  The wave's
+  // 16 counts (each at most 64) go to LDS as bytes, four to a word, in one write
+  uint64_t mk[LT_E];
+  uint32_t pk[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < LT_E; ++e) {
+    mk[e] = __ballot(e * 256 + tid < n && key[e] >= tau);
+    pk[e >> 2] |= (uint32_t)__popcll(mk[e]) << (8 * (e & 3));
+  }
+  if (lane == 0) *(lds_u32x4*)(cnt + 4 * wid) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+  lds_barrier();
+  // lane l takes the count of slot l = 4 e + w (entry slot e of wave w)
+  const int le = lane >> 2, lw = lane & 3;
+  const uint32_t cl = (cnt[4 * lw + (le >> 2)] >> (8 * (le & 3))) & 0xFFu;
+  const uint32_t incl = wave_incl_scan(cl);
+  const uint32_t excl = incl - cl;
+#pragma unroll
+  for (int e = 0; e < LT_E; ++e) {
+    const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)excl, e * 4 + wid);
+    if ((mk[e] >> lane) & 1ull) {
+      const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[e] >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mk[e], 0u));
+      ov[pos] = v[e];
+      oi[pos] = id0 + e * 256 + tid;
+    }
+  }
+  if (tid == 0) {
+    *bc = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    tu_row[region] = tau;
+    if (P <= 128) tu_row[128 + region] = max(max(wt[4], wt[5]), max(wt[6], wt[7]));
+  }
+}
+
 }  // namespace li

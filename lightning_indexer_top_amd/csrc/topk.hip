@@ -797,9 +797,41 @@ static int mb_chunks(int R, int S) {
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// li_topk_select on few long rows: every workgroup takes a region of TK_LOCAL_CHUNK
+// scores of its row (16 a thread, entry e * 256 + tid, loads all in flight) and
+// lists its entries above a threshold of its own (list_above_local_threshold);
+// the finalize then selects among the lists.
+constexpr int TK_LOCAL_CHUNK = LT_E * 256;
+
+__global__ __launch_bounds__(256) void topk_local_filter_kernel(const float* __restrict__ scores,
+                                                                const int32_t* __restrict__ nv, int S, int k,
+                                                                float* __restrict__ cval, int32_t* __restrict__ cid,
+                                                                uint32_t* __restrict__ bcnt,
+                                                                uint32_t* __restrict__ tau_used) {
+  __shared__ __attribute__((aligned(16))) uint32_t scratch[24];
+  const int r = blockIdx.y, p = blockIdx.x, P = gridDim.x, tid = threadIdx.x;
+  int n_row = S;
+  if (nv) n_row = min(max(nv[r], 0), S);
+  const int lo = p * TK_LOCAL_CHUNK;
+  const int n = max(min(n_row - lo, TK_LOCAL_CHUNK), 0);
+  const float* row = scores + (int64_t)r * S + lo;
+  float v[LT_E];
+#pragma unroll
+  for (int e = 0; e < LT_E; ++e) {
+    const int i = e * 256 + tid;
+    v[e] = i < n ? row[i] : 0.0f;
+  }
+  list_above_local_threshold(v, n, k, P, p, cval + (int64_t)r * S + lo, cid + (int64_t)r * S + lo, lo,
+                             bcnt + (int64_t)r * P + p, tau_used + (int64_t)r * 256, scratch);
+}
+
+// Workspace of the multi-workgroup selection: the row thresholds (the sampled one,
+// or the regions' own: 256 words a row), the region counts (256 words a row), then
+// the candidate values and ids (R x S each).
 template <typename Sc>
 static size_t topk_mb_ws_bytes(int R, int S) {
-  return a256((size_t)R * 8) + a256((size_t)R * 256 * 4) + a256((size_t)R * S * sizeof(Sc)) + a256((size_t)R * S * 4);
+  return a256((size_t)R * 256 * 4) + a256((size_t)R * 256 * 4) + a256((size_t)R * S * sizeof(Sc)) +
+         a256((size_t)R * S * 4);
 }
 
 bool topk_use_mb(int R, int S) { return R < 160 && S >= 16384; }
@@ -810,12 +842,25 @@ static hipError_t launch_topk_mb(const Sc* scores, const int32_t* nv, int R, int
   typedef typename ScoreTraits<Sc>::K K;
   uint8_t* p = (uint8_t*)ws;
   K* tau = (K*)p;
-  p += a256((size_t)R * 8);
+  p += a256((size_t)R * 256 * 4);
   uint32_t* bcnt = (uint32_t*)p;
   p += a256((size_t)R * 256 * 4);
   Sc* cval = (Sc*)p;
   p += a256((size_t)R * S * sizeof(Sc));
   int32_t* cid = (int32_t*)p;
+  if constexpr (sizeof(Sc) == 4) {
+    // regions of LT_E x 256 scores, each listed above a threshold of its own
+    const int Pl = (S + TK_LOCAL_CHUNK - 1) / TK_LOCAL_CHUNK;
+    if (Pl <= 256) {
+      uint32_t* tau_used = (uint32_t*)tau;
+      topk_local_filter_kernel<<<dim3(Pl, R), 256, 0, st>>>((const float*)scores, nv, S, k, (float*)cval, cid, bcnt,
+                                                            tau_used);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_topk_finalize_f32((const float*)scores, nv, R, S, k, Pl, TK_LOCAL_CHUNK, bcnt,
+                                      (const float*)cval, cid, idx, (float*)val, nullptr, tau_used, st, true);
+    }
+  }
   const int P = mb_chunks(R, S);
   const int chunk = (S + P - 1) / P;
   topk_thresh_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, tau);
@@ -827,8 +872,8 @@ static hipError_t launch_topk_mb(const Sc* scores, const int32_t* nv, int R, int
 
 void topk_mb_layout(void* ws, int R, int S, uint32_t** counters, uint32_t** bcnt, float** cval, int32_t** cid) {
   uint8_t* p = (uint8_t*)ws;
-  *counters = (uint32_t*)p;  // the threshold area: 8 bytes per row
-  p += a256((size_t)R * 8);
+  *counters = (uint32_t*)p;  // the threshold area: 256 words per row
+  p += a256((size_t)R * 256 * 4);
   *bcnt = (uint32_t*)p;
   p += a256((size_t)R * 256 * 4);
   *cval = (float*)p;

@@ -142,8 +142,8 @@ def test_decode_select_fused(over, topk, nvs):
     # region is marked unfiltered (regions [R][P], P of them per row), and the
     # finalize cleared the sample flags (1024 words per row after the top-k's area)
     off = _a256(R * S * 4)
-    bcnt = ws[off + _a256(R * 8):off + _a256(R * 8) + R * 256 * 4].view(torch.int32).cpu().numpy()
-    flags_at = off + _a256(R * 8) + _a256(R * 256 * 4) + 2 * _a256(R * S * 4)
+    bcnt = ws[off + _a256(R * 256 * 4):off + _a256(R * 256 * 4) + R * 256 * 4].view(torch.int32).cpu().numpy()
+    flags_at = off + _a256(R * 256 * 4) + _a256(R * 256 * 4) + 2 * _a256(R * S * 4)
     flags = ws[flags_at:flags_at + R * 1024 * 4].view(torch.int32).cpu().numpy()
     n = np.full(R, S) if nv is None else np.minimum(nv, S)
     regions = bcnt[:R * 256]
@@ -166,7 +166,7 @@ def test_decode_select_fused(over, topk, nvs):
     qr, wr = d["q"].flip(0).contiguous(), d["w"].flip(0).contiguous()
     i5, v5 = li.indexer_topk(qr, wr, d["k"], topk, d["k_scale"], d["nv"], workspace=ws)
     torch.cuda.synchronize()
-    assert (ws[off + _a256(R * 8):off + _a256(R * 8) + R * 256 * 4].view(torch.int32).cpu().numpy()[:R * 256] != -1).all()
+    assert (ws[off + _a256(R * 256 * 4):off + _a256(R * 256 * 4) + R * 256 * 4].view(torch.int32).cpu().numpy()[:R * 256] != -1).all()
     s5 = li.indexer_score(qr, wr, d["k"], d["k_scale"], d["nv"])
     i6, v6 = li.topk_select(s5, topk, d["nv"])
     assert torch.equal(i5, i6) and torch.equal(v5, v6)
@@ -197,7 +197,7 @@ def check_local_thresholds(ws, R, S, topk, nv, v1, d, sp, x, i1):
     the whole row; either way the result equals score-then-select bit for bit, on
     repeated calls, other queries and a workspace of arbitrary bytes."""
     off = _a256(R * S * 4)
-    bc_at = off + _a256(R * 8)
+    bc_at = off + _a256(R * 256 * 4)
     flags_at = bc_at + _a256(R * 256 * 4) + 2 * _a256(R * S * 4)
     tu_at = flags_at + _a256(R * 1024 * 4)
     tu = ws[tu_at:tu_at + R * 256 * 4].view(torch.int32).cpu().numpy().view(np.uint32).reshape(R, 256)
@@ -275,7 +275,7 @@ def test_decode_select_planted_threshold(bogus):
     li.indexer_topk(d["q"], d["w"], d["k"], topk, d["k_scale"], None, workspace=ws)
     torch.cuda.synchronize()
     off = _a256(R * S * 4)
-    flags_at = off + _a256(R * 8) + _a256(R * 256 * 4) + 2 * _a256(R * S * 4)
+    flags_at = off + _a256(R * 256 * 4) + _a256(R * 256 * 4) + 2 * _a256(R * S * 4)
     pub_at = flags_at + _a256(R * 1024 * 4) + _a256(R * 256 * 4)
     pub = ws[pub_at:pub_at + R * 128].view(torch.int64).cpu().numpy().view(np.uint64).reshape(R, 16)[:, 0]
     epoch = int(pub[0] >> np.uint64(32))
