@@ -162,19 +162,19 @@ li_status li_topk_select_noalloc(const float *scores, const int32_t *nv, int R, 
  * li_indexer_topk -- li_indexer_score followed by li_topk_select, with the same
  * arguments, without handing the score matrix back: for many query rows (a prefill
  * chunk) the selection runs inside the scoring kernel and the [B*T, S] scores are
- * never written to memory.  For few long rows (decode) the scoring kernel lists
- * each row's candidates above a threshold taken from a sample of its own scores,
- * and one exact pass selects among them.
+ * never written to memory.  For few long rows (decode) every region of a row lists
+ * its entries above a threshold of the region's own ("Latent Sparse Attention",
+ * section "What the kernels do about the top-p": a threshold, then a list of the
+ * entries above it) -- inside the scoring kernel for fp8 keys at 33-64 heads, in
+ * the selection otherwise -- and one exact pass selects among the lists, or over
+ * the whole row when a region's threshold lies above the row's kth value.
  *
  *   idx [B*T, topk] int32, val [B*T, topk] fp32 or NULL (ascending key index)
  *   ws  workspace of at least li_indexer_topk_workspace_bytes(q_type, k_type, B, T,
  *       S, H, topk) bytes: the size of the path this shape and these dtypes take,
- *       0 for the fused many-row path (ws may then be NULL).  The
- *       decode path keeps per-row flags there (after the score and top-k areas),
- *       which every call leaves at zero: a zero-filled workspace is ready for the
- *       first call.  Any other contents give the same results, that call being
- *       slower (its rows wait up to 200 us, then select over the whole row).
- *       Calls that share a workspace must not overlap.
+ *       0 for the fused many-row path (ws may then be NULL), else the scores
+ *       ([B*T, S] fp32) and li_topk_workspace_bytes(B*T, S, topk).  Its contents on
+ *       entry do not matter.  Calls that share a workspace must not overlap.
  *
  * Requires q_type == LI_BF16 and k_type in {LI_BF16, LI_FP8_E4M3}, or the fp32
  * combinations accepted by li_indexer_score.  1 <= topk <= LI_TOPK_MAX.

@@ -366,16 +366,12 @@ bool prefill_fused_apply(int q_type, int k_type, int T, int H, int topk) {
 }
 
 size_t indexer_topk_ws_bytes(int q_type, int k_type, int B, int T, int S, int H, int topk) {
-  // the same predicates, in the same order, as launch_indexer_topk: the fused
-  // prefill kernel needs nothing; decode-shaped rows need the scores, the
-  // multi-workgroup top-k's lists and the selection flags; anything else the
-  // scores and the top-k's own workspace
+  // the same predicate as launch_indexer_topk: the fused prefill kernel needs
+  // nothing; every other path the scores and the top-k's own workspace (the held
+  // decode path lists its candidates into the top-k's regions)
+  (void)H;
   if (use_fused(q_type, k_type, T, H, topk)) return 0;
-  const size_t base = align256((size_t)B * T * S * sizeof(float)) + topk_ws_bytes(B * T, S, topk);
-  if (held_select_apply(q_type, k_type, B * T, S, H, topk) || select_score_apply(q_type, k_type, B * T, S, H, topk))
-    return base + align256((size_t)B * T * 1024 * sizeof(uint32_t)) + align256((size_t)B * T * 256 * sizeof(uint32_t)) +
-           align256((size_t)B * T * 128);
-  return base;
+  return align256((size_t)B * T * S * sizeof(float)) + topk_ws_bytes(B * T, S, topk);
 }
 
 hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const void* k, int k_type, const float* ks,
@@ -400,39 +396,20 @@ hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const 
   void* tws = (uint8_t*)ws + align256((size_t)B * T * S * sizeof(float));
   if (held_select_apply(q_type, k_type, B * T, S, H, topk)) {
     // few long rows, fp8 keys, 33-64 heads: each scoring workgroup lists its own
-    // entries above a threshold of its own, one finalize selects
-    uint32_t *unused, *bcnt;
+    // entries above a threshold of its own (into the top-k's threshold area and
+    // regions), one finalize selects
+    uint32_t *tau_used, *bcnt;
     float* cval;
     int32_t* cid;
-    topk_mb_layout(tws, B * T, S, &unused, &bcnt, &cval, &cid);
-    uint32_t* counters = (uint32_t*)((uint8_t*)tws + topk_ws_bytes(B * T, S, topk));
-    uint32_t* tau_used = counters + align256((size_t)B * T * 1024 * sizeof(uint32_t)) / sizeof(uint32_t);
+    topk_mb_layout(tws, B * T, S, &tau_used, &bcnt, &cval, &cid);
     int P = 0, chunk = 0;
     hipError_t e = launch_score_held_select(q, w, k, ks, nv, B, T, S, H, topk, scores, bcnt, cval, cid, tau_used, &P,
                                             &chunk, st);
     if (e != hipSuccess) return e;
-    return launch_topk_finalize_f32(scores, nv, B * T, S, topk, P, chunk, bcnt, cval, cid, idx, val, nullptr,
-                                    tau_used, st, true);
+    return launch_topk_finalize_f32(scores, nv, B * T, S, topk, P, chunk, bcnt, cval, cid, idx, val, tau_used, st);
   }
-  if (select_score_apply(q_type, k_type, B * T, S, H, topk)) {
-    // few long rows: the scoring kernel lists the candidates, one finalize selects
-    uint32_t *unused, *bcnt;
-    float* cval;
-    int32_t* cid;
-    topk_mb_layout(tws, B * T, S, &unused, &bcnt, &cval, &cid);
-    // after the top-k's area: the sample flags (1024 words per row), the threshold
-    // each region used (256 words per row), the published thresholds (one 128-byte
-    // line per row)
-    uint32_t* counters = (uint32_t*)((uint8_t*)tws + topk_ws_bytes(B * T, S, topk));
-    uint32_t* tau_used = counters + align256((size_t)B * T * 1024 * sizeof(uint32_t)) / sizeof(uint32_t);
-    uint64_t* taupub = (uint64_t*)(tau_used + align256((size_t)B * T * 256 * sizeof(uint32_t)) / sizeof(uint32_t));
-    int P = 0, chunk = 0;
-    hipError_t e = launch_score_select(q, k_type, w, k, ks, nv, B, T, S, H, topk, scores, counters, bcnt, cval, cid,
-                                       taupub, tau_used, &P, &chunk, st);
-    if (e != hipSuccess) return e;
-    return launch_topk_finalize_f32(scores, nv, B * T, S, topk, P, chunk, bcnt, cval, cid, idx, val, counters,
-                                    tau_used, st);
-  }
+  // otherwise score, then select (few long rows: every region of a row lists its
+  // entries above a threshold of its own, as above)
   hipError_t e = launch_score(q, q_type, w, k, k_type, ks, nv, B, T, S, H, scores, st);
   if (e != hipSuccess) return e;
   return launch_topk_f32(scores, nv, B * T, S, topk, idx, val, tws, st);
@@ -440,10 +417,8 @@ hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const 
 
 size_t indexer_topk_paged_ws_bytes(int B, int T, int S, int H, int topk) {
   (void)H;
-  // scores, the top-k's lists and the selection flags (either path fits)
-  return align256((size_t)B * T * S * sizeof(float)) + topk_ws_bytes(B * T, S, topk) +
-         align256((size_t)B * T * 1024 * sizeof(uint32_t)) + align256((size_t)B * T * 256 * sizeof(uint32_t)) +
-         align256((size_t)B * T * 128);
+  // the scores and the top-k's workspace (either path fits)
+  return align256((size_t)B * T * S * sizeof(float)) + topk_ws_bytes(B * T, S, topk);
 }
 
 hipError_t launch_indexer_topk_paged(const uint16_t* q, const float* w, const uint8_t* k_pool, const float* ks_pool,
@@ -454,33 +429,15 @@ hipError_t launch_indexer_topk_paged(const uint16_t* q, const float* w, const ui
   float* scores = (float*)ws;
   void* tws = (uint8_t*)ws + align256((size_t)R * S * sizeof(float));
   if (held_select_apply(DT_BF16, DT_FP8, R, S, H, topk)) {
-    uint32_t *unused, *bcnt;
+    uint32_t *tau_used, *bcnt;
     float* cval;
     int32_t* cid;
-    topk_mb_layout(tws, R, S, &unused, &bcnt, &cval, &cid);
-    uint32_t* counters = (uint32_t*)((uint8_t*)tws + topk_ws_bytes(R, S, topk));
-    uint32_t* tau_used = counters + align256((size_t)R * 1024 * sizeof(uint32_t)) / sizeof(uint32_t);
+    topk_mb_layout(tws, R, S, &tau_used, &bcnt, &cval, &cid);
     int P = 0, chunk = 0;
     hipError_t e = launch_score_held_select(q, w, k_pool, ks_pool, nv, B, T, S, H, topk, scores, bcnt, cval, cid,
                                             tau_used, &P, &chunk, st, page_table, max_pages, num_pages);
     if (e != hipSuccess) return e;
-    return launch_topk_finalize_f32(scores, nv, R, S, topk, P, chunk, bcnt, cval, cid, idx, val, nullptr, tau_used,
-                                    st, true);
-  }
-  if (select_score_apply_paged(R, S, H, topk)) {
-    uint32_t *unused, *bcnt;
-    float* cval;
-    int32_t* cid;
-    topk_mb_layout(tws, R, S, &unused, &bcnt, &cval, &cid);
-    uint32_t* counters = (uint32_t*)((uint8_t*)tws + topk_ws_bytes(R, S, topk));
-    uint32_t* tau_used = counters + align256((size_t)R * 1024 * sizeof(uint32_t)) / sizeof(uint32_t);
-    uint64_t* taupub = (uint64_t*)(tau_used + align256((size_t)R * 256 * sizeof(uint32_t)) / sizeof(uint32_t));
-    int P = 0, chunk = 0;
-    hipError_t e = launch_score_select(q, DT_FP8, w, k_pool, ks_pool, nv, B, T, S, H, topk, scores, counters, bcnt,
-                                       cval, cid, taupub, tau_used, &P, &chunk, st, page_table, max_pages, num_pages);
-    if (e != hipSuccess) return e;
-    return launch_topk_finalize_f32(scores, nv, R, S, topk, P, chunk, bcnt, cval, cid, idx, val, counters, tau_used,
-                                    st);
+    return launch_topk_finalize_f32(scores, nv, R, S, topk, P, chunk, bcnt, cval, cid, idx, val, tau_used, st);
   }
   hipError_t e = launch_score_paged(q, w, k_pool, ks_pool, page_table, max_pages, num_pages, nv, B, T, S, H, scores,
                                     st);

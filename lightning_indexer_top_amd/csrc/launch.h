@@ -61,27 +61,9 @@ bool prefill_scores_apply(int q_type, int k_type, int T, int H);
 hipError_t launch_prefill_scores(const uint16_t* q, const float* w, const uint16_t* k, const int32_t* nv, int B,
                                  int T, int S, int H, float* scores, hipStream_t st);
 
-// Few long rows (decode): the scoring kernel also lists each row's candidates.
-// Its workgroups take the row's threshold from the first 32-key tile of every wave
-// (published with one flag per wave, counters[r * 1024 + wave]) and list their own
-// range's entries at or above it into the multi-workgroup top-k's regions (bcnt /
-// cval / cid, P regions of chunk keys per row); the first to compute a row's
-// threshold publishes it (taupub[16 r], one word per 128-byte line) for the later ones, and
-// every region records the threshold it used (tau_used[r * 256 + p]); the finalize
-// then selects exactly (if all of a row's regions used one threshold) and clears
-// the row's flags (reset).
-// select_score_apply tells whether the shape takes this path.
-bool select_score_apply(int q_type, int k_type, int R, int S, int H, int topk);
-// (page_table non-NULL: fp8 keys in pool pages of 64, see launch_score_paged)
-hipError_t launch_score_select(const void* q, int k_type, const float* w, const void* k, const float* ks,
-                               const int32_t* nv, int B, int T, int S, int H, int topk, float* scores,
-                               uint32_t* counters, uint32_t* bcnt, float* cval, int32_t* cid, uint64_t* taupub,
-                               uint32_t* tau_used, int* P, int* chunk, hipStream_t st,
-                               const int32_t* page_table = nullptr, int max_pages = 0, int num_pages = 0);
-bool select_score_apply_paged(int R, int S, int H, int topk);
 // Few long rows, fp8 keys, 33-64 heads: the held-scores kernel lists each
 // workgroup's entries above a threshold of its own (no waiting), the finalize
-// (local_tau) selects exactly or over the whole row.
+// selects exactly or over the whole row.
 bool held_select_apply(int q_type, int k_type, int R, int S, int H, int topk);
 hipError_t launch_score_held_select(const void* q, const float* w, const void* k, const float* ks, const int32_t* nv,
                                     int B, int T, int S, int H, int topk, float* scores, uint32_t* bcnt, float* cval,
@@ -102,11 +84,14 @@ hipError_t launch_indexer_topk_paged(const uint16_t* q, const float* w, const ui
 hipError_t launch_attn_paged(const uint16_t* q, const uint16_t* kv_pool, const int32_t* slot_table, int max_slots,
                              int num_slots, const int32_t* idx, int B, int Hq, int S, int k, float sm_scale,
                              uint16_t* out, float* lse, hipStream_t st);
-void topk_mb_layout(void* ws, int R, int S, uint32_t** counters, uint32_t** bcnt, float** cval, int32_t** cid);
+void topk_mb_layout(void* ws, int R, int S, uint32_t** thresholds, uint32_t** bcnt, float** cval, int32_t** cid);
+// The exact selection over per-region candidate lists (regions of `chunk` keys, P
+// per row, counts bcnt [R, P]); tau_used: the thresholds each region listed above
+// ([R, 256]: P thresholds, then with P <= 128 the regions' largest keys at 128),
+// or NULL when every region used one threshold that at least k entries cleared.
 hipError_t launch_topk_finalize_f32(const float* scores, const int32_t* nv, int R, int S, int k, int P, int chunk,
                                     const uint32_t* bcnt, const float* cval, const int32_t* cid, int32_t* idx,
-                                    float* val, uint32_t* reset, const uint32_t* tau_used, hipStream_t st,
-                                    bool local_tau = false);
+                                    float* val, const uint32_t* tau_used, hipStream_t st);
 
 // fused scoring + selection for many query rows (prefill); falls back to
 // score-then-select where the fused kernel does not apply

@@ -233,109 +233,6 @@ __device__ __forceinline__ f32x16 f8_dot(const i32x8 h0, const i32x8 h1, const i
   return c;
 }
 
-// Selection epilogue of the scoring kernel (decode rows, see select_score_apply):
-// after every wave of the workgroup has stored its scores, the row's threshold is
-// the j-th largest of the samples (sample_rank) and the workgroup lists its own
-// visible range's entries at or above it into its region of the candidate list.
-// Samples: the first 32-key tile of the row's waves (every stride-th wave when
-// there are more than 128 of them), stored device-coherent by their waves, which
-// raise their own flag (counters[r * SEL_FLAGS + wave of the row]) right after that
-// tile; the threshold is taken once all P * 4 flags of the row are up (waiting for
-// that, boundedly), else the region is marked unfiltered.
-// Whatever the threshold, the finalize's check (at least k listed) keeps the
-// selection exact.
-constexpr int SEL_FLAGS = 1024;  // sample flags per row: 256 workgroups x 4 waves
-
-__device__ __forceinline__ void score_select_epilogue(const float* __restrict__ out_row, int r, int nvis, int key0, int key_end,
-                                      int kpb, int k, const uint32_t* __restrict__ counters,
-                                      uint32_t* __restrict__ bcnt, float* __restrict__ cval,
-                                      int32_t* __restrict__ cid, uint64_t* __restrict__ taupub,
-                                      uint32_t* __restrict__ tau_used, uint32_t epoch, int S, uint8_t* lds) {
-  constexpr int SE = 16;  // samples per thread: at most 4,096
-  uint32_t* hist = (uint32_t*)lds;  // 256 bins
-  uint32_t* wsum = hist + 256;      // 4 waves
-  uint32_t* res = wsum + 4;         // 2
-  uint32_t* cnt_uw = res + 4;       // MB_BATCH * 4 + 1
-  uint32_t* s_flag = cnt_uw + 72;   // -, sample count, published-threshold found, its value
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int P = gridDim.x, bx = blockIdx.x;
-  uint32_t* bc = bcnt + (int64_t)r * P + bx;
-  if (nvis <= k) {  // the final pass takes the whole row
-    if (tid == 0) *bc = 0u;
-    return;
-  }
-  const int W = P * 4;  // waves of the row, one flag each
-  // The row's threshold, if a workgroup of this launch has already published it:
-  // one 64-bit word, epoch << 32 | threshold, stored without any ordering, alone
-  // in a 128-byte line per row (device-coherent accesses to one line shared by
-  // the rows queue behind each other).  A word from another launch carries
-  // another epoch.  Every region records the threshold
-  // it filtered with, and the final pass uses the lists only if all of a row's
-  // regions agree, so even a word that matched by accident could not change a
-  // result.
-  if (tid == 0) {
-    const uint64_t pv = __hip_atomic_load(&taupub[r * 16], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_flag[2] = (uint32_t)(pv >> 32) == epoch ? 1u : 0u;
-    s_flag[3] = (uint32_t)pv;
-  }
-  __syncthreads();
-  uint32_t tau = s_flag[3];
-  if (s_flag[2] == 0u) {
-  // Workgroups of a fast XCD can finish before a slow one's waves have stored their
-  // sample; every workgroup of the launch is resident (one per slot), so waiting a
-  // little costs nothing on the critical path.  The wait is bounded by the realtime
-  // clock (100 MHz), after which the region goes unfiltered.
-  const uint32_t* fl = counters + (int64_t)r * SEL_FLAGS;
-  const uint64_t give_up = __builtin_amdgcn_s_memrealtime() + 20000;  // 200 us
-  bool all_set = false;
-  for (;;) {
-    bool mine_set = true;
-    for (int i = tid; i < W; i += 256)
-      mine_set = mine_set && __hip_atomic_load(&fl[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1u;
-    const bool expired = tid == 0 && __builtin_amdgcn_s_memrealtime() >= give_up;
-    all_set = __syncthreads_and(mine_set);
-    // both decisions are workgroup-wide votes, so every wave leaves together
-    if (all_set || __syncthreads_or(expired)) break;
-    __builtin_amdgcn_s_sleep(127);  // about 3 us between polls
-  }
-  if (tid == 0) s_flag[1] = 0;
-  __syncthreads();
-  if (!all_set) {
-    if (tid == 0) *bc = REGION_UNFILTERED;
-    return;
-  }
-  const int stride = (W + 127) / 128;  // at most 128 sampled wave tiles
-  uint32_t key[SE];
-  bool valid[SE];
-  uint32_t mine = 0;
-#pragma unroll
-  for (int e = 0; e < SE; ++e) {
-    const int s = e * 256 + tid;
-    const int wt = (s >> 5) * stride, bx2 = wt >> 2;
-    const int kk = bx2 * kpb + 32 * (wt & 3) + (s & 31);
-    valid[e] = wt < W && kk < min(bx2 * kpb + kpb, nvis);
-    const float x = __hip_atomic_load(&out_row[valid[e] ? kk : 0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    key[e] = valid[e] ? ord_f32(x) : 0u;
-    mine += valid[e] ? 1u : 0u;
-  }
-  mine = wave_incl_scan(mine);
-  if (lane == 63) atomicAdd(&s_flag[1], mine);
-  __syncthreads();
-  const int m = (int)s_flag[1];
-  tau = block_kth8<256, SE, 2>(key, valid, sample_rank(k, m, nvis), hist, wsum, res);
-  if (tid == 0)
-    __hip_atomic_store(&taupub[r * 16], ((uint64_t)epoch << 32) | tau, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (tid == 0) tau_used[(int64_t)r * 256 + bx] = tau;
-  const int vis_end = min(key_end, nvis);
-  const uint32_t written = key0 < vis_end ? filter_region<float>(out_row, key0, vis_end, tau,
-                                                                  cval + (int64_t)r * S + key0,
-                                                                  cid + (int64_t)r * S + key0, cnt_uw)
-                                          : 0u;
-  if (tid == 0) *bc = written;
-  (void)wid;
-}
-
 // Selection epilogue of the held-scores form (few long rows): the workgroup's
 // scores (keys key0 .. key0 + n - 1, 16 per thread, entry e * 256 + tid) come from
 // LDS into registers, go out to the score row, and are listed above a threshold of
@@ -373,21 +270,20 @@ __device__ __forceinline__ void held_select_epilogue(const float* held_g, int n,
 constexpr int PAGE = 64;
 constexpr int PAGED_MAX_KPB = 64 * PAGE;
 
-template <int HT, bool FP8, int NST, int WPE, bool SEL, bool STG = false, bool PAGED = false, bool LSEL = false>
+template <int HT, bool FP8, int NST, int WPE, bool STG = false, bool PAGED = false, bool LSEL = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 void score_stream_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ k,
                          const float* __restrict__ ks, const int32_t* __restrict__ nv, int T, int S, int H,
-                         int keys_per_block, float* __restrict__ scores, int topk, uint32_t* __restrict__ counters,
-                         uint32_t* __restrict__ bcnt, float* __restrict__ cval, int32_t* __restrict__ cid,
-                         uint64_t* __restrict__ taupub, uint32_t* __restrict__ tau_used, uint32_t epoch,
+                         int keys_per_block, float* __restrict__ scores, int topk, uint32_t* __restrict__ bcnt,
+                         float* __restrict__ cval, int32_t* __restrict__ cid, uint32_t* __restrict__ tau_used,
                          const int32_t* __restrict__ page_table, int max_pages, int num_pages) {
   static_assert(!PAGED || FP8, "paged keys are fp8");
-  static_assert(!LSEL || (STG && !SEL), "the local selection runs on the held scores");
+  static_assert(!LSEL || STG, "the local selection runs on the held scores");
   typedef TileGeom<FP8> G;
   static_assert(NST >= 1 && NST <= 3, "ring depth");
   // STG: the workgroup's scores are held in LDS behind the ring and written in one
   // pass at the end (keys_per_block floats of dynamic LDS)
-  constexpr bool STAGE = STG && !SEL;
+  constexpr bool STAGE = STG;
   // fp8: the query codes occupy the last SPL ring stages until every wave has
   // read its operands; those stages are filled after that
   constexpr int SPL = FP8 ? (QSplit<HT>::BYTES + 4 * G::BYTES - 1) / (4 * G::BYTES) : 0;
@@ -644,32 +540,11 @@ _Pragma("unroll") \
     LI_TILE_PART();
     if (hf == 0 && key < key_end) {
       const float v = key < nvis ? part * sc : -INFINITY;
-      if (SEL && iter == 1)  // the wave's sample tile: stored device-coherent
-        __hip_atomic_store(&out_row[key], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else if (STAGE)  // written out to LDS (no compiler-visible LDS access beside the ring's loads)
+      if (STAGE)  // written out to LDS (no compiler-visible LDS access beside the ring's loads)
         asm volatile("ds_write_b32 %0, %1" : : "v"(stage0 + 4u * (uint32_t)(key - key0)), "v"(v) : "memory");
       else
         out_row[key] = v;
     }
-    if (SEL && iter == 1) {
-      // publish the sample at once: wait for the store (and the loads before it;
-      // every tile later waited for is issued after this point, so the counts
-      // above stay exact), then raise the wave's own flag (a word of its own: no
-      // two waves write one address)
-      LI_WAIT_VMCNT(0);
-      if (lane == 0)
-        __hip_atomic_store(&counters[(int64_t)r * SEL_FLAGS + blockIdx.x * 4 + wave], 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  if constexpr (SEL) {
-    if (iter == 0 && lane == 0)  // no tile: flagged without a sample
-      __hip_atomic_store(&counters[(int64_t)r * SEL_FLAGS + blockIdx.x * 4 + wave], 1u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    LI_WAIT_VMCNT(0);
-    __syncthreads();
-    score_select_epilogue(out_row, r, nvis, key0, key_end, keys_per_block, topk, counters, bcnt, cval, cid, taupub,
-                          tau_used, epoch, S, lds);
   }
   if constexpr (STAGE) {
     // every load has landed; the held scores of keys key0 .. vis_end - 1 go out in
@@ -791,7 +666,7 @@ static hipError_t launch_stream(const uint16_t* qq, const float* w, const uint8_
                                 const int32_t* nv, int R, int T, int S, int H, float* scores,
                                 const int32_t* page_table, int max_pages, int num_pages, hipStream_t st) {
   typedef StreamCfg<HT, F8> C;
-  auto kern = score_stream_kernel<HT, F8, C::NST, STG ? 2 : C::WPE, false, STG, PAGED>;
+  auto kern = score_stream_kernel<HT, F8, C::NST, STG ? 2 : C::WPE, STG, PAGED>;
   int kpb = stream_keys_per_block(R, S, STG ? 2 : C::BPC);
   if (STG) kpb = std::min(kpb, STAGE_KEYS);
   if (PAGED) kpb = std::min(kpb, PAGED_MAX_KPB);
@@ -804,7 +679,7 @@ static hipError_t launch_stream(const uint16_t* qq, const float* w, const uint8_
   (void)attr;
   dim3 grid((S + kpb - 1) / kpb, R);
   kern<<<grid, 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, 0, nullptr, nullptr, nullptr, nullptr,
-                               nullptr, nullptr, 0u, page_table, max_pages, num_pages);
+                               page_table, max_pages, num_pages);
   return hipGetLastError();
 }
 
@@ -871,39 +746,6 @@ hipError_t launch_score(const void* q, int q_type, const float* w, const void* k
   return hipGetLastError();
 }
 
-// ---- scoring with the selection epilogue (few long rows) ----------------------
-template <int HT, bool F8>
-static int select_blocks_per_row(int R, int S, bool paged, int* kpb_out) {
-  int kpb = stream_keys_per_block(R, S, StreamCfg<HT, F8>::BPC);
-  if (paged) kpb = std::min(kpb, PAGED_MAX_KPB);
-  if (kpb_out) *kpb_out = kpb;
-  return (S + kpb - 1) / kpb;
-}
-
-static bool select_score_shape(int k_type, int R, int S, int H, int topk, bool paged) {
-  if ((k_type != DT_FP8 && k_type != DT_BF16) || H < 1 || H > 128) return false;
-  if (!topk_use_mb(R, S) || topk > 2048) return false;
-  // the finalize takes at most 256 regions per row,
-  const bool f8 = k_type == DT_FP8;
-  // and every wave streams at least eight tiles, so that the row's samples (each
-  // wave's first tile) are counted long before its workgroups finish
-  int P, kpb;
-  if (H <= 32) P = f8 ? select_blocks_per_row<1, true>(R, S, paged, &kpb) : select_blocks_per_row<1, false>(R, S, paged, &kpb);
-  else if (H <= 64) P = f8 ? select_blocks_per_row<2, true>(R, S, paged, &kpb) : select_blocks_per_row<2, false>(R, S, paged, &kpb);
-  else P = f8 ? select_blocks_per_row<4, true>(R, S, paged, &kpb) : select_blocks_per_row<4, false>(R, S, paged, &kpb);
-  // and all workgroups of the launch are resident at once (the epilogue may wait
-  // for the row's other workgroups to count their samples)
-  const int bpc = H <= 32 ? StreamCfg<1, true>::BPC : (H <= 64 ? StreamCfg<2, true>::BPC : StreamCfg<4, true>::BPC);
-  const int bpc_b = H <= 32 ? StreamCfg<1, false>::BPC : (H <= 64 ? StreamCfg<2, false>::BPC : StreamCfg<4, false>::BPC);
-  return P <= 256 && kpb >= 1024 && (int64_t)P * R <= (int64_t)num_cus() * (f8 ? bpc : bpc_b);
-}
-
-bool select_score_apply(int q_type, int k_type, int R, int S, int H, int topk) {
-  return q_type == DT_BF16 && select_score_shape(k_type, R, S, H, topk, false);
-}
-
-bool select_score_apply_paged(int R, int S, int H, int topk) { return select_score_shape(DT_FP8, R, S, H, topk, true); }
-
 // Few long rows with fp8 keys and 33-64 heads: the held-scores kernel with the
 // workgroup-local selection epilogue, then the finalize.
 bool held_select_apply(int q_type, int k_type, int R, int S, int H, int topk) {
@@ -921,7 +763,7 @@ static hipError_t launch_held_select(const uint16_t* qq, const float* w, const u
                                      int* chunk_out, const int32_t* page_table, int max_pages, int num_pages,
                                      hipStream_t st) {
   typedef StreamCfg<2, true> C;
-  auto kern = score_stream_kernel<2, true, C::NST, 2, false, true, PAGED, true>;
+  auto kern = score_stream_kernel<2, true, C::NST, 2, true, PAGED, true>;
   const int kpb = std::min(stream_keys_per_block(R, S, 2), STAGE_KEYS);
   // the epilogue reads all HELD_E * 256 held slots (those past the block's keys
   // are masked), so the held area is always allocated whole
@@ -934,8 +776,8 @@ static hipError_t launch_held_select(const uint16_t* qq, const float* w, const u
   const int P = (S + kpb - 1) / kpb;
   *P_out = P;
   *chunk_out = kpb;
-  kern<<<dim3(P, R), 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, topk, nullptr, bcnt, cval, cid, nullptr,
-                                     tau_used, 0u, page_table, max_pages, num_pages);
+  kern<<<dim3(P, R), 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, topk, bcnt, cval, cid, tau_used,
+                                     page_table, max_pages, num_pages);
   return hipGetLastError();
 }
 
@@ -951,56 +793,5 @@ hipError_t launch_score_held_select(const void* q, const float* w, const void* k
                                    bcnt, cval, cid, tau_used, P_out, chunk_out, nullptr, 0, 0, st);
 }
 
-// launch epochs of the selection kernel: a published threshold carries the epoch of
-// the launch that computed it
-static uint32_t next_select_epoch() {
-  static std::atomic<uint32_t> e{0};
-  uint32_t v = e.fetch_add(1u, std::memory_order_relaxed) + 1u;
-  if (v == 0u) v = e.fetch_add(1u, std::memory_order_relaxed) + 1u;
-  return v;
-}
-
-hipError_t launch_score_select(const void* q, int k_type, const float* w, const void* k, const float* ks,
-                               const int32_t* nv, int B, int T, int S, int H, int topk, float* scores,
-                               uint32_t* counters, uint32_t* bcnt, float* cval, int32_t* cid, uint64_t* taupub,
-                               uint32_t* tau_used, int* P_out, int* chunk_out, hipStream_t st,
-                               const int32_t* page_table, int max_pages, int num_pages) {
-  const int R = B * T;
-  const uint32_t epoch = next_select_epoch();
-  const bool f8 = k_type == DT_FP8;
-  const bool paged = page_table != nullptr;
-  const uint16_t* qq = (const uint16_t*)q;
-  const uint8_t* kk = (const uint8_t*)k;
-#define LI_LAUNCH_SELECT(HT_, F8_, PG_)                                                                             \
-  do {                                                                                                              \
-    typedef StreamCfg<HT_, F8_> C;                                                                                  \
-    auto kern = score_stream_kernel<HT_, F8_, C::NST, C::WPE, true, false, PG_>;                                   \
-    const size_t lds = stream_lds_bytes<HT_, F8_>();                                                                \
-    int kpb;                                                                                                        \
-    const int P = select_blocks_per_row<HT_, F8_>(R, S, PG_, &kpb);                                                 \
-    static const bool attr = [&] {                                                                                  \
-      (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);          \
-      return true;                                                                                                  \
-    }();                                                                                                            \
-    (void)attr;                                                                                                     \
-    *P_out = P;                                                                                                     \
-    *chunk_out = kpb;                                                                                               \
-    kern<<<dim3(P, R), 256, lds, st>>>(qq, w, kk, ks, nv, T, S, H, kpb, scores, topk, counters, bcnt, cval, cid,    \
-                                       taupub, tau_used, epoch, page_table, max_pages, num_pages);                  \
-  } while (0)
-  if (paged) {
-    if (H <= 32) LI_LAUNCH_SELECT(1, true, true);
-    else if (H <= 64) LI_LAUNCH_SELECT(2, true, true);
-    else LI_LAUNCH_SELECT(4, true, true);
-  } else if (H <= 32) {
-    if (f8) LI_LAUNCH_SELECT(1, true, false); else LI_LAUNCH_SELECT(1, false, false);
-  } else if (H <= 64) {
-    if (f8) LI_LAUNCH_SELECT(2, true, false); else LI_LAUNCH_SELECT(2, false, false);
-  } else {
-    if (f8) LI_LAUNCH_SELECT(4, true, false); else LI_LAUNCH_SELECT(4, false, false);
-  }
-#undef LI_LAUNCH_SELECT
-  return hipGetLastError();
-}
 
 }  // namespace li

@@ -436,8 +436,7 @@ template <typename Sc>
 __device__ void finalize_lists(int r, const Sc* __restrict__ scores, const int32_t* __restrict__ nv, int S, int k,
                                int P, int chunk, const uint32_t* __restrict__ bcnt, const Sc* __restrict__ cval,
                                const int32_t* __restrict__ cid, int32_t* __restrict__ idx_out,
-                               Sc* __restrict__ val_out, uint32_t* __restrict__ reset,
-                               const uint32_t* __restrict__ tau_used, bool local_tau) {
+                               Sc* __restrict__ val_out, const uint32_t* __restrict__ tau_used) {
   typedef typename ScoreTraits<Sc>::K K;
   constexpr int NW = TK_THREADS / 64;
   constexpr int E = MB_KEEP / TK_THREADS;
@@ -451,33 +450,21 @@ __device__ void finalize_lists(int r, const Sc* __restrict__ scores, const int32
   const int tid = threadIdx.x;
   int n = S;
   if (nv) n = min(max(nv[r], 0), S);
-  // the sample flags of a fused scoring pass (4 P per row, rows 1024 apart): clear
-  // for the next one
-  if (reset)
-    for (int i = tid; i < 4 * P; i += TK_THREADS) reset[(int64_t)r * 1024 + i] = 0u;
   if (tid == 0) s_unfiltered = 0;
   __syncthreads();
   // exclusive prefix of the region counts (P <= 256): one wave, four per lane.  A
-  // region left unfiltered, or regions filtered with different thresholds (where
-  // they record theirs and should share one), make the lists unusable.  Regions
-  // that filtered with thresholds of their own (local_tau) leave the largest of
-  // them as the floor the selected kth value must reach.
+  // region left unfiltered makes the lists unusable.  Regions that filtered with
+  // thresholds of their own (tau_used) leave the largest of them as the floor the
+  // selected kth value must reach.
   if (tid < 64) {
     uint32_t c4[4], tot = 0, fl = 0;
     bool unf = false;
-    const uint32_t t0 = tau_used ? tau_used[(int64_t)r * 256] : 0u;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int b = 4 * tid + e;
       c4[e] = b < P ? bcnt[(int64_t)r * P + b] : 0u;
       unf = unf || c4[e] == REGION_UNFILTERED;
-      if (tau_used && b < P) {
-        const uint32_t t = tau_used[(int64_t)r * 256 + b];
-        if (local_tau)
-          fl = max(fl, t);
-        else
-          unf = unf || t != t0;
-      }
+      if (tau_used && b < P) fl = max(fl, tau_used[(int64_t)r * 256 + b]);
       tot += c4[e];
     }
     if (__ballot(unf) && tid == 0) s_unfiltered = 1;
@@ -550,11 +537,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_kernel(const Sc* __r
                                                                   const int32_t* __restrict__ cid,
                                                                   int32_t* __restrict__ idx_out,
                                                                   Sc* __restrict__ val_out,
-                                                                  uint32_t* __restrict__ reset,
-                                                                  const uint32_t* __restrict__ tau_used,
-                                                                  bool local_tau) {
-  finalize_lists<Sc>(blockIdx.x, scores, nv, S, k, P, chunk, bcnt, cval, cid, idx_out, val_out, reset, tau_used,
-                     local_tau);
+                                                                  const uint32_t* __restrict__ tau_used) {
+  finalize_lists<Sc>(blockIdx.x, scores, nv, S, k, P, chunk, bcnt, cval, cid, idx_out, val_out, tau_used);
 }
 
 // The finalize of lists filtered with thresholds of their own (at most LF_MAXP
@@ -732,7 +716,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_finalize_local_kernel(const f
     return;
   }
   if (s_state[2]) {
-    finalize_lists<float>(r, scores, nv, S, k, P, chunk, bcnt, cval, cid, idx_out, val_out, nullptr, tau_used, true);
+    finalize_lists<float>(r, scores, nv, S, k, P, chunk, bcnt, cval, cid, idx_out, val_out, tau_used);
     return;
   }
   uint32_t key[LF_E];
@@ -858,7 +842,7 @@ static hipError_t launch_topk_mb(const Sc* scores, const int32_t* nv, int R, int
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       return launch_topk_finalize_f32((const float*)scores, nv, R, S, k, Pl, TK_LOCAL_CHUNK, bcnt,
-                                      (const float*)cval, cid, idx, (float*)val, nullptr, tau_used, st, true);
+                                      (const float*)cval, cid, idx, (float*)val, tau_used, st);
     }
   }
   const int P = mb_chunks(R, S);
@@ -866,13 +850,13 @@ static hipError_t launch_topk_mb(const Sc* scores, const int32_t* nv, int R, int
   topk_thresh_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, tau);
   topk_filter_kernel<Sc><<<dim3(P, R), MB_THREADS, 0, st>>>(scores, nv, S, k, chunk, tau, cval, cid, bcnt);
   topk_finalize_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val,
-                                                      nullptr, nullptr, false);
+                                                      nullptr);
   return hipGetLastError();
 }
 
-void topk_mb_layout(void* ws, int R, int S, uint32_t** counters, uint32_t** bcnt, float** cval, int32_t** cid) {
+void topk_mb_layout(void* ws, int R, int S, uint32_t** thresholds, uint32_t** bcnt, float** cval, int32_t** cid) {
   uint8_t* p = (uint8_t*)ws;
-  *counters = (uint32_t*)p;  // the threshold area: 256 words per row
+  *thresholds = (uint32_t*)p;  // the threshold area: 256 words per row
   p += a256((size_t)R * 256 * 4);
   *bcnt = (uint32_t*)p;
   p += a256((size_t)R * 256 * 4);
@@ -883,15 +867,14 @@ void topk_mb_layout(void* ws, int R, int S, uint32_t** counters, uint32_t** bcnt
 
 hipError_t launch_topk_finalize_f32(const float* scores, const int32_t* nv, int R, int S, int k, int P, int chunk,
                                     const uint32_t* bcnt, const float* cval, const int32_t* cid, int32_t* idx,
-                                    float* val, uint32_t* reset, const uint32_t* tau_used, hipStream_t st,
-                                    bool local_tau) {
-  if (local_tau && tau_used && !reset && P >= 1 && P <= LF_MAXP) {
+                                    float* val, const uint32_t* tau_used, hipStream_t st) {
+  if (tau_used && P >= 1 && P <= LF_MAXP) {
     topk_finalize_local_kernel<<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val,
                                                          tau_used);
     return hipGetLastError();
   }
-  topk_finalize_kernel<float><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val, reset,
-                                                        tau_used, local_tau);
+  topk_finalize_kernel<float><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, chunk, bcnt, cval, cid, idx, val,
+                                                        tau_used);
   return hipGetLastError();
 }
 

@@ -101,8 +101,10 @@ def test_indexer_topk_workspace_follows_the_path():
     # top-k's own workspace
     n = ws(li.LI_BF16, li.LI_FP8_E4M3, 1, 16, 1000, 64, 16)
     assert n >= 16 * 1000 * 4 + L.li_topk_workspace_bytes(16, 1000, 16)
-    # decode rows: scores, candidate lists, flags
-    assert ws(li.LI_BF16, li.LI_FP8_E4M3, 16, 1, 131072, 64, 512) >= 16 * 131072 * 4 * 3
+    # decode rows: the scores, then the top-k's thresholds, counts and candidate lists
+    assert ws(li.LI_BF16, li.LI_FP8_E4M3, 16, 1, 131072, 64, 512) == \
+        16 * 131072 * 4 + L.li_topk_workspace_bytes(16, 131072, 512)
+    assert L.li_topk_workspace_bytes(16, 131072, 512) >= 16 * 131072 * 4 * 2
     assert ws(li.LI_BF16, li.LI_BF16, 0, 16, 1000, 64, 16) == 0
 
 
