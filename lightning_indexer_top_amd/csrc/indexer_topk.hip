@@ -157,6 +157,7 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
   int nvis = S;
   if (nv) nvis = min(max(nv[r], 0), S);
   if (!active) nvis = 0;
+  nvis = __builtin_amdgcn_readfirstlane(nvis);  // one row per wave: uniform
 
   // keys needed by the workgroup: the largest visible count of its rows
   __shared__ int s_kend;
@@ -213,28 +214,14 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
   // loop then only waits on its own next-tile loads where they are stored
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int kt = it * PS_NK;
-    const bool more = it + 1 < ntiles;
-    if (more) {
-      PS_LOAD(0, kt + PS_NK); PS_LOAD(1, kt + PS_NK); PS_LOAD(2, kt + PS_NK); PS_LOAD(3, kt + PS_NK);
-    }
-    const uint8_t* buf = tiles[it & 1];
-    if (kt < nvis) {  // uniform per wave
-      // software pipeline over the tile's 32-key sub-tiles (up to 64 heads):
-      // the MFMAs of sub-tile s + 1 issue before the ReLU x weight reduction of
-      // sub-tile s, so that reduction runs in the shadow of the matrix cores.
-      // With 128 heads a second accumulator set does not fit the register file:
-      // each group of 32 heads is scored, then reduced.
-      constexpr bool PIPE = HT <= 2;
-      constexpr int NS = PS_NK / 32;
-      f32x16 acc[PIPE ? 2 : 1][PIPE ? HT : 1];
-      bf16x8 bop[8];
-#define PS_BOP(sub)                                                                                             \
+  constexpr bool PIPE = HT <= 2;
+  constexpr int NS = PS_NK / 32;
+  bf16x8 bop[8];
+#define PS_BOP(sub, buf)                                                                                        \
   do {                                                                                                          \
     const int n_ = 32 * (sub) + col;                                                                            \
     _Pragma("unroll") for (int kk = 0; kk < 8; ++kk) bop[kk] =                                                  \
-        __builtin_bit_cast(bf16x8, *(const uint4*)(buf + n_ * 256 + (((8 * hf + kk) ^ (n_ & 15)) << 4)));       \
+        __builtin_bit_cast(bf16x8, *(const uint4*)((buf) + n_ * 256 + (((8 * hf + kk) ^ (n_ & 15)) << 4)));     \
   } while (0)
 #define PS_MMA(slot, ht, aset)                                                                                  \
   do {                                                                                                          \
@@ -242,76 +229,154 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
     _Pragma("unroll") for (int kk = 0; kk < 8; ++kk) acc[slot][ht] =                                            \
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[aset][kk], bop[kk], acc[slot][ht], 0, 0, 0);                  \
   } while (0)
-      if constexpr (PIPE) {
-        PS_BOP(0);
+// ReLU x weight over this lane's heads of one accumulator slot, then the other
+// lane half's partial sum (same key, the other heads)
+#define PS_RED(part, slot)                                                                                      \
+  do {                                                                                                          \
+    _Pragma("unroll") for (int ht = 0; ht < HT; ++ht)                                                           \
+      _Pragma("unroll") for (int i = 0; i < 16; ++i) part = fmaf(wv[ht][i], relu_bits_f(acc[slot][ht][i]), part); \
+    part += __uint_as_float(                                                                                    \
+        __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false)[1]);      \
+  } while (0)
+// The MFMAs of one sub-tile into slot ns (both head tiles' chains alternating),
+// each followed by two ReLU x weight steps of the sub-tile held in slot os, in
+// this order: the reduction runs while the matrix cores work.  Then the other
+// lane half's partial sum (same key, the other heads).
+#define PS_MMA_RED(ns, os, part)                                                                                \
+  do {                                                                                                          \
+    _Pragma("unroll") for (int ht = 0; ht < HT; ++ht) acc[ns][ht] = f32x16{};                                   \
+    _Pragma("unroll") for (int kk = 0; kk < 8; ++kk) {                                                          \
+      _Pragma("unroll") for (int ht = 0; ht < HT; ++ht) {                                                       \
+        acc[ns][ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ht][kk], bop[kk], acc[ns][ht], 0, 0, 0);        \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                         \
+          const int e_ = 2 * (HT * kk + ht) + j;                                                                \
+          part = fmaf(wv[e_ >> 4][e_ & 15], relu_bits_f(acc[os][e_ >> 4][e_ & 15]), part);                      \
+        }                                                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                                      \
+      }                                                                                                         \
+    }                                                                                                           \
+    part += __uint_as_float(                                                                                    \
+        __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false)[1]);      \
+  } while (0)
+  // the score of key kt + 32 s + col (lanes of the first half): written out, or
+  // listed when it beats theta
+  auto emit = [&](int kt, int s, float part) {
+    const int key = kt + 32 * s + col;
+    if constexpr (SCORES) {
+      if (active && hf == 0 && key < kend) scores[r * S + key] = key < nvis ? part : -INFINITY;
+    } else {
+      const uint32_t ok = ord_f32(part);
+      const uint64_t mk = __ballot(hf == 0 && key < nvis && ok > theta);
+      if (mk) {
+        if ((mk >> lane) & 1ull) {
+          const int pos = cnt + __popcll(mk & ((1ull << lane) - 1));
+          sk[pos] = ok;
+          si[pos] = key;
+        }
+        cnt += __popcll(mk);
+      }
+    }
+  };
+  // room for the next tile's entries
+  auto make_room = [&]() {
+    if (!SCORES && cnt > PS_CAP - PS_NK) {
+      theta = ps_compact(sk, si, whist[wave], cnt, topk);
+      cnt = topk;
+    }
+  };
+  if constexpr (PIPE) {
+    // Software pipeline over 32-key sub-tiles (up to 64 heads), carried across
+    // tiles: the MFMAs of sub-tile s + 1 issue before the ReLU x weight reduction
+    // of sub-tile s, so the reduction runs in the shadow of the matrix cores; the
+    // last sub-tile of a tile is reduced after the barrier that publishes the
+    // next tile, beside that tile's first MFMAs.  Sub-tile s accumulates in slot
+    // s & 1.
+    f32x16 acc[2][HT];
+    if (ntiles > 0 && nvis > 0) {
+      PS_BOP(0, tiles[0]);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) PS_MMA(0, ht, ht);
+    }
+    for (int it = 0; it < ntiles; ++it) {
+      const int kt = it * PS_NK;
+      const bool more = it + 1 < ntiles;
+      if (more) {
+        PS_LOAD(0, kt + PS_NK); PS_LOAD(1, kt + PS_NK); PS_LOAD(2, kt + PS_NK); PS_LOAD(3, kt + PS_NK);
+      }
+      const uint8_t* buf = tiles[it & 1];
+      const bool cur = kt < nvis;  // uniform per wave
+      if (cur) {
+#pragma unroll
+        for (int s = 0; s + 1 < NS; ++s) {
+          PS_BOP(s + 1, buf);
+          float part = 0.0f;
+          PS_MMA_RED((s + 1) & 1, s & 1, part);
+          emit(kt, s, part);
+        }
+      }
+      // keep the store of the next tile after the sub-tiles above: hoisted above
+      // them, the store would wait for the tile's global loads before any MFMA
+      asm volatile("" ::: "memory");
+      if (more) {
+        uint8_t* nb = tiles[(it + 1) & 1];
+        PS_STORE(0, nb); PS_STORE(1, nb); PS_STORE(2, nb); PS_STORE(3, nb);
+      }
+      __syncthreads();
+      const bool nxt = more && kt + PS_NK < nvis;
+      float part = 0.0f;
+      if (nxt && cur) {
+        PS_BOP(0, tiles[(it + 1) & 1]);
+        PS_MMA_RED(0, (NS - 1) & 1, part);
+      } else if (nxt) {
+        PS_BOP(0, tiles[(it + 1) & 1]);
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) PS_MMA(0, ht, ht);
+      } else if (cur) {
+        PS_RED(part, (NS - 1) & 1);
       }
+      if (cur) {
+        emit(kt, NS - 1, part);
+        make_room();
+      }
+    }
+  } else {
+    // 128 heads: a second accumulator set does not fit the register file, so each
+    // group of 32 heads is scored, then reduced
+    f32x16 acc[1][1];
+    for (int it = 0; it < ntiles; ++it) {
+      const int kt = it * PS_NK;
+      const bool more = it + 1 < ntiles;
+      if (more) {
+        PS_LOAD(0, kt + PS_NK); PS_LOAD(1, kt + PS_NK); PS_LOAD(2, kt + PS_NK); PS_LOAD(3, kt + PS_NK);
+      }
+      const uint8_t* buf = tiles[it & 1];
+      if (kt < nvis) {  // uniform per wave
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        float part = 0.0f;
-        if constexpr (!PIPE) {
-          PS_BOP(s);
+        for (int s = 0; s < NS; ++s) {
+          float part = 0.0f;
+          PS_BOP(s, buf);
 #pragma unroll
           for (int ht = 0; ht < HT; ++ht) {
             PS_MMA(0, 0, ht);
 #pragma unroll
             for (int i = 0; i < 16; ++i) part = fmaf(wv[ht][i], relu_bits_f(acc[0][0][i]), part);
           }
-        } else {
-          if (s + 1 < NS) {
-            PS_BOP(s + 1);
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) PS_MMA((s + 1) & 1, ht, ht);
-          }
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) part = fmaf(wv[ht][i], relu_bits_f(acc[s & 1][ht][i]), part);
-          }
+          part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                                   false, false)[1]);
+          emit(kt, s, part);
         }
-        // lanes 0..31 add the partial sum of lanes 32..63 (same key, other heads)
-        part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
-                                                                 false, false)[1]);
-        if (PIPE && s + 1 < NS) {
-          // interleave: one MFMA, then four VALU operations of the reduction
-#pragma unroll
-          for (int g = 0; g < 8 * HT; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-          }
-        }
-        const int key = kt + 32 * s + col;
-        if constexpr (SCORES) {
-          if (active && hf == 0 && key < kend) scores[r * S + key] = key < nvis ? part : -INFINITY;
-          continue;
-        }
-        const uint32_t ok = ord_f32(part);
-        const uint64_t mk = __ballot(hf == 0 && key < nvis && ok > theta);
-        if (mk) {
-          if ((mk >> lane) & 1ull) {
-            const int pos = cnt + __popcll(mk & ((1ull << lane) - 1));
-            sk[pos] = ok;
-            si[pos] = key;
-          }
-          cnt += __popcll(mk);
-        }
+        make_room();
       }
-      // room for the next tile's entries
-      if (!SCORES && cnt > PS_CAP - PS_NK) {
-        theta = ps_compact(sk, si, whist[wave], cnt, topk);
-        cnt = topk;
+      asm volatile("" ::: "memory");
+      if (more) {
+        uint8_t* nb = tiles[(it + 1) & 1];
+        PS_STORE(0, nb); PS_STORE(1, nb); PS_STORE(2, nb); PS_STORE(3, nb);
       }
+      __syncthreads();
     }
-    // keep the store of the next tile after this tile's compute: hoisted above
-    // it, the store would wait for the tile's global loads before any MFMA issues
-    asm volatile("" ::: "memory");
-    if (more) {
-      uint8_t* nb = tiles[(it + 1) & 1];
-      PS_STORE(0, nb); PS_STORE(1, nb); PS_STORE(2, nb); PS_STORE(3, nb);
-    }
-    __syncthreads();
   }
+#undef PS_MMA_RED
+#undef PS_RED
 #undef PS_MMA
 #undef PS_BOP
 #undef PS_LOAD
