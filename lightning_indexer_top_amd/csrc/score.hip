@@ -250,10 +250,12 @@ __device__ __forceinline__ void held_select_epilogue(const float* held_g, int n,
   float v[HELD_E];
 #pragma unroll
   for (int e = 0; e < HELD_E; ++e) v[e] = held[e * 256 + tid];
+  // scores go out as streaming stores: nothing of them is left dirty in L2 for the
+  // write-back at the end of the kernel
 #pragma unroll
   for (int e = 0; e < HELD_E; ++e) {
     const int i = e * 256 + tid;
-    if (i < n) out_row[key0 + i] = v[e];
+    if (i < n) __builtin_nontemporal_store(v[e], &out_row[key0 + i]);
   }
   list_above_local_threshold(v, n, k, P, (int)blockIdx.x, cval + (int64_t)r * S + key0, cid + (int64_t)r * S + key0,
                              key0, bcnt + (int64_t)r * P + blockIdx.x, tau_used + (int64_t)r * 256, scratch);
@@ -543,7 +545,7 @@ _Pragma("unroll") \
       if (STAGE)  // written out to LDS (no compiler-visible LDS access beside the ring's loads)
         asm volatile("ds_write_b32 %0, %1" : : "v"(stage0 + 4u * (uint32_t)(key - key0)), "v"(v) : "memory");
       else
-        out_row[key] = v;
+        __builtin_nontemporal_store(v, &out_row[key]);
     }
   }
   if constexpr (STAGE) {
@@ -560,7 +562,7 @@ _Pragma("unroll") \
       // the ring is free: its LDS holds the selection's thresholds and counts
       held_select_epilogue(held, max(n, 0), r, key0, topk, out_row, bcnt, cval, cid, tau_used, S, ring);
     } else {
-      for (int i = (int)threadIdx.x; i < n; i += 256) out_row[key0 + i] = held[i];
+      for (int i = (int)threadIdx.x; i < n; i += 256) __builtin_nontemporal_store(held[i], &out_row[key0 + i]);
     }
   }
 #undef LI_TILE_PART
