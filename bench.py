@@ -184,7 +184,7 @@ def oracle_baseline(value, unit, sample, seconds):
 # each scaled by what the same counter reads for a plain 1 GiB copy: FETCH x2.0,
 # WRITE x1.0).  Valid only for the kernel sources it was taken on; null otherwise.
 SCORE_TRAFFIC = {"sources": ["lightning_indexer_top_amd/csrc/score.hip", "lightning_indexer_top_amd/csrc/common.h"],
-                 "sha256_16": "2cd3e3b636d13997", "fetch_kib": 272514.4, "write_kib": 8192.0}
+                 "sha256_16": "ebd11ec84b9c566a", "fetch_kib": 272517.0, "write_kib": 8192.0}
 
 
 # ---- measured ceilings ------------------------------------------------------
@@ -327,8 +327,8 @@ def bench_decode(torch, li, workloads, steps, warmup):
         traffic = round((SCORE_TRAFFIC["fetch_kib"] + SCORE_TRAFFIC["write_kib"]) * 1024)
     log(f"[decode] step {ms * 1e3:.1f} us, score kernel {score_ms * 1e3:.1f} us ({score_in_step_ms * 1e3:.1f} us "
         f"between the step's events) -> {achieved:.0f} GB/s")
-    # the same step through the fused entry point (li_indexer_topk: the scoring
-    # kernel lists candidates above a sampled threshold, one exact pass selects)
+    # the same step through the fused entry point (li_indexer_topk: every scoring
+    # workgroup lists its scores above a threshold of its own, one exact pass selects)
     fws_n = L.li_indexer_topk_workspace_bytes(li.LI_BF16, li.LI_FP8_E4M3, B, 1, S, H, k)
     fws = torch.zeros(fws_n, dtype=torch.uint8, device="cuda")
     fused_args = [(_p(q), li.LI_BF16, _p(w), _p(keys[r]), li.LI_FP8_E4M3, _p(scales[r]), None, B, 1, S, H, 128, k,

@@ -46,6 +46,21 @@ def test_decode_heads_and_tail(key, H):
     assert_scores_close(g, o, f"{key} H={H}")
 
 
+def test_held_scores_multi_tile_with_visible_ends():
+    """fp8 keys at 64 heads on few long rows: on 256 CUs every workgroup streams
+    3,072 keys (24 tiles a wave) and holds its scores in LDS until its last tile;
+    the visible counts end inside a workgroup, inside a tile and at a workgroup
+    edge.  Every element against the oracle."""
+    S = 524288
+    nv = np.array([S - 777, 300001, 3072 * 51], np.int32)
+    print("held scores multi-tile", S, nv.tolist(), flush=True)
+    sp = workloads.spec("batched_decode", B=3, S=S, H=64, seed=0x5EED0190)
+    g, o, _ = run(sp, nv=nv)
+    assert_scores_close(g, o, "held scores, multi-tile workgroups")
+    for r in range(3):
+        assert np.all(np.isneginf(g[r, nv[r]:])), f"row {r}: keys past the visible count"
+
+
 @pytest.mark.parametrize("spread", [False, True])
 @pytest.mark.parametrize("H", [8, 64, 100])
 def test_fp8_keys_summation_bound(H, spread):
