@@ -297,25 +297,47 @@ constexpr uint32_t REGION_UNFILTERED = 0xFFFFFFFFu;
 // the entries above it), with the threshold taken by each of the P regions of a
 // row from its own scores, so that no workgroup waits for another.  A workgroup of
 // 256 threads holds the n <= 4096 scores of its region, 16 per thread (entry
-// e * 256 + tid in v[e]).  With j = max(ceil(3 k / P), 16), each wave finds the
-// c-th largest of its 64 per-thread maxima, c = ceil(j / 4), by a binary search on
-// the 32-bit ordered key (one compare and one ballot count per bit), and the
-// region's threshold is the smallest of its four waves': every wave holds at least
-// c entries at or above it, so at least j are listed (all of a wave's entries when
-// fewer than c of its threads hold any).  The entries at or above the threshold
-// go to ov / oi (values, ids id0 + entry) in index order; the region records its
-// count (*bc), its threshold (tu_row[region]) and, with at most 128 regions a row,
-// its largest key (tu_row[128 + region]; it is always listed).  A row's top k lies
-// among the lists whenever its kth listed value reaches every region's threshold:
-// the finalize checks that and otherwise selects over the whole row.  scratch:
-// 96 bytes of LDS (16-byte aligned); both barriers order LDS only.
+// e * 256 + tid in v[e]).  Each wave finds the c-th largest of its 64 per-thread
+// maxima, c = ceil(j / 4), by a binary search on a 32-bit ordered key (one compare
+// and one ballot count per bit), and the region's threshold is the smallest of its
+// four waves': every wave holds at least c entries at or above it, so at least j
+// are listed (all of a wave's entries when fewer than c of its threads hold any).
+// fp32 scores: the key is the whole ordered value and j = max(ceil(3 k / P), 16).
+// fp64 scores: the key is the upper 32 bits of the ordered value (an entry is
+// listed when its upper half reaches the threshold, so every unlisted entry lies
+// below threshold << 32), and j = max(u + 6 sqrt(u) + 8, 16) with u = ceil(k / P),
+// the region's expected share of the top k plus six of its standard deviations:
+// for k = 2,048 over 32 regions the lists stay near 6,000 entries, within the exact
+// pass.  The entries at or above the threshold go to ov / oi (values, ids id0 +
+// entry) in index order; the region records its count (*bc), its threshold
+// (tu_row[region]) and, with at most 128 regions a row, its largest key
+// (tu_row[128 + region]; it is always listed).  A row's top k lies among the
+// lists whenever its kth listed value reaches every region's threshold: the
+// finalize checks that and otherwise selects over the whole row.  scratch: 96
+// bytes of LDS (16-byte aligned); both barriers order LDS only.
 constexpr int LT_E = 16;  // entries per thread: regions of at most 4,096 scores
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
-__device__ __forceinline__ void list_above_local_threshold(const float (&v)[LT_E], int n, int k, int P, int region,
-                                                           float* __restrict__ ov, int32_t* __restrict__ oi,
+__device__ __forceinline__ uint32_t lt_key(float x) { return ord_f32(x); }
+__device__ __forceinline__ uint32_t lt_key(double x) { return (uint32_t)(ord_f64(x) >> 32); }
+
+// Listed entries a region aims for (see above).
+template <typename Sc>
+__device__ __forceinline__ uint32_t lt_listed_target(int k, int P) {
+  if constexpr (sizeof(Sc) == 4) {
+    return (uint32_t)max((3 * k + P - 1) / P, 16);
+  } else {
+    const int u = (k + P - 1) / P;
+    const int sq = (int)ceilf(sqrtf((float)u));
+    return (uint32_t)max(u + 6 * sq + 8, 16);
+  }
+}
+
+template <typename Sc>
+__device__ __forceinline__ void list_above_local_threshold(const Sc (&v)[LT_E], int n, int k, int P, int region,
+                                                           Sc* __restrict__ ov, int32_t* __restrict__ oi,
                                                            int id0, uint32_t* __restrict__ bc,
                                                            uint32_t* __restrict__ tu_row, void* scratch) {
   lds_u32* wt = (lds_u32*)(uintptr_t)lds_addr(scratch);  // 4 wave thresholds, 4 wave maxima
@@ -326,10 +348,10 @@ __device__ __forceinline__ void list_above_local_threshold(const float (&v)[LT_E
   uint32_t m = 0u;  // entries past n hold the smallest key, 0
 #pragma unroll
   for (int e = 0; e < LT_E; ++e) {
-    key[e] = e * 256 + tid < n ? ord_f32(v[e]) : 0u;
+    key[e] = e * 256 + tid < n ? lt_key(v[e]) : 0u;
     m = max(m, key[e]);
   }
-  const uint32_t c = ((uint32_t)max((3 * k + P - 1) / P, 16) + 3u) / 4u;
+  const uint32_t c = (lt_listed_target<Sc>(k, P) + 3u) / 4u;
   uint32_t t = 0u;  // the largest t with at least c maxima >= t
 #pragma unroll
   for (int bit = 31; bit >= 0; --bit) {

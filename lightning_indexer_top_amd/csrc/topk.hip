@@ -523,8 +523,10 @@ __device__ void finalize_lists(int r, const Sc* __restrict__ scores, const int32
   for (int e = 0; e < E; ++e) key[e] = valid[e] ? ScoreTraits<Sc>::ord(val[e]) : (K)0;
   // every unlisted entry of a region lies below its threshold; when the kth listed
   // value reaches the largest threshold no unlisted entry can enter the top k
+  // (fp64 regions record the upper half of their threshold key)
+  const K floor = (K)s_floor << (8 * sizeof(K) - 32);
   if (!write_top_listed<Sc, E>(key, val, id, valid, (uint32_t)k, io, vo, hist, wsum8, res8, scan1, scan2,
-                               (K)s_floor))
+                               floor))
     select_block<Sc>(scores + (int64_t)r * S, nullptr, n, k, io, vo);
 }
 
@@ -781,15 +783,16 @@ static int mb_chunks(int R, int S) {
 
 static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// li_topk_select on few long rows: every workgroup takes a region of TK_LOCAL_CHUNK
+// The selection on few long rows: every workgroup takes a region of TK_LOCAL_CHUNK
 // scores of its row (16 a thread, entry e * 256 + tid, loads all in flight) and
 // lists its entries above a threshold of its own (list_above_local_threshold);
 // the finalize then selects among the lists.
 constexpr int TK_LOCAL_CHUNK = LT_E * 256;
 
-__global__ __launch_bounds__(256) void topk_local_filter_kernel(const float* __restrict__ scores,
+template <typename Sc>
+__global__ __launch_bounds__(256) void topk_local_filter_kernel(const Sc* __restrict__ scores,
                                                                 const int32_t* __restrict__ nv, int S, int k,
-                                                                float* __restrict__ cval, int32_t* __restrict__ cid,
+                                                                Sc* __restrict__ cval, int32_t* __restrict__ cid,
                                                                 uint32_t* __restrict__ bcnt,
                                                                 uint32_t* __restrict__ tau_used) {
   __shared__ __attribute__((aligned(16))) uint32_t scratch[24];
@@ -798,12 +801,12 @@ __global__ __launch_bounds__(256) void topk_local_filter_kernel(const float* __r
   if (nv) n_row = min(max(nv[r], 0), S);
   const int lo = p * TK_LOCAL_CHUNK;
   const int n = max(min(n_row - lo, TK_LOCAL_CHUNK), 0);
-  const float* row = scores + (int64_t)r * S + lo;
-  float v[LT_E];
+  const Sc* row = scores + (int64_t)r * S + lo;
+  Sc v[LT_E];
 #pragma unroll
   for (int e = 0; e < LT_E; ++e) {
     const int i = e * 256 + tid;
-    v[e] = i < n ? row[i] : 0.0f;
+    v[e] = i < n ? row[i] : (Sc)0;
   }
   list_above_local_threshold(v, n, k, P, p, cval + (int64_t)r * S + lo, cid + (int64_t)r * S + lo, lo,
                              bcnt + (int64_t)r * P + p, tau_used + (int64_t)r * 256, scratch);
@@ -832,17 +835,22 @@ static hipError_t launch_topk_mb(const Sc* scores, const int32_t* nv, int R, int
   Sc* cval = (Sc*)p;
   p += a256((size_t)R * S * sizeof(Sc));
   int32_t* cid = (int32_t*)p;
-  if constexpr (sizeof(Sc) == 4) {
+  {
     // regions of LT_E x 256 scores, each listed above a threshold of its own
     const int Pl = (S + TK_LOCAL_CHUNK - 1) / TK_LOCAL_CHUNK;
     if (Pl <= 256) {
       uint32_t* tau_used = (uint32_t*)tau;
-      topk_local_filter_kernel<<<dim3(Pl, R), 256, 0, st>>>((const float*)scores, nv, S, k, (float*)cval, cid, bcnt,
-                                                            tau_used);
+      topk_local_filter_kernel<Sc><<<dim3(Pl, R), 256, 0, st>>>(scores, nv, S, k, cval, cid, bcnt, tau_used);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      return launch_topk_finalize_f32((const float*)scores, nv, R, S, k, Pl, TK_LOCAL_CHUNK, bcnt,
-                                      (const float*)cval, cid, idx, (float*)val, tau_used, st);
+      if constexpr (sizeof(Sc) == 4) {
+        return launch_topk_finalize_f32((const float*)scores, nv, R, S, k, Pl, TK_LOCAL_CHUNK, bcnt,
+                                        (const float*)cval, cid, idx, (float*)val, tau_used, st);
+      } else {
+        topk_finalize_kernel<Sc><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, Pl, TK_LOCAL_CHUNK, bcnt, cval, cid,
+                                                            idx, val, tau_used);
+        return hipGetLastError();
+      }
     }
   }
   const int P = mb_chunks(R, S);

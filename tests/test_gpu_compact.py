@@ -13,7 +13,10 @@ pytestmark = pytest.mark.gpu
 
 
 def run(sp, m, k, nv=None):
-    x = workloads.compact_inputs(sp)
+    return run_x(workloads.compact_inputs(sp), m, k, nv)
+
+
+def run_x(x, m, k, nv=None):
     sl, idx, val = li.compact_search_rerank(dev(x["q"], "bf16"), dev(x["w"]), dev(x["P"]), dev(x["c"]), dev(x["cs"]),
                                             dev(x["k_full"], "bf16"), m, k, dev(nv) if nv is not None else None)
     torch.cuda.synchronize()
@@ -40,3 +43,35 @@ def test_visible_counts():
     sl, idx, val, ref = run(sp, 1024, 256, nv)
     assert np.array_equal(sl, ref["shortlist"]) and np.array_equal(idx, ref["idx"])
     assert (idx[0, 100:] == -1).all()
+
+
+def check(sl, idx, val, ref, what):
+    assert np.array_equal(sl, ref["shortlist"]), f"{what}: shortlist differs"
+    assert np.array_equal(idx, ref["idx"]), f"{what}: final indices differ"
+    fin = ref["idx"] >= 0
+    assert np.array_equal(val[fin], ref["val"][fin]), f"{what}: final values differ"
+
+
+def test_multi_region_lists():
+    """Rows of at least 16,384 keys take the selection on few long rows: every
+    4,096-key region lists its fp64 stage-1 scores above a threshold of its own (on
+    the upper half of the ordered value) and one exact pass selects the shortlist.
+    A ragged last region, a visible count inside a region, one below the shortlist
+    size."""
+    print("compact multi-region", flush=True)
+    sp = workloads.spec("compact_search", B=3, S=40000, H=64, seed=0x5EED0710)
+    nv = np.array([40000, 17000, 1500], np.int32)
+    check(*run(sp, 2048, 512, nv), "multi-region")
+
+
+def test_concentrated_shortlist():
+    """Every one of row 0's best stage-1 scores in one 4,096-key region (its
+    compact-key scales multiplied by 64): that region's own threshold lies above
+    the row's 2,048th value, so its lists cannot be used and the row is selected
+    whole; row 1 is left as drawn.  Both bit-exact."""
+    print("compact concentrated", flush=True)
+    sp = workloads.spec("compact_search", B=2, S=40000, H=64, seed=0x5EED0720)
+    x = workloads.compact_inputs(sp)
+    x["cs"] = np.array(x["cs"], copy=True)
+    x["cs"][0, 4096:8192] *= 64.0
+    check(*run_x(x, 2048, 512), "concentrated")

@@ -53,3 +53,13 @@ def test_pq_search_full_size():
     x = workloads.pq_inputs(sp)
     print("inputs ready; oracle on every sequence", flush=True)
     check(*run(x, sp["m"], sp["topk"]))
+
+
+def test_multi_region_visible_counts():
+    """Rows of at least 16,384 keys: the shortlist comes from per-region lists (fp64
+    scores listed on the upper half of the ordered value) and one exact pass, with a
+    ragged last region and a visible count inside a region."""
+    print("pq multi-region", flush=True)
+    sp = workloads.spec("pq_search", B=2, S=40000, H=64, seed=0x5EED1200, pq_train_stride=1, pq_iters=4)
+    nv = np.array([40000, 23456], np.int32)
+    check(*run(workloads.pq_inputs(sp), 2048, 512, nv))
