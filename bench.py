@@ -202,9 +202,12 @@ def probe_lib():
     return L
 
 
-READ_PROBE_CONFIGS = [(0, 4), (0, 8), (1, 4), (1, 8), (2, 2), (2, 3)]  # (access pattern, workgroups per CU)
+# (access pattern, workgroups per CU)
+READ_PROBE_CONFIGS = [(0, 4), (0, 8), (1, 4), (1, 8), (2, 2), (2, 3), (3, 2), (3, 3), (4, 2), (4, 3)]
 READ_PROBE_MODES = {0: "grid-stride register loads", 1: "contiguous range per wave, register loads",
-                    2: "contiguous range per wave, DMA into LDS"}
+                    2: "contiguous range per wave, DMA into LDS",
+                    3: "contiguous range per wave, DMA into LDS, non-temporal",
+                    4: "4 KB tiles taken in turn by a workgroup's waves, DMA into LDS, non-temporal"}
 
 
 def measure_probes(torch, read_bytes=1 << 30, n_buf=4, reps=3, mfma_iters=4000):

@@ -27,8 +27,11 @@ int li_probe_read_blocks(int blocks_per_cu);
 /* Reads all `bytes` of `buf` once with 16-byte loads, no stores but one word per
  * workgroup into sink.  mode 0: grid-stride loads into registers, 8 in flight per
  * lane; 1: a contiguous range per wave, 8 consecutive 1 KB wave loads in flight;
- * 2: a contiguous range per wave by DMA into LDS, 12 in flight.  buf 16-byte
- * aligned, bytes a multiple of 16, 1 <= blocks_per_cu <= 16. */
+ * 2: a contiguous range per wave by DMA into LDS, 12 in flight; 3: as 2 with the
+ * non-temporal cache policy; 4: a contiguous range per workgroup whose four waves
+ * take 4 KB tiles in turn, 3 tiles in flight per wave, DMA into LDS, non-temporal
+ * (bytes a multiple of 16 KB).  buf 16-byte aligned, bytes a multiple of 16,
+ * 1 <= blocks_per_cu <= 16; returns 0, or 1 for invalid arguments. */
 int li_probe_read(const void *buf, size_t bytes, uint32_t *sink, int mode, int blocks_per_cu, hipStream_t stream);
 
 /* Workgroups of the matrix-core probe (4 waves each); `sink` holds 4 floats per

@@ -16,6 +16,12 @@ namespace li {
 
 constexpr int WAVE = 64;
 
+// Cache-policy operand of global_load_lds for data read once per launch: nt
+// (non-temporal).  Such lines are inserted for early eviction instead of
+// displacing reused ones; on a read-once HBM stream it raised the measured read
+// rate of the same access pattern from 6.1 to 6.95-7.1 TB/s.
+constexpr int CPOL_STREAM = 2;
+
 // Orderable unsigned images of floating-point values: a > b (as numbers, -0 == +0
 // excluded) iff ord(a) > ord(b).  NaNs with the sign bit clear order above +inf.
 __device__ __forceinline__ uint32_t ord_f32(float f) {

@@ -3,10 +3,13 @@
 //
 //   li_probe_read  -- a read-only HBM stream: every byte of a device buffer is read
 //                     once with 16-byte loads (no stores in the stream but one word
-//                     per workgroup), in one of three access patterns: grid-stride
+//                     per workgroup), in one of five access patterns: grid-stride
 //                     register loads, a contiguous range per wave into registers,
-//                     or a contiguous range per wave by DMA into LDS (the decode
-//                     scoring kernel's pattern).
+//                     a contiguous range per wave by DMA into LDS, the same with
+//                     the non-temporal cache policy, or the decode scoring kernel's
+//                     own pattern (a contiguous range per workgroup whose four waves
+//                     take 4 KB tiles in turn, three in flight per wave, DMA into
+//                     LDS, non-temporal).
 //   li_probe_mfma_bf16 -- a register-resident loop of v_mfma_f32_32x32x16_bf16:
 //                     four independent accumulator chains per wave, operands held
 //                     in VGPRs, either constant bits or pseudo-random normal-range
@@ -79,9 +82,10 @@ __global__ __launch_bounds__(RD_THREADS) void probe_read_chunk(const uint4* __re
   sink_block(acc, sink);
 }
 
-// Mode 2: every wave streams its own contiguous range into LDS by DMA
-// (global_load_lds, 1 KB per wave load), U loads in flight, never read back.
-template <int U>
+// Modes 2 and 3: every wave streams its own contiguous range into LDS by DMA
+// (global_load_lds, 1 KB per wave load), U loads in flight, never read back;
+// CPOL 0 (default cache policy) or 2 (non-temporal).
+template <int U, int CPOL>
 __global__ __launch_bounds__(RD_THREADS) void probe_read_dma(const uint4* __restrict__ p, int64_t n16,
                                                              uint32_t* __restrict__ sink) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[RD_THREADS / 64][U][1024];
@@ -93,10 +97,35 @@ __global__ __launch_bounds__(RD_THREADS) void probe_read_dma(const uint4* __rest
   int slot = 0;
   for (int64_t i = lo; i + 64 <= hi; i += 64) {
     __builtin_amdgcn_global_load_lds((const void*)(p + i + lane),
-                                     (__attribute__((address_space(3))) void*)&ring[w][slot][0], 16, 0, 0);
+                                     (__attribute__((address_space(3))) void*)&ring[w][slot][0], 16, 0, CPOL);
     slot = slot + 1 == U ? 0 : slot + 1;
     // keep U loads in flight: the slot issued next is free once the load U back has landed
     __builtin_amdgcn_s_waitcnt((U - 1) | (7 << 4) | (15 << 8));
+  }
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  sink_block(lane == 0 ? (uint32_t)hi : 0u, sink);
+}
+
+// Mode 4: the decode scoring kernel's stream.  A workgroup owns a contiguous range
+// (a multiple of 16 KB); its four waves take 4 KB tiles in turn (wave w reads tiles
+// w, w + 4, ...), four 1 KB DMA loads a tile, NST tiles in flight per wave,
+// non-temporal.
+template <int NST>
+__global__ __launch_bounds__(RD_THREADS) void probe_read_tiles(const uint8_t* __restrict__ p, int64_t bytes,
+                                                               int64_t per_block, uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NST][RD_THREADS / 64][4096];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t lo = blockIdx.x * per_block;
+  const int64_t hi = lo + per_block < bytes ? lo + per_block : bytes;
+  int st = 0;
+  for (int64_t t = lo + w * 4096; t + 4096 <= hi; t += 4 * 4096) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(p + t + j * 1024 + lane * 16),
+                                       (__attribute__((address_space(3))) void*)&ring[st][w][j * 1024], 16, 0, 2);
+    st = st + 1 == NST ? 0 : st + 1;
+    // keep NST tiles in flight: the stage issued next is free once the tile NST back has landed
+    __builtin_amdgcn_s_waitcnt((4 * (NST - 1)) | (7 << 4) | (15 << 8));
   }
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
   sink_block(lane == 0 ? (uint32_t)hi : 0u, sink);
@@ -164,9 +193,10 @@ extern "C" {
 int li_probe_read_blocks(int blocks_per_cu) { return cus() * blocks_per_cu; }
 
 int li_probe_read(const void* buf, size_t bytes, uint32_t* sink, int mode, int blocks_per_cu, hipStream_t stream) {
-  if (!buf || !sink || ((uintptr_t)buf & 15u) || (bytes & 15u) || mode < 0 || mode > 2 || blocks_per_cu < 1 ||
+  if (!buf || !sink || ((uintptr_t)buf & 15u) || (bytes & 15u) || mode < 0 || mode > 4 || blocks_per_cu < 1 ||
       blocks_per_cu > 16)
     return 1;
+  if (mode == 4 && (bytes & 16383u)) return 1;  // whole 16 KB groups of tiles
   const int g = li_probe_read_blocks(blocks_per_cu);
   const uint4* p = (const uint4*)buf;
   const int64_t n = (int64_t)(bytes / 16);
@@ -174,8 +204,16 @@ int li_probe_read(const void* buf, size_t bytes, uint32_t* sink, int mode, int b
     probe_read_stride<8><<<g, RD_THREADS, 0, stream>>>(p, n, sink);
   else if (mode == 1)
     probe_read_chunk<8><<<g, RD_THREADS, 0, stream>>>(p, n, sink);
-  else
-    probe_read_dma<12><<<g, RD_THREADS, 0, stream>>>(p, n, sink);
+  else if (mode == 2)
+    probe_read_dma<12, 0><<<g, RD_THREADS, 0, stream>>>(p, n, sink);
+  else if (mode == 3)
+    probe_read_dma<12, 2><<<g, RD_THREADS, 0, stream>>>(p, n, sink);
+  else {
+    int64_t per = ((int64_t)bytes + g - 1) / g;
+    per = (per + 16383) / 16384 * 16384;
+    probe_read_tiles<3><<<(int)(((int64_t)bytes + per - 1) / per), RD_THREADS, 0, stream>>>((const uint8_t*)buf,
+                                                                                      (int64_t)bytes, per, sink);
+  }
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -60,7 +60,8 @@ struct TileGeom {
 
 // Issue the loads of one full tile into its LDS stage.  goff[j] is this lane's
 // byte offset inside the tile for load instruction j (precomputed); a tile of fp8
-// keys also brings its 32 scales (16 bytes from each of lanes 0-7).
+// keys also brings its 32 scales (16 bytes from each of lanes 0-7).  Keys are read
+// once per launch, so the loads carry the streaming cache policy.
 template <bool FP8>
 __device__ __forceinline__ void issue_tile_full(const uint8_t* tile_base, const float* scale_base, uint32_t lds_tile,
                                                 const uint32_t* goff, int lane) {
@@ -68,11 +69,11 @@ __device__ __forceinline__ void issue_tile_full(const uint8_t* tile_base, const 
 #pragma unroll
   for (int j = 0; j < G::LOADS; ++j)
     __builtin_amdgcn_global_load_lds((const void*)(tile_base + goff[j]), (lds_void*)(uintptr_t)(lds_tile + j * 1024),
-                                     16, 0, 0);
+                                     16, 0, CPOL_STREAM);
   if constexpr (FP8) {
     if (lane < 8)
       __builtin_amdgcn_global_load_lds((const void*)(scale_base + 4 * lane), (lds_void*)(uintptr_t)(lds_tile + G::KBYTES),
-                                       16, 0, 0);
+                                       16, 0, CPOL_STREAM);
   }
 }
 
@@ -89,12 +90,12 @@ __device__ __attribute__((noinline)) void issue_tile_tail(const uint8_t* tile_ba
     const int c = (s % G::CPR) ^ G::sw(n);
     const int nl = n < nkeys ? n : nkeys - 1;
     __builtin_amdgcn_global_load_lds((const void*)(tile_base + (int64_t)nl * G::ROW + c * 16),
-                                     (lds_void*)(uintptr_t)(lds_tile + j * 1024), 16, 0, 0);
+                                     (lds_void*)(uintptr_t)(lds_tile + j * 1024), 16, 0, CPOL_STREAM);
   }
   if constexpr (FP8) {
     if (lane < nkeys)
       __builtin_amdgcn_global_load_lds((const void*)(scale_base + lane), (lds_void*)(uintptr_t)(lds_tile + G::KBYTES), 4,
-                                       0, 0);
+                                       0, CPOL_STREAM);
   }
 }
 
