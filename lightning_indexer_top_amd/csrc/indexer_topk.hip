@@ -195,8 +195,8 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
 
   uint32_t* sk = cand_k[wave];
   int32_t* si = cand_i[wave];
-  int cnt = 0;          // listed entries
-  uint32_t theta = 0u;  // orderable key to beat
+  int cnt = 0;                 // listed entries
+  float theta_f = -INFINITY;   // score to beat (every finite score beats it at first)
 
   const int ntiles = (kend + PS_NK - 1) / PS_NK;
   // four named registers, not an array: an array here is kept in scratch memory
@@ -229,19 +229,16 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
     _Pragma("unroll") for (int kk = 0; kk < 8; ++kk) acc[slot][ht] =                                            \
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[aset][kk], bop[kk], acc[slot][ht], 0, 0, 0);                  \
   } while (0)
-// ReLU x weight over this lane's heads of one accumulator slot, then the other
-// lane half's partial sum (same key, the other heads)
+// ReLU x weight over this lane's heads of one accumulator slot: the partial sum of
+// the lane half's heads (the other half's comes in at emission)
 #define PS_RED(part, slot)                                                                                      \
   do {                                                                                                          \
     _Pragma("unroll") for (int ht = 0; ht < HT; ++ht)                                                           \
       _Pragma("unroll") for (int i = 0; i < 16; ++i) part = fmaf(wv[ht][i], relu_bits_f(acc[slot][ht][i]), part); \
-    part += __uint_as_float(                                                                                    \
-        __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false)[1]);      \
   } while (0)
 // The MFMAs of one sub-tile into slot ns (both head tiles' chains alternating),
 // each followed by two ReLU x weight steps of the sub-tile held in slot os, in
-// this order: the reduction runs while the matrix cores work.  Then the other
-// lane half's partial sum (same key, the other heads).
+// this order: the reduction runs while the matrix cores work.
 #define PS_MMA_RED(ns, os, part)                                                                                \
   do {                                                                                                          \
     _Pragma("unroll") for (int ht = 0; ht < HT; ++ht) acc[ns][ht] = f32x16{};                                   \
@@ -255,22 +252,45 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
         __builtin_amdgcn_sched_barrier(0);                                                                      \
       }                                                                                                         \
     }                                                                                                           \
-    part += __uint_as_float(                                                                                    \
-        __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false)[1]);      \
   } while (0)
-  // the score of key kt + 32 s + col (lanes of the first half): written out, or
-  // listed when it beats theta
-  auto emit = [&](int kt, int s, float part) {
+  // Sub-tiles s and s + 1 (s even) leave together: pa / pb hold each lane half's
+  // partial sums of their keys, and one lane-half swap gives lane l the score of
+  // key kt + 32 s + l (sub-tile s in lanes 0..31, s + 1 in lanes 32..63), which
+  // is written out, or listed when it beats theta (compared as floats: -0 and +0
+  // are equal as in the orderable image; lanes ascend with the key, so the list
+  // stays in index order).
+  auto emit2 = [&](int kt, int s, float pa, float pb) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
+    const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int key = kt + 32 * s + lane;
+    if constexpr (SCORES) {
+      if (active && key < kend) scores[r * S + key] = key < nvis ? v : -INFINITY;
+    } else {
+      const uint64_t mk = __ballot(key < nvis && v > theta_f);
+      if (mk) {
+        if ((mk >> lane) & 1ull) {
+          const int pos = cnt + __popcll(mk & ((1ull << lane) - 1));
+          sk[pos] = ord_f32(v);
+          si[pos] = key;
+        }
+        cnt += __popcll(mk);
+      }
+    }
+  };
+  // One sub-tile on its own (128 heads, where a second partial sum held across
+  // sub-tiles costs spills): lanes 0..31 end with the scores of keys kt + 32 s + l.
+  auto emit1 = [&](int kt, int s, float part) {
+    part += __uint_as_float(
+        __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false)[1]);
     const int key = kt + 32 * s + col;
     if constexpr (SCORES) {
       if (active && hf == 0 && key < kend) scores[r * S + key] = key < nvis ? part : -INFINITY;
     } else {
-      const uint32_t ok = ord_f32(part);
-      const uint64_t mk = __ballot(hf == 0 && key < nvis && ok > theta);
+      const uint64_t mk = __ballot(hf == 0 && key < nvis && part > theta_f);
       if (mk) {
         if ((mk >> lane) & 1ull) {
           const int pos = cnt + __popcll(mk & ((1ull << lane) - 1));
-          sk[pos] = ok;
+          sk[pos] = ord_f32(part);
           si[pos] = key;
         }
         cnt += __popcll(mk);
@@ -280,7 +300,7 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
   // room for the next tile's entries
   auto make_room = [&]() {
     if (!SCORES && cnt > PS_CAP - PS_NK) {
-      theta = ps_compact(sk, si, whist[wave], cnt, topk);
+      theta_f = unord_f32(ps_compact(sk, si, whist[wave], cnt, topk));
       cnt = topk;
     }
   };
@@ -305,14 +325,17 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
       }
       const uint8_t* buf = tiles[it & 1];
       const bool cur = kt < nvis;  // uniform per wave
+      // partial sums of sub-tiles 0 and 1, then 2 (3 is reduced after the barrier)
+      float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f;
+      static_assert(NS == 4, "sub-tiles leave in pairs");
       if (cur) {
-#pragma unroll
-        for (int s = 0; s + 1 < NS; ++s) {
-          PS_BOP(s + 1, buf);
-          float part = 0.0f;
-          PS_MMA_RED((s + 1) & 1, s & 1, part);
-          emit(kt, s, part);
-        }
+        PS_BOP(1, buf);
+        PS_MMA_RED(1, 0, p0);
+        PS_BOP(2, buf);
+        PS_MMA_RED(0, 1, p1);
+        emit2(kt, 0, p0, p1);
+        PS_BOP(3, buf);
+        PS_MMA_RED(1, 0, p2);
       }
       // keep the store of the next tile after the sub-tiles above: hoisted above
       // them, the store would wait for the tile's global loads before any MFMA
@@ -335,7 +358,7 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
         PS_RED(part, (NS - 1) & 1);
       }
       if (cur) {
-        emit(kt, NS - 1, part);
+        emit2(kt, 2, p2, part);
         make_room();
       }
     }
@@ -361,9 +384,7 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
 #pragma unroll
             for (int i = 0; i < 16; ++i) part = fmaf(wv[ht][i], relu_bits_f(acc[0][0][i]), part);
           }
-          part += __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
-                                                                   false, false)[1]);
-          emit(kt, s, part);
+          emit1(kt, s, part);
         }
         make_room();
       }
