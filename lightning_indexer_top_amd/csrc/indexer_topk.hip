@@ -15,13 +15,19 @@
 // in 128-key bf16 tiles (double buffered, loaded cooperatively, XOR-swizzled so
 // the operand reads are conflict free); each wave scores each 32-key sub-tile
 // with 16 v_mfma_f32_32x32x16_bf16 (64 heads) and reduces ReLU x weight over the
-// heads in registers.  Selection per row: a running threshold theta (the current
+// heads in registers.  fp8 keys (E4M3 codes + one fp32 scale per key, the
+// indexer's FP8 key cache of "Long context", "The Architectural Answer",
+// Derivation 4) are read as stored, widened to bf16 on their way into LDS (exact:
+// every E4M3 value is a bf16 value), and the key's scale multiplies the head sum
+// (it is positive, so it commutes with the ReLU).  Selection per row: a running threshold theta (the current
 // k-th best) and a candidate list of CAP entries in LDS kept in key-index order.
 // A score is listed when it beats theta; when the list is full the wave compacts
 // it to the exact current top-k (bisection on the orderable score bits for the
 // k-th value, ties to the smaller index, order-preserving) and raises theta.
 // Keys arrive in increasing index order, so an entry equal to theta loses its
 // tie and a strict comparison is exact.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -131,13 +137,27 @@ __device__ uint32_t ps_compact(uint32_t* sk, int32_t* si, uint32_t* hw, int cnt,
   return T;
 }
 
+// Eight key elements into the bf16 LDS tile: bf16 chunks as they are; eight E4M3
+// codes widened exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1), element e of
+// the chunk from byte e.
+__device__ __forceinline__ uint4 widen(const uint4 v) { return v; }
+__device__ __forceinline__ uint4 widen(const uint2 v) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+                    __builtin_bit_cast(uint32_t, d));
+}
+
 // SCORES: write every score to scores [B*T, S] (masked keys -inf) instead of
 // selecting (the same contraction for li_indexer_score at prefill shapes).
-template <int HT, bool SCORES>
+template <int HT, bool SCORES, bool F8K = false>
 __global__ __launch_bounds__(PS_WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
-                           const uint16_t* __restrict__ k, const int32_t* __restrict__ nv, int T, int S, int H,
-                           int topk, int32_t* __restrict__ idx_out, float* __restrict__ val_out,
+                           const void* __restrict__ k, const float* __restrict__ ks, const int32_t* __restrict__ nv,
+                           int T, int S, int H, int topk, int32_t* __restrict__ idx_out, float* __restrict__ val_out,
                            float* __restrict__ scores) {
   // LDS: two key tiles (64 keys x 256 B, 16-byte chunks XOR-swizzled by key),
   // then per wave a candidate list (orderable keys, ids)
@@ -186,7 +206,9 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
     }
   }
 
-  const uint16_t* kbase = k + (int64_t)b * S * 128;
+  // key rows: 256 bytes (bf16) or 128 bytes (fp8 codes) each
+  const uint8_t* kbase = (const uint8_t*)k + (int64_t)b * S * (F8K ? 128 : 256);
+  const float* sbase = F8K ? ks + (int64_t)b * S : nullptr;
   // cooperative tile load: thread tid moves the 16-byte chunks
   // c = tid + 512 j (key c >> 4, chunk c & 15)
   static_assert(PS_NK * 16 == PS_CPT * PS_WAVES * 64, "whole chunks per thread");
@@ -199,15 +221,28 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
   float theta_f = -INFINITY;   // score to beat (every finite score beats it at first)
 
   const int ntiles = (kend + PS_NK - 1) / PS_NK;
-  // four named registers, not an array: an array here is kept in scratch memory
+  // four named registers, not an array: an array here is kept in scratch memory.
+  // A chunk is 8 key elements: 16 bytes of a bf16 row, 8 bytes of an fp8 row.
   static_assert(PS_CPT == 4, "chunk registers below");
-  uint4 reg0, reg1, reg2, reg3;
+  typedef typename std::conditional<F8K, uint2, uint4>::type chunk_t;
+  chunk_t reg0, reg1, reg2, reg3;
 #define PS_LOAD(j, key0) \
-  reg##j = *(const uint4*)(kbase + (int64_t)min((key0) + cn0 + KSTEP * j, S - 1) * 128 + cc * 8)
+  reg##j = *(const chunk_t*)(kbase + (int64_t)min((key0) + cn0 + KSTEP * j, S - 1) * (F8K ? 128 : 256) + \
+                             cc * (F8K ? 8 : 16))
 #define PS_STORE(j, buf) \
-  *(uint4*)((buf) + (cn0 + KSTEP * j) * 256 + ((cc ^ ((cn0 + KSTEP * j) & 15)) << 4)) = reg##j
+  *(uint4*)((buf) + (cn0 + KSTEP * j) * 256 + ((cc ^ ((cn0 + KSTEP * j) & 15)) << 4)) = widen(reg##j)
+  // scales of this lane's keys of a tile: kt + lane and kt + 64 + lane (the keys
+  // whose scores it holds when a pair of sub-tiles leaves)
+  float scA = 1.0f, scB = 1.0f, nscA = 1.0f, nscB = 1.0f;
+  auto load_scales = [&](int kt, float& a, float& b2) {
+    if constexpr (F8K) {
+      a = sbase[min(kt + lane, S - 1)];
+      b2 = sbase[min(kt + 64 + lane, S - 1)];
+    }
+  };
   if (ntiles > 0) {
     PS_LOAD(0, 0); PS_LOAD(1, 0); PS_LOAD(2, 0); PS_LOAD(3, 0);
+    load_scales(0, scA, scB);
     PS_STORE(0, tiles[0]); PS_STORE(1, tiles[0]); PS_STORE(2, tiles[0]); PS_STORE(3, tiles[0]);
   }
   // every load issued so far (query block, weights, first tile) has landed: the
@@ -259,9 +294,10 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
   // is written out, or listed when it beats theta (compared as floats: -0 and +0
   // are equal as in the orderable image; lanes ascend with the key, so the list
   // stays in index order).
-  auto emit2 = [&](int kt, int s, float pa, float pb) {
+  auto emit2 = [&](int kt, int s, float pa, float pb, float sc) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
-    const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if constexpr (F8K) v *= sc;
     const int key = kt + 32 * s + lane;
     if constexpr (SCORES) {
       if (active && key < kend) scores[r * S + key] = key < nvis ? v : -INFINITY;
@@ -282,6 +318,13 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
   auto emit1 = [&](int kt, int s, float part) {
     part += __uint_as_float(
         __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false)[1]);
+    if constexpr (F8K) {
+      // the scale of key kt + 32 s + col: held by lane col (s even) or 32 + col (s odd)
+      // of scA (s < 2) or scB
+      const float sc = s < 2 ? scA : scB;
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc), false, false);
+      part *= (s & 1) ? __uint_as_float(x[1]) : sc;
+    }
     const int key = kt + 32 * s + col;
     if constexpr (SCORES) {
       if (active && hf == 0 && key < kend) scores[r * S + key] = key < nvis ? part : -INFINITY;
@@ -322,6 +365,7 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
       const bool more = it + 1 < ntiles;
       if (more) {
         PS_LOAD(0, kt + PS_NK); PS_LOAD(1, kt + PS_NK); PS_LOAD(2, kt + PS_NK); PS_LOAD(3, kt + PS_NK);
+        load_scales(kt + PS_NK, nscA, nscB);
       }
       const uint8_t* buf = tiles[it & 1];
       const bool cur = kt < nvis;  // uniform per wave
@@ -333,7 +377,7 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
         PS_MMA_RED(1, 0, p0);
         PS_BOP(2, buf);
         PS_MMA_RED(0, 1, p1);
-        emit2(kt, 0, p0, p1);
+        emit2(kt, 0, p0, p1, scA);
         PS_BOP(3, buf);
         PS_MMA_RED(1, 0, p2);
       }
@@ -358,9 +402,11 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
         PS_RED(part, (NS - 1) & 1);
       }
       if (cur) {
-        emit2(kt, 2, p2, part);
+        emit2(kt, 2, p2, part, scB);
         make_room();
       }
+      scA = nscA;
+      scB = nscB;
     }
   } else {
     // 128 heads: a second accumulator set does not fit the register file, so each
@@ -371,6 +417,7 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
       const bool more = it + 1 < ntiles;
       if (more) {
         PS_LOAD(0, kt + PS_NK); PS_LOAD(1, kt + PS_NK); PS_LOAD(2, kt + PS_NK); PS_LOAD(3, kt + PS_NK);
+        load_scales(kt + PS_NK, nscA, nscB);
       }
       const uint8_t* buf = tiles[it & 1];
       if (kt < nvis) {  // uniform per wave
@@ -394,6 +441,8 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
         PS_STORE(0, nb); PS_STORE(1, nb); PS_STORE(2, nb); PS_STORE(3, nb);
       }
       __syncthreads();
+      scA = nscA;
+      scB = nscB;
     }
   }
 #undef PS_MMA_RED
@@ -425,26 +474,38 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
 }
 
 bool prefill_scores_apply(int q_type, int k_type, int T, int H) {
-  return q_type == DT_BF16 && k_type == DT_BF16 && T >= 2 * PS_WAVES && H <= 128;
+  return q_type == DT_BF16 && (k_type == DT_BF16 || k_type == DT_FP8) && T >= 2 * PS_WAVES && H <= 128;
 }
 
-hipError_t launch_prefill_scores(const uint16_t* q, const float* w, const uint16_t* k, const int32_t* nv, int B,
-                                 int T, int S, int H, float* scores, hipStream_t st) {
+// One launch of the tiled kernel: scores (SC) or the fused selection, bf16 or fp8
+// keys, 32 / 64 / 128 heads.
+template <bool SC>
+static hipError_t launch_prefill(const uint16_t* q, const float* w, const void* k, int k_type, const float* ks,
+                                 const int32_t* nv, int B, int T, int S, int H, int topk, int32_t* idx, float* val,
+                                 float* scores, hipStream_t st) {
   const int blocks = B * ((T + PS_WAVES - 1) / PS_WAVES);
-  if (H <= 32)
-    prefill_select_kernel<1, true><<<blocks, PS_WAVES * 64, 0, st>>>(q, w, k, nv, T, S, H, 0, nullptr, nullptr,
-                                                                    scores);
-  else if (H <= 64)
-    prefill_select_kernel<2, true><<<blocks, PS_WAVES * 64, 0, st>>>(q, w, k, nv, T, S, H, 0, nullptr, nullptr,
-                                                                    scores);
-  else
-    prefill_select_kernel<4, true><<<blocks, PS_WAVES * 64, 0, st>>>(q, w, k, nv, T, S, H, 0, nullptr, nullptr,
-                                                                    scores);
+  const dim3 g(blocks), t(PS_WAVES * 64);
+  const bool f8 = k_type == DT_FP8;
+  if (H <= 32) {
+    if (f8) prefill_select_kernel<1, SC, true><<<g, t, 0, st>>>(q, w, k, ks, nv, T, S, H, topk, idx, val, scores);
+    else prefill_select_kernel<1, SC, false><<<g, t, 0, st>>>(q, w, k, ks, nv, T, S, H, topk, idx, val, scores);
+  } else if (H <= 64) {
+    if (f8) prefill_select_kernel<2, SC, true><<<g, t, 0, st>>>(q, w, k, ks, nv, T, S, H, topk, idx, val, scores);
+    else prefill_select_kernel<2, SC, false><<<g, t, 0, st>>>(q, w, k, ks, nv, T, S, H, topk, idx, val, scores);
+  } else {
+    if (f8) prefill_select_kernel<4, SC, true><<<g, t, 0, st>>>(q, w, k, ks, nv, T, S, H, topk, idx, val, scores);
+    else prefill_select_kernel<4, SC, false><<<g, t, 0, st>>>(q, w, k, ks, nv, T, S, H, topk, idx, val, scores);
+  }
   return hipGetLastError();
 }
 
+hipError_t launch_prefill_scores(const uint16_t* q, const float* w, const void* k, int k_type, const float* ks,
+                                 const int32_t* nv, int B, int T, int S, int H, float* scores, hipStream_t st) {
+  return launch_prefill<true>(q, w, k, k_type, ks, nv, B, T, S, H, 0, nullptr, nullptr, scores, st);
+}
+
 static bool use_fused(int q_type, int k_type, int T, int H, int topk) {
-  return q_type == DT_BF16 && k_type == DT_BF16 && T >= 2 * PS_WAVES && topk <= PS_KMAX && H <= 128;
+  return prefill_scores_apply(q_type, k_type, T, H) && topk <= PS_KMAX;
 }
 
 bool prefill_fused_apply(int q_type, int k_type, int T, int H, int topk) {
@@ -463,21 +524,8 @@ size_t indexer_topk_ws_bytes(int q_type, int k_type, int B, int T, int S, int H,
 hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const void* k, int k_type, const float* ks,
                                const int32_t* nv, int B, int T, int S, int H, int topk, int32_t* idx, float* val,
                                void* ws, hipStream_t st) {
-  if (use_fused(q_type, k_type, T, H, topk)) {
-    const int blocks = B * ((T + PS_WAVES - 1) / PS_WAVES);
-    const uint16_t* qq = (const uint16_t*)q;
-    const uint16_t* kk = (const uint16_t*)k;
-    if (H <= 32)
-      prefill_select_kernel<1, false><<<blocks, PS_WAVES * 64, 0, st>>>(qq, w, kk, nv, T, S, H, topk, idx, val,
-                                                                       nullptr);
-    else if (H <= 64)
-      prefill_select_kernel<2, false><<<blocks, PS_WAVES * 64, 0, st>>>(qq, w, kk, nv, T, S, H, topk, idx, val,
-                                                                       nullptr);
-    else
-      prefill_select_kernel<4, false><<<blocks, PS_WAVES * 64, 0, st>>>(qq, w, kk, nv, T, S, H, topk, idx, val,
-                                                                       nullptr);
-    return hipGetLastError();
-  }
+  if (use_fused(q_type, k_type, T, H, topk))
+    return launch_prefill<false>((const uint16_t*)q, w, k, k_type, ks, nv, B, T, S, H, topk, idx, val, nullptr, st);
   float* scores = (float*)ws;
   void* tws = (uint8_t*)ws + align256((size_t)B * T * S * sizeof(float));
   if (held_select_apply(q_type, k_type, B * T, S, H, topk)) {

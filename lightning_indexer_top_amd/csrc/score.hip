@@ -713,7 +713,7 @@ hipError_t launch_score(const void* q, int q_type, const float* w, const void* k
                         const int32_t* nv, int B, int T, int S, int H, float* scores, hipStream_t st) {
   const int R = B * T;
   if (prefill_scores_apply(q_type, k_type, T, H))
-    return launch_prefill_scores((const uint16_t*)q, w, (const uint16_t*)k, nv, B, T, S, H, scores, st);
+    return launch_prefill_scores((const uint16_t*)q, w, k, k_type, ks, nv, B, T, S, H, scores, st);
   if (q_type == DT_BF16 && (k_type == DT_FP8 || k_type == DT_BF16)) {
     const uint16_t* qq = (const uint16_t*)q;
     const uint8_t* kk = (const uint8_t*)k;

@@ -85,6 +85,33 @@ def test_fused_prefill_shapes(T, S, H, k):
     _fused_check(x, sp, k, f"T={T} S={S} H={H} k={k}")
 
 
+@pytest.mark.parametrize("T,S,H,k", [(100, 20000, 64, 512), (16, 5000, 8, 64), (40, 3000, 100, 200)])
+def test_fused_prefill_fp8_keys(T, S, H, k):
+    # fp8 keys through the fused prefill kernel: no workspace, the selection of the
+    # GPU's own (scaled) scores, and the oracle band
+    print("fused prefill fp8", T, S, H, k, flush=True)
+    sp = workloads.spec("prefill_chunk", T=T, S=S, H=H, key="fp8", seed=0x5EED0E00 + T + S)
+    x, d = inputs(sp)
+    B = 1
+    assert li.indexer_topk_workspace_bytes(li.LI_BF16, li.LI_FP8_E4M3, B, T, S, H, k) == 0
+    g_idx = torch.empty((B * T, k), dtype=torch.int32, device="cuda")
+    g_val = torch.empty((B * T, k), dtype=torch.float32, device="cuda")
+    st = li.lib().li_indexer_topk(d["q"].data_ptr(), li.LI_BF16, d["w"].data_ptr(), d["k"].data_ptr(),
+                                  li.LI_FP8_E4M3, d["k_scale"].data_ptr(), d["nv"].data_ptr(), B, T, S, H, 128, k,
+                                  g_idx.data_ptr(), g_val.data_ptr(), None, 0,
+                                  torch.cuda.current_stream().cuda_stream)
+    assert st == 0, li.lib().li_last_error()
+    g_scores = li.indexer_score(d["q"], d["w"], d["k"], d["k_scale"], d["nv"])
+    torch.cuda.synchronize()
+    g_idx = g_idx.cpu().numpy()
+    r_idx, r_val = oracle.topk(g_scores.cpu().numpy().astype(np.float64), k, x["nv"])
+    assert np.array_equal(g_idx, r_idx)
+    fin = r_idx >= 0
+    assert np.array_equal(g_val.cpu().numpy().astype(np.float64)[fin], r_val[fin])
+    o = oracle.indexer_score(x["q"], oracle.BF16, x["w"], x["k"], oracle.FP8_E4M3, x["k_scale"], x["nv"])
+    assert_topk_band(g_idx, o, k, x["nv"], f"fp8 T={T} S={S} H={H} k={k}")
+
+
 def test_fused_prefill_ties_and_masks():
     # integer-valued queries and keys: many exactly equal scores, so the list
     # compactions resolve ties by index; visible counts 0, below k, at k, ragged

@@ -137,6 +137,50 @@ def test_prefill_tiled_scores(B, T, S, H):
         assert np.isneginf(g[r, nv[r]:]).all() and np.isfinite(g[r, : nv[r]]).all()
 
 
+@pytest.mark.parametrize("B,T,S,H", [(2, 17, 1000, 64), (1, 40, 3001, 100), (3, 64, 513, 8), (1, 16, 5000, 32)])
+def test_prefill_fp8_keys(B, T, S, H):
+    # fp8 keys at prefill shapes: the tiled kernel widens the codes to bf16 on their
+    # way into LDS and multiplies each key's head sum by its scale; ragged rows, key
+    # tails and visible counts in [0, S]
+    print("prefill fp8 keys", B, T, S, H, flush=True)
+    sp = workloads.spec("prefill_chunk", B=B, T=T, S=S, H=H, key="fp8", seed=0x5EED0D00 + T + S)
+    rng = np.random.default_rng(T * S + 1)
+    nv = rng.integers(0, S + 1, B * T).astype(np.int32)
+    nv[0], nv[-1] = 0, S
+    g, o, _ = run(sp, nv=nv)
+    assert_scores_close(g, o, f"prefill fp8 B={B} T={T} S={S} H={H}")
+    for r in range(B * T):
+        assert np.isneginf(g[r, nv[r]:]).all() and np.isfinite(g[r, : nv[r]]).all()
+
+
+def test_prefill_fp8_every_code():
+    """Exact widening of every finite E4M3 code in every byte position of a chunk:
+    query row r has q = +1 (head 0) and -1 (head 1) at dimension d_r and zeros
+    elsewhere, w = (1, 2^-16), scales powers of two, so each score is one decoded
+    code, ReLU'd from either side, with no rounding anywhere: the GPU's fp32 scores
+    must equal the oracle's (which decodes the codes itself) bit for bit."""
+    print("prefill fp8 every code", flush=True)
+    T, H = 16, 2
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)  # 0x7F, 0xFF are NaN
+    S = 2 * len(codes)
+    d_r = np.array([8 * r + (r % 8) for r in range(T)])  # every byte offset of a chunk, several chunks
+    k = codes[(np.arange(S)[:, None] + 7 * np.arange(128)[None, :]) % len(codes)][None]  # [1, S, 128]
+    ks = np.ldexp(1.0, (np.arange(S) % 5) - 2).astype(np.float32)[None]
+    qf = np.zeros((1, T, H, 128), np.float32)
+    for r in range(T):
+        qf[0, r, 0, d_r[r]] = 1.0
+        qf[0, r, 1, d_r[r]] = -1.0
+    q = (qf.view(np.uint32) >> 16).astype(np.uint16)  # exact bf16 of +-1 and 0
+    w = np.tile(np.array([1.0, 2.0 ** -16], np.float32), (1, T, 1))
+    g = li.indexer_score(dev(q, "bf16"), dev(w), dev(k, "fp8"), dev(ks))
+    torch.cuda.synchronize()
+    o = oracle.indexer_score(q, oracle.BF16, w, k, oracle.FP8_E4M3, ks)
+    assert np.array_equal(g.cpu().numpy(), o.astype(np.float32))
+    # every code reached some row at each of its byte offsets
+    seen = {(int(k[0, s, d_r[r]]), int(d_r[r] % 8)) for r in range(T) for s in range(S)}
+    assert len(seen) == len(codes) * 8
+
+
 def test_visible_count_edges():
     print("nv edges", flush=True)
     sp = workloads.spec("batched_decode", B=1, T=6, S=700, H=64, seed=0x5EED0400)
