@@ -184,7 +184,7 @@ def oracle_baseline(value, unit, sample, seconds):
 # each scaled by what the same counter reads for a plain 1 GiB copy: FETCH x2.0,
 # WRITE x1.0).  Valid only for the kernel sources it was taken on; null otherwise.
 SCORE_TRAFFIC = {"sources": ["lightning_indexer_top_amd/csrc/score.hip", "lightning_indexer_top_amd/csrc/common.h"],
-                 "sha256_16": "ebd11ec84b9c566a", "fetch_kib": 272517.0, "write_kib": 8192.0}
+                 "sha256_16": "4921648ae2f57cfb", "fetch_kib": 272516.0, "write_kib": 8192.0}
 
 
 # ---- measured ceilings ------------------------------------------------------
@@ -418,14 +418,28 @@ def prefill_sample_rows(T):
     return np.asarray(rows, np.int64)
 
 
-def bench_prefill(torch, li, workloads, steps, warmup, cpu=True):
-    sp = workloads.spec("prefill_chunk")
+def oracle_kt(key):
+    import oracle
+    return {"bf16": oracle.BF16, "fp8": oracle.FP8_E4M3, "f32": oracle.F32}[key]
+
+
+def bench_prefill_fp8(torch, li, workloads, steps, warmup, cpu=True):
+    return bench_prefill(torch, li, workloads, steps, warmup, cpu=cpu, key="fp8")
+
+
+def bench_prefill(torch, li, workloads, steps, warmup, cpu=True, key="bf16"):
+    """The prefill chunk; key="fp8": the same chunk with its keys stored as E4M3
+    codes + one fp32 scale per key (the tiled kernel widens them in LDS)."""
+    sp = workloads.spec("prefill_chunk", key=key)
     B, T, S, H, k = sp["B"], sp["T"], sp["S"], sp["H"], sp["topk"]
-    log(f"[prefill] generating inputs T={T} S={S} H={H}")
+    tag = "prefill" if key == "bf16" else "prefill_fp8"
+    log(f"[{tag}] generating inputs T={T} S={S} H={H} keys {key}")
     x = workloads.indexer_inputs(sp)
-    q, w, kk, nv = to_dev(torch, x["q"], "bf16"), to_dev(torch, x["w"]), to_dev(torch, x["k"], "bf16"), \
+    q, w, kk, nv = to_dev(torch, x["q"], "bf16"), to_dev(torch, x["w"]), to_dev(torch, x["k"], key), \
         to_dev(torch, x["nv"])
-    nb = li.indexer_topk_workspace_bytes(li.LI_BF16, li.LI_BF16, B, T, S, H, k)
+    ks = to_dev(torch, x["k_scale"]) if key == "fp8" else None
+    kt = li.LI_FP8_E4M3 if key == "fp8" else li.LI_BF16
+    nb = li.indexer_topk_workspace_bytes(li.LI_BF16, kt, B, T, S, H, k)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
     idx = torch.empty((B * T, k), dtype=torch.int32, device="cuda")
     ev = []
@@ -433,7 +447,7 @@ def bench_prefill(torch, li, workloads, steps, warmup, cpu=True):
     def step(i):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        li.indexer_topk(q, w, kk, k, None, nv, with_values=False, workspace=ws, out=(idx, None))
+        li.indexer_topk(q, w, kk, k, ks, nv, with_values=False, workspace=ws, out=(idx, None))
         e1.record()
         ev.append((e0, e1))
 
@@ -448,7 +462,7 @@ def bench_prefill(torch, li, workloads, steps, warmup, cpu=True):
     def step2(i):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        li.indexer_score(q, w, kk, None, nv, out=scores)
+        li.indexer_score(q, w, kk, ks, nv, out=scores)
         e1.record()
         ev2.append((e0, e1))
 
@@ -457,8 +471,10 @@ def bench_prefill(torch, li, workloads, steps, warmup, cpu=True):
     ms2 = float(np.mean([a.elapsed_time(b) for a, b in ev2[-n2:]]))
     tf2 = flop / (ms2 * 1e-3) / 1e12
     del scores
-    log(f"[prefill] fused {ms:.2f} ms -> {tf:.1f} TFLOP/s; scores only {ms2:.2f} ms -> {tf2:.1f} TFLOP/s")
-    res = {"workload": "prefill_chunk T=4096 S=131072 H=64 bf16 causal top-512", "ms": round(ms, 4),
+    log(f"[{tag}] fused {ms:.2f} ms -> {tf:.1f} TFLOP/s; scores only {ms2:.2f} ms -> {tf2:.1f} TFLOP/s")
+    kdesc = "bf16" if key == "bf16" else "fp8 e4m3 + fp32 scale"
+    res = {"workload": f"prefill_chunk T=4096 S=131072 H=64 bf16 queries, {kdesc} keys, causal top-512",
+           "ms": round(ms, 4),
            "value": round(tf, 2), "unit": "TFLOP/s", "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
            "flop": flop, "workspace_bytes": nb, "unfused_score_ms": round(ms2, 4),
            "unfused_score_tflops": round(tf2, 2), "unfused_frac_bf16_peak": round(tf2 / BF16_PEAK_TFLOPS, 4)}
@@ -466,8 +482,8 @@ def bench_prefill(torch, li, workloads, steps, warmup, cpu=True):
         import oracle
         rows = prefill_sample_rows(T)
         t0 = time.perf_counter()
-        o = oracle.indexer_score(x["q"][:, rows], oracle.BF16, x["w"][:, rows], x["k"], oracle.BF16, None,
-                                 x["nv"][rows])
+        o = oracle.indexer_score(x["q"][:, rows], oracle.BF16, x["w"][:, rows], x["k"], oracle_kt(key),
+                                 x["k_scale"], x["nv"][rows])
         oracle.topk(o, k, x["nv"][rows])
         dt = time.perf_counter() - t0
         sflop = prefill_flop(x["nv"][rows], H)
@@ -926,7 +942,8 @@ def bench_paged(torch, li, workloads, steps, warmup, cpu=True):
     return res
 
 
-SECONDARY = {"tiny_decode": bench_tiny, "prefill_chunk": bench_prefill, "compact_search": bench_compact,
+SECONDARY = {"tiny_decode": bench_tiny, "prefill_chunk": bench_prefill, "prefill_chunk_fp8": bench_prefill_fp8,
+             "compact_search": bench_compact,
              "select_attend": bench_select_attend, "pooled_decode": bench_pooled, "paged_decode": bench_paged,
              "pq_search": bench_pq, "layer_stream": bench_stream}
 
