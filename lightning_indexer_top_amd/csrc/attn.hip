@@ -7,28 +7,29 @@
 // selected row is a 576-element latent shared by every query head; keys use all 576
 // elements and values the first 512.
 //
-// One workgroup of 8 waves handles one sequence and 32 query heads, two waves per
-// SIMD.  Selected rows arrive 32 at a time (a chunk) by direct global-to-LDS loads
-// into a ring of NBUF chunk buffers.  Per chunk:
-//   logits  S^T[row, head] = K . Q^T as four 16 x 16 tiles (row half x head half),
-//           each split over two waves by alternate 32-element K-steps
-//           (v_mfma_f32_16x16x32_bf16); the second wave's partial sum goes
-//           through LDS to the first, which owns the tile's softmax;
+// One workgroup of 8 waves handles one sequence and 32 query heads, as two
+// independent halves of four waves: half h takes chunks h, h + 2, h + 4, ... (a
+// chunk is 32 selected rows), each into its own two of the four LDS chunk buffers
+// (direct global-to-LDS loads, the next chunk in flight while one is computed), and
+// its four waves meet at barriers of their own (an LDS counter), so the two waves
+// that share a SIMD belong to different halves and one runs while the other waits.
+// Per chunk, wave w of a half:
+//   logits  one 16 x 16 tile S^T[row, head] = K . Q^T (rows 16 (w >> 1) .., heads
+//           16 (w & 1) ..) over all 18 K-steps (v_mfma_f32_16x16x32_bf16), the
+//           query operand in VGPRs;
 //   softmax in base 2 against a per-head reference maximum that moves only when a
-//           logit exceeds it by more than 2^8 (then the outputs and sums are
-//           rescaled), so the common chunk needs no cross-wave maximum;
-//   values  O^T[dv, head] += V^T . P^T with v_mfma_f32_32x32x16_bf16, each wave
-//           owning 64 of the 512 value columns; V^T comes from the same LDS rows by
-//           transpose reads, P^T (bf16) from a small LDS tile.
-// The chunks are software-pipelined: the logits of chunk c + 1 are computed beside
-// the softmax of chunk c, with two workgroup barriers per chunk.
+//           logit exceeds it by more than 2^8 (a flag in LDS then sends the half's
+//           waves through the rescale path), probabilities (bf16) into the half's
+//           LDS tile;
+//   values  O^T[dv, head] += V^T . P^T for its 128 of the 512 value columns and all
+//           32 heads (v_mfma_f32_32x32x16_bf16), V^T by transpose reads
+//           (ds_read_b64_tr_b16).
+// At the end the halves' outputs, reference maxima and sums are merged through LDS.
 
 #include "common.h"
 #include "launch.h"
 
 namespace li {
-
-constexpr int ATTN_NBUF = 4;  // chunk buffers
 
 constexpr int AT_DQK = 576;
 constexpr int AT_DV = 512;
@@ -36,10 +37,12 @@ constexpr int AT_CH = 32;                   // rows per chunk
 constexpr int AT_RB = 2 * AT_DQK;           // bytes per row
 constexpr int AT_PPR = AT_RB / 16;          // 16-byte pieces per row (72)
 constexpr int AT_CHB = AT_CH * AT_RB;       // bytes per chunk buffer
+constexpr int AT_NBUF = 4;                  // chunk buffers: two per half
 constexpr int AT_KMAX = 2048;               // selected rows per sequence at most
 constexpr int AT_PHS = 80;                  // LDS bytes per head of the probability tile
 constexpr int AT_OSTR = 2 * AT_DV + 16;     // LDS bytes per head of the output staging
 constexpr float AT_MARGIN = 8.0f;           // reference-maximum slack, base-2 units
+constexpr int AT_SPIN = 1 << 22;            // bound of a half-barrier wait (never reached)
 static_assert(AT_CH * AT_PPR == 36 * 64, "36 load instructions of 64 pieces per chunk");
 
 // The pieces of a row are swizzled inside each run of 8: piece p of row r sits in
@@ -52,69 +55,35 @@ static_assert(AT_CH * AT_PPR == 36 * 64, "36 load instructions of 64 pieces per 
 // read of 16 lanes: 4 rows x 2 adjacent pieces).
 __device__ __forceinline__ int at_sw(int r) { return ((((r & 3) << 1) | ((r >> 2) & 1)) ^ ((r >> 2) & 2)); }
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
 // Workgroup barrier after this wave's LDS accesses have completed.  Written out so
 // that no fence makes the wave wait for its row loads still in flight.
 __device__ __forceinline__ void at_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-// Reads of the chunk buffers are written out as well (the compiler would make each
-// of them wait for every row load in flight), and wait for themselves before the
-// statement ends: the nine 16-byte logit operands at ka + 128 i, then the eight
-// transpose reads (ds_read_b64_tr_b16: in each group of 16 lanes, lane 4 a + b
-// receives element b of the 4-element rows read by lanes a, a + 4, a + 8, a + 12)
-// of the value operands, v[4 t + e] at a_t(e & 1) plus 16 rows (18432 bytes) for
-// e >= 2; then six 4-byte reads of row indices (ia[i] -> id[i]) for the loads to come.
-__device__ __forceinline__ void at_read_kv(i32x4 (&r)[9], i32x2 (&v)[8], int (&id)[6], uint32_t ka, uint32_t a00,
-                                           uint32_t a01, uint32_t a10, uint32_t a11, const uint32_t (&ia)[6]) {
-  asm volatile(
-      "ds_read_b128 %0, %23\n\t"
-      "ds_read_b128 %1, %23 offset:128\n\t"
-      "ds_read_b128 %2, %23 offset:256\n\t"
-      "ds_read_b128 %3, %23 offset:384\n\t"
-      "ds_read_b128 %4, %23 offset:512\n\t"
-      "ds_read_b128 %5, %23 offset:640\n\t"
-      "ds_read_b128 %6, %23 offset:768\n\t"
-      "ds_read_b128 %7, %23 offset:896\n\t"
-      "ds_read_b128 %8, %23 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %9, %24\n\t"
-      "ds_read_b64_tr_b16 %10, %25\n\t"
-      "ds_read_b64_tr_b16 %11, %24 offset:18432\n\t"
-      "ds_read_b64_tr_b16 %12, %25 offset:18432\n\t"
-      "ds_read_b64_tr_b16 %13, %26\n\t"
-      "ds_read_b64_tr_b16 %14, %27\n\t"
-      "ds_read_b64_tr_b16 %15, %26 offset:18432\n\t"
-      "ds_read_b64_tr_b16 %16, %27 offset:18432\n\t"
-      "ds_read_b32 %17, %28\n\t"
-      "ds_read_b32 %18, %29\n\t"
-      "ds_read_b32 %19, %30\n\t"
-      "ds_read_b32 %20, %31\n\t"
-      "ds_read_b32 %21, %32\n\t"
-      "ds_read_b32 %22, %33\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
-        "=&v"(r[8]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
-        "=&v"(v[7]), "=&v"(id[0]), "=&v"(id[1]), "=&v"(id[2]), "=&v"(id[3]), "=&v"(id[4]), "=&v"(id[5])
-      : "v"(ka), "v"(a00), "v"(a01), "v"(a10), "v"(a11), "v"(ia[0]), "v"(ia[1]), "v"(ia[2]), "v"(ia[3]), "v"(ia[4]),
-        "v"(ia[5])
-      : "memory");
+// Barrier of the four waves of a half: once this wave's LDS accesses have completed,
+// one lane adds 1 to the half's counter, then the wave waits until the counter
+// reaches `target` (4 x the number of such barriers the half has passed).  Every
+// wave of the half passes the same sequence of barriers; the wait is bounded.
+__device__ __forceinline__ void at_half_barrier(uint32_t ctr, uint32_t target, int lane) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if (lane == 0) {
+    const uint32_t one = 1;
+    asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(ctr), "v"(one) : "memory");
+  }
+  for (int i = 0; i < AT_SPIN; ++i) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(ctr) : "memory");
+    if (__builtin_amdgcn_readfirstlane(v) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
 }
 
-// The probability operands of the value product (two 16-byte reads) and the
-// rescale flag, read together.
-__device__ __forceinline__ void at_read_p(i32x4& p0, i32x4& p1, int& flag, uint32_t pa, uint32_t fa) {
-  asm volatile(
-      "ds_read_b128 %0, %3\n\t"
-      "ds_read_b128 %1, %3 offset:32\n\t"
-      "ds_read_b32 %2, %4\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(p0), "=&v"(p1), "=&v"(flag)
-      : "v"(pa), "v"(fa)
-      : "memory");
-}
-
-// The nine 16-byte operands at a + 128 i (the query's, read once).
+// Reads of the chunk buffers are written out (the compiler would make each of them
+// wait for every row load in flight) and wait for themselves before the statement
+// ends.
+// The nine 16-byte operands at a + 128 i.
 __device__ __forceinline__ void at_read_k(i32x4 (&r)[9], uint32_t a) {
   asm volatile(
       "ds_read_b128 %0, %9\n\t"
@@ -133,23 +102,52 @@ __device__ __forceinline__ void at_read_k(i32x4 (&r)[9], uint32_t a) {
       : "memory");
 }
 
-// s_waitcnt vmcnt(n) for the counts the row-load pipeline uses (0 and multiples
-// of 4 or 5 up to 15); any other count waits for everything.
-__device__ __forceinline__ void at_wait_loads(int n) {
-  switch (n) {
-    case 15: LI_WAIT_VMCNT(15); break;
-    case 12: LI_WAIT_VMCNT(12); break;
-    case 10: LI_WAIT_VMCNT(10); break;
-    case 8: LI_WAIT_VMCNT(8); break;
-    case 5: LI_WAIT_VMCNT(5); break;
-    case 4: LI_WAIT_VMCNT(4); break;
-    default: LI_WAIT_VMCNT(0); break;
-  }
+// Eight transpose reads (ds_read_b64_tr_b16: in each group of 16 lanes, lane 4 a + b
+// receives element b of the 4-element rows read by lanes a, a + 4, a + 8, a + 12) of
+// value operands: v[4 t + e] at a_t(e & 1), plus 16 rows (18432 bytes) for e >= 2.
+__device__ __forceinline__ void at_read_v(i32x2 (&v)[8], uint32_t a00, uint32_t a01, uint32_t a10, uint32_t a11) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:18432\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:18432\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %11\n\t"
+      "ds_read_b64_tr_b16 %6, %10 offset:18432\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:18432\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a00), "v"(a01), "v"(a10), "v"(a11)
+      : "memory");
 }
 
-__device__ __forceinline__ void at_write_zero(uint32_t a) {
-  const i32x4 z = {0, 0, 0, 0};
-  asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(z) : "memory");
+// The probability operands of the value product (two 16-byte reads) and the
+// rescale flag, read together.
+__device__ __forceinline__ void at_read_p(i32x4& p0, i32x4& p1, int& flag, uint32_t pa, uint32_t fa) {
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %3 offset:32\n\t"
+      "ds_read_b32 %2, %4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(p0), "=&v"(p1), "=&v"(flag)
+      : "v"(pa), "v"(fa)
+      : "memory");
+}
+
+__device__ __forceinline__ int at_read_i32(uint32_t a) {
+  int r;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(a) : "memory");
+  return r;
+}
+
+__device__ __forceinline__ float at_read_f32(uint32_t a) {
+  float r;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r) : "v"(a) : "memory");
+  return r;
+}
+
+__device__ __forceinline__ void at_write_f32(uint32_t a, float v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(a), "v"(v) : "memory");
 }
 
 // PAGED: the latent rows live in a pool read at page size 1 ("Long context",
@@ -157,7 +155,7 @@ __device__ __forceinline__ void at_write_zero(uint32_t a) {
 // management": the token-level sparse read takes pages of one token);
 // slot_table[b * max_slots + s] is the pool row of token s of sequence b.  Slots
 // outside [0, num_slots) are clamped into it.
-template <int NBUF, bool PAGED>
+template <bool PAGED>
 __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ kv,
                                                           const int32_t* __restrict__ idx, int B, int Hq, int S, int k,
@@ -165,12 +163,12 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
                                                           float* __restrict__ lse,
                                                           const int32_t* __restrict__ slot_table, int max_slots,
                                                           int num_slots) {
-  __shared__ __attribute__((aligned(1024))) uint8_t kvbuf[NBUF * AT_CHB];
-  __shared__ int sidx[AT_KMAX];
-  __shared__ f32x4 spart[4][64];
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[32 * AT_PHS];
-  __shared__ float mx[2][32];
-  __shared__ int sflag;
+  __shared__ __attribute__((aligned(1024))) uint8_t kvbuf[AT_NBUF * AT_CHB];
+  __shared__ __attribute__((aligned(16))) int sidx[AT_KMAX];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][32 * AT_PHS];
+  __shared__ float mx[2][2][32];
+  __shared__ int sflag[2];
+  __shared__ uint32_t hbar[2];
 
   // block -> (sequence, head tile): the head tiles of one sequence land on blocks
   // 8 apart, which the dispatcher places on the same XCD, so they share its L2.
@@ -182,13 +180,14 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
   if (b >= B) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave >> 2, w4 = wave & 3;
   const int g = lane >> 4, c16 = lane & 15;  // 16 x 16 tile: lane group, column
   const int hf = lane >> 5, ho = lane & 31;  // 32 x 32 tile: lane half, column (= head)
-  const int tile = wave & 3, rh = tile >> 1, hh = tile & 1, kh = wave >> 2;
-  const int hs = 16 * hh + c16;  // head of this lane's logits
-  i32x4 qb[9];                   // Q^T operands, read from LDS in the prologue
+  const int rh = w4 >> 1, hh = w4 & 1;       // this wave's logit tile
+  const int hs = 16 * hh + c16;              // head of this lane's logits
+  const int nch = (k + AT_CH - 1) / AT_CH;
 
-  // the selected rows' indices, -1 for entries that select nothing
+  // the selected rows' indices (pool rows when paged), -1 for entries that select nothing
   {
     const int32_t* irow = idx + (int64_t)b * k;
     for (int i = tid; i < k; i += 512) {
@@ -200,219 +199,219 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
       sidx[i] = v;
     }
   }
-  if (tid == 0) sflag = 0;
+  if (tid < 2) {
+    sflag[tid] = 0;
+    hbar[tid] = 0;
+  }
   LI_WAIT_VMCNT(0);  // no index load is left in the row-load counts
   __syncthreads();
 
-  // Row loads: load instruction j (0..35) of a chunk fills slots 64 j .. 64 j + 63;
-  // wave w issues j = w + 8 u.  Skipped and missing rows load row 0 and are zeroed
-  // once landed.
-  const int nd = wave < 4 ? 5 : 4;
-  int drow[5], doff[5];
+  const uint8_t* kvb = (const uint8_t*)(kv + (PAGED ? 0 : (int64_t)b * S * AT_DQK));
+  const uint32_t kv_lds = lds_addr(kvbuf), sidx_lds = lds_addr(sidx);
+  // Row loads of a half's chunk: load instruction j (0..35) fills slots 64 j ..
+  // 64 j + 63; wave w4 of the half issues j = w4 + 4 u.  Rows that select nothing load
+  // row 0 and are zeroed once landed.
+  // lane l's row of load u: (64 (w4 + 4 u) + l) / 72, i.e. row r0(u) for lanes below
+  // bnd(u) and r0(u) + 1 above (a load instruction spans at most two rows)
+  int drow[9];
+  uint32_t doff[9];
 #pragma unroll
-  for (int u = 0; u < 5; ++u) {
-    const int s = 64 * (wave + 8 * u) + lane;
+  for (int u = 0; u < 9; ++u) {
+    const int s = 64 * (w4 + 4 * u) + lane;
     const int r = s / AT_PPR;
     const int ps = s - AT_PPR * r;
     drow[u] = r;
-    doff[u] = 16 * ((ps & ~7) | ((ps ^ at_sw(r)) & 7));
+    doff[u] = 16u * (uint32_t)((ps & ~7) | ((ps ^ at_sw(r)) & 7));
   }
-  const uint8_t* kvb = (const uint8_t*)(kv + (PAGED ? 0 : (int64_t)b * S * AT_DQK));
-  const uint32_t kv_lds = lds_addr(kvbuf);
-  const int nch = (k + AT_CH - 1) / AT_CH;
-  // the row indices of this wave's loads of chunk c (LDS reads), then the loads
-  auto row_ids = [&](int c, int (&id)[5]) {
-    const int c0 = c * AT_CH;
+  // the half's chunk c sits in buffer 2 half + (c / 2) % 2
+  auto buf_of = [&](int c) -> uint32_t { return kv_lds + (uint32_t)((2 * half + ((c >> 1) & 1)) * AT_CHB); };
+  // issue this wave's loads of chunk c; returns the chunk's valid rows (bit r: row
+  // 32 c + r selects something), from one index read per lane
+  auto issue = [&](int c) -> uint32_t {
+    const int row = c * AT_CH + (lane & 31);
+    int idv = at_read_i32(sidx_lds + 4u * (uint32_t)min(row, k - 1));
+    if (row >= k) idv = -1;
+    const uint32_t lb = buf_of(c) + 1024u * w4;
 #pragma unroll
-    for (int u = 0; u < 5; ++u) {
-      const int row = c0 + drow[u];
-      const int v = sidx[min(row, k - 1)];
-      id[u] = row < k ? v : -1;
+    for (int u = 0; u < 9; ++u) {
+      const int j = w4 + 4 * u;
+      const int r0 = (64 * j) / AT_PPR;
+      const int bnd = AT_PPR * (r0 + 1) - 64 * j;
+      const int i0 = __builtin_amdgcn_readlane(idv, r0), i1 = __builtin_amdgcn_readlane(idv, min(r0 + 1, 31));
+      const int id = lane < bnd ? i0 : i1;
+      const uint8_t* src = kvb + (int64_t)max(id, 0) * AT_RB + doff[u];
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(uintptr_t)(lb + 4096u * u), 16, 0, 0);
     }
+    return (uint32_t)__ballot(lane < 32 && idv >= 0);
   };
-  auto issue_ids = [&](int c, const int* id) {  // id[0..4]
-    const uint32_t lb = kv_lds + (uint32_t)((c % NBUF) * AT_CHB) + 1024u * wave;
+  // once this wave's loads of chunk c have landed: zero the slots of the rows that
+  // select nothing (vr: the chunk's valid rows)
+  auto zero_fill = [&](int c, uint32_t vr) {
+    if (vr != 0xFFFFFFFFu) {
+      const uint32_t lb = buf_of(c) + 1024u * w4 + 16u * lane;
 #pragma unroll
-    for (int u = 0; u < 5; ++u) {
-      if (u < 4 || wave < 4) {
-        const uint8_t* src = kvb + (int64_t)max(id[u], 0) * AT_RB + doff[u];
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(uintptr_t)(lb + 8192u * u), 16, 0, 0);
-      }
-    }
-  };
-  auto issue = [&](int c) {
-    int id[5];
-    row_ids(c, id);
-    issue_ids(c, id);
-  };
-  // the 32 heads' query rows, laid out like a chunk, into buffer NBUF - 1 (before
-  // that buffer's first chunk): the same slots, row = head
-  auto issue_q = [&]() {
-    const uint8_t* qb0 = (const uint8_t*)(q + ((int64_t)b * Hq + 32 * ht) * AT_DQK);
-    const uint32_t lb = kv_lds + (uint32_t)((NBUF - 1) * AT_CHB) + 1024u * wave;
-#pragma unroll
-    for (int u = 0; u < 5; ++u) {
-      if (u < 4 || wave < 4) {
-        const uint8_t* src = qb0 + drow[u] * AT_RB + doff[u];
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(uintptr_t)(lb + 8192u * u), 16, 0, 0);
+      for (int u = 0; u < 9; ++u) {
+        if (!((vr >> drow[u]) & 1u)) {
+          const i32x4 z = {0, 0, 0, 0};
+          asm volatile("ds_write_b128 %0, %1" : : "v"(lb + 4096u * u), "v"(z) : "memory");
+        }
       }
     }
   };
 
+  // the 32 heads' query rows, laid out like a chunk, into buffer 3 (half 1's second
+  // buffer) before its first chunk: every wave issues 4 or 5 of the 36 loads
+  {
+    const uint8_t* qb0 = (const uint8_t*)(q + ((int64_t)b * Hq + 32 * ht) * AT_DQK);
+    const uint32_t lb = kv_lds + (uint32_t)(3 * AT_CHB) + 1024u * wave;
+#pragma unroll
+    for (int u = 0; u < 5; ++u) {
+      if (u < 4 || wave < 4) {
+        const int s = 64 * (wave + 8 * u) + lane;
+        const int r = s / AT_PPR;
+        const int ps = s - AT_PPR * r;
+        const uint8_t* src = qb0 + r * AT_RB + 16 * ((ps & ~7) | ((ps ^ at_sw(r)) & 7));
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(uintptr_t)(lb + 8192u * u), 16, 0, 0);
+      }
+    }
+  }
+  // the first chunk of each half (buffers 0 and 2)
+  uint32_t vr_cur = 0, vr_next = 0;
+  if (half < nch) vr_cur = issue(half);
+
   // per-lane LDS offsets inside a chunk buffer
-  const int R = 16 * rh + c16;  // logit operand row
-  const uint32_t koff = 16u * (AT_PPR * R + ((g ^ at_sw(R)) ^ (4 * kh)));
-  uint32_t voff[2][2];
+  // logit operand: row R = 16 rh + c16; K-steps 2 i (dims 64 i + 8 g ..) at koff0 +
+  // 128 i, 2 i + 1 (dims 64 i + 32 + 8 g ..) at koff1 + 128 i
+  const int R = 16 * rh + c16;
+  const uint32_t koff0 = 16u * (uint32_t)(AT_PPR * R + (g ^ at_sw(R)));
+  const uint32_t koff1 = 16u * (uint32_t)(AT_PPR * R + ((g ^ at_sw(R)) ^ 4));
+  // value operands: columns 128 w4 + 64 tt + 32 t .. of rows R0 (+ 8 e1, + 16)
+  uint32_t voff[2][2][2];
   {
     const int R0 = 4 * hf + ((lane >> 2) & 3);
     const int x = 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int e1 = 0; e1 < 2; ++e1) {
-        const int sw = at_sw(R0 + 8 * e1);  // the same for the rows 16 on
-        voff[t][e1] = 16u * (AT_PPR * (R0 + 8 * e1) + 8 * wave + ((x ^ sw) ^ (4 * t))) + 8u * (lane & 1);
-      }
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e1 = 0; e1 < 2; ++e1) {
+          const int sw = at_sw(R0 + 8 * e1);  // the same for the rows 16 on
+          voff[tt][t][e1] =
+              16u * (uint32_t)(AT_PPR * (R0 + 8 * e1) + 16 * w4 + 8 * tt + ((x ^ sw) ^ (4 * t))) + 8u * (lane & 1);
+        }
   }
-  const uint32_t pw_off = hs * AT_PHS + 2 * (16 * rh + 8 * (g & 1) + 4 * (g >> 1));
-  const int pr_off = ho * AT_PHS + 16 * hf;
+  const uint32_t pb_lds = lds_addr(pbuf[half]);
+  const uint32_t pw_off = pb_lds + (uint32_t)(hs * AT_PHS + 2 * (16 * rh + 8 * (g & 1) + 4 * (g >> 1)));
+  const uint32_t pr_lds = pb_lds + (uint32_t)(ho * AT_PHS + 16 * hf);
+  const uint32_t flag_lds = lds_addr(&sflag[half]), ctr_lds = lds_addr(&hbar[half]);
+  uint32_t hgen = 0;  // half-barriers passed
 
-  // rows of chunk c that select something (bit r: row 32 c + r): the index read,
-  // then the vote
-  auto row_index = [&](int c) -> int {
-    const int row = c * AT_CH + lane;
-    const int id = sidx[min(row, k - 1)];
-    return lane < AT_CH && row < k ? id : -1;
-  };
-  auto valid_rows = [&](int id) -> uint32_t { return (uint32_t)__ballot(id >= 0); };
-  // once this wave's loads of chunk c have landed: zero the slots of the rows that
-  // select nothing (vr: valid_rows(c))
-  auto zero_fill = [&](int c, uint32_t vr) {
-    if (vr != 0xFFFFFFFFu) {
-      const uint32_t lb = kv_lds + (uint32_t)((c % NBUF) * AT_CHB) + 1024u * wave + 16u * lane;
-#pragma unroll
-      for (int u = 0; u < 5; ++u)
-        if ((u < 4 || wave < 4) && !((vr >> drow[u]) & 1u)) at_write_zero(lb + 8192u * u);
-    }
-  };
-  // chunk c's operands: the logit rows of this wave's 9 K-steps and the V^T values,
-  // together with the row indices of chunk c + NBUF (this wave's loads, id[0..4])
-  // and of chunk c + 1 (row c + 1 + lane, id[5])
-  const uint32_t sidx_lds = lds_addr(sidx);
-  auto read_chunk = [&](int c, i32x4 (&ka)[9], i32x2 (&vv)[8], int (&id)[6]) {
-    const uint32_t bufa = kv_lds + (uint32_t)((c % NBUF) * AT_CHB);
-    uint32_t ia[6];
-#pragma unroll
-    for (int u = 0; u < 5; ++u) ia[u] = sidx_lds + 4u * (uint32_t)min((c + NBUF) * AT_CH + drow[u], k - 1);
-    ia[5] = sidx_lds + 4u * (uint32_t)min((c + 1) * AT_CH + lane, k - 1);
-    at_read_kv(ka, vv, id, bufa + koff, bufa + voff[0][0], bufa + voff[0][1], bufa + voff[1][0], bufa + voff[1][1],
-               ia);
-#pragma unroll
-    for (int u = 0; u < 5; ++u)
-      if ((c + NBUF) * AT_CH + drow[u] >= k) id[u] = -1;
-    if (lane >= AT_CH || (c + 1) * AT_CH + lane >= k) id[5] = -1;
-  };
-  // partial logits over the 9 K-steps, two accumulation chains
-  auto logit_mfma = [&](const i32x4 (&ka)[9], f32x4& s0, f32x4& s1) {
-    s0 = (f32x4){};
-    s1 = (f32x4){};
-#pragma unroll
-    for (int i = 0; i < 9; ++i) {
-      const bf16x8 a = __builtin_bit_cast(bf16x8, ka[i]), bq = __builtin_bit_cast(bf16x8, qb[i]);
-      if (i & 1)
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, s1, 0, 0, 0);
-      else
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, s0, 0, 0, 0);
-    }
-  };
-  auto write_p = [&](const float (&p)[4]) {
-    const bf16x4 v = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
-    *(bf16x4*)(pbuf + pw_off) = v;
-  };
+  // the query operands, once the query rows (and the first chunks) have landed
+  i32x4 qb0[9], qb1[9];
+  LI_WAIT_VMCNT(0);
+  if (half < nch) zero_fill(half, vr_cur);
+  at_barrier();
+  {
+    const uint32_t qa = kv_lds + (uint32_t)(3 * AT_CHB) + 16u * (uint32_t)(AT_PPR * hs);
+    at_read_k(qb0, qa + 16u * (uint32_t)(g ^ at_sw(hs)));
+    at_read_k(qb1, qa + 16u * (uint32_t)((g ^ at_sw(hs)) ^ 4));
+  }
+  at_barrier();  // buffer 3 is free for half 1's second chunk
 
   // softmax in base 2: exp(tau x - m) == 2^(tau log2(e) x - m / ln 2)
   const float tau2 = tau * 1.4426950408889634f;
   float m_s = -INFINITY, l_s = 0.0f, m_o = -INFINITY;
-  f32x16 o[2];
-  o[0] = (f32x16){};
-  o[1] = (f32x16){};
-  f32x4 sown;  // this wave's partial logits of the next chunk
-  uint32_t vr_c = 0, vr_c1 = 0;  // valid rows of the current and the next chunk
-  const uint32_t pr_lds = lds_addr(pbuf) + pr_off, flag_lds = lds_addr(&sflag);
+  f32x16 o[2][2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) o[tt][t] = (f32x16){};
 
-  // One step of the software pipeline over chunks.  Chunk c is loaded during step
-  // c - NBUF - 1 (the first NBUF + 1 up front); its logit and value operands are
-  // read in phase A of step c - 1, which frees its buffer for chunk c + NBUF; its
-  // softmax runs in phase A and its value product in phase B of step c.  Two
-  // barriers per step: Y (partial logits and probabilities are in LDS) and X (the
-  // chunk after next has landed).  vcur: chunk c's value operands; vnext receives
-  // chunk c + 1's.
-  auto step = [&](int c, const i32x2 (&vcur)[8], i32x2 (&vnext)[8]) {
-    // ---- phase A: logits of chunk c + 1 (MFMA) beside the softmax of chunk c
-    f32x4 s = sown;
-    const uint32_t vrow = vr_c;
-    if (!kh) s += spart[tile][lane];
-    // (with the operands: the row indices of the loads issued after barrier Y, and
-    // chunk c + 2's)
-    int nid[6];
-    nid[5] = -1;
-    const bool load_next = c + NBUF + 1 < nch;
-    f32x4 s0, s1;
-    const bool more = c + 1 < nch;
-    if (more) {
+  for (int c = half; c < nch; c += 2) {
+    // ---- the half's chunk c has landed (this wave's loads); zero the rows that
+    // select nothing; every wave of the half is past chunk c - 2
+    LI_WAIT_VMCNT(0);
+    if (c != half) zero_fill(c, vr_cur);
+    at_half_barrier(ctr_lds, 4u * ++hgen, lane);
+    // its buffer of chunk c - 2 takes chunk c + 2
+    if (c + 2 < nch) vr_next = issue(c + 2);
+    const uint32_t buf = buf_of(c);
+
+    // ---- logits of rows 16 rh + 4 g + j, head hs, over all 18 K-steps
+    f32x4 s0 = {}, s1 = {};
+    {
       i32x4 ka[9];
-      read_chunk(c + 1, ka, vnext, nid);
-      logit_mfma(ka, s0, s1);
+      at_read_k(ka, buf + koff0);
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, ka[i]), bq = __builtin_bit_cast(bf16x8, qb0[i]);
+        if (i & 1)
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, s1, 0, 0, 0);
+        else
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, s0, 0, 0, 0);
+      }
+      at_read_k(ka, buf + koff1);
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, ka[i]), bq = __builtin_bit_cast(bf16x8, qb1[i]);
+        if (i & 1)
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, s0, 0, 0, 0);
+        else
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, s1, 0, 0, 0);
+      }
     }
-    const int rid2 = nid[5];
-    // the tile's owner: logits of rows 16 rh + 4 g + j (j < 4), head hs
+    const f32x4 s = s0 + s1;
     float st[4], lsum = 0.0f;
-    if (!kh) {
+    {
       bool ex = false;
       float p[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = 16 * rh + 4 * g + j;
-        st[j] = ((vrow >> row) & 1u) ? s[j] * tau2 : -INFINITY;
+        const bool valid = (vr_cur >> (16 * rh + 4 * g + j)) & 1u;
+        st[j] = valid ? s[j] * tau2 : -INFINITY;
         ex |= st[j] > m_s + AT_MARGIN;
         p[j] = st[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st[j] - m_s);
         lsum += p[j];
       }
-      write_p(p);
-      if (__ballot(ex) != 0ull && lane == 0) sflag = c + 1;
+      const bf16x4 v = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+      asm volatile("ds_write_b64 %0, %1" : : "v"(pw_off), "v"(__builtin_bit_cast(i32x2, v)) : "memory");
+      if (__ballot(ex) != 0ull && lane == 0) {
+        const int f = c + 1;
+        asm volatile("ds_write_b32 %0, %1" : : "v"(flag_lds), "v"(f) : "memory");
+      }
     }
-    if (more) sown = s0 + s1;
-    at_barrier();
-    // chunk c + 1 has been read by every wave: its buffer takes chunk c + NBUF + 1
-    if (load_next) issue_ids(c + NBUF + 1, nid);
+    at_half_barrier(ctr_lds, 4u * ++hgen, lane);
 
-    // ---- phase B: value product of chunk c, loads of chunk c + NBUF + 1
+    // ---- probabilities and flag; the rescale path when some logit passed its head's
+    // reference maximum by the margin
     i32x4 pp0, pp1;
     int flag;
     at_read_p(pp0, pp1, flag, pr_lds, flag_lds);
     if (flag == c + 1) {
-      // some logit passed its head's reference maximum by the margin: move the
-      // references to the exact maxima and recompute this chunk's probabilities
-      if (!kh) {
-        float ml = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
-        ml = fmaxf(ml, __shfl_xor(ml, 16, WAVE));
-        ml = fmaxf(ml, __shfl_xor(ml, 32, WAVE));
-        if (g == 0) mx[rh][hs] = ml;
-      }
-      at_barrier();
+      // move the references to the exact maxima and recompute this chunk's probabilities
+      float ml = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
+      ml = fmaxf(ml, __shfl_xor(ml, 16, WAVE));
+      ml = fmaxf(ml, __shfl_xor(ml, 32, WAVE));
+      if (g == 0) at_write_f32(lds_addr(&mx[half][rh][hs]), ml);
+      at_half_barrier(ctr_lds, 4u * ++hgen, lane);
       {
-        const float mn = fmaxf(m_o, fmaxf(mx[0][ho], mx[1][ho]));
+        const float mn = fmaxf(m_o, fmaxf(at_read_f32(lds_addr(&mx[half][0][ho])),
+                                          at_read_f32(lds_addr(&mx[half][1][ho]))));
         const float al = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_o - mn);
         m_o = mn;
         if (__ballot(al != 1.0f) != 0ull) {
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
+          for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[t][r] *= al;
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[tt][t][r] *= al;
         }
       }
-      if (!kh) {
-        const float mn = fmaxf(m_s, fmaxf(mx[0][hs], mx[1][hs]));
+      {
+        const float mn = fmaxf(m_s, fmaxf(at_read_f32(lds_addr(&mx[half][0][hs])),
+                                          at_read_f32(lds_addr(&mx[half][1][hs]))));
         const float al = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_s - mn);
         m_s = mn;
         float p[4];
@@ -423,97 +422,93 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
           lsum += p[j];
         }
         l_s = l_s * al + lsum;
-        write_p(p);
+        const bf16x4 v = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+        asm volatile("ds_write_b64 %0, %1" : : "v"(pw_off), "v"(__builtin_bit_cast(i32x2, v)) : "memory");
       }
-      at_barrier();
-      pp0 = *(const i32x4*)(pbuf + pr_off);
-      pp1 = *(const i32x4*)(pbuf + pr_off + 32);
-    } else if (!kh) {
+      at_half_barrier(ctr_lds, 4u * ++hgen, lane);
+      at_read_p(pp0, pp1, flag, pr_lds, flag_lds);
+    } else {
       l_s += lsum;
     }
-    // O^T[dv, head] += V^T . P^T over the chunk's two 16-row K-steps
+
+    // ---- O^T[dv, head] += V^T . P^T over the chunk's two 16-row K-steps, for this
+    // wave's two 64-column blocks
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int tt = 0; tt < 2; ++tt) {
+      i32x2 vv[8];
+      at_read_v(vv, buf + voff[tt][0][0], buf + voff[tt][0][1], buf + voff[tt][1][0], buf + voff[tt][1][1]);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const i32x4 a4 = {vcur[4 * t + 2 * s2].x, vcur[4 * t + 2 * s2].y, vcur[4 * t + 2 * s2 + 1].x,
-                          vcur[4 * t + 2 * s2 + 1].y};
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
-                                                       __builtin_bit_cast(bf16x8, s2 ? pp1 : pp0), o[t], 0, 0, 0);
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const i32x4 a4 = {vv[4 * t + 2 * s2].x, vv[4 * t + 2 * s2].y, vv[4 * t + 2 * s2 + 1].x,
+                            vv[4 * t + 2 * s2 + 1].y};
+          o[tt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
+                                                             __builtin_bit_cast(bf16x8, s2 ? pp1 : pp0), o[tt][t], 0,
+                                                             0, 0);
+        }
       }
     }
-    // the second wave of each tile hands over its partial logits of chunk c + 1
-    // (read in phase A of the next step)
-    if (kh && more) spart[tile][lane] = sown;
-    const uint32_t vr2 = valid_rows(rid2);
-    if (c + 2 < nch) {
-      at_wait_loads(nd * (min(nch - 1, c + NBUF + 1) - (c + 2)));
-      zero_fill(c + 2, vr2);
-    }
-    vr_c = vr_c1;
-    vr_c1 = vr2;
-    at_barrier();
-  };
+    vr_cur = vr_next;
+  }
 
-  // prologue: chunks 0 and 1, the query rows (into buffer NBUF - 1) and chunks
-  // 2 .. NBUF - 2 in flight; once chunks 0, 1 and the query have landed, the Q^T
-  // operands and chunk 0's operands and logits; then chunks NBUF - 1 and NBUF
-  i32x2 va[8], vb[8];
-  issue(0);
-  if (1 < nch) issue(1);
-  issue_q();
-  for (int c = 2; c < NBUF - 1 && c < nch; ++c) issue(c);
-  vr_c = valid_rows(row_index(0));
-  vr_c1 = valid_rows(row_index(1));
-  at_wait_loads(nd * max(0, min(nch - 1, NBUF - 2) - 1));
-  zero_fill(0, vr_c);
-  if (1 < nch) zero_fill(1, vr_c1);
-  at_barrier();
+  // ---- merge the two halves: the softmax sums of each half (four lane groups of a
+  // tile, then its two row halves), the reference maxima and the outputs of half 1
+  // through LDS into half 0, which normalises and stores
   {
-    // Q^T operand of this wave's K-steps 2 i + kh (dims 64 i + 32 kh + 8 g .. + 7 of
-    // head hs)
-    at_read_k(qb, kv_lds + (uint32_t)((NBUF - 1) * AT_CHB) + 16u * (AT_PPR * hs + ((g ^ at_sw(hs)) ^ (4 * kh))));
-    i32x4 ka[9];
-    int unused[6];
-    f32x4 s0, s1;
-    read_chunk(0, ka, va, unused);
-    logit_mfma(ka, s0, s1);
-    sown = s0 + s1;
-    if (kh) spart[tile][lane] = sown;
-  }
-  at_barrier();
-  // every wave has its query operands and chunk 0's: their buffers take chunks
-  // NBUF - 1 and NBUF (chunk 1 has landed and is zero-filled already)
-  for (int c = NBUF - 1; c <= NBUF && c < nch; ++c) issue(c);
-  for (int c = 0; c < nch; c += 2) {
-    step(c, va, vb);
-    if (c + 1 < nch) step(c + 1, vb, va);
-  }
-
-  // the softmax sums: the four lane groups of each tile owner, then the two row
-  // halves (the last step ended with a barrier, so mx is free)
-  if (!kh) {
     float l = l_s;
     l += __shfl_xor(l, 16, WAVE);
     l += __shfl_xor(l, 32, WAVE);
-    if (g == 0) mx[rh][hs] = l;
+    if (g == 0) at_write_f32(lds_addr(&mx[half][rh][hs]), l);
   }
+  LI_WAIT_VMCNT(0);
   at_barrier();
-  const float lt = mx[0][ho] + mx[1][ho];
+  const float lh = at_read_f32(lds_addr(&mx[half][0][ho])) + at_read_f32(lds_addr(&mx[half][1][ho]));
+  // half 1's outputs (64 per lane), reference maxima and sums, after the ring
+  float* mg = (float*)kvbuf + (size_t)w4 * 66 * 64;
+  if (half == 1) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mg[((tt * 2 + t) * 16 + r) * 64 + lane] = o[tt][t][r];
+    mg[64 * 64 + lane] = m_o;
+    mg[65 * 64 + lane] = lh;
+  }
+  __syncthreads();
+  const float m1 = mg[64 * 64 + lane], l1 = mg[65 * 64 + lane];
+  const float mm = fmaxf(m_o, m1);
+  const float a0 = m_o == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_o - mm);
+  const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mm);
+  const float lt = lh * a0 + l1 * a1;
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (half == 0) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          o[tt][t][r] = (o[tt][t][r] * a0 + mg[((tt * 2 + t) * 16 + r) * 64 + lane] * a1) * inv;
+  }
+  __syncthreads();  // the merge area is read; the staging below reuses the ring
   // normalised outputs staged through LDS as [head][dv] bf16, then stored 16 bytes
   // per lane
+  if (half == 0) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int dv = 64 * wave + 32 * t + 8 * r4 + 4 * hf;
-      const bf16x4 v = {(__bf16)(o[t][4 * r4] * inv), (__bf16)(o[t][4 * r4 + 1] * inv),
-                        (__bf16)(o[t][4 * r4 + 2] * inv), (__bf16)(o[t][4 * r4 + 3] * inv)};
-      *(bf16x4*)(kvbuf + ho * AT_OSTR + 2 * dv) = v;
-    }
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int dv = 128 * w4 + 64 * tt + 32 * t + 8 * r4 + 4 * hf;
+          const bf16x4 v = {(__bf16)o[tt][t][4 * r4], (__bf16)o[tt][t][4 * r4 + 1], (__bf16)o[tt][t][4 * r4 + 2],
+                            (__bf16)o[tt][t][4 * r4 + 3]};
+          *(bf16x4*)(kvbuf + ho * AT_OSTR + 2 * dv) = v;
+        }
   }
-  at_barrier();
+  __syncthreads();
   uint16_t* obase = out + ((int64_t)b * Hq + 32 * ht) * AT_DV;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -521,8 +516,8 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
     const int h = pc >> 6, part = pc & 63;
     *(uint4*)(obase + (int64_t)h * AT_DV + 8 * part) = *(const uint4*)(kvbuf + h * AT_OSTR + 16 * part);
   }
-  if (lse && wave == 0 && hf == 0)
-    lse[(int64_t)b * Hq + 32 * ht + ho] = lt > 0.0f ? (m_o + log2f(lt)) * 0.6931471805599453f : -INFINITY;
+  if (lse && half == 0 && w4 == 0 && hf == 0)
+    lse[(int64_t)b * Hq + 32 * ht + ho] = lt > 0.0f ? (mm + log2f(lt)) * 0.6931471805599453f : -INFINITY;
 }
 
 size_t attn_ws_bytes(int B, int Hq, int k, int dv) {
@@ -535,8 +530,7 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* kv, const int32_t* idx
   (void)ws;
   const int nt = Hq / 32;
   const int blocks = ((B + 7) / 8) * 8 * nt;
-  sparse_attn_kernel<ATTN_NBUF, false><<<blocks, 512, 0, st>>>(q, kv, idx, B, Hq, S, k, sm_scale, out, lse, nullptr, 0,
-                                                               0);
+  sparse_attn_kernel<false><<<blocks, 512, 0, st>>>(q, kv, idx, B, Hq, S, k, sm_scale, out, lse, nullptr, 0, 0);
   return hipGetLastError();
 }
 
@@ -545,8 +539,8 @@ hipError_t launch_attn_paged(const uint16_t* q, const uint16_t* kv_pool, const i
                              uint16_t* out, float* lse, hipStream_t st) {
   const int nt = Hq / 32;
   const int blocks = ((B + 7) / 8) * 8 * nt;
-  sparse_attn_kernel<ATTN_NBUF, true><<<blocks, 512, 0, st>>>(q, kv_pool, idx, B, Hq, S, k, sm_scale, out, lse,
-                                                              slot_table, max_slots, num_slots);
+  sparse_attn_kernel<true><<<blocks, 512, 0, st>>>(q, kv_pool, idx, B, Hq, S, k, sm_scale, out, lse, slot_table,
+                                                   max_slots, num_slots);
   return hipGetLastError();
 }
 
