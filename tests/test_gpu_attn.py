@@ -27,7 +27,10 @@ def run(B, Hq, S, k, seed, idx=None, tau=1 / math.sqrt(192)):
     return bf16_host(out), lse.cpu().numpy(), o_out, o_lse
 
 
-@pytest.mark.parametrize("B,Hq,S,k", [(2, 128, 3000, 512), (3, 32, 500, 100), (1, 64, 5000, 2048), (2, 96, 64, 1)])
+# k = 1 and 33: the second half of a workgroup takes no chunk or a one-row chunk;
+# k = 64: one full chunk each
+@pytest.mark.parametrize("B,Hq,S,k", [(2, 128, 3000, 512), (3, 32, 500, 100), (1, 64, 5000, 2048), (2, 96, 64, 1),
+                                      (2, 32, 700, 33), (1, 128, 2000, 64)])
 def test_matches_oracle(B, Hq, S, k):
     print("attn", B, Hq, S, k, flush=True)
     g, gl, o, ol = run(B, Hq, S, k, seed=0x5EED0800 + k)
@@ -61,12 +64,14 @@ def bf16_bits(x):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-@pytest.mark.parametrize("pos,scale", [(40, 4.0), (300, 0.6), (509, 4.0)])
+@pytest.mark.parametrize("pos,scale", [(10, 4.0), (40, 4.0), (200, 2.0), (300, 0.6), (509, 4.0)])
 def test_late_dominant_row(pos, scale):
     """A selected row planted as a multiple of one query makes that head's logit jump
     far above everything seen in the earlier chunks (and others' by less), so the
     running softmax reference has to move mid-sequence; sequence 1 also starts with
-    two chunks of skipped entries."""
+    two chunks of skipped entries.  Chunks (32 selected rows) alternate between the two
+    halves of the workgroup, so positions 10 and 200 move a reference in the first half,
+    40, 300 and 509 in the second, and the final merge rescales the other half."""
     print("attn dominant", pos, scale, flush=True)
     B, Hq, S, k, seed = 2, 64, 4000, 512, 0x5EED0B00 + pos
     tau = 1 / math.sqrt(192)
