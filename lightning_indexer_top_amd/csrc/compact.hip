@@ -97,8 +97,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
   const int key0 = blockIdx.x * kpb, kend = min(key0 + kpb, S);
   const int8_t* cbase = ck + (int64_t)b * S * DC;
   const float* sbase = cks + (int64_t)b * S;
-  // the next 64-key tile is loaded while this one is scored (compact keys and
-  // scales in VGPRs); loads past the range read the last key and are not used
+  // the next tiles are loaded while this one is scored (compact keys and scales in
+  // VGPRs); loads past the range read the last key and are not used
 #define LI_S1_LOAD(X, kb)                                                                      \
   do {                                                                                         \
     X##0 = *(const i32x4*)(cbase + (int64_t)min((kb) + col, S - 1) * DC + 16 * hf);            \
@@ -138,16 +138,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     }                                                                                                          \
     if ((kb) + lane < kend) s1[(int64_t)b * S + (kb) + lane] = (double)X##s * acc;                             \
   } while (0)
-  i32x4 A0, A1, B0, B1;
-  float As, Bs;
+  // three tiles rotate: two are in flight while one is scored (one HBM round trip
+  // is several tiles' worth of scoring)
+  i32x4 A0, A1, B0, B1, C0, C1;
+  float As, Bs, Cs;
   int kb = key0 + 64 * wave;
   LI_S1_LOAD(A, kb);
-  for (; kb < kend; kb += 512) {
-    LI_S1_LOAD(B, kb + 256);
+  LI_S1_LOAD(B, kb + 256);
+  for (; kb < kend; kb += 768) {
+    LI_S1_LOAD(C, kb + 512);
     LI_S1_TILE(A, kb);
     if (kb + 256 >= kend) break;
-    LI_S1_LOAD(A, kb + 512);
+    LI_S1_LOAD(A, kb + 768);
     LI_S1_TILE(B, kb + 256);
+    if (kb + 512 >= kend) break;
+    LI_S1_LOAD(B, kb + 1024);
+    LI_S1_TILE(C, kb + 512);
   }
 #undef LI_S1_LOAD
 #undef LI_S1_TILE
