@@ -160,16 +160,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 }
 
 // Stage 2.  A quad of lanes serves two shortlisted candidates: lane g computes,
-// for both, the dots of heads g, g + 4, g + 8, ..., eight heads at a time, each
-// an fp64 fma chain over the 128 dimensions in ascending order, against the
-// query block held as fp64 in LDS (rows padded to 129 doubles, so the quad's four
-// heads sit in different banks); every query operand read serves both candidates.
-// The keys stay in VGPRs as bf16 and each element is widened once per eight
-// FMAs.  After each group of eight heads per lane (32 consecutive heads) the head
-// chain advances over those heads in ascending order in all four lanes, each step
-// taking its dot from the owning lane with a quad broadcast (DPP).
+// for both, the dots of heads 8 g .. 8 g + 7 of each group of 32 heads, each an fp64
+// fma chain over the 128 dimensions in ascending order, against the query block
+// held as fp64 in LDS dimension-major ([j][head]), so a lane's eight query
+// operands of one dimension are four 16-byte reads from one address (the quad's
+// four lanes read 256 contiguous bytes, every quad of the wave the same ones), and
+// they are read one dimension ahead of the FMAs that use them.  Every query
+// operand read serves both candidates.  The keys stay in VGPRs as bf16 and each
+// element is widened once per group.  After each group the head chain advances
+// over its 32 heads in ascending order in all four lanes, each step taking its dot
+// from the owning lane with a quad broadcast (DPP).
 constexpr int S2_THREADS = 256;
-constexpr int S2_QROW = 129;  // LDS row stride of the query block, doubles
 constexpr int S2_CPB = S2_THREADS / 2;  // candidates per workgroup
 
 template <int G>
@@ -185,21 +186,32 @@ __device__ __forceinline__ double quad_bcast(double v) {
                "+v"(v[i + 1].z), "+v"(v[i + 1].w), "+v"(v[i + 2].x), "+v"(v[i + 2].y), "+v"(v[i + 2].z),       \
                "+v"(v[i + 2].w), "+v"(v[i + 3].x), "+v"(v[i + 3].y), "+v"(v[i + 3].z), "+v"(v[i + 3].w))
 
+// eight fp64 query operands (16-byte LDS reads at a, a + 16, a + 32, a + 48)
+__device__ __forceinline__ void s2_read_q(double (&v)[8], const double* a) {
+  const double2* p = (const double2*)a;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double2 x = p[i];
+    v[2 * i] = x.x;
+    v[2 * i + 1] = x.y;
+  }
+}
+
 template <int U>
 __global__ __launch_bounds__(S2_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void compact_stage2_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ kf,
     const int32_t* __restrict__ sl, const int32_t* __restrict__ nv, int S, int H, int m, double* __restrict__ s2,
     int32_t* __restrict__ cnt) {
   static_assert(U % 8 == 0, "eight heads per lane at a time");
-  extern __shared__ double sqd[];  // [4 U][S2_QROW] query as fp64 (zero past H), then [4 U] weights
-  constexpr int HP = 4 * U;
+  constexpr int HP = 4 * U;  // heads, padded to whole groups of 32
+  extern __shared__ __attribute__((aligned(16))) double sqd[];  // [128][HP] query as fp64 (zero past H), [HP] w
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   for (int i = tid; i < HP * 128; i += S2_THREADS) {
     const int h = i >> 7, j = i & 127;
-    sqd[h * S2_QROW + j] = h < H ? (double)bf16_to_f32(q[((int64_t)b * H + h) * 128 + j]) : 0.0;
+    sqd[j * HP + h] = h < H ? (double)bf16_to_f32(q[((int64_t)b * H + h) * 128 + j]) : 0.0;
   }
-  double* sw = sqd + HP * S2_QROW;
+  double* sw = sqd + 128 * HP;
   for (int i = tid; i < HP; i += S2_THREADS) sw[i] = i < H ? (double)w[(int64_t)b * H + i] : 0.0;
   __syncthreads();
   const int c0 = blockIdx.x * S2_CPB + 2 * (tid >> 2), g = tid & 3;
@@ -220,52 +232,63 @@ __global__ __launch_bounds__(S2_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
     k1[i] = kp1[i];
   }
   double acc0 = 0.0, acc1 = 0.0;
-#pragma unroll
-  for (int ug = 0; ug < U; ug += 8) {
-    // groups of eight heads one after the other: the keys count as rewritten
-    // here, so no work of this group moves into the previous one
+#pragma unroll 1
+  for (int hb = 0; hb < HP; hb += 32) {
+    // the keys count as rewritten here, so their widened values are not hoisted
+    // out of the loop (kept for every group they would need 512 registers)
     LI_TOUCH4(k0, 0); LI_TOUCH4(k0, 4); LI_TOUCH4(k0, 8); LI_TOUCH4(k0, 12);
     LI_TOUCH4(k1, 0); LI_TOUCH4(k1, 4); LI_TOUCH4(k1, 8); LI_TOUCH4(k1, 12);
-    const double* qrow = sqd + (4 * ug + g) * S2_QROW;  // head 4 (ug + t) + g is row 4 t ahead
+    // this lane's heads hb + 8 g .. hb + 8 g + 7; dimension j's operands at qrow + j HP
+    const double* qrow = sqd + hb + 8 * g;
     double d0[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     double d1[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    double qa[8], qb[8];
+    s2_read_q(qa, qrow);
+    // dimensions in pairs: the odd one's operands are read before the even one's FMAs,
+    // the next even one's before the odd one's
+#define LI_S2_FMA(QV, KV0, KV1)                                                     \
+  _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                   \
+    d0[t] = fma(QV[t], KV0, d0[t]);                                                 \
+    d1[t] = fma(QV[t], KV1, d1[t]);                                                 \
+  }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t w0[4] = {k0[i].x, k0[i].y, k0[i].z, k0[i].w};
       const uint32_t w1[4] = {k1[i].x, k1[i].y, k1[i].z, k1[i].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 8 * i + e;
-        const uint32_t b0 = (e & 1) ? (w0[e >> 1] & 0xFFFF0000u) : (w0[e >> 1] << 16);
-        const uint32_t b1 = (e & 1) ? (w1[e >> 1] & 0xFFFF0000u) : (w1[e >> 1] << 16);
-        const double kv0 = (double)__uint_as_float(b0), kv1 = (double)__uint_as_float(b1);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const double qv = qrow[4 * t * S2_QROW + j];
-          d0[t] = fma(qv, kv0, d0[t]);
-          d1[t] = fma(qv, kv1, d1[t]);
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int j = 8 * i + 2 * e2;
+        s2_read_q(qb, qrow + (j + 1) * HP);
+        {
+          const double kv0 = (double)__uint_as_float(w0[e2] << 16), kv1 = (double)__uint_as_float(w1[e2] << 16);
+          LI_S2_FMA(qa, kv0, kv1)
         }
-        // advance all chains together, two elements at a time (run one after
-        // the other they would keep every widened key value and query operand live)
-        if (e & 1)
-          asm volatile("" : "+v"(d0[0]), "+v"(d0[1]), "+v"(d0[2]), "+v"(d0[3]), "+v"(d0[4]), "+v"(d0[5]),
-                       "+v"(d0[6]), "+v"(d0[7]), "+v"(d1[0]), "+v"(d1[1]), "+v"(d1[2]), "+v"(d1[3]), "+v"(d1[4]),
-                       "+v"(d1[5]), "+v"(d1[6]), "+v"(d1[7]));
+        if (j + 2 < 128) s2_read_q(qa, qrow + (j + 2) * HP);
+        {
+          const double kv0 = (double)__uint_as_float(w0[e2] & 0xFFFF0000u);
+          const double kv1 = (double)__uint_as_float(w1[e2] & 0xFFFF0000u);
+          LI_S2_FMA(qb, kv0, kv1)
+        }
+        // all sixteen chains advance together, a pair of dimensions at a time (run one
+        // after the other they would keep every query operand live)
+        asm volatile("" : "+v"(d0[0]), "+v"(d0[1]), "+v"(d0[2]), "+v"(d0[3]), "+v"(d0[4]), "+v"(d0[5]),
+                     "+v"(d0[6]), "+v"(d0[7]), "+v"(d1[0]), "+v"(d1[1]), "+v"(d1[2]), "+v"(d1[3]), "+v"(d1[4]),
+                     "+v"(d1[5]), "+v"(d1[6]), "+v"(d1[7]));
       }
     }
-    // head chain over heads 4 ug .. 4 ug + 31, ascending
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int h = 4 * (ug + t);
-#define LI_STEP(G_)                                                             \
-  if (h + G_ < H) {                                                             \
-    const double x0 = quad_bcast<G_>(d0[t]), x1 = quad_bcast<G_>(d1[t]);       \
-    acc0 = fma(sw[h + G_], x0 > 0.0 ? x0 : 0.0, acc0);                          \
-    acc1 = fma(sw[h + G_], x1 > 0.0 ? x1 : 0.0, acc1);                          \
+#undef LI_S2_FMA
+    // head chain over heads hb .. hb + 31, ascending: head hb + 8 G + t is lane G's d[t]
+#define LI_STEP(G_)                                                               \
+  _Pragma("unroll") for (int t = 0; t < 8; ++t) {                                 \
+    const int h = hb + 8 * (G_) + t;                                              \
+    const double x0 = quad_bcast<G_>(d0[t]), x1 = quad_bcast<G_>(d1[t]);          \
+    if (h < H) {                                                                  \
+      acc0 = fma(sw[h], x0 > 0.0 ? x0 : 0.0, acc0);                               \
+      acc1 = fma(sw[h], x1 > 0.0 ? x1 : 0.0, acc1);                               \
+    }                                                                             \
   }
-      LI_STEP(0) LI_STEP(1) LI_STEP(2) LI_STEP(3)
+    LI_STEP(0) LI_STEP(1) LI_STEP(2) LI_STEP(3)
 #undef LI_STEP
-    }
   }
   if (g == 0 && c0 < m) s2[(int64_t)b * m + c0] = v0 ? acc0 : -INFINITY;
   if (g == 0 && c0 + 1 < m) s2[(int64_t)b * m + c0 + 1] = v1 ? acc1 : -INFINITY;
@@ -340,7 +363,7 @@ hipError_t launch_compact(const uint16_t* q, const float* w, const float* P, con
   stage2_attrs();
   const dim3 g2((m + S2_CPB - 1) / S2_CPB, B);
 #define LI_STAGE2(U_)                                                                                    \
-  compact_stage2_kernel<U_><<<g2, S2_THREADS, sizeof(double) * (size_t)(4 * U_) * (S2_QROW + 1), st>>>( \
+  compact_stage2_kernel<U_><<<g2, S2_THREADS, sizeof(double) * (size_t)(4 * U_) * (128 + 1), st>>>( \
       q, w, kf, sl, nv, S, H, m, s2, cnt)
   if (H <= 32)
     LI_STAGE2(8);
@@ -532,7 +555,7 @@ hipError_t launch_pq(const uint16_t* q, const float* w, const int8_t* cb, float 
   stage2_attrs();
   const dim3 g2((m + S2_CPB - 1) / S2_CPB, B);
 #define LI_STAGE2(U_)                                                                                    \
-  compact_stage2_kernel<U_><<<g2, S2_THREADS, sizeof(double) * (size_t)(4 * U_) * (S2_QROW + 1), st>>>( \
+  compact_stage2_kernel<U_><<<g2, S2_THREADS, sizeof(double) * (size_t)(4 * U_) * (128 + 1), st>>>( \
       q, w, kf, sl, nv, S, H, m, s2, cnt)
   if (H <= 32)
     LI_STAGE2(8);
