@@ -207,9 +207,18 @@ __global__ __launch_bounds__(S2_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
   extern __shared__ __attribute__((aligned(16))) double sqd[];  // [128][HP] query as fp64 (zero past H), [HP] w
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  for (int i = tid; i < HP * 128; i += S2_THREADS) {
-    const int h = i >> 7, j = i & 127;
-    sqd[j * HP + h] = h < H ? (double)bf16_to_f32(q[((int64_t)b * H + h) * 128 + j]) : 0.0;
+  // a thread widens eight dimensions of one head; neighbouring threads take
+  // neighbouring heads, so each 8-byte store lands next to the last one's
+  for (int i = tid; i < HP * 16; i += S2_THREADS) {
+    const int h = i % HP, jb = i / HP;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (h < H) x = *(const uint4*)(q + ((int64_t)b * H + h) * 128 + 8 * jb);
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sqd[(8 * jb + 2 * e) * HP + h] = (double)__uint_as_float(xw[e] << 16);
+      sqd[(8 * jb + 2 * e + 1) * HP + h] = (double)__uint_as_float(xw[e] & 0xFFFF0000u);
+    }
   }
   double* sw = sqd + 128 * HP;
   for (int i = tid; i < HP; i += S2_THREADS) sw[i] = i < H ? (double)w[(int64_t)b * H + i] : 0.0;
