@@ -97,10 +97,12 @@ def test_indexer_topk_workspace_follows_the_path():
     # none: the prefill chunk (4096 rows over 131072 keys) asks for 0 bytes
     assert ws(li.LI_BF16, li.LI_BF16, 1, 4096, 131072, 64, 512) == 0
     assert ws(li.LI_BF16, li.LI_BF16, 1, 16, 1000, 64, 16) == 0
-    # the same shape with fp8 keys scores then selects: the score matrix plus the
-    # top-k's own workspace
-    n = ws(li.LI_BF16, li.LI_FP8_E4M3, 1, 16, 1000, 64, 16)
-    assert n >= 16 * 1000 * 4 + L.li_topk_workspace_bytes(16, 1000, 16)
+    # fp8 keys take the same tiled kernel (the fp8 tiles widened to bf16 in LDS)
+    assert ws(li.LI_BF16, li.LI_FP8_E4M3, 1, 16, 1000, 64, 16) == 0
+    # past the fused kernel's k (512) the call scores then selects: the score matrix
+    # plus the top-k's own workspace
+    n = ws(li.LI_BF16, li.LI_FP8_E4M3, 1, 16, 1000, 64, 600)
+    assert n >= 16 * 1000 * 4 + L.li_topk_workspace_bytes(16, 1000, 600)
     # decode rows: the scores, then the top-k's thresholds, counts and candidate lists
     assert ws(li.LI_BF16, li.LI_FP8_E4M3, 16, 1, 131072, 64, 512) == \
         16 * 131072 * 4 + L.li_topk_workspace_bytes(16, 131072, 512)

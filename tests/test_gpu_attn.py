@@ -28,9 +28,10 @@ def run(B, Hq, S, k, seed, idx=None, tau=1 / math.sqrt(192)):
 
 
 # k = 1 and 33: the second half of a workgroup takes no chunk or a one-row chunk;
-# k = 64: one full chunk each
+# k = 64: one full chunk each; k = 2048: 32 chunks a half
 @pytest.mark.parametrize("B,Hq,S,k", [(2, 128, 3000, 512), (3, 32, 500, 100), (1, 64, 5000, 2048), (2, 96, 64, 1),
-                                      (2, 32, 700, 33), (1, 128, 2000, 64)])
+                                      (2, 32, 700, 33), (1, 128, 2000, 64), (2, 64, 700, 33), (2, 128, 64, 1),
+                                      (3, 128, 900, 300)])
 def test_matches_oracle(B, Hq, S, k):
     print("attn", B, Hq, S, k, flush=True)
     g, gl, o, ol = run(B, Hq, S, k, seed=0x5EED0800 + k)
@@ -51,10 +52,11 @@ def test_skipped_and_repeated_entries():
     np.testing.assert_allclose(gl, ol, rtol=1e-3, atol=1e-3)
 
 
-def test_nothing_selected():
-    print("attn empty", flush=True)
+@pytest.mark.parametrize("Hq", [32, 128])
+def test_nothing_selected(Hq):
+    print("attn empty", Hq, flush=True)
     idx = -np.ones((1, 40), np.int32)
-    g, gl, o, ol = run(1, 32, 100, 40, seed=0x5EED0A00, idx=idx)
+    g, gl, o, ol = run(1, Hq, 100, 40, seed=0x5EED0A00, idx=idx)
     assert (g == 0).all() and np.isneginf(gl).all()
 
 
