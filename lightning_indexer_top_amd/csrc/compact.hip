@@ -24,37 +24,41 @@ constexpr int DC = 32;
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// One wave per (b, h).
-__global__ __launch_bounds__(64) void compact_query_kernel(const uint16_t* __restrict__ q, const float* __restrict__ w,
-                                                           const float* __restrict__ P, int H,
-                                                           int8_t* __restrict__ q8, double* __restrict__ W) {
-  const int bh = blockIdx.x;
-  const int i = threadIdx.x;
-  const uint16_t* qr = q + (int64_t)bh * 128;
+// One workgroup per sequence and 8 heads: thread t computes output t & 31 of head
+// 8 blockIdx.x + (t >> 5), so each wave serves two heads, one per 32-lane half.
+__global__ __launch_bounds__(256) void compact_query_kernel(const uint16_t* __restrict__ q,
+                                                            const float* __restrict__ w,
+                                                            const float* __restrict__ P, int H,
+                                                            int8_t* __restrict__ q8, double* __restrict__ W) {
+  const int b = blockIdx.y, h = 8 * blockIdx.x + (threadIdx.x >> 5), i = threadIdx.x & 31;
+  const bool hv = h < H;
+  const int64_t bh = (int64_t)b * H + min(h, H - 1);
+  const uint16_t* qr = q + bh * 128;
   double y = 0.0;
-  if (i < DC) {
-    // the chain runs in ascending j; its operands arrive 64 at a time
+  // the chain runs in ascending j; its operands arrive 64 at a time
 #pragma unroll
-    for (int j0 = 0; j0 < 128; j0 += 64) {
-      float pv[64];
-      uint16_t qv[64];
+  for (int j0 = 0; j0 < 128; j0 += 64) {
+    float pv[64];
+    uint16_t qv[64];
 #pragma unroll
-      for (int j = 0; j < 64; ++j) {
-        pv[j] = P[i * 128 + j0 + j];
-        qv[j] = qr[j0 + j];
-      }
-#pragma unroll
-      for (int j = 0; j < 64; ++j) y = fma((double)pv[j], (double)bf16_to_f32(qv[j]), y);
+    for (int j = 0; j < 64; ++j) {
+      pv[j] = P[i * 128 + j0 + j];
+      qv[j] = qr[j0 + j];
     }
+#pragma unroll
+    for (int j = 0; j < 64; ++j) y = fma((double)pv[j], (double)bf16_to_f32(qv[j]), y);
   }
-  const double amax = wave_max_d(i < DC ? fabs(y) : 0.0);
+  // max |y| over the head's 32 outputs (one half of the wave)
+  double amax = fabs(y);
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) amax = fmax(amax, __shfl_xor(amax, o, WAVE));
   const double s = amax > 0.0 ? amax / 127.0 : 1.0;
-  if (i < DC) {
+  if (hv) {
     double t = rint(y / s);
     t = fmin(fmax(t, -127.0), 127.0);
-    q8[(int64_t)bh * DC + i] = (int8_t)(int)t;
+    q8[bh * DC + i] = (int8_t)(int)t;
+    if (i == 0) W[bh] = (double)w[bh] * s;
   }
-  if (i == 0) W[bh] = (double)w[bh] * s;
 }
 
 // Stage 1.  A wave scores 64 keys at a time: the exact int32 dots D[h][s] of the
@@ -72,7 +76,9 @@ template <int HT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void compact_stage1_kernel(
     const int8_t* __restrict__ q8, const double* __restrict__ W, const int8_t* __restrict__ ck,
     const float* __restrict__ cks, int S, int H, int kpb, double* __restrict__ s1) {
-  constexpr bool WREG = HT <= 2;  // head weights in VGPRs (up to 64 heads), else LDS broadcasts
+  // head weights in VGPRs up to 32 heads, else LDS broadcasts (64 heads' fp64 weights
+  // would take 128 VGPRs and halve the waves per SIMD)
+  constexpr bool WREG = HT <= 1;
   __shared__ __attribute__((aligned(16))) double sW[WREG ? 2 : 32 * HT];
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -358,7 +364,7 @@ hipError_t launch_compact(const uint16_t* q, const float* w, const float* P, con
   void* tk_ws = p;
   int32_t* sl = shortlist ? shortlist : sl_ws;
 
-  compact_query_kernel<<<B * H, 64, 0, st>>>(q, w, P, H, q8, W);
+  compact_query_kernel<<<dim3((H + 7) / 8, B), 256, 0, st>>>(q, w, P, H, q8, W);
   const int kpb = stage1_keys_per_block(B, S);
   const dim3 g1((S + kpb - 1) / kpb, B);
   if (H <= 32)
