@@ -259,21 +259,25 @@ __device__ __forceinline__ bool write_top_listed(const typename ScoreTraits<Sc>:
   return true;
 }
 
+// LDS scratch of the selections below, declared once by the kernel whatever
+// entries-per-thread instance runs.
+struct SelScratch {
+  uint32_t scan1[TK_THREADS / 64], scan2[TK_THREADS / 64];
+  uint32_t hist[KW_BINS];
+  uint64_t wsum8[2 * (TK_THREADS / 64)];  // minima and maxima of the keys, per wave
+  uint32_t res[3];
+};
+
 // A row of at most MB_KEEP entries whose ids ascend along the row (a row of scores
 // by position, or a list of candidates kept in index order): every entry is held
 // in registers, and the selection above writes the k best in position order, which
 // is ascending-id order, so no sort is needed.  Rows whose ids do not ascend take
-// select_block.
-template <typename S>
+// select_block.  E entries per thread (n <= E * TK_THREADS): every pass of the
+// selection loops over them, so short rows take a small E.
+template <typename S, int E>
 __device__ void select_small(const S* __restrict__ row, const int32_t* __restrict__ idrow, int n, int k,
-                             int32_t* __restrict__ idx_out, S* __restrict__ val_out) {
+                             int32_t* __restrict__ idx_out, S* __restrict__ val_out, SelScratch& sc) {
   typedef typename ScoreTraits<S>::K K;
-  constexpr int NW = TK_THREADS / 64;
-  constexpr int E = MB_KEEP / TK_THREADS;
-  __shared__ uint32_t scan1[NW], scan2[NW];
-  __shared__ uint32_t hist[KW_BINS];
-  __shared__ uint64_t wsum8[2 * NW];
-  __shared__ uint32_t res3[3];
   const int tid = threadIdx.x;
   K key[E];
   S val[E];
@@ -309,7 +313,8 @@ __device__ void select_small(const S* __restrict__ row, const int32_t* __restric
     }
     return;
   }
-  write_top_listed<S, E>(key, val, id, valid, (uint32_t)k, idx_out, val_out, hist, wsum8, res3, scan1, scan2);
+  write_top_listed<S, E>(key, val, id, valid, (uint32_t)k, idx_out, val_out, sc.hist, sc.wsum8, sc.res, sc.scan1,
+                         sc.scan2);
 }
 
 template <typename S>
@@ -324,8 +329,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restric
   const int32_t* idrow = ids ? ids + (int64_t)r * row_stride : nullptr;
   int32_t* io = idx_out + (int64_t)r * k;
   S* vo = val_out ? val_out + (int64_t)r * k : nullptr;
-  if (n <= MB_KEEP)
-    select_small<S>(row, idrow, n, k, io, vo);
+  __shared__ SelScratch sc;
+  if (n <= 2 * TK_THREADS)
+    select_small<S, 2>(row, idrow, n, k, io, vo, sc);
+  else if (n <= MB_KEEP)
+    select_small<S, MB_KEEP / TK_THREADS>(row, idrow, n, k, io, vo, sc);
   else
     select_block<S>(row, idrow, n, k, io, vo);
 }
@@ -432,21 +440,64 @@ __global__ __launch_bounds__(MB_THREADS) void topk_filter_kernel(const Sc* __res
 // positions from a prefix scan.  Rows whose list cannot be used take the
 // whole-row path.
 
+// The selection over a usable list of c entries (region offsets off[0..P]), E
+// entries per thread (c <= E * TK_THREADS): every pass of the selection loops over
+// them, so short lists take a small E.  sc: the caller's LDS scratch.
+template <typename Sc, int E>
+__device__ void finalize_listed(int r, const Sc* __restrict__ scores, int S, int n, int k, int P, int chunk,
+                                uint32_t c, const uint32_t* off, uint32_t floor32, const Sc* __restrict__ cval,
+                                const int32_t* __restrict__ cid, int32_t* __restrict__ io, Sc* __restrict__ vo,
+                                SelScratch& sc) {
+  typedef typename ScoreTraits<Sc>::K K;
+  const int tid = threadIdx.x;
+  // entries E*tid .. E*tid+E-1 of the concatenated regions (index order)
+  K key[E];
+  Sc val[E];
+  int32_t id[E];
+  bool valid[E];
+  // every load is issued (entries past the list read its last entry) before any
+  // is used; a thread's entries are consecutive, so after one binary search for
+  // the region of its first entry the later ones only step forward
+  int rg;
+  {
+    const uint32_t jf = min((uint32_t)(E * tid), c - 1u);
+    int lo2 = 0, hi2 = P - 1;  // region b with off[b] <= jf < off[b+1]
+    while (lo2 < hi2) {
+      const int mid = (lo2 + hi2 + 1) >> 1;
+      if (off[mid] <= jf) lo2 = mid; else hi2 = mid - 1;
+    }
+    rg = lo2;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t j0 = (uint32_t)(E * tid + e);
+    valid[e] = j0 < c;
+    const uint32_t j = valid[e] ? j0 : c - 1u;
+    while (rg + 1 < P && off[rg + 1] <= j) ++rg;
+    const int64_t src = (int64_t)r * S + (int64_t)rg * chunk + (j - off[rg]);
+    val[e] = cval[src];
+    id[e] = cid[src];
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = valid[e] ? ScoreTraits<Sc>::ord(val[e]) : (K)0;
+  // every unlisted entry of a region lies below its threshold; when the kth listed
+  // value reaches the largest threshold no unlisted entry can enter the top k
+  // (fp64 regions record the upper half of their threshold key)
+  const K floor = (K)floor32 << (8 * sizeof(K) - 32);
+  if (!write_top_listed<Sc, E>(key, val, id, valid, (uint32_t)k, io, vo, sc.hist, sc.wsum8, sc.res, sc.scan1,
+                               sc.scan2, floor))
+    select_block<Sc>(scores + (int64_t)r * S, nullptr, n, k, io, vo);
+}
+
 template <typename Sc>
 __device__ void finalize_lists(int r, const Sc* __restrict__ scores, const int32_t* __restrict__ nv, int S, int k,
                                int P, int chunk, const uint32_t* __restrict__ bcnt, const Sc* __restrict__ cval,
                                const int32_t* __restrict__ cid, int32_t* __restrict__ idx_out,
                                Sc* __restrict__ val_out, const uint32_t* __restrict__ tau_used) {
-  typedef typename ScoreTraits<Sc>::K K;
-  constexpr int NW = TK_THREADS / 64;
-  constexpr int E = MB_KEEP / TK_THREADS;
   __shared__ uint32_t off[257];
   __shared__ int s_unfiltered;
   __shared__ uint32_t s_floor;
-  __shared__ uint32_t scan1[NW], scan2[NW];
-  __shared__ uint32_t hist[KW_BINS];
-  __shared__ uint64_t wsum8[2 * NW];  // minima and maxima of the keys, per wave
-  __shared__ uint32_t res8[3];
+  __shared__ SelScratch sc;
   const int tid = threadIdx.x;
   int n = S;
   if (nv) n = min(max(nv[r], 0), S);
@@ -491,43 +542,13 @@ __device__ void finalize_lists(int r, const Sc* __restrict__ scores, const int32
     select_block<Sc>(scores + (int64_t)r * S, nullptr, n, k, io, vo);
     return;
   }
-  // entries E*tid .. E*tid+E-1 of the concatenated regions (index order)
-  K key[E];
-  Sc val[E];
-  int32_t id[E];
-  bool valid[E];
-  // every load is issued (entries past the list read its last entry) before any
-  // is used; a thread's entries are consecutive, so after one binary search for
-  // the region of its first entry the later ones only step forward
-  int rg;
-  {
-    const uint32_t jf = min((uint32_t)(E * tid), c - 1u);
-    int lo2 = 0, hi2 = P - 1;  // region b with off[b] <= jf < off[b+1]
-    while (lo2 < hi2) {
-      const int mid = (lo2 + hi2 + 1) >> 1;
-      if (off[mid] <= jf) lo2 = mid; else hi2 = mid - 1;
-    }
-    rg = lo2;
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t j0 = (uint32_t)(E * tid + e);
-    valid[e] = j0 < c;
-    const uint32_t j = valid[e] ? j0 : c - 1u;
-    while (rg + 1 < P && off[rg + 1] <= j) ++rg;
-    const int64_t src = (int64_t)r * S + (int64_t)rg * chunk + (j - off[rg]);
-    val[e] = cval[src];
-    id[e] = cid[src];
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = valid[e] ? ScoreTraits<Sc>::ord(val[e]) : (K)0;
-  // every unlisted entry of a region lies below its threshold; when the kth listed
-  // value reaches the largest threshold no unlisted entry can enter the top k
-  // (fp64 regions record the upper half of their threshold key)
-  const K floor = (K)s_floor << (8 * sizeof(K) - 32);
-  if (!write_top_listed<Sc, E>(key, val, id, valid, (uint32_t)k, io, vo, hist, wsum8, res8, scan1, scan2,
-                               floor))
-    select_block<Sc>(scores + (int64_t)r * S, nullptr, n, k, io, vo);
+  if (c <= 2u * TK_THREADS)
+    finalize_listed<Sc, 2>(r, scores, S, n, k, P, chunk, c, off, s_floor, cval, cid, io, vo, sc);
+  else if (c <= 4u * TK_THREADS)
+    finalize_listed<Sc, 4>(r, scores, S, n, k, P, chunk, c, off, s_floor, cval, cid, io, vo, sc);
+  else
+    finalize_listed<Sc, MB_KEEP / TK_THREADS>(r, scores, S, n, k, P, chunk, c, off, s_floor, cval, cid, io, vo,
+                                              sc);
 }
 
 template <typename Sc>
