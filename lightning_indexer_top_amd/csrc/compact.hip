@@ -17,6 +17,7 @@
 // in ascending key index.
 #include "common.h"
 #include "launch.h"
+#include "select.h"
 
 namespace li {
 
@@ -72,14 +73,31 @@ __global__ __launch_bounds__(256) void compact_query_kernel(const uint16_t* __re
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
-template <int HT>
+//
+// LIST (a workgroup's keys are exactly one region of the shortlist selection's
+// per-region lists, LT_E * 256 keys): the scores also go to LDS, and once the
+// workgroup's tiles are done it lists its region's entries above a threshold of its
+// own (list_above_local_threshold), so the selection only runs its exact pass over
+// the lists; s1 is still written for the rows whose lists cannot be used.
+struct S1List {
+  const int32_t* nv;
+  int m;
+  double* cval;
+  int32_t* cid;
+  uint32_t* bcnt;
+  uint32_t* tau_used;
+};
+
+template <int HT, bool LIST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void compact_stage1_kernel(
     const int8_t* __restrict__ q8, const double* __restrict__ W, const int8_t* __restrict__ ck,
-    const float* __restrict__ cks, int S, int H, int kpb, double* __restrict__ s1) {
+    const float* __restrict__ cks, int S, int H, int kpb, double* __restrict__ s1, S1List ls) {
   // head weights in VGPRs up to 32 heads, else LDS broadcasts (64 heads' fp64 weights
   // would take 128 VGPRs and halve the waves per SIMD)
   constexpr bool WREG = HT <= 1;
   __shared__ __attribute__((aligned(16))) double sW[WREG ? 2 : 32 * HT];
+  __shared__ __attribute__((aligned(16))) double sv[LIST ? LT_E * 256 : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t lscr[LIST ? 24 : 1];
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, col = lane & 31;
@@ -142,7 +160,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
       /* the next head group's MFMAs stay after this group's chain */                                          \
       asm volatile("" : "+v"(X##0), "+v"(X##1));                                                               \
     }                                                                                                          \
-    if ((kb) + lane < kend) s1[(int64_t)b * S + (kb) + lane] = (double)X##s * acc;                             \
+    const double sc_ = (double)X##s * acc;                                                                     \
+    if ((kb) + lane < kend) s1[(int64_t)b * S + (kb) + lane] = sc_;                                            \
+    if constexpr (LIST) sv[(kb) - key0 + lane] = sc_;                                                          \
   } while (0)
   // three tiles rotate: two are in flight while one is scored (one HBM round trip
   // is several tiles' worth of scoring)
@@ -163,6 +183,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
   }
 #undef LI_S1_LOAD
 #undef LI_S1_TILE
+  if constexpr (LIST) {
+    __syncthreads();
+    double v[LT_E];
+#pragma unroll
+    for (int e = 0; e < LT_E; ++e) v[e] = sv[e * 256 + tid];
+    int n_row = S;
+    if (ls.nv) n_row = min(max(ls.nv[b], 0), S);
+    const int n = max(min(n_row - key0, kpb), 0);
+    const int P = gridDim.x;
+    list_above_local_threshold<double>(v, n, ls.m, P, (int)blockIdx.x, ls.cval + (int64_t)b * S + key0,
+                                       ls.cid + (int64_t)b * S + key0, key0, ls.bcnt + (int64_t)b * P + blockIdx.x,
+                                       ls.tau_used + (int64_t)b * 256, lscr);
+  }
 }
 
 // Stage 2.  A quad of lanes serves two shortlisted candidates: lane g computes,
@@ -367,13 +400,30 @@ hipError_t launch_compact(const uint16_t* q, const float* w, const float* P, con
   compact_query_kernel<<<dim3((H + 7) / 8, B), 256, 0, st>>>(q, w, P, H, q8, W);
   const int kpb = stage1_keys_per_block(B, S);
   const dim3 g1((S + kpb - 1) / kpb, B);
+  // the shortlist's per-region lists straight from stage 1 when its workgroups are
+  // the selection's regions
+  int region = 0;
+  const bool listed = topk_f64_rows_listed(B, S, &region) && kpb == region;
+  S1List ls{nv, m, nullptr, nullptr, nullptr, nullptr};
+  if (listed) topk_mb_layout_f64(tk_ws, B, S, &ls.tau_used, &ls.bcnt, &ls.cval, &ls.cid);
+#define LI_STAGE1(HT_)                                                                     \
+  do {                                                                                     \
+    if (listed)                                                                            \
+      compact_stage1_kernel<HT_, true><<<g1, 256, 0, st>>>(q8, W, ck, cks, S, H, kpb, s1, ls);  \
+    else                                                                                   \
+      compact_stage1_kernel<HT_, false><<<g1, 256, 0, st>>>(q8, W, ck, cks, S, H, kpb, s1, ls); \
+  } while (0)
   if (H <= 32)
-    compact_stage1_kernel<1><<<g1, 256, 0, st>>>(q8, W, ck, cks, S, H, kpb, s1);
+    LI_STAGE1(1);
   else if (H <= 64)
-    compact_stage1_kernel<2><<<g1, 256, 0, st>>>(q8, W, ck, cks, S, H, kpb, s1);
+    LI_STAGE1(2);
   else
-    compact_stage1_kernel<4><<<g1, 256, 0, st>>>(q8, W, ck, cks, S, H, kpb, s1);
-  hipError_t e = launch_topk_f64_rows(s1, nv, B, S, m, sl, nullptr, tk_ws, st);
+    LI_STAGE1(4);
+#undef LI_STAGE1
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = listed ? launch_topk_finalize_f64(s1, nv, B, S, m, ls.bcnt, ls.cval, ls.cid, sl, nullptr, ls.tau_used, st)
+             : launch_topk_f64_rows(s1, nv, B, S, m, sl, nullptr, tk_ws, st);
   if (e != hipSuccess) return e;
   stage2_attrs();
   const dim3 g2((m + S2_CPB - 1) / S2_CPB, B);

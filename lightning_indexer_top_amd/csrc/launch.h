@@ -37,6 +37,17 @@ hipError_t launch_topk_f64(const double* scores, int64_t row_stride, const int32
 size_t topk_f64_rows_ws_bytes(int R, int S);
 hipError_t launch_topk_f64_rows(const double* scores, const int32_t* nv, int R, int S, int k, int32_t* idx,
                                 double* val, void* ws, hipStream_t st);
+// Whether launch_topk_f64_rows takes rows of S scores through per-region lists
+// (regions of *region scores, each listed above a threshold of its own): a
+// scoring kernel whose workgroups cover exactly those regions may list them itself
+// (list_above_local_threshold into the buffers topk_mb_layout_f64 names in the
+// same workspace) and then call launch_topk_finalize_f64.
+bool topk_f64_rows_listed(int R, int S, int* region);
+void topk_mb_layout_f64(void* ws, int R, int S, uint32_t** thresholds, uint32_t** bcnt, double** cval,
+                        int32_t** cid);
+hipError_t launch_topk_finalize_f64(const double* scores, const int32_t* nv, int R, int S, int k, const uint32_t* bcnt,
+                                    const double* cval, const int32_t* cid, int32_t* idx, double* val,
+                                    const uint32_t* tau_used, hipStream_t st);
 
 // two-stage compact search (workspace layout in compact.hip)
 size_t compact_ws_bytes(int B, int S, int H, int m, int k);

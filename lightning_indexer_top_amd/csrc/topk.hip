@@ -546,6 +546,8 @@ __device__ void finalize_lists(int r, const Sc* __restrict__ scores, const int32
     finalize_listed<Sc, 2>(r, scores, S, n, k, P, chunk, c, off, s_floor, cval, cid, io, vo, sc);
   else if (c <= 4u * TK_THREADS)
     finalize_listed<Sc, 4>(r, scores, S, n, k, P, chunk, c, off, s_floor, cval, cid, io, vo, sc);
+  else if (c <= 6u * TK_THREADS)
+    finalize_listed<Sc, 6>(r, scores, S, n, k, P, chunk, c, off, s_floor, cval, cid, io, vo, sc);
   else
     finalize_listed<Sc, MB_KEEP / TK_THREADS>(r, scores, S, n, k, P, chunk, c, off, s_floor, cval, cid, io, vo,
                                               sc);
@@ -931,6 +933,32 @@ hipError_t launch_topk_f64_rows(const double* scores, const int32_t* nv, int R, 
                                 double* val, void* ws, hipStream_t st) {
   if (topk_use_mb(R, S)) return launch_topk_mb<double>(scores, nv, R, S, k, idx, val, ws, st);
   return launch_topk_f64(scores, S, nv, nullptr, R, S, k, idx, val, st);
+}
+
+bool topk_f64_rows_listed(int R, int S, int* region) {
+  *region = TK_LOCAL_CHUNK;
+  return topk_use_mb(R, S) && (S + TK_LOCAL_CHUNK - 1) / TK_LOCAL_CHUNK <= 256;
+}
+
+void topk_mb_layout_f64(void* ws, int R, int S, uint32_t** thresholds, uint32_t** bcnt, double** cval,
+                        int32_t** cid) {
+  uint8_t* p = (uint8_t*)ws;
+  *thresholds = (uint32_t*)p;
+  p += a256((size_t)R * 256 * 4);
+  *bcnt = (uint32_t*)p;
+  p += a256((size_t)R * 256 * 4);
+  *cval = (double*)p;
+  p += a256((size_t)R * S * sizeof(double));
+  *cid = (int32_t*)p;
+}
+
+hipError_t launch_topk_finalize_f64(const double* scores, const int32_t* nv, int R, int S, int k, const uint32_t* bcnt,
+                                    const double* cval, const int32_t* cid, int32_t* idx, double* val,
+                                    const uint32_t* tau_used, hipStream_t st) {
+  const int P = (S + TK_LOCAL_CHUNK - 1) / TK_LOCAL_CHUNK;
+  topk_finalize_kernel<double><<<R, TK_THREADS, 0, st>>>(scores, nv, S, k, P, TK_LOCAL_CHUNK, bcnt, cval, cid, idx,
+                                                         val, tau_used);
+  return hipGetLastError();
 }
 
 // ---- static scratch for callers that cannot allocate ---------------------------
