@@ -480,10 +480,10 @@ __global__ __launch_bounds__(64) void pq_query_kernel(const uint16_t* __restrict
 // 16 hf + 4 ks .. + 3) of both the query (A operand) and the key (B operand), so a
 // lane's 16 code bytes (one 16-byte load per key) give its four B operands through
 // 16 codebook reads.  Four v_mfma_i32_32x32x32_i8 per 32 heads and 32 keys.
-template <int HT>
+template <int HT, bool LIST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pq_stage1_kernel(
     const int8_t* __restrict__ q8, const double* __restrict__ W, const uint32_t* __restrict__ cb,
-    const uint8_t* __restrict__ codes, int S, int H, int kpb, double* __restrict__ s1) {
+    const uint8_t* __restrict__ codes, int S, int H, int kpb, double* __restrict__ s1, S1List ls) {
   constexpr bool WREG = HT <= 1;  // head weights in VGPRs up to 32 heads (64 would spill), else LDS broadcasts
   __shared__ __attribute__((aligned(16))) uint32_t scb[PQ_PIECES * 256];
   __shared__ __attribute__((aligned(16))) double sW[WREG ? 2 : 32 * HT];
@@ -571,6 +571,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
 #undef LI_PQ_LOAD
 #undef LI_PQ_TILE
+  if constexpr (LIST) {
+    // this workgroup's region of scores, read back (its own writes: the barrier
+    // orders them), then listed above the region's own threshold
+    __shared__ __attribute__((aligned(16))) uint32_t lscr[24];
+    __syncthreads();
+    int n_row = S;
+    if (ls.nv) n_row = min(max(ls.nv[b], 0), S);
+    const int n = max(min(n_row - key0, kpb), 0);
+    double v[LT_E];
+#pragma unroll
+    for (int e = 0; e < LT_E; ++e) v[e] = e * 256 + tid < n ? s1[(int64_t)b * S + key0 + e * 256 + tid] : 0.0;
+    const int P = gridDim.x;
+    list_above_local_threshold<double>(v, n, ls.m, P, (int)blockIdx.x, ls.cval + (int64_t)b * S + key0,
+                                       ls.cid + (int64_t)b * S + key0, key0, ls.bcnt + (int64_t)b * P + blockIdx.x,
+                                       ls.tau_used + (int64_t)b * 256, lscr);
+  }
 }
 
 size_t pq_ws_bytes(int B, int S, int H, int m, int k) {
@@ -609,13 +625,28 @@ hipError_t launch_pq(const uint16_t* q, const float* w, const int8_t* cb, float 
   const int kpb = stage1_keys_per_block(B, S);
   const dim3 g1((S + kpb - 1) / kpb, B);
   const uint32_t* cbw = (const uint32_t*)cb;
+  int region = 0;
+  const bool listed = topk_f64_rows_listed(B, S, &region) && kpb == region;
+  S1List ls{nv, m, nullptr, nullptr, nullptr, nullptr};
+  if (listed) topk_mb_layout_f64(tk_ws, B, S, &ls.tau_used, &ls.bcnt, &ls.cval, &ls.cid);
+#define LI_PQ1(HT_)                                                                          \
+  do {                                                                                       \
+    if (listed)                                                                              \
+      pq_stage1_kernel<HT_, true><<<g1, 256, 0, st>>>(q8, W, cbw, codes, S, H, kpb, s1, ls);  \
+    else                                                                                     \
+      pq_stage1_kernel<HT_, false><<<g1, 256, 0, st>>>(q8, W, cbw, codes, S, H, kpb, s1, ls); \
+  } while (0)
   if (H <= 32)
-    pq_stage1_kernel<1><<<g1, 256, 0, st>>>(q8, W, cbw, codes, S, H, kpb, s1);
+    LI_PQ1(1);
   else if (H <= 64)
-    pq_stage1_kernel<2><<<g1, 256, 0, st>>>(q8, W, cbw, codes, S, H, kpb, s1);
+    LI_PQ1(2);
   else
-    pq_stage1_kernel<4><<<g1, 256, 0, st>>>(q8, W, cbw, codes, S, H, kpb, s1);
-  hipError_t e = launch_topk_f64_rows(s1, nv, B, S, m, sl, nullptr, tk_ws, st);
+    LI_PQ1(4);
+#undef LI_PQ1
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = listed ? launch_topk_finalize_f64(s1, nv, B, S, m, ls.bcnt, ls.cval, ls.cid, sl, nullptr, ls.tau_used, st)
+             : launch_topk_f64_rows(s1, nv, B, S, m, sl, nullptr, tk_ws, st);
   if (e != hipSuccess) return e;
   stage2_attrs();
   const dim3 g2((m + S2_CPB - 1) / S2_CPB, B);
