@@ -332,6 +332,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(const S* __restric
   __shared__ SelScratch sc;
   if (n <= 2 * TK_THREADS)
     select_small<S, 2>(row, idrow, n, k, io, vo, sc);
+  else if (n <= 4 * TK_THREADS)
+    select_small<S, 4>(row, idrow, n, k, io, vo, sc);
   else if (n <= MB_KEEP)
     select_small<S, MB_KEEP / TK_THREADS>(row, idrow, n, k, io, vo, sc);
   else
