@@ -600,9 +600,11 @@ static int stream_keys_per_block(int R, int S, int blocks_per_cu) {
   return (int)kpb;
 }
 
-// Generic fp32 path (fp32 queries or keys): one thread per key, fp32 FMAs, the
-// query row staged in LDS.  dot_h accumulates over the key dimension in ascending
-// order, the head sum over h in ascending order, then the key scale.
+// Generic fp32 path (fp32 queries or keys): a quad of lanes per key, fp32 FMAs,
+// the query row staged in LDS.  Lane g accumulates dimensions 32 g .. 32 g + 31 of
+// four heads at a time in ascending order; the quad's partial dots are summed as
+// (p0 + p1) + (p2 + p3), the head sum runs over h in ascending order, then the key
+// scale.  The order is fixed, so results are deterministic.
 template <typename QT, int KT>
 __global__ __launch_bounds__(256) void score_valu_kernel(const QT* __restrict__ q, const float* __restrict__ w,
                                                          const void* __restrict__ k, const float* __restrict__ ks,
@@ -619,46 +621,79 @@ __global__ __launch_bounds__(256) void score_valu_kernel(const QT* __restrict__ 
   }
   for (int i = threadIdx.x; i < H; i += blockDim.x) sq[H * 128 + i] = w[(int64_t)r * H + i];
   __syncthreads();
-  const int s = blockIdx.x * blockDim.x + threadIdx.x;
-  if (s >= S) return;
+  // a quad of lanes per key: lane g holds dimensions 32 g .. 32 g + 31
+  const int g = threadIdx.x & 3;
+  const int s = blockIdx.x * 64 + (threadIdx.x >> 2);
   int nvis = S;
   if (nv) nvis = min(max(nv[r], 0), S);
-  if (s >= nvis) {
-    scores[(int64_t)r * S + s] = -INFINITY;
-    return;
-  }
-  float kv[128];
-  const int64_t row = (int64_t)b * S + s;
+  const int64_t row = (int64_t)b * S + min(s, S - 1);
+  float kv[32];
   if constexpr (KT == 0) {
-    const float4* kp = (const float4*)((const float*)k + row * 128);
+    const float4* kp = (const float4*)((const float*)k + row * 128 + 32 * g);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      float4 v = kp[j];
+    for (int j = 0; j < 8; ++j) {
+      const float4 v = kp[j];
       kv[4 * j] = v.x; kv[4 * j + 1] = v.y; kv[4 * j + 2] = v.z; kv[4 * j + 3] = v.w;
     }
   } else if constexpr (KT == 1) {
-    const uint16_t* kp = (const uint16_t*)k + row * 128;
+    const uint4* kp = (const uint4*)((const uint16_t*)k + row * 128 + 32 * g);
 #pragma unroll
-    for (int j = 0; j < 128; ++j) kv[j] = bf16_to_f32(kp[j]);
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = kp[j];
+      const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kv[8 * j + 2 * e] = __uint_as_float(x[e] << 16);
+        kv[8 * j + 2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u);
+      }
+    }
   } else {
-    const uint32_t* kp = (const uint32_t*)((const uint8_t*)k + row * 128);
+    const uint4* kp = (const uint4*)((const uint8_t*)k + row * 128 + 32 * g);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t v = kp[j];
-      auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
-      auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
-      kv[4 * j] = p0[0]; kv[4 * j + 1] = p0[1]; kv[4 * j + 2] = p1[0]; kv[4 * j + 3] = p1[1];
+    for (int j = 0; j < 2; ++j) {
+      const uint4 v = kp[j];
+      const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8(x[e], false);
+        const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8(x[e], true);
+        kv[16 * j + 4 * e] = p0[0]; kv[16 * j + 4 * e + 1] = p0[1];
+        kv[16 * j + 4 * e + 2] = p1[0]; kv[16 * j + 4 * e + 3] = p1[1];
+      }
     }
   }
+  // the quad's four partial dots of a head, summed as (p0 + p1) + (p2 + p3) in every lane
+  auto quad_sum = [](float x) {
+    x += __shfl_xor(x, 1, WAVE);
+    return x + __shfl_xor(x, 2, WAVE);
+  };
+  const float* qs = sq + 32 * g;
   float acc = 0.0f;
-  for (int h = 0; h < H; ++h) {
-    float dot = 0.0f;
+  int h = 0;
+  for (; h + 4 <= H; h += 4) {  // four heads' chains at a time
+    float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f, d3 = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 128; ++j) dot = fmaf(sq[h * 128 + j], kv[j], dot);
-    acc = fmaf(sq[H * 128 + h], fmaxf(dot, 0.0f), acc);
+    for (int j = 0; j < 32; ++j) {
+      d0 = fmaf(qs[h * 128 + j], kv[j], d0);
+      d1 = fmaf(qs[(h + 1) * 128 + j], kv[j], d1);
+      d2 = fmaf(qs[(h + 2) * 128 + j], kv[j], d2);
+      d3 = fmaf(qs[(h + 3) * 128 + j], kv[j], d3);
+    }
+    d0 = quad_sum(d0); d1 = quad_sum(d1); d2 = quad_sum(d2); d3 = quad_sum(d3);
+    acc = fmaf(sq[H * 128 + h], fmaxf(d0, 0.0f), acc);
+    acc = fmaf(sq[H * 128 + h + 1], fmaxf(d1, 0.0f), acc);
+    acc = fmaf(sq[H * 128 + h + 2], fmaxf(d2, 0.0f), acc);
+    acc = fmaf(sq[H * 128 + h + 3], fmaxf(d3, 0.0f), acc);
+  }
+  for (; h < H; ++h) {
+    float d0 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) d0 = fmaf(qs[h * 128 + j], kv[j], d0);
+    d0 = quad_sum(d0);
+    acc = fmaf(sq[H * 128 + h], fmaxf(d0, 0.0f), acc);
   }
   if (ks) acc *= ks[row];
-  scores[(int64_t)r * S + s] = acc;
+  if (g == 0 && s < S) scores[(int64_t)r * S + s] = s < nvis ? acc : -INFINITY;
 }
 
 // One launch of the streaming kernel.  STG: scores held in LDS (two workgroups per
@@ -722,7 +757,7 @@ hipError_t launch_score(const void* q, int q_type, const float* w, const void* k
     if (H <= 64) return launch_stream<2, false, false, false>(qq, w, kk, ks, nv, R, T, S, H, scores, nullptr, 0, 0, st);
     return launch_stream<4, false, false, false>(qq, w, kk, ks, nv, R, T, S, H, scores, nullptr, 0, 0, st);
   }
-  dim3 grid((S + 255) / 256, R);
+  dim3 grid((S + 63) / 64, R);  // 64 keys a workgroup, a quad of lanes each
   const size_t lds = sizeof(float) * (size_t)H * 129;
   static const bool attr_set = [] {
     // H <= 128 needs up to 66 KB of dynamic LDS

@@ -103,11 +103,15 @@ def test_fp8_keys_summation_bound(H, spread):
     assert (err <= bound).all(), f"H={H}: worst error / condition {np.max(err / np.maximum(cond, 1e-300)):.3e}"
 
 
-@pytest.mark.parametrize("combo", [("f32", "f32"), ("f32", "fp8"), ("f32", "bf16"), ("bf16", "f32")])
-def test_fp32_paths(combo):
+# H = 12: three groups of four heads; H = 7: one group and three single heads;
+# S = 1500 and 1001: a ragged last workgroup of 64 keys
+@pytest.mark.parametrize("combo,H,S", [(("f32", "f32"), 12, 1500), (("f32", "fp8"), 12, 1500),
+                                       (("f32", "bf16"), 12, 1500), (("bf16", "f32"), 12, 1500),
+                                       (("f32", "f32"), 7, 1001), (("bf16", "f32"), 7, 1001)])
+def test_fp32_paths(combo, H, S):
     qt, kt = combo
-    print("fp32 path", combo, flush=True)
-    sp = workloads.spec("tiny_decode", B=2, S=1500, H=12, q=qt, key=kt, seed=0x5EED0200)
+    print("fp32 path", combo, H, S, flush=True)
+    sp = workloads.spec("tiny_decode", B=2, S=S, H=H, q=qt, key=kt, seed=0x5EED0200 + H)
     g, o, _ = run(sp)
     assert_scores_close(g, o, str(combo))
 
