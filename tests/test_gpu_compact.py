@@ -75,3 +75,24 @@ def test_concentrated_shortlist():
     x["cs"] = np.array(x["cs"], copy=True)
     x["cs"][0, 4096:8192] *= 64.0
     check(*run_x(x, 2048, 512), "concentrated")
+
+
+def test_stage1_region_lists():
+    """32 sequences of 131,072 keys: each stage-1 workgroup scores exactly one
+    4,096-key region and lists its shortlist candidates itself.  Visible counts
+    inside a region, on a region edge, below one region, below the shortlist size
+    and zero; row 1 has every best score in one region (its lists cannot be used,
+    so the row is selected whole).  Every row bit-exact."""
+    print("compact stage-1 region lists", flush=True)
+    sp = workloads.spec("compact_search", seed=0x5EED0730)
+    B, S = sp["B"], sp["S"]
+    x = workloads.compact_inputs(sp)
+    x["cs"] = np.array(x["cs"], copy=True)
+    x["cs"][1, 8192:12288] *= 64.0
+    nv = np.full(B, S, np.int32)
+    nv[2:8] = [100000, 8192, 4096, 3000, 1500, 0]
+    nv[9] = 16385
+    sl, idx, val, ref = run_x(x, 2048, 512, nv)
+    check(sl, idx, val, ref, "stage-1 region lists")
+    assert (idx[7] == -1).all() and (idx[6, 1500:] == -1).all()
+

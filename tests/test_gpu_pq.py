@@ -63,3 +63,19 @@ def test_multi_region_visible_counts():
     sp = workloads.spec("pq_search", B=2, S=40000, H=64, seed=0x5EED1200, pq_train_stride=1, pq_iters=4)
     nv = np.array([40000, 23456], np.int32)
     check(*run(workloads.pq_inputs(sp), 2048, 512, nv))
+
+
+def test_stage1_region_lists():
+    """32 sequences of 131,072 keys: each PQ stage-1 workgroup scores exactly one
+    4,096-key region and lists its shortlist candidates itself (its scores read back
+    after the workgroup barrier).  Visible counts inside a region, on a region edge,
+    below one region, below the shortlist size and zero; every row bit-exact."""
+    print("pq stage-1 region lists", flush=True)
+    sp = workloads.spec("pq_search", seed=0x5EED1300, pq_iters=2)
+    B, S = sp["B"], sp["S"]
+    nv = np.full(B, S, np.int32)
+    nv[1:6] = [77777, 12288, 4000, 1999, 0]
+    sl, idx, val, ref = run(workloads.pq_inputs(sp), sp["m"], sp["topk"], nv)
+    check(sl, idx, val, ref)
+    assert (idx[5] == -1).all()
+
