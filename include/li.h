@@ -165,7 +165,7 @@ li_status li_topk_select_noalloc(const float *scores, const int32_t *nv, int R, 
  * never written to memory.  For few long rows (decode) every region of a row lists
  * its entries above a threshold of the region's own ("Latent Sparse Attention",
  * section "What the kernels do about the top-p": a threshold, then a list of the
- * entries above it) -- inside the scoring kernel for fp8 keys at 33-64 heads, in
+ * entries above it) -- inside the scoring kernel for fp8 keys at up to 64 heads, in
  * the selection otherwise -- and one exact pass selects among the lists, or over
  * the whole row when a region's threshold lies above the row's kth value.
  *

@@ -529,7 +529,7 @@ hipError_t launch_indexer_topk(const void* q, int q_type, const float* w, const 
   float* scores = (float*)ws;
   void* tws = (uint8_t*)ws + align256((size_t)B * T * S * sizeof(float));
   if (held_select_apply(q_type, k_type, B * T, S, H, topk)) {
-    // few long rows, fp8 keys, 33-64 heads: each scoring workgroup lists its own
+    // few long rows, fp8 keys, at most 64 heads: each scoring workgroup lists its own
     // entries above a threshold of its own (into the top-k's threshold area and
     // regions), one finalize selects
     uint32_t *tau_used, *bcnt;

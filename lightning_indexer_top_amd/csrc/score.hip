@@ -721,15 +721,15 @@ static hipError_t launch_stream(const uint16_t* qq, const float* w, const uint8_
   return hipGetLastError();
 }
 
-// fp8 keys at 33-64 heads hold their scores in LDS and write them once per
+// fp8 keys at up to 64 heads hold their scores in LDS and write them once per
 // workgroup: writes interleaved with the key stream cost several times their bytes
 template <bool PAGED>
 static hipError_t launch_stream_fp8(const uint16_t* qq, const float* w, const uint8_t* kk, const float* ks,
                                     const int32_t* nv, int R, int T, int S, int H, float* scores,
                                     const int32_t* page_table, int max_pages, int num_pages, hipStream_t st) {
-  if (H <= 32)
-    return launch_stream<1, true, false, PAGED>(qq, w, kk, ks, nv, R, T, S, H, scores, page_table, max_pages,
-                                                num_pages, st);
+  // up to 64 heads one kernel: with 32 heads or fewer the second head tile has zero
+  // weights (its MFMAs are hidden under the key stream, and the held-scores form
+  // streams faster than the 32-head one)
   if (H <= 64)
     return launch_stream<2, true, true, PAGED>(qq, w, kk, ks, nv, R, T, S, H, scores, page_table, max_pages,
                                                num_pages, st);
@@ -784,10 +784,10 @@ hipError_t launch_score(const void* q, int q_type, const float* w, const void* k
   return hipGetLastError();
 }
 
-// Few long rows with fp8 keys and 33-64 heads: the held-scores kernel with the
+// Few long rows with fp8 keys and at most 64 heads: the held-scores kernel with the
 // workgroup-local selection epilogue, then the finalize.
 bool held_select_apply(int q_type, int k_type, int R, int S, int H, int topk) {
-  if (q_type != DT_BF16 || k_type != DT_FP8 || H <= 32 || H > 64) return false;
+  if (q_type != DT_BF16 || k_type != DT_FP8 || H < 1 || H > 64) return false;
   if (!topk_use_mb(R, S) || topk > 2048) return false;
   const int kpb = std::min(stream_keys_per_block(R, S, 2), STAGE_KEYS);
   const int P = (S + kpb - 1) / kpb;

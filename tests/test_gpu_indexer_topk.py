@@ -144,7 +144,7 @@ def _a256(x):
 ])
 def test_decode_select_fused(over, topk, nvs):
     """Few long rows: li_indexer_topk lists every region's entries above a threshold
-    of the region's own (inside the scoring kernel for fp8 keys at 33-64 heads,
+    of the region's own (inside the scoring kernel for fp8 keys at up to 64 heads,
     after it otherwise) and one finalize selects.  The result must equal
     score-then-select bit for bit, pass the oracle band on every row, repeat on the
     same workspace, follow other queries on that workspace, and come out the same
