@@ -382,21 +382,38 @@ def bench_tiny(torch, li, workloads, steps, warmup, cpu=True):
     ws_n = L.li_topk_workspace_bytes(B, S, k)
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device="cuda")
 
-    def step(i):
+    def step_on(stream):
         s = L.li_indexer_score(_p(q), li.LI_F32, _p(w), _p(kk), li.LI_F32, None, None, B, 1, S, H, 128, _p(scores),
-                               st)
-        s |= L.li_topk_select(_p(scores), None, B, S, k, _p(idx), _p(val), _p(ws), ctypes.c_size_t(ws_n), st)
+                               stream)
+        s |= L.li_topk_select(_p(scores), None, B, S, k, _p(idx), _p(val), _p(ws), ctypes.c_size_t(ws_n), stream)
         if s:
             raise RuntimeError(L.li_last_error().decode())
+
+    def step(i):
+        step_on(st)
 
     for i in range(warmup + 5):
         step(i)
     n = max(200, steps * 10)
     ms = burst_ms(torch, step, n)
+    # the same step captured GRAPH_STEPS times in one HIP graph and replayed (no host
+    # launch per call; neither call records a memset)
+    GRAPH_STEPS = 20
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(GRAPH_STEPS):
+                step_on(ctypes.c_void_p(side.cuda_stream))
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    graph_ms = burst_ms(torch, lambda i: g.replay(), 20) / GRAPH_STEPS
     res = {"workload": "tiny_decode B=1 S=4096 H=8 fp32 top-64", "us_per_step": round(ms * 1e3, 2),
            "value": round(ms * 1e3, 2), "unit": "us per step (score + top-k, back-to-back)",
-           "keys_per_s": round(B * S / (ms * 1e-3), 1)}
-    log(f"[tiny] {ms * 1e3:.1f} us per step")
+           "keys_per_s": round(B * S / (ms * 1e-3), 1), "graph_us_per_step": round(graph_ms * 1e3, 2)}
+    log(f"[tiny] {ms * 1e3:.1f} us per step, {graph_ms * 1e3:.1f} us replayed from a HIP graph")
     if cpu:
         import oracle
         reps = 20
