@@ -184,7 +184,7 @@ def oracle_baseline(value, unit, sample, seconds):
 # each scaled by what the same counter reads for a plain 1 GiB copy: FETCH x2.0,
 # WRITE x1.0).  Valid only for the kernel sources it was taken on; null otherwise.
 SCORE_TRAFFIC = {"sources": ["lightning_indexer_top_amd/csrc/score.hip", "lightning_indexer_top_amd/csrc/common.h"],
-                 "sha256_16": "41b399e9a35b7ca6", "fetch_kib": 272520.4, "write_kib": 8192.0}
+                 "sha256_16": "b7f501919c9095cd", "fetch_kib": 272531.5, "write_kib": 8192.0}
 
 
 # ---- measured ceilings ------------------------------------------------------
