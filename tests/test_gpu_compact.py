@@ -77,14 +77,16 @@ def test_concentrated_shortlist():
     check(*run_x(x, 2048, 512), "concentrated")
 
 
-def test_stage1_region_lists():
+@pytest.mark.parametrize("H", [64, 32, 128])
+def test_stage1_region_lists(H):
     """32 sequences of 131,072 keys: each stage-1 workgroup scores exactly one
-    4,096-key region and lists its shortlist candidates itself.  Visible counts
-    inside a region, on a region edge, below one region, below the shortlist size
-    and zero; row 1 has every best score in one region (its lists cannot be used,
-    so the row is selected whole).  Every row bit-exact."""
-    print("compact stage-1 region lists", flush=True)
-    sp = workloads.spec("compact_search", seed=0x5EED0730)
+    4,096-key region and lists its shortlist candidates itself (one, two and four
+    32-head tiles).  Visible counts inside a region, on a region edge, below one
+    region, below the shortlist size and zero; row 1 has every best score in one
+    region (its lists cannot be used, so the row is selected whole).  Every row
+    bit-exact."""
+    print("compact stage-1 region lists", H, flush=True)
+    sp = workloads.spec("compact_search", H=H, seed=0x5EED0730 + H)
     B, S = sp["B"], sp["S"]
     x = workloads.compact_inputs(sp)
     x["cs"] = np.array(x["cs"], copy=True)

@@ -65,13 +65,15 @@ def test_multi_region_visible_counts():
     check(*run(workloads.pq_inputs(sp), 2048, 512, nv))
 
 
-def test_stage1_region_lists():
+@pytest.mark.parametrize("H", [64, 32, 128])
+def test_stage1_region_lists(H):
     """32 sequences of 131,072 keys: each PQ stage-1 workgroup scores exactly one
     4,096-key region and lists its shortlist candidates itself (its scores read back
-    after the workgroup barrier).  Visible counts inside a region, on a region edge,
-    below one region, below the shortlist size and zero; every row bit-exact."""
-    print("pq stage-1 region lists", flush=True)
-    sp = workloads.spec("pq_search", seed=0x5EED1300, pq_iters=2)
+    after the workgroup barrier; one, two and four 32-head tiles).  Visible counts
+    inside a region, on a region edge, below one region, below the shortlist size
+    and zero; every row bit-exact."""
+    print("pq stage-1 region lists", H, flush=True)
+    sp = workloads.spec("pq_search", H=H, seed=0x5EED1300 + H, pq_iters=2)
     B, S = sp["B"], sp["S"]
     nv = np.full(B, S, np.int32)
     nv[1:6] = [77777, 12288, 4000, 1999, 0]
