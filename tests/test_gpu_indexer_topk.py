@@ -140,6 +140,7 @@ def _a256(x):
     (dict(B=4, S=70001, H=100), 512, None),
     (dict(B=6, S=140000), 512, [140000, 0, 300, 513, 139999, 70000]),
     (dict(B=8, S=131072, H=32), 2048, None),
+    (dict(B=5, S=100000, H=8), 512, [100000, 12345, 0, 600, 99999]),
     (dict(B=6, S=131072), 1, None),
 ])
 def test_decode_select_fused(over, topk, nvs):
