@@ -25,7 +25,7 @@ def run_x(x, m, k, nv=None):
 
 
 @pytest.mark.parametrize("B,S,H,m,k", [(3, 5000, 64, 2048, 512), (2, 3001, 64, 256, 64), (2, 700, 16, 128, 128),
-                                       (1, 2048, 128, 2048, 2048)])
+                                       (1, 2048, 128, 2048, 2048), (2, 3001, 100, 256, 64), (2, 9000, 48, 512, 100)])
 def test_bit_exact(B, S, H, m, k):
     print("compact", B, S, H, m, k, flush=True)
     sp = workloads.spec("compact_search", B=B, S=S, H=H, seed=0x5EED0600 + S)
