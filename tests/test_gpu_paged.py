@@ -36,7 +36,7 @@ def paged_keys(codes, scales, extra, seed):
 
 
 @pytest.mark.parametrize("B,S,H,k", [(3, 20037, 64, 512), (2, 40000, 32, 512), (4, 5000, 128, 64),
-                                     (8, 131072, 64, 512), (2, 100, 64, 16)])
+                                     (8, 131072, 64, 512), (2, 100, 64, 16), (3, 30001, 8, 256)])
 def test_paged_indexer_equals_unpaged(B, S, H, k):
     print("paged indexer", B, S, H, k, flush=True)
     sp = workloads.spec("batched_decode", B=B, S=S, H=H, seed=0x5EED0D00 + S + H)
@@ -59,7 +59,8 @@ def test_paged_indexer_equals_unpaged(B, S, H, k):
             assert_topk_band(gi.cpu().numpy(), o, k, nv, "paged top-k")
 
 
-@pytest.mark.parametrize("B,Hq,S,k", [(2, 128, 3000, 512), (3, 64, 900, 100), (1, 32, 70, 70)])
+@pytest.mark.parametrize("B,Hq,S,k", [(2, 128, 3000, 512), (3, 64, 900, 100), (1, 32, 70, 70),
+                                      (2, 96, 5000, 2048)])
 def test_paged_attention_equals_unpaged(B, Hq, S, k):
     print("paged attention", B, Hq, S, k, flush=True)
     kv = synth.normal_bf16(0x5EED0D10 + S, 5, (B, S, 576))
