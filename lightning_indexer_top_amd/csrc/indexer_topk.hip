@@ -44,6 +44,24 @@ constexpr int PS_KMAX = 512;   // largest k the fused kernel takes (CAP - NK - k
 // max(x, 0) on the bit pattern (exact, -0 -> +0).
 __device__ __forceinline__ float relu_bits_f(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// part + w * x, where w is the value that lane i of this lane's row of 16 holds in
+// wb (DPP row_newbcast on the fma's first source): one VGPR carries 16 weights per
+// lane row.  Every lane of the wave must be active (a disabled source lane would
+// leave part unchanged); i is a constant once the callers' loops are unrolled.
+__device__ __forceinline__ float fmac_bcast(float part, float wb, float x, int i) {
+#define LI_FMAC_B(n)                                                                              \
+  case n:                                                                                         \
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #n " row_mask:0xf bank_mask:0xf"               \
+        : "+v"(part) : "v"(wb), "v"(x));                                                          \
+    break;
+  switch (i) {
+    LI_FMAC_B(0) LI_FMAC_B(1) LI_FMAC_B(2) LI_FMAC_B(3) LI_FMAC_B(4) LI_FMAC_B(5) LI_FMAC_B(6) LI_FMAC_B(7)
+    LI_FMAC_B(8) LI_FMAC_B(9) LI_FMAC_B(10) LI_FMAC_B(11) LI_FMAC_B(12) LI_FMAC_B(13) LI_FMAC_B(14) LI_FMAC_B(15)
+  }
+#undef LI_FMAC_B
+  return part;
+}
+
 // hist[d] += 1 for every lane with valid set (one wave, LDS atomics); when all
 // such lanes share one digit a single atomic adds them.
 __device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t d, bool valid) {
@@ -187,9 +205,15 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
   __syncthreads();
   const int kend = s_kend;
 
-  // query block (A operand) and head weights in accumulator row order
+  // query block (A operand) and head weights in accumulator row order: register i
+  // of a 32 x 32 accumulator holds head 32 ht + (i & 3) + 8 (i >> 2) + 4 hf.  Up to
+  // 64 heads every lane keeps its 16 weights per head tile (wv); at 128 heads they
+  // would not fit beside the query block, so lane n of each row of 16 keeps the
+  // weight of register n for its lane half (wb) and the reduction broadcasts it.
+  constexpr bool WB = HT > 2;
+  constexpr int NW = WB ? 1 : 16;
   bf16x8 a[HT][8];
-  float wv[HT][16];
+  float wv[HT][NW];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const int h = ht * 32 + col;
@@ -200,8 +224,9 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
       a[ht][kk] = __builtin_bit_cast(bf16x8, v);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int hh = ht * 32 + (i & 3) + 8 * (i >> 2) + 4 * hf;
+    for (int i = 0; i < NW; ++i) {
+      const int n = WB ? (lane & 15) : i;
+      const int hh = ht * 32 + (n & 3) + 8 * (n >> 2) + 4 * hf;
       wv[ht][i] = (hh < H && active) ? w[r * H + hh] : 0.0f;
     }
   }
@@ -409,9 +434,13 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
       scB = nscB;
     }
   } else {
-    // 128 heads: a second accumulator set does not fit the register file, so each
-    // group of 32 heads is scored, then reduced
-    f32x16 acc[1][1];
+    // 128 heads: a second accumulator set of all four head tiles does not fit the
+    // register file, so each sub-tile is scored one group of 32 heads at a time, the
+    // MFMAs of group g + 1 (slot (g + 1) & 1) interleaved with the reduction of group
+    // g (slot g & 1), weights broadcast from wb; the chain order of the reduction
+    // (group by group, register by register) is unchanged.
+    static_assert(HT == 4, "the 128-head path");
+    f32x16 acc[2][1];
     for (int it = 0; it < ntiles; ++it) {
       const int kt = it * PS_NK;
       const bool more = it + 1 < ntiles;
@@ -420,17 +449,26 @@ void prefill_select_kernel(const uint16_t* __restrict__ q, const float* __restri
         load_scales(kt + PS_NK, nscA, nscB);
       }
       const uint8_t* buf = tiles[it & 1];
-      if (kt < nvis) {  // uniform per wave
+      if (kt < nvis) {  // uniform per wave: every lane runs the reductions
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           float part = 0.0f;
           PS_BOP(s, buf);
+          PS_MMA(0, 0, 0);
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            PS_MMA(0, 0, ht);
+          for (int g = 1; g < HT; ++g) {
+            const int ns = g & 1, os = ns ^ 1;
+            acc[ns][0] = f32x16{};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) part = fmaf(wv[ht][i], relu_bits_f(acc[0][0][i]), part);
+            for (int kk = 0; kk < 8; ++kk) {
+              acc[ns][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[g][kk], bop[kk], acc[ns][0], 0, 0, 0);
+#pragma unroll
+              for (int j = 0; j < 2; ++j) part = fmac_bcast(part, wv[g - 1][0], relu_bits_f(acc[os][0][2 * kk + j]), 2 * kk + j);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) part = fmac_bcast(part, wv[HT - 1][0], relu_bits_f(acc[(HT - 1) & 1][0][i]), i);
           emit1(kt, s, part);
         }
         make_room();
