@@ -444,12 +444,17 @@ def bench_prefill_fp8(torch, li, workloads, steps, warmup, cpu=True):
     return bench_prefill(torch, li, workloads, steps, warmup, cpu=cpu, key="fp8")
 
 
-def bench_prefill(torch, li, workloads, steps, warmup, cpu=True, key="bf16"):
+def bench_prefill_h128(torch, li, workloads, steps, warmup, cpu=True):
+    return bench_prefill(torch, li, workloads, steps, warmup, cpu=cpu, heads=128)
+
+
+def bench_prefill(torch, li, workloads, steps, warmup, cpu=True, key="bf16", heads=None):
     """The prefill chunk; key="fp8": the same chunk with its keys stored as E4M3
-    codes + one fp32 scale per key (the tiled kernel widens them in LDS)."""
-    sp = workloads.spec("prefill_chunk", key=key)
+    codes + one fp32 scale per key (the tiled kernel widens them in LDS); heads:
+    another indexer head count on the same chunk."""
+    sp = workloads.spec("prefill_chunk", key=key, **({"H": heads} if heads else {}))
     B, T, S, H, k = sp["B"], sp["T"], sp["S"], sp["H"], sp["topk"]
-    tag = "prefill" if key == "bf16" else "prefill_fp8"
+    tag = ("prefill" if key == "bf16" else "prefill_fp8") + (f"_h{H}" if heads else "")
     log(f"[{tag}] generating inputs T={T} S={S} H={H} keys {key}")
     x = workloads.indexer_inputs(sp)
     q, w, kk, nv = to_dev(torch, x["q"], "bf16"), to_dev(torch, x["w"]), to_dev(torch, x["k"], key), \
@@ -490,7 +495,7 @@ def bench_prefill(torch, li, workloads, steps, warmup, cpu=True, key="bf16"):
     del scores
     log(f"[{tag}] fused {ms:.2f} ms -> {tf:.1f} TFLOP/s; scores only {ms2:.2f} ms -> {tf2:.1f} TFLOP/s")
     kdesc = "bf16" if key == "bf16" else "fp8 e4m3 + fp32 scale"
-    res = {"workload": f"prefill_chunk T=4096 S=131072 H=64 bf16 queries, {kdesc} keys, causal top-512",
+    res = {"workload": f"prefill_chunk T={T} S={S} H={H} bf16 queries, {kdesc} keys, causal top-{k}",
            "ms": round(ms, 4),
            "value": round(tf, 2), "unit": "TFLOP/s", "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
            "flop": flop, "workspace_bytes": nb, "unfused_score_ms": round(ms2, 4),
@@ -972,6 +977,8 @@ SECONDARY = {"tiny_decode": bench_tiny, "prefill_chunk": bench_prefill, "prefill
              "compact_search": bench_compact,
              "select_attend": bench_select_attend, "pooled_decode": bench_pooled, "paged_decode": bench_paged,
              "pq_search": bench_pq, "layer_stream": bench_stream}
+# run only when named with --workload (not part of the default line)
+OPTIONAL = {"prefill_chunk_h128": bench_prefill_h128}
 
 
 def main():
@@ -984,7 +991,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run four plain 1 GiB device copies (calibrates the HBM byte counters)")
     ap.add_argument("--probes", action="store_true", help="only run the roofline probes")
-    ap.add_argument("--workload", choices=sorted(SECONDARY), default=None,
+    ap.add_argument("--workload", choices=sorted(SECONDARY) + sorted(OPTIONAL), default=None,
                     help="only time this secondary workload and print its result")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -1014,7 +1021,8 @@ def main():
         print(json.dumps(measure_probes(torch)), flush=True)
         return
     if args.workload:
-        res = SECONDARY[args.workload](torch, li, workloads, args.steps, args.warmup, cpu=not args.no_cpu)
+        res = {**SECONDARY, **OPTIONAL}[args.workload](torch, li, workloads, args.steps, args.warmup,
+                                                       cpu=not args.no_cpu)
         print(json.dumps(dict(res, steps=args.steps, warmup=args.warmup)), flush=True)
         return
     dec = bench_decode(torch, li, workloads, args.steps, args.warmup)
